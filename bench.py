@@ -1,0 +1,258 @@
+"""Benchmark of the fused tile-pipelined GEMM kernels on one MI355X.
+
+One step = one fused AllGather -> GEMM call at its single-GPU share
+(R = 8 shards of 1024 x 8192 bf16, B 8192 x 3584, 128-row chunks arriving in a
+seeded order with 0-20 us release delays, bf16 output): the workload the
+headline metric is quoted on.  Prints ONE JSON line.  The same line carries
+the other single-GPU workloads (GEMM+ReduceScatter, MoE dispatch+grouped
+GEMM, the skinny AllGather+GEMM) under "configs", each with its unfused
+baseline, plus the roofline of the fused kernel and the CPU-oracle baseline.
+
+Inputs are seeded synthetic tensors (workloads/), resident in HBM before the
+timed region.  Several copies of each workload are rotated so consecutive
+steps do not find their operands in the 256 MiB last-level (MALL) cache.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6        # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
+PEAK_HBM_GBS = 8000.0            # HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="", help="comma list of workloads to run (ag,rs,moe,skinny_ag)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the unfused and library yardsticks")
+    ap.add_argument("--copies", type=int, default=0, help="rotated input copies (0 = auto)")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup, stream):
+    """Run fn warmup+steps times; return (wall ms/step, mean event ms/launch)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    kern = sum(a.elapsed_time(b) for a, b in ev) / steps
+    return wall, kern
+
+
+def bench_ag(name, args, stream, extra=True):
+    import torch
+    import workloads as wl
+    from tile_pipelined_gemm_amd import mk
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = wl.CONFIGS[name]["make"](args.seed)
+    foot = (sum(s.nbytes for s in w.shards) * 2 + w.B.nbytes + w.M * w.N * 2)
+    copies = args.copies or max(1, min(4, int(3 * 256e6 // foot) + 1))
+    probs = [AgProblem(w) for _ in range(copies)]
+    flops = probs[0].flops
+    # algorithmic bytes: gather (read+write A), GEMM reads A and B once, writes C once
+    abytes = 2 * w.M * w.K * 2 + w.M * w.K * 2 + w.K * w.N * 2 + w.M * w.N * (2 if w.out_dtype == "bf16" else 4)
+
+    def fused(i):
+        probs[i % copies].run(stream=stream, check=False)
+
+    wall, kern = timed(fused, args.steps, args.warmup, stream)
+    for p in probs:
+        assert mk.mk_poll_status(p.ws, stream) == mk.MK_OK
+    r = dict(workload=wl.CONFIGS[name]["desc"], M=w.M, K=w.K, N=w.N, R=w.R, chunk_rows=w.unit_rows,
+             copies=copies, ms=wall, kernel_ms=kern, tflops=flops / kern / 1e9,
+             gbs=abytes / kern / 1e6, flops=flops, alg_bytes=abytes)
+    if extra:
+        lau = mk.make_launch(mode=1)
+
+        def unfused(i):
+            probs[i % copies].run(launch=lau, stream=stream, check=False)
+
+        uw, uk = timed(unfused, max(3, args.steps // 2), 2, stream)
+        r["unfused_ms"] = uk
+        r["speedup_vs_unfused"] = uk / kern
+        # hipBLASLt yardstick on the already gathered A (not the target)
+        Ag = [p.Ag for p in probs]
+        Bs = [p.B for p in probs]
+
+        def lib(i):
+            torch.matmul(Ag[i % copies], Bs[i % copies])
+
+        _, lk = timed(lib, max(3, args.steps // 2), 2, stream)
+        r["torch_matmul_ms"] = lk
+        r["torch_matmul_tflops"] = flops / lk / 1e9
+    return r
+
+
+def bench_rs(args, stream, extra=True):
+    import workloads as wl
+    from tile_pipelined_gemm_amd import mk
+    from tile_pipelined_gemm_amd.harness import RsProblem
+    w = wl.CONFIGS["rs"]["make"](args.seed)
+    copies = args.copies or 1      # 2.3 GB of operands per copy: far beyond the MALL already
+    probs = [RsProblem(w) for _ in range(copies)]
+    del w.partials[:]
+    flops = probs[0].flops
+    M, K, N, R = probs[0].w.M, probs[0].w.K, probs[0].w.N, probs[0].w.R
+    abytes = M * K * 2 + K * N * 2 + (R - 1) * M * N * 4 + M * N * 4
+
+    def fused(i):
+        probs[i % copies].run(stream=stream, check=False)
+
+    wall, kern = timed(fused, max(3, args.steps // 2), 2, stream)
+    for p in probs:
+        assert mk.mk_poll_status(p.ws, stream) == mk.MK_OK
+    r = dict(workload=wl.CONFIGS["rs"]["desc"], M=M, K=K, N=N, R=R, ms=wall, kernel_ms=kern,
+             tflops=flops / kern / 1e9, gbs=abytes / kern / 1e6, flops=flops, alg_bytes=abytes,
+             hbm_frac=abytes / kern / 1e6 / PEAK_HBM_GBS)
+    if extra:
+        for nr in (16, 32):
+            lau = mk.make_launch(n_reduce=nr)
+            _, k2 = timed(lambda i: probs[i % copies].run(launch=lau, stream=stream, check=False), 3, 1, stream)
+            r[f"roles_n_reduce{nr}_ms"] = k2
+        lau = mk.make_launch(mode=1)
+        _, uk = timed(lambda i: probs[i % copies].run(launch=lau, stream=stream, check=False), 3, 1, stream)
+        r["unfused_ms"] = uk
+        r["speedup_vs_unfused"] = uk / kern
+    return r
+
+
+def bench_moe(args, stream, extra=True):
+    import workloads as wl
+    from tile_pipelined_gemm_amd import mk
+    from tile_pipelined_gemm_amd.harness import MoeProblem
+    w = wl.CONFIGS["moe"]["make"](args.seed)
+    probs = [MoeProblem(w) for _ in range(args.copies or 2)]
+    copies = len(probs)
+    probs[0].run(stream=stream)
+    stream.synchronize()
+    rows = probs[0].local_rows()
+    flops = 2.0 * rows * w.H * w.F
+    abytes = (w.L * w.H * w.F * 2 + 2 * rows * w.H * 2 + rows * w.F * 2 + w.T * w.H * 2 + w.T * w.E * 4)
+
+    def fused(i):
+        probs[i % copies].run(stream=stream, check=False)
+
+    wall, kern = timed(fused, max(3, args.steps // 2), 2, stream)
+    for p in probs:
+        assert mk.mk_poll_status(p.ws, stream) == mk.MK_OK
+    r = dict(workload=wl.CONFIGS["moe"]["desc"], T=w.T, H=w.H, E=w.E, k=w.k, L=w.L, F=w.F, local_rows=rows,
+             ms=wall, kernel_ms=kern, tflops=flops / kern / 1e9, gbs=abytes / kern / 1e6,
+             flops=flops, alg_bytes=abytes)
+    if extra:
+        lau = mk.make_launch(mode=1)
+        _, uk = timed(lambda i: probs[i % copies].run(launch=lau, stream=stream, check=False), 3, 1, stream)
+        r["unfused_ms"] = uk
+        r["speedup_vs_unfused"] = uk / kern
+    return r
+
+
+def cpu_baseline(seed):
+    """The oracle (numpy float64) on a bounded row sample of the AG workload."""
+    import numpy as np
+    import oracle.ag_gemm as og
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 0) for i in threadpool_info()), default=0) or os.cpu_count()
+    except Exception:
+        cores = os.cpu_count()
+    w = wl.CONFIGS["ag"]["make"](seed)
+    rows = np.arange(0, w.M, 4)            # every 4th row: 2048 x 8192 x 3584
+    t0 = time.perf_counter()
+    og.ag_gemm_rows(w.shards, w.B, rows)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * w.K * w.N
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"float64 rows of C = gather(A) @ B: {len(rows)} of {w.M} rows (every 4th), "
+                       f"K={w.K}, N={w.N}; {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from tile_pipelined_gemm_amd import mk
+    mk.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    only = set(x for x in args.only.split(",") if x)
+
+    def want(x):
+        return not only or x in only
+
+    extra = not args.no_extra
+    configs = {}
+    primary = None
+    if want("ag"):
+        log("bench: ag")
+        primary = bench_ag("ag", args, stream, extra)
+        configs["ag"] = primary
+    if want("skinny_ag"):
+        log("bench: skinny_ag")
+        configs["skinny_ag"] = bench_ag("skinny_ag", args, stream, extra)
+    if want("rs"):
+        log("bench: rs")
+        configs["rs"] = bench_rs(args, stream, extra)
+    if want("moe"):
+        log("bench: moe")
+        configs["moe"] = bench_moe(args, stream, extra)
+    cpu = None
+    if primary is not None and not args.no_cpu:
+        log("bench: cpu baseline")
+        cpu = cpu_baseline(args.seed)
+    if primary is None:
+        primary = next(iter(configs.values()))
+    value = primary["flops"] / primary["ms"] / 1e9
+    out = {
+        "metric": "fused AG+GEMM / GEMM+RS TFLOP/s at 1 MI355X; % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(primary["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": primary["workload"], "M": primary.get("M"), "K": primary.get("K"),
+                   "N": primary.get("N"), "R": primary.get("R"), "parallelism": "single GPU share"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(primary["flops"] / primary["kernel_ms"] / 1e9, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(primary["flops"] / primary["kernel_ms"] / 1e9 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "configs": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in configs.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * mk.h -- C ABI of libmk: persistent, role-specialised fused GEMM kernels for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the data-parallel hot path of the fused
+ * communication+GEMM kernels described on the mKernel pages:
+ *   [P1] "Conozca mKernel, una biblioteca de núcleo fusionado con múltiples GPU
+ *        y múltiples nodos para comunicación impulsada por GPU" (7minutos.es),
+ *        section "Los cinco núcleos fusionados" and explainer slide
+ *        "04 / 07 — Granos";
+ *   [P3] the Arabic translation (k7ail.com), table "الحبات الخمس المنصهرة".
+ * Per [P1] section "¿Qué hace mKernel?", each operation is ONE persistent
+ * kernel whose workgroups assign themselves roles (compute, copy, reduce) and
+ * the number of workgroups per role can be tuned per shape.
+ *
+ * This library runs one GPU's share of each operation.  The peers' data (A
+ * shards, partial sums, token rows) are resident device buffers; copy-role
+ * workgroups move them under an arrival schedule while compute-role
+ * workgroups run the GEMM tile by tile as their operands land.
+ *
+ * Conventions for every entry point
+ *   - Matrices are dense row-major.  Pointers marked "device" must be device
+ *     memory of the current HIP device, 16-byte aligned; row lengths in
+ *     elements must be multiples of 8 (16 bytes of bf16).
+ *   - Pointer arrays (a_shards, partials, out_owner, W) and mk_arrival /
+ *     mk_launch are HOST memory, read during the call only.
+ *   - The caller owns every buffer.  The library allocates no device memory.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default).
+ *     Argument and schedule errors are returned synchronously, before any
+ *     HIP call, and nothing is launched.  A watchdog expiry inside a kernel
+ *     (a wait that exceeded launch->spin_limit_us) is sticky in the
+ *     workspace and is reported by mk_poll_status() after the stream syncs.
+ *   - One call may be in flight per workspace.  A workspace must be zero
+ *     filled before its first use (mk_workspace_init does that); every
+ *     kernel leaves it ready for the next call.
+ *   - Return value: MK_OK (0) or a negative mk_status; mk_last_error() gives
+ *     a thread-local description.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mk_dtype { MK_BF16 = 0, MK_F32 = 1 } mk_dtype;
+
+typedef enum mk_status {
+  MK_OK = 0,
+  MK_ERR_INVALID = -1,      /* bad pointer, shape, dtype or option */
+  MK_ERR_UNSUPPORTED = -2,  /* valid request outside this build's limits */
+  MK_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+  MK_ERR_HIP = -4,          /* a HIP runtime call failed */
+  MK_ERR_TIMEOUT = -5,      /* a kernel wait exceeded its watchdog */
+  MK_ERR_SCHEDULE = -6      /* arrival schedule is not a permutation / bad delays */
+} mk_status;
+
+/* Limits of this build. */
+#define MK_MAX_RANKS 64     /* R: shards, partial-sum contributors, owners */
+#define MK_MAX_UNITS 256    /* delivery units in one schedule */
+#define MK_MAX_EXPERTS 1024 /* E */
+#define MK_MAX_TOPK 16      /* k */
+#define MK_MAX_LOCAL 64     /* L: local experts */
+
+/*
+ * Arrival schedule (host memory).  Unit c becomes available to copy no
+ * earlier than `delay_ns[c]` nanoseconds after the kernel's first copy
+ * workgroup starts; units are handed to copy workgroups in `order`.
+ *   order     [n_units] permutation of 0..n_units-1 (issue order)
+ *   delay_ns  [n_units] or NULL (= all zero); each <= 1e9
+ *   n_units   number of delivery units (<= MK_MAX_UNITS)
+ *   unit_rows AG: gathered rows per unit; MoE: tokens per source block
+ *   withhold  -1, or one unit id that is never delivered: waits on it expire
+ *             after spin_limit_us and the call reports MK_ERR_TIMEOUT.  Used
+ *             to test failure handling; every kernel still exits.
+ * The schedule decides WHEN operands land, never the result.
+ */
+typedef struct mk_arrival {
+  const int32_t* order;
+  const uint32_t* delay_ns;
+  int32_t n_units;
+  int32_t unit_rows;
+  int32_t withhold;
+} mk_arrival;
+
+/* Launch options.  A zero-filled struct (or NULL) selects per-shape defaults. */
+typedef struct mk_launch {
+  int32_t mode;           /* 0 fused persistent kernel; 1 unfused baseline:
+                             the same steps as separate kernels in stream order */
+  int32_t grid;           /* persistent workgroups; 0 = CUs x occupancy */
+  int32_t n_copy;         /* copy-role workgroups (AG, MoE); 0 = default */
+  int32_t n_reduce;       /* GEMM+RS: reduce-role workgroups; 0 = default;
+                             -1 = each compute workgroup reduces its own tiles */
+  int32_t tile;           /* tile configuration id; 0 = default (see mk_tile_name) */
+  uint32_t spin_limit_us; /* watchdog for every wait; 0 = 2,000,000 us */
+  int32_t* tile_log;      /* device int32 or NULL: per-tile record, see each op */
+  int32_t reserved[4];
+} mk_launch;
+
+/* ---------------------------------------------------------------------------
+ * AllGather -> GEMM  ([P1] "Los cinco núcleos fusionados", row AllGather + GEMM)
+ *
+ * Each of R ranks holds a shard A_r [m_shard x K] (bf16).  The gathered
+ * A = [A_0; A_1; ...; A_{R-1}] (rank order, M = R*m_shard rows) is assembled
+ * in `a_gathered` [M x K] by copy workgroups, unit by unit (unit_rows rows
+ * each) under `arrival`; compute workgroups produce C = A @ B, B [K x N]
+ * bf16, C [M x N] of `c_dtype` (fp32 accumulation, one final rounding to
+ * nearest-even for bf16), starting each output tile as soon as the units
+ * covering its rows have landed.
+ *   arrival NULL = one unit per shard, issued in rank order, no delay.
+ *   tile_log (optional): per tile in queue order, 4 int32 {tile_row,
+ *   tile_col, first unit, last unit}.
+ * ------------------------------------------------------------------------- */
+size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_t N, int32_t unit_rows);
+int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
+               const void* B, int64_t N, void* C, int c_dtype, void* a_gathered,
+               const mk_arrival* arrival, const mk_launch* launch,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * GEMM -> ReduceScatter  ([P1] "Los cinco núcleos fusionados", row
+ * GEMM + ReduceScatter)
+ *
+ * This GPU's contribution is A @ B (A [M x K], B [K x N] bf16, fp32
+ * accumulate).  The other R-1 contributions are resident fp32 partial sums
+ * partials[p] [M x N].  The reduced S = A@B + P_1 + ... + P_{R-1} (summed in
+ * fp32 in exactly that order) is scattered by row block: out_owner[r]
+ * [(M/R) x N] of `out_dtype` receives rows [r*M/R, (r+1)*M/R).  Each output
+ * tile is reduced and written to its owner as soon as its GEMM tile is done.
+ *   M must be divisible by R; M/R must be a multiple of the tile height.
+ *   tile_log (optional): per output tile id (tile_row*tiles_n + tile_col),
+ *   2 int32 {owner, production rank}.
+ * ------------------------------------------------------------------------- */
+size_t mk_gemm_rs_workspace(int64_t M, int64_t K, int64_t N, int R, int out_dtype);
+int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
+               const float* const* partials, int R, void* const* out_owner, int out_dtype,
+               const mk_launch* launch, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * MoE dispatch -> grouped GEMM  ([P1] "Los cinco núcleos fusionados", row
+ * Envío MoE + GEMM)
+ *
+ * Routing: topk_idx[t, :] = the k experts with the largest logits[t, :]
+ * (fp32, finite), descending; equal values (+0 == -0) go to the lower id.
+ * Dispatch: counts[e] = tokens choosing e; offsets = exclusive prefix sum
+ * (E+1 entries); perm[p] = t*k + j for the p-th (token, slot) pair in
+ * (expert, token) ascending order.  n_local_rows[0] = offsets[expert_begin+L]
+ * - offsets[expert_begin].
+ * Landing: row q of Xs is X[token of perm[offsets[expert_begin] + q]]; copy
+ * workgroups write it as the token's source block lands (blocks of
+ * arrival->unit_rows tokens, issued in arrival->order).  Grouped GEMM: for
+ * local expert e, Y rows of e = Xs rows of e @ W[e] (W[e] [H x F] bf16),
+ * each M-tile starting once all of its rows have landed.
+ *   Xs has room for T*min(k, L) rows [x H] bf16, Y for T*min(k, L) rows [x F].
+ *   tile_log (optional): per grouped-GEMM M-tile id, 4 int32 {local expert,
+ *   first row (expert-relative), rows, landed count seen}.
+ * ------------------------------------------------------------------------- */
+size_t mk_moe_dispatch_gemm_workspace(int64_t T, int64_t H, int E, int k, int L, int64_t F);
+int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t T, int64_t H, int E, int k,
+                         const void* const* W, int expert_begin, int L, int64_t F,
+                         int32_t* topk_idx, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         int32_t* n_local_rows, void* Xs, void* Y, int y_dtype,
+                         const mk_arrival* arrival, const mk_launch* launch,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Support
+ * ------------------------------------------------------------------------- */
+/* Zero-fill a workspace with a fill kernel (no memset node), asynchronously. */
+int mk_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+/* Synchronise `stream`; return MK_ERR_TIMEOUT (and clear it) if any kernel of a
+ * previous call on this workspace hit its watchdog, else MK_OK. */
+int mk_poll_status(void* workspace, void* stream);
+const char* mk_status_string(int status);
+const char* mk_last_error(void);
+/* Name of tile configuration `id` (NULL if out of range); id 0 is "auto". */
+const char* mk_tile_name(int id);
+int mk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

@@ -1,0 +1,132 @@
+"""The C-ABI library loads, exports every symbol include/mk.h declares, and
+rejects bad arguments synchronously, before any HIP call (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from tile_pipelined_gemm_amd import mk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # a 16-byte aligned, never dereferenced "device pointer"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mk.load()
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "mk.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    decl = declared_symbols()
+    assert set(decl) == set(mk.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_support_functions(lib):
+    assert lib.mk_version() >= 1
+    assert lib.mk_status_string(mk.MK_ERR_TIMEOUT) == b"watchdog timeout"
+    assert mk.mk_tile_name(0) == "auto" and mk.mk_tile_name(1) == "256x256"
+    assert mk.mk_tile_name(99) is None
+
+
+def _ag(lib, R=2, m=64, K=128, N=64, c_dtype=mk.MK_BF16, arrival=None, ws_bytes=1 << 20, ws=FAKE,
+        shards=None, launch=None):
+    sh = (C.c_void_p * R)(*([FAKE] * R)) if shards is None else shards
+    return lib.mk_ag_gemm(sh, R, m, K, FAKE, N, FAKE, c_dtype, FAKE, arrival, launch, ws, ws_bytes, None)
+
+
+def test_ag_validation(lib):
+    assert _ag(lib, R=0) == mk.MK_ERR_UNSUPPORTED
+    assert _ag(lib, K=100) == mk.MK_ERR_UNSUPPORTED
+    assert _ag(lib, N=12) == mk.MK_ERR_UNSUPPORTED
+    assert _ag(lib, c_dtype=7) == mk.MK_ERR_INVALID
+    assert _ag(lib, shards=(C.c_void_p * 2)(FAKE, None)) == mk.MK_ERR_INVALID
+    assert _ag(lib, shards=(C.c_void_p * 2)(FAKE, FAKE + 2)) == mk.MK_ERR_INVALID   # misaligned
+    assert _ag(lib, ws=None) == mk.MK_ERR_WORKSPACE
+    assert _ag(lib, ws_bytes=16) == mk.MK_ERR_WORKSPACE
+    assert b"workspace" in lib.mk_last_error()
+
+
+@pytest.mark.parametrize("order,delays,n_units,unit_rows,withhold", [
+    ([0, 0, 1, 2], None, 4, 32, -1),          # not a permutation
+    ([0, 1, 2, 4], None, 4, 32, -1),          # id out of range
+    ([0, 1, 2, 3], None, 4, 16, -1),          # does not cover M = 128
+    ([0, 1, 2, 3], [0, 5, 2_000_000_000, 1], 4, 32, -1),   # delay above 1 s
+    ([0, 1, 2, 3], None, 4, 32, 9),           # withheld unit out of range
+])
+def test_ag_schedule_rejected(lib, order, delays, n_units, unit_rows, withhold):
+    arr, keep = mk.make_arrival(order, delays, unit_rows, withhold)
+    arr.n_units = n_units
+    assert _ag(lib, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE
+
+
+def test_ag_too_many_units(lib):
+    arr, keep = mk.make_arrival(list(range(512)), None, 1)
+    assert _ag(lib, R=4, m=128, arrival=C.byref(arr)) == mk.MK_ERR_UNSUPPORTED
+
+
+def test_ag_bad_launch_options(lib):
+    lau = mk.make_launch(mode=3)
+    assert _ag(lib, launch=C.byref(lau)) == mk.MK_ERR_INVALID
+    lau = mk.make_launch(tile=42)
+    rc = _ag(lib, launch=C.byref(lau))
+    assert rc in (mk.MK_ERR_INVALID, mk.MK_ERR_HIP)   # device query may come first without a GPU
+
+
+def test_valid_call_without_gpu_reports_hip_error(lib):
+    # Everything validates; the first HIP call then fails cleanly (no device here).
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _ag(lib) == mk.MK_ERR_HIP
+
+
+def _rs(lib, M=512, K=64, N=64, R=4, out_dtype=mk.MK_F32, ws_bytes=1 << 24, partials=True, lau=None):
+    P = (C.c_void_p * R)(*([FAKE] * R))
+    O = (C.c_void_p * R)(*([FAKE] * R))
+    return lib.mk_gemm_rs(FAKE, FAKE, M, K, N, P if partials else None, R, O, out_dtype, lau, FAKE, ws_bytes, None)
+
+
+def test_rs_validation(lib):
+    assert _rs(lib, M=510) == mk.MK_ERR_INVALID              # M % R
+    assert _rs(lib, K=60) == mk.MK_ERR_UNSUPPORTED
+    assert _rs(lib, R=65) == mk.MK_ERR_UNSUPPORTED
+    assert _rs(lib, out_dtype=5) == mk.MK_ERR_INVALID
+    assert _rs(lib, partials=False) == mk.MK_ERR_INVALID
+    assert _rs(lib, M=4 * 96) == mk.MK_ERR_UNSUPPORTED       # 96 rows per owner: not a tile multiple
+    assert _rs(lib, ws_bytes=64) == mk.MK_ERR_WORKSPACE
+    lau = mk.make_launch(n_reduce=-5)
+    assert _rs(lib, lau=C.byref(lau)) == mk.MK_ERR_INVALID
+
+
+def test_rs_workspace_sizes(lib):
+    f32 = lib.mk_gemm_rs_workspace(8192, 3584, 8192, 8, mk.MK_F32)
+    bf = lib.mk_gemm_rs_workspace(8192, 3584, 8192, 8, mk.MK_BF16)
+    assert bf - f32 == 8192 * 8192 * 4
+
+
+def _moe(lib, T=256, H=128, E=64, k=4, eb=0, L=8, F=128, y=mk.MK_BF16, arrival=None, ws_bytes=1 << 24):
+    W = (C.c_void_p * L)(*([FAKE] * L))
+    return lib.mk_moe_dispatch_gemm(FAKE, FAKE, T, H, E, k, W, eb, L, F, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, y, arrival, None, FAKE, ws_bytes, None)
+
+
+def test_moe_validation(lib):
+    assert _moe(lib, k=65) == mk.MK_ERR_INVALID
+    assert _moe(lib, k=17, E=64) == mk.MK_ERR_INVALID
+    assert _moe(lib, E=2048) == mk.MK_ERR_UNSUPPORTED
+    assert _moe(lib, eb=60, L=8) == mk.MK_ERR_INVALID
+    assert _moe(lib, H=100) == mk.MK_ERR_UNSUPPORTED
+    assert _moe(lib, L=0) == mk.MK_ERR_UNSUPPORTED
+    assert _moe(lib, y=3) == mk.MK_ERR_INVALID
+    assert _moe(lib, ws_bytes=100) == mk.MK_ERR_WORKSPACE
+    arr, keep = mk.make_arrival([0, 1, 1, 3], None, 64)
+    assert _moe(lib, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE

@@ -1,0 +1,131 @@
+"""AllGather -> GEMM on the GPU (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.ag_gemm as og
+from oracle.numerics import out_to_f64
+import workloads as wl
+from tests.tol import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(gpu, w, **kw):
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    prob = AgProblem(w)
+    prob.Ag.fill_(float("nan"))          # any read before a chunk lands would poison the output
+    prob.run(**kw)
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+    return prob
+
+
+def test_tiny_config_matches_oracle(gpu):
+    w = wl.CONFIGS["tiny_ag"]["make"]()
+    prob = _run(gpu, w)
+    C64, _ = og.ag_gemm(w.shards, w.B, "f32", order=w.order, unit_rows=w.unit_rows)
+    assert_close(prob.output().astype(np.float64), C64, "f32", "tiny AG+GEMM")
+    # the gathered buffer holds the shards in rank order
+    from tile_pipelined_gemm_amd.harness import to_numpy
+    assert np.array_equal(to_numpy(prob.Ag), og.gather(w.shards))
+
+
+def test_integer_inputs_bit_exact(gpu):
+    # |partial sums| <= 4K < 2^24: fp32 accumulation is exact, so bits must match.
+    w = wl.make_ag(4, 96, 512, 264, seed=5, dist="int", unit_rows=32, out_dtype="f32")
+    prob = _run(gpu, w)
+    C64, C = og.ag_gemm(w.shards, w.B, "f32")
+    assert np.array_equal(prob.output(), C)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+def test_ragged_shapes_every_tile_config(gpu, tile):
+    # M = 300, K = 200, N = 136: ragged in every dimension, several tiles.
+    w = wl.make_ag(3, 100, 200, 136, seed=11, unit_rows=20, max_delay_ns=3000)
+    prob = _run(gpu, w, launch=gpu.make_launch(tile=tile))
+    C64, _ = og.ag_gemm(w.shards, w.B, "bf16")
+    assert_close(out_to_f64(prob.output(), "bf16"), C64, "bf16", f"ragged tile {tile}")
+
+
+def test_mid_size_many_tiles(gpu):
+    w = wl.make_ag(8, 128, 1024, 768, seed=12, unit_rows=32, max_delay_ns=20000)
+    prob = _run(gpu, w)
+    C64, _ = og.ag_gemm(w.shards, w.B, "bf16")
+    assert_close(out_to_f64(prob.output(), "bf16"), C64, "bf16", "mid AG")
+
+
+def test_output_independent_of_schedule_and_roles(gpu):
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = wl.make_ag(8, 128, 512, 512, seed=13, unit_rows=32, max_delay_ns=20000)
+    prob = AgProblem(w)
+    n = w.M // w.unit_rows
+    runs = [dict(order=np.arange(n)), dict(order=np.arange(n)[::-1].copy()),
+            dict(order=w.order, delay_ns=w.delay_ns),
+            dict(order=w.order, launch=gpu.make_launch(n_copy=1)),
+            dict(order=w.order, launch=gpu.make_launch(n_copy=64, grid=80)),
+            dict(launch=gpu.make_launch(mode=1))]
+    outs = []
+    for kw in runs:
+        prob.Ag.fill_(float("nan"))
+        prob.C.zero_()
+        prob.run(**kw)
+        torch.cuda.synchronize()
+        assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+        outs.append(prob.output())
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(outs[0], o), f"run {i} differs"
+
+
+def test_tile_log_records_chunk_dependencies(gpu):
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = wl.make_ag(4, 256, 256, 512, seed=14, unit_rows=64)
+    prob = AgProblem(w)
+    log = torch.full((4 * 64,), -1, dtype=torch.int32, device="cuda")
+    prob.run(launch=gpu.make_launch(tile=1, tile_log=log))
+    torch.cuda.synchronize()
+    L = log.cpu().numpy().reshape(-1, 4)
+    n_tiles = (w.M // 256) * (w.N // 256)
+    seen = set()
+    for q in range(n_tiles):
+        tm, tn, u0, u1 = L[q]
+        assert (u0, u1) == og.tile_units(tm, 256, w.unit_rows, w.M)
+        seen.add((tm, tn))
+    assert len(seen) == n_tiles
+    assert np.all(L[n_tiles:] == -1)
+
+
+def test_withheld_chunk_times_out_and_kernel_exits(gpu):
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = wl.make_ag(4, 64, 256, 256, seed=15, unit_rows=32)
+    prob = AgProblem(w)
+    prob.run(withhold=int(w.order[3]), launch=gpu.make_launch(spin_limit_us=20000))
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_ERR_TIMEOUT
+    # the workspace is reusable and the status was cleared
+    prob.run()
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+    C64, _ = og.ag_gemm(w.shards, w.B, "bf16")
+    assert_close(out_to_f64(prob.output(), "bf16"), C64, "bf16", "after timeout")
+
+
+def _sampled_rows(w, prob, n_rows, seed, what):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.choice(w.M, n_rows, replace=False), [0, w.M - 1]]))
+    ref = og.ag_gemm_rows(w.shards, w.B, rows)
+    got = out_to_f64(prob.output()[rows], w.out_dtype)
+    assert_close(got, ref, w.out_dtype, what)
+
+
+def test_full_size_ag_config_sampled(gpu):
+    w = wl.CONFIGS["ag"]["make"]()
+    prob = _run(gpu, w)
+    _sampled_rows(w, prob, 96, 0, "AG 8192x8192x3584")
+    assert not np.any(np.isnan(out_to_f64(prob.output(), "bf16")))
+
+
+def test_full_size_skinny_config_sampled(gpu):
+    w = wl.CONFIGS["skinny_ag"]["make"]()
+    prob = _run(gpu, w)
+    _sampled_rows(w, prob, 24, 1, "skinny AG 128x8192x28672")

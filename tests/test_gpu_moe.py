@@ -1,0 +1,110 @@
+"""MoE dispatch -> grouped GEMM on the GPU (through the C ABI) against the CPU
+oracle: routing, counts, offsets and the dispatch permutation bit-exact, the
+grouped GEMM within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe as om
+from oracle.numerics import out_to_f64
+import workloads as wl
+from tests.tol import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(gpu, w, **kw):
+    from tile_pipelined_gemm_amd.harness import MoeProblem
+    prob = MoeProblem(w)
+    prob.Xs.fill_(float("nan"))
+    prob.run(**kw)
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+    return prob
+
+
+def _check_exact(prob, ref):
+    got = prob.outputs()
+    assert np.array_equal(got["topk"], ref["topk"])
+    assert np.array_equal(got["counts"], ref["counts"])
+    assert np.array_equal(got["offsets"], ref["offsets"])
+    assert np.array_equal(got["perm"], ref["perm"])
+    assert got["n_local"] == ref["n_local"]
+    return got
+
+
+@pytest.mark.parametrize("eb,L", [(0, 8), (5, 11)])
+def test_small_matches_oracle(gpu, eb, L):
+    w = wl.make_moe(320, 136, 64, 4, L, 136, seed=31, expert_begin=eb, block_tokens=64)
+    prob = _run(gpu, w)
+    ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, eb, "bf16")
+    got = _check_exact(prob, ref)
+    assert_close(out_to_f64(got["Y"], "bf16"), ref["Y64"], "bf16", "MoE small")
+
+
+def test_ties_and_signed_zero_routing(gpu):
+    rng = np.random.default_rng(32)
+    vals = np.array([-1.0, -0.0, 0.0, 0.5, 1.0], np.float32)
+    logits = vals[rng.integers(0, 5, size=(256, 96))]
+    logits[:16] = 0.0
+    logits[16:32] = -0.0
+    w = wl.make_moe(256, 64, 96, 6, 16, 64, seed=32, logits=logits, block_tokens=32)
+    prob = _run(gpu, w, launch=None)
+    ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 0, "bf16")
+    _check_exact(prob, ref)
+    assert np.all(prob.outputs()["topk"][:32] == np.arange(6))
+
+
+def test_integer_inputs_bit_exact_f32(gpu):
+    w = wl.make_moe(512, 256, 32, 4, 8, 256, seed=33, dist="int", block_tokens=128, out_dtype="f32")
+    prob = _run(gpu, w)
+    ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 0, "f32")
+    got = _check_exact(prob, ref)
+    assert np.array_equal(got["Y"], ref["Y"])
+
+
+def test_schedule_roles_and_baseline_bitwise_identical(gpu):
+    from tile_pipelined_gemm_amd.harness import MoeProblem
+    w = wl.make_moe(1024, 256, 64, 8, 16, 512, seed=34, block_tokens=128)
+    prob = MoeProblem(w)
+    nb = len(w.order)
+    outs = []
+    for kw in [dict(), dict(order=np.arange(nb)[::-1].copy()), dict(delay_ns=np.full(nb, 5000)),
+               dict(launch=gpu.make_launch(n_copy=1)), dict(launch=gpu.make_launch(mode=1)),
+               dict(launch=gpu.make_launch(tile=2))]:
+        prob.Xs.fill_(float("nan"))
+        prob.Y.zero_()
+        prob.run(**kw)
+        torch.cuda.synchronize()
+        assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+        o = prob.outputs()
+        outs.append(np.concatenate([o["perm"].view(np.uint32), o["Y"].ravel().astype(np.uint32)]))
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(outs[0], o), f"variant {i} differs"
+
+
+def test_withheld_block_times_out(gpu):
+    from tile_pipelined_gemm_amd.harness import MoeProblem
+    w = wl.make_moe(512, 64, 32, 4, 8, 64, seed=35, block_tokens=64)
+    prob = MoeProblem(w)
+    prob.run(withhold=int(w.order[0]), launch=gpu.make_launch(spin_limit_us=20000))
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_ERR_TIMEOUT
+    prob.run()
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+
+
+def test_full_size_moe_config_sampled(gpu):
+    w = wl.CONFIGS["moe"]["make"]()
+    prob = _run(gpu, w)
+    topk = om.route_topk(w.logits, w.k)
+    counts, offsets, perm = om.dispatch(topk, w.E)
+    ref = dict(topk=topk, counts=counts, offsets=offsets, perm=perm,
+               n_local=int(offsets[w.L] - offsets[0]))
+    got = _check_exact(prob, ref)
+    rng = np.random.default_rng(4)
+    n = ref["n_local"]
+    rows = np.unique(np.concatenate([rng.choice(n, 128, replace=False), [0, n - 1]]))
+    Y64, _ = om.grouped_gemm(w.X, w.W, offsets, perm, w.k, 0, "bf16", rows=rows)
+    assert_close(out_to_f64(got["Y"][rows], "bf16"), Y64, "bf16", "MoE full")

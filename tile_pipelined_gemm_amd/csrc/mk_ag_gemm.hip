@@ -1,0 +1,305 @@
+// AllGather -> GEMM as one persistent kernel.
+//
+// [P1] "Los cinco núcleos fusionados", row AllGather + GEMM: every rank holds a
+// shard of A; while the shards are gathered, the local GEMM starts on the
+// tiles whose rows have already arrived.  [P1] "¿Qué hace mKernel?": the
+// kernel is persistent and its workgroups pick their roles themselves.
+//
+// Roles (by start-order ticket):
+//   copy    tickets [0, n_copy): take (unit, part) work items in arrival order,
+//           wait for the unit's release time, copy its rows from the owning
+//           shard into the gathered buffer, publish with an agent-scope
+//           release on the unit's arrival counter.  When the copy queue is
+//           empty a copy workgroup becomes a compute workgroup.
+//   compute take output tiles from a queue ordered by when their rows land,
+//           acquire the arrival counters of the units under the tile, run the
+//           MFMA K loop and store the tile.
+// Producers always hold earlier tickets than the consumers that wait on
+// them, so the spin waits cannot deadlock even if the grid is not fully
+// co-resident.  Every wait is bounded by a watchdog.
+#include <string.h>
+
+#include <algorithm>
+
+#include "mk_device.h"
+#include "mk_host.h"
+#include "mk_tiles.h"
+
+using namespace mk;
+
+namespace {
+
+enum { MODE_FUSED = 0, MODE_COPY = 1, MODE_GEMM = 2 };
+
+struct AgParams {
+  const uint16_t* shard[MK_MAX_RANKS];
+  const uint16_t* B;
+  void* C;
+  uint16_t* Ag;
+  WsHeader* hdr;
+  uint32_t* unit_cnt;   // [n_units] parts landed
+  int32_t* tile_log;
+  uint64_t spin_limit;
+  int R, m_shard, M, K, N, c_bf16;
+  int n_units, unit_rows, parts, part_rows;
+  int mode, n_copy, tiles_m, tiles_n, n_tiles, withhold;
+  uint16_t order[MK_MAX_UNITS];
+  uint16_t rb_order[MK_MAX_UNITS];   // tile rows in landing order
+  uint32_t delay_ticks[MK_MAX_UNITS];
+};
+
+constexpr int COPY_UNROLL = 8;
+
+__device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uint32_t* sb) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  uint64_t t0 = 0;
+  if (tid == 0) {
+    const uint64_t now = now_ticks();
+    const uint64_t old = atomicCAS((unsigned long long*)&h->t0, 0ull, (unsigned long long)now);
+    t0 = old ? old : now;
+  }
+  const uint32_t n_work = (uint32_t)p.n_units * p.parts;
+  const int cpr = p.K / 8;                         // 16-byte chunks per row
+  const int64_t n16 = (int64_t)p.part_rows * cpr;
+  for (;;) {
+    const uint32_t w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
+    if (w >= n_work) break;
+    const int j = w / p.parts, part = w % p.parts;
+    const int c = p.order[j];
+    if (c == p.withhold) continue;               // never delivered (failure tests)
+    if (tid == 0) wait_until(t0 + p.delay_ticks[c], p.spin_limit);
+    __syncthreads();
+    const int row0 = c * p.unit_rows + part * p.part_rows;
+    for (int64_t base = 0; base < n16; base += (int64_t)nt * COPY_UNROLL) {
+      u32x4 v[COPY_UNROLL];
+#pragma unroll
+      for (int u = 0; u < COPY_UNROLL; ++u) {
+        const int64_t i = base + (int64_t)u * nt + tid;
+        if (i < n16) {
+          const int row = row0 + (int)(i / cpr), c16 = (int)(i % cpr);
+          const u32x4* src = (const u32x4*)(p.shard[row / p.m_shard] + (int64_t)(row % p.m_shard) * p.K);
+          v[u] = src[c16];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < COPY_UNROLL; ++u) {
+        const int64_t i = base + (int64_t)u * nt + tid;
+        if (i < n16) {
+          const int row = row0 + (int)(i / cpr), c16 = (int)(i % cpr);
+          ((u32x4*)(p.Ag + (int64_t)row * p.K))[c16] = v[u];
+        }
+      }
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      add_release(&p.unit_cnt[c], 1u);
+      add_release(&h->aux[0], 1u);                 // parts landed in total
+    }
+  }
+}
+
+template <class G>
+__device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, u32x4* lds, uint32_t* sb) {
+  const int tid = threadIdx.x;
+  const uint32_t all_parts = (uint32_t)p.n_units * p.parts;
+  bool all_landed = (p.mode == MODE_GEMM);
+  G g;
+  for (;;) {
+    const uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+    if (q >= (uint32_t)p.n_tiles) break;
+    const int tm = p.rb_order[q / p.tiles_n], tn = q % p.tiles_n;
+    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    const int u0 = m0 / p.unit_rows, u1 = (min(p.M, m0 + G::BM) - 1) / p.unit_rows;
+    if (!all_landed) {
+      uint32_t ok = 1, all = 0;
+      if (tid == 0) {
+        for (int u = u0; u <= u1 && ok; ++u) ok = wait_geq(&p.unit_cnt[u], p.parts, h, p.spin_limit);
+        // Once every part has landed (and one acquire has been taken after
+        // that), no later tile of this workgroup needs to wait.
+        if (ok && ld_relaxed(&h->aux[0]) >= all_parts) {
+          fence_acquire();
+          all = 1;
+        }
+      }
+      const uint32_t v = wg_bcast(ok | (all << 1), sb);
+      if (!(v & 1u)) continue;
+      all_landed = (v >> 1) & 1u;
+    }
+    g.bind(p.Ag + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
+    g.run(lds);
+    if (p.c_bf16) {
+      uint16_t* C = (uint16_t*)p.C;
+      g.for_each([&](int r, int c, float v) {
+        const int gr = m0 + r, gc = n0 + c;
+        if (gr < p.M && gc < p.N) C[(int64_t)gr * p.N + gc] = f2bf(v);
+      });
+    } else {
+      float* C = (float*)p.C;
+      g.for_each([&](int r, int c, float v) {
+        const int gr = m0 + r, gc = n0 + c;
+        if (gr < p.M && gc < p.N) C[(int64_t)gr * p.N + gc] = v;
+      });
+    }
+    if (p.tile_log && tid == 0) {
+      int32_t* L = p.tile_log + 4 * (int64_t)q;
+      L[0] = tm; L[1] = tn; L[2] = u0; L[3] = u1;
+    }
+  }
+}
+
+// Last workgroup out restores the workspace for the next call.
+__device__ __forceinline__ void ag_finish(const AgParams& p, WsHeader* h, uint32_t* sb) {
+  __syncthreads();
+  uint32_t last = 0;
+  if (threadIdx.x == 0) {
+    fence_release();
+    last = add_relaxed(&h->done, 1u) == gridDim.x - 1;
+    if (last) fence_acquire();
+  }
+  last = wg_bcast(last, sb);
+  if (!last) return;
+  for (int i = threadIdx.x; i < p.n_units; i += blockDim.x) st_relaxed(&p.unit_cnt[i], 0u);
+  if (threadIdx.x == 0) {
+    st_relaxed(&h->ticket, 0u);
+    st_relaxed(&h->tile_next, 0u);
+    st_relaxed(&h->copy_next, 0u);
+    st_relaxed(&h->abort, 0u);
+    st_relaxed(&h->aux[0], 0u);
+    __hip_atomic_store(&h->t0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_relaxed(&h->done, 0u);
+  }
+}
+
+template <class G>
+__global__ __launch_bounds__(G::NT) void ag_kernel(const AgParams p) {
+  __shared__ u32x4 lds[G::LDS_U4];
+  __shared__ uint32_t sb[2];
+  WsHeader* h = p.hdr;
+  const uint32_t ticket = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->ticket, 1u) : 0u, sb);
+  if (p.mode == MODE_COPY || (p.mode == MODE_FUSED && ticket < (uint32_t)p.n_copy)) ag_copy_role(p, h, sb);
+  if (p.mode != MODE_COPY) ag_compute_role<G>(p, h, lds, sb);
+  ag_finish(p, h, sb);
+}
+
+}  // namespace
+
+extern "C" size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_t N, int32_t unit_rows) {
+  (void)R; (void)m_shard; (void)K; (void)N; (void)unit_rows;
+  return sizeof(WsHeader) + MK_MAX_UNITS * sizeof(uint32_t);
+}
+
+template <class G>
+static int run_ag(AgParams& p, const mk_launch& o, const mkh::Schedule& s, const mkh::DevInfo* d,
+                  hipStream_t st) {
+  p.tiles_m = (p.M + G::BM - 1) / G::BM;
+  p.tiles_n = (p.N + G::BN - 1) / G::BN;
+  p.n_tiles = p.tiles_m * p.tiles_n;
+  if (p.tiles_m > MK_MAX_UNITS) return mkh::fail(MK_ERR_UNSUPPORTED, "M too large: %d tile rows", p.tiles_m);
+  // Tile rows ordered by the issue position of the last unit under them.
+  std::vector<int> rb(p.tiles_m), key(p.tiles_m);
+  for (int t = 0; t < p.tiles_m; ++t) {
+    const int u0 = t * G::BM / p.unit_rows, u1 = (std::min(p.M, (t + 1) * G::BM) - 1) / p.unit_rows;
+    int k = 0;
+    for (int u = u0; u <= u1; ++u) k = std::max(k, s.pos[u]);
+    rb[t] = t;
+    key[t] = k;
+  }
+  std::stable_sort(rb.begin(), rb.end(), [&](int a, int b) { return key[a] < key[b]; });
+  for (int t = 0; t < p.tiles_m; ++t) p.rb_order[t] = (uint16_t)rb[t];
+
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ag_kernel<G>, G::NT, 0);
+  if (e != hipSuccess) return mkh::hip_fail(e, "occupancy query");
+  if (occ < 1) return mkh::fail(MK_ERR_UNSUPPORTED, "kernel does not fit on a CU");
+  const int full = d->n_cu * occ;
+  const int grid = o.grid > 0 ? std::min(o.grid, full) : full;
+  const uint32_t n_work = (uint32_t)p.n_units * p.parts;
+
+  if (o.mode == 1) {   // unfused baseline: copy kernel, then GEMM kernel
+    p.mode = MODE_COPY;
+    p.n_copy = grid;
+    hipLaunchKernelGGL(ag_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "copy kernel launch");
+    p.mode = MODE_GEMM;
+    p.n_copy = 0;
+    hipLaunchKernelGGL(ag_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "gemm kernel launch");
+    return MK_OK;
+  }
+  p.mode = MODE_FUSED;
+  int n_copy = o.n_copy > 0 ? o.n_copy : std::max(1, grid / 4);
+  n_copy = std::min<int>(n_copy, (int)std::min<uint32_t>(n_work, (uint32_t)grid));
+  p.n_copy = n_copy;
+  hipLaunchKernelGGL(ag_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "fused kernel launch");
+  return MK_OK;
+}
+
+extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
+                          const void* B, int64_t N, void* C, int c_dtype, void* a_gathered,
+                          const mk_arrival* arrival, const mk_launch* launch,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  using mkh::fail;
+  if (!a_shards) return fail(MK_ERR_INVALID, "a_shards is NULL");
+  if (R < 1 || R > MK_MAX_RANKS) return fail(MK_ERR_UNSUPPORTED, "R=%d outside [1,%d]", R, MK_MAX_RANKS);
+  if (m_shard < 1 || K < 8 || N < 8) return fail(MK_ERR_INVALID, "empty or too small shape");
+  if (K % 8 || N % 8) return fail(MK_ERR_UNSUPPORTED, "K (%lld) and N (%lld) must be multiples of 8",
+                                  (long long)K, (long long)N);
+  const int64_t M = (int64_t)R * m_shard;
+  if (M > (1 << 30) || K > (1 << 20) || N > (1 << 30) || K * N * 2 >= (1ll << 31))
+    return fail(MK_ERR_UNSUPPORTED, "dimension too large");
+  if (!B || !C || !a_gathered) return fail(MK_ERR_INVALID, "B, C and a_gathered must be non-NULL");
+  if (c_dtype != MK_BF16 && c_dtype != MK_F32) return fail(MK_ERR_INVALID, "c_dtype %d", c_dtype);
+  for (int r = 0; r < R; ++r)
+    if (!a_shards[r] || !mkh::aligned16(a_shards[r])) return fail(MK_ERR_INVALID, "shard %d NULL or misaligned", r);
+  if (!mkh::aligned16(B) || !mkh::aligned16(C) || !mkh::aligned16(a_gathered))
+    return fail(MK_ERR_INVALID, "B, C and a_gathered must be 16-byte aligned");
+  mkh::Schedule s;
+  int rc = mkh::make_schedule(arrival, M, R, &s);
+  if (rc) return rc;
+  if (!workspace) return fail(MK_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < mk_ag_gemm_workspace(R, m_shard, K, N, s.unit_rows))
+    return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes,
+                mk_ag_gemm_workspace(R, m_shard, K, N, s.unit_rows));
+  const mk_launch o = mkh::launch_opts(launch);
+  if (o.mode != 0 && o.mode != 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
+  if (o.grid < 0 || o.n_copy < 0) return fail(MK_ERR_INVALID, "negative grid or n_copy");
+  const mkh::DevInfo* d = mkh::dev_info();
+  if (!d) return MK_ERR_HIP;
+
+  AgParams p;
+  memset(&p, 0, sizeof p);
+  for (int r = 0; r < R; ++r) p.shard[r] = (const uint16_t*)a_shards[r];
+  p.B = (const uint16_t*)B;
+  p.C = C;
+  p.Ag = (uint16_t*)a_gathered;
+  p.hdr = (WsHeader*)workspace;
+  p.unit_cnt = (uint32_t*)((char*)workspace + sizeof(WsHeader));
+  p.tile_log = o.tile_log;
+  p.spin_limit = mkh::spin_ticks(o, d);
+  p.R = R; p.m_shard = (int)m_shard; p.M = (int)M; p.K = (int)K; p.N = (int)N;
+  p.c_bf16 = c_dtype == MK_BF16;
+  p.n_units = s.n_units;
+  p.unit_rows = s.unit_rows;
+  p.withhold = s.withhold;
+  // Split each unit into parts of about 256 KiB so several copy workgroups share it.
+  const int64_t row_bytes = K * 2;
+  int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(s.unit_rows, (256 << 10) / row_bytes));
+  while (s.unit_rows % part_rows) --part_rows;
+  p.part_rows = part_rows;
+  p.parts = s.unit_rows / part_rows;
+  for (int j = 0; j < s.n_units; ++j) {
+    p.order[j] = (uint16_t)s.order[j];
+    p.delay_ticks[j] = (uint32_t)mkh::ns_to_ticks(s.delay_ns[j], d->wall_khz);
+  }
+  const hipStream_t st = (hipStream_t)stream;
+  const int tile = o.tile ? o.tile : mk_default_tile(M, N, K);
+  switch (tile) {
+    case TILE_256x256: return run_ag<TileGemm<256, 256, 2, 2>>(p, o, s, d, st);
+    case TILE_128x128: return run_ag<TileGemm<128, 128, 2, 2>>(p, o, s, d, st);
+    case TILE_256x128: return run_ag<TileGemm<256, 128, 2, 2>>(p, o, s, d, st);
+    case TILE_128x256: return run_ag<TileGemm<128, 256, 2, 2>>(p, o, s, d, st);
+    default: return fail(MK_ERR_INVALID, "tile id %d", tile);
+  }
+}

@@ -1,0 +1,298 @@
+// Device building blocks shared by the persistent fused kernels (gfx950).
+//
+//  * WsHeader / flag helpers: role tickets, work queues and per-unit arrival
+//    counters live in the caller's workspace; producers publish with an
+//    agent-scope release, consumers spin with relaxed loads and then take an
+//    agent-scope acquire fence (gfx950 has one L2 per XCD, so cross-XCD
+//    visibility needs exactly these fences).
+//  * TileGemm: a bf16 MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate) block
+//    tile with a double-buffered, XOR-swizzled LDS stage per operand.  B is
+//    row-major [K x N]; each 8x8 bf16 block of B is transposed in registers on
+//    its way into LDS so that both MFMA operands are read as contiguous
+//    16-byte k-runs (ds_read_b128).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Status codes stored in the workspace (positive; the host negates them).
+enum : uint32_t { ST_OK = 0, ST_TIMEOUT = 5 };
+
+// Fixed header at the start of every workspace (256 bytes).
+struct WsHeader {
+  uint32_t ticket;     // role tickets, handed out in workgroup start order
+  uint32_t tile_next;  // compute tile queue head
+  uint32_t copy_next;  // copy work queue head
+  uint32_t done;       // workgroups that have finished
+  uint32_t status;     // sticky ST_* code, cleared by the host
+  uint32_t abort;      // set on watchdog expiry so every other wait gives up
+  uint32_t red_next;   // reduce queue head
+  uint32_t prod_next;  // produced-tile FIFO tail
+  uint64_t t0;         // wall-clock ticks when the first copy workgroup started
+  uint32_t aux[54];
+};
+static_assert(sizeof(WsHeader) == 256, "header size");
+
+// ---------------------------------------------------------------- atomics
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_relaxed(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_release(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+
+// Constant-rate (100 MHz on MI300-class parts) wall clock shared by all CUs.
+__device__ __forceinline__ uint64_t now_ticks() { return wall_clock64(); }
+
+// Thread-0 helper: spin until *p >= target.  Returns false if the watchdog
+// expired (status and abort are then set) or another wait already aborted.
+__device__ inline bool wait_geq(const uint32_t* p, uint32_t target, WsHeader* h,
+                                uint64_t limit_ticks) {
+  if (ld_relaxed(p) >= target) {
+    fence_acquire();
+    return true;
+  }
+  const uint64_t t_begin = now_ticks();
+  while (ld_relaxed(p) < target) {
+    if (ld_relaxed(&h->abort)) return false;
+    if (now_ticks() - t_begin > limit_ticks) {
+      st_relaxed(&h->status, ST_TIMEOUT);
+      st_relaxed(&h->abort, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  fence_acquire();
+  return true;
+}
+
+// Thread-0 helper: wait until the wall clock reaches `deadline`, but never
+// longer than `limit_ticks` (a corrupt deadline cannot stall the kernel).
+__device__ inline void wait_until(uint64_t deadline, uint64_t limit_ticks) {
+  const uint64_t t_begin = now_ticks();
+  for (uint64_t t = t_begin; t < deadline && t - t_begin < limit_ticks; t = now_ticks())
+    __builtin_amdgcn_s_sleep(8);
+}
+
+// Value of thread 0 broadcast to the workgroup (uses one LDS word).
+__device__ __forceinline__ uint32_t wg_bcast(uint32_t v, uint32_t* slot) {
+  if (threadIdx.x == 0) *slot = v;
+  __syncthreads();
+  uint32_t r = *slot;
+  __syncthreads();
+  return r;
+}
+
+// fp32 -> bf16 bits, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f2bf(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// --------------------------------------------------------------- LDS layout
+// An operand stage holds ROWS rows of 64 bf16 = 8 chunks of 16 bytes.  Chunk c
+// of row n sits at 16-byte unit 9*n + n/8 + c: the one-chunk pad per row makes
+// eight consecutive rows read at the same chunk hit distinct bank groups
+// (MFMA fragment reads), and the extra unit every 8 rows does the same for
+// rows 8 apart (the transposed B writes).  Every offset is affine in the loop
+// indices, so the compiler folds them into instruction immediates.
+__host__ __device__ constexpr uint32_t lds_units(uint32_t rows) { return rows * 9 + rows / 8; }
+__device__ __forceinline__ uint32_t lofs(uint32_t n, uint32_t c) { return n * 9 + (n >> 3) + c; }
+
+// Raw buffer resource over [p, p + bytes); loads at or past `bytes` return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+constexpr uint32_t OOB = 0x80000000u;   // a voffset that is always past the end
+
+// ------------------------------------------------------------ block tile GEMM
+// BM x BN output tile per workgroup, WM x WN waves, each wave owning a
+// (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA blocks; K advances 64 at a
+// time.  Rows past `mrows`, columns past `ncols` and k past K read as zero,
+// so ragged edges need no special path (K and N are multiples of 8).
+template <int BM_, int BN_, int WM_, int WN_>
+struct TileGemm {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 64;
+  static constexpr int NT = 64 * WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int A_CH = BM * 8;        // 16-byte chunks per A stage
+  static constexpr int A_PT = (A_CH + NT - 1) / NT;
+  static constexpr int B_NB = BN / 8;        // 8-column groups
+  static constexpr int B_BL = 8 * B_NB;      // 8x8 blocks per B stage
+  static constexpr int B_PT = (B_BL + NT - 1) / NT;
+  static constexpr int SA = lds_units(BM), SB = lds_units(BN);   // 16-byte units per stage
+  static constexpr int LDS_U4 = 2 * (SA + SB);
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(NT % 64 == 0 && NT % B_NB == 0, "thread/operand mapping");
+
+  u32x4 ra[A_PT];
+  u32x4 rb[B_PT][8];
+  f32x16 acc[FM][FN];
+  __amdgpu_buffer_rsrc_t rsA, rsB;
+  uint32_t voA, voB, ldaB, ldbB;   // per-thread byte offsets; row pitches in bytes
+  int K, ncols;
+
+  __device__ __forceinline__ void zero_acc() {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  }
+
+  // Bind the operands of one output tile: A at its first row (mrows valid
+  // rows), B at its first column (ncols valid columns), B_end = one past the
+  // last element of B.
+  __device__ __forceinline__ void bind(const uint16_t* A, int64_t lda, int mrows,
+                                       const uint16_t* B, int64_t ldb, int ncols_, const uint16_t* B_end,
+                                       int K_) {
+    const int tid = threadIdx.x;
+    K = K_;
+    ncols = ncols_;
+    ldaB = (uint32_t)(lda * 2);
+    ldbB = (uint32_t)(ldb * 2);
+    const int rows = mrows < BM ? mrows : BM;
+    rsA = make_rsrc(A, (uint32_t)(rows > 0 ? rows : 0) * ldaB);
+    rsB = make_rsrc(B, (uint32_t)((B_end - B) * 2));
+    voA = (uint32_t)(tid >> 3) * ldaB + (uint32_t)(tid & 7) * 16u;
+    const int kb = tid / B_NB, nb = tid % B_NB;
+    voB = (nb * 8 < ncols) ? (uint32_t)(kb * 8) * ldbB + (uint32_t)nb * 16u : OOB;
+  }
+
+  // Global -> registers for the K-step starting at k0.
+  __device__ __forceinline__ void load(int k0) {
+    const int tid = threadIdx.x;
+    const uint32_t va = (k0 + (tid & 7) * 8 < K) ? voA : OOB;
+#pragma unroll
+    for (int i = 0; i < A_PT; ++i)
+      if (A_CH % NT == 0 || tid + i * NT < A_CH)
+        ra[i] = bload(rsA, va, (uint32_t)(i * (NT / 8)) * ldaB + (uint32_t)k0 * 2u);
+#pragma unroll
+    for (int i = 0; i < B_PT; ++i)
+      if (B_BL % NT == 0 || tid + i * NT < B_BL) {
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr)
+          rb[i][rr] = bload(rsB, voB, (uint32_t)(k0 + i * (NT / B_NB) * 8 + rr) * ldbB);
+      }
+  }
+
+  // Registers -> LDS stage; B blocks are transposed to [n][k].
+  __device__ __forceinline__ void store(u32x4* __restrict__ lds, int stage) {
+    const int tid = threadIdx.x;
+    u32x4* sa = lds + stage * (SA + SB);
+    u32x4* sb = sa + SA;
+    const uint32_t ra0 = lofs(tid >> 3, tid & 7);
+#pragma unroll
+    for (int i = 0; i < A_PT; ++i)
+      if (A_CH % NT == 0 || tid + i * NT < A_CH) sa[ra0 + i * lds_units(NT / 8)] = ra[i];
+    const uint32_t kb0 = tid / B_NB, nb = tid % B_NB;
+#pragma unroll
+    for (int i = 0; i < B_PT; ++i)
+      if (B_BL % NT == 0 || tid + i * NT < B_BL) {
+        const uint32_t base = nb * 73 + kb0 + i * (NT / B_NB);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          u32x4 col;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t lo = rb[i][2 * m][j >> 1], hi = rb[i][2 * m + 1][j >> 1];
+            col[m] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+          }
+          sb[base + j * 9] = col;
+        }
+      }
+  }
+
+  // Operand fragments of k-substep ks (16 deep) from one LDS stage.
+  __device__ __forceinline__ void frags(const u32x4* __restrict__ sa, const u32x4* __restrict__ sb,
+                                        int ks, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w % WM, wn = w / WM;
+    const uint32_t ba = lofs(wm * TM + (lane & 31), lane >> 5) + ks * 2;
+    const uint32_t bb = lofs(wn * TN + (lane & 31), lane >> 5) + ks * 2;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = __builtin_bit_cast(bf16x8, sa[ba + i * lds_units(32)]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, sb[bb + j * lds_units(32)]);
+  }
+
+  // 64-deep MFMA update from one LDS stage; the fragments of substep ks+1 are
+  // read while the MFMAs of substep ks run.
+  __device__ __forceinline__ void mma(const u32x4* __restrict__ lds, int stage) {
+    const u32x4* sa = lds + stage * (SA + SB);
+    const u32x4* sb = sa + SA;
+    bf16x8 af[2][FM], bfr[2][FN];
+    frags(sa, sb, 0, af[0], bfr[0]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int cur = ks & 1;
+      if (ks < 3) frags(sa, sb, ks + 1, af[cur ^ 1], bfr[cur ^ 1]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Full K loop for the bound tile.  Ends with a barrier so LDS may be reused.
+  __device__ __forceinline__ void run(u32x4* __restrict__ lds) {
+    zero_acc();
+    const int nk = (K + BK - 1) / BK;
+    load(0);
+    store(lds, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool more = kt + 1 < nk;
+      if (more) load((kt + 1) * BK);
+      mma(lds, kt & 1);
+      if (more) store(lds, (kt + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  // Visit every accumulator element: f(row_in_tile, col_in_tile, value).
+  // MFMA 32x32 output layout: lane l, register r holds
+  //   row = 8*(r/4) + 4*(l/32) + r%4,  col = l%32  (within its 32x32 block).
+  template <class Fn>
+  __device__ __forceinline__ void for_each(Fn&& f) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w % WM, wn = w / WM;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = wn * TN + j * 32 + (lane & 31);
+          f(row, col, acc[i][j][r]);
+        }
+  }
+};
+
+}  // namespace mk

@@ -1,0 +1,316 @@
+// GEMM -> ReduceScatter as one persistent kernel.
+//
+// [P1] "Los cinco núcleos fusionados", row GEMM + ReduceScatter: C = A @ B is
+// reduced across ranks and scattered, each output tile being reduced and sent
+// to the rank that owns it as soon as it is produced.  On one GPU the other
+// ranks' contributions are resident fp32 partial sums, and the owners are the
+// R row blocks of the output.
+//
+// Roles:
+//   compute  tickets [0, n_compute): GEMM tiles from a queue.  With reduce
+//            workgroups present, a finished fp32 tile is staged, published
+//            (release) and its id appended to a produced-tile FIFO; a compute
+//            workgroup whose queue is empty turns into a reduce workgroup.
+//            Without them (n_reduce <= 0) the compute workgroup stages the
+//            tile and reduces it itself right away.
+//   reduce   tickets [n_compute, grid): pop produced tiles in production order,
+//            acquire, sum local + P_1 + ... + P_{R-1} in that fixed fp32 order
+//            (so every role split and schedule gives identical bits) and
+//            store the result in the owner's block.
+#include <string.h>
+
+#include <algorithm>
+
+#include "mk_device.h"
+#include "mk_host.h"
+#include "mk_tiles.h"
+
+using namespace mk;
+
+namespace {
+
+enum { MODE_EPI = 0, MODE_ROLES = 1, MODE_GEMM = 2, MODE_REDUCE = 3 };
+
+struct RsParams {
+  const uint16_t* A;
+  const uint16_t* B;
+  const float* P[MK_MAX_RANKS];   // R-1 partial sums
+  void* out[MK_MAX_RANKS];        // R owner blocks
+  float* stage;                   // fp32 staging [M x N], or NULL to stage in out (fp32)
+  WsHeader* hdr;
+  uint32_t* fifo;                 // [n_tiles] produced tile id + 1
+  int32_t* tile_log;
+  uint64_t spin_limit;
+  int M, K, N, R, out_bf16, mb;   // mb = rows per owner
+  int mode, n_compute, tiles_m, tiles_n, n_tiles;
+};
+
+__device__ __forceinline__ float* stage_ptr(const RsParams& p, int gr, int gc) {
+  if (p.stage) return p.stage + (int64_t)gr * p.N + gc;
+  const int o = gr / p.mb;
+  return (float*)p.out[o] + (int64_t)(gr - o * p.mb) * p.N + gc;
+}
+
+// Reduce one staged tile: out = stage + P_1 + ... + P_{R-1}, 4 columns per access.
+template <int BM, int BN>
+__device__ __forceinline__ void reduce_tile(const RsParams& p, int t) {
+  const int tm = t / p.tiles_n, tn = t % p.tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  constexpr int V = BN / 4;                  // float4 per tile row
+  constexpr int UNROLL = 4;
+  const int nt = blockDim.x;
+  for (int base = 0; base < BM * V; base += nt * UNROLL) {
+    f32x4 v[UNROLL];
+    int gr[UNROLL], gc[UNROLL];
+    bool ok[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int idx = base + u * nt + threadIdx.x;
+      gr[u] = m0 + idx / V;
+      gc[u] = n0 + (idx % V) * 4;
+      ok[u] = idx < BM * V && gr[u] < p.M && gc[u] < p.N;
+      if (ok[u]) v[u] = *(const f32x4*)stage_ptr(p, gr[u], gc[u]);
+    }
+    for (int q = 0; q < p.R - 1; ++q) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+        if (ok[u]) {
+          const f32x4 w = *(const f32x4*)(p.P[q] + (int64_t)gr[u] * p.N + gc[u]);
+          v[u] += w;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+      if (ok[u]) {
+        const int o = gr[u] / p.mb;
+        const int64_t i = (int64_t)(gr[u] - o * p.mb) * p.N + gc[u];
+        if (p.out_bf16) {
+          u32x2 b;
+          b[0] = (uint32_t)f2bf(v[u][0]) | ((uint32_t)f2bf(v[u][1]) << 16);
+          b[1] = (uint32_t)f2bf(v[u][2]) | ((uint32_t)f2bf(v[u][3]) << 16);
+          *(u32x2*)((uint16_t*)p.out[o] + i) = b;
+        } else {
+          *(f32x4*)((float*)p.out[o] + i) = v[u];
+        }
+      }
+  }
+}
+
+template <class G>
+__device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, u32x4* lds, uint32_t* sb) {
+  const int tid = threadIdx.x;
+  G g;
+  for (;;) {
+    const uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+    if (q >= (uint32_t)p.n_tiles) break;
+    const int t = (int)q;
+    const int tm = t / p.tiles_n, tn = t % p.tiles_n;
+    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    g.bind(p.A + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
+    g.run(lds);
+    // Stage the fp32 tile (in the owner block for fp32 output, else in the
+    // workspace staging area).
+    float* __restrict__ S = p.stage ? p.stage + (int64_t)m0 * p.N
+                                    : (float*)p.out[m0 / p.mb] + (int64_t)(m0 % p.mb) * p.N;
+    g.for_each([&](int r, int c, float v) __attribute__((always_inline)) {
+      const int gr = m0 + r, gc = n0 + c;
+      if (gr < p.M && gc < p.N) S[(int64_t)r * p.N + gc] = v;
+    });
+    if (p.mode == MODE_EPI) {
+      // This workgroup reduces its own tile right away (its staged writes are
+      // visible to its own waves after the barrier).
+      __syncthreads();
+      reduce_tile<G::BM, G::BN>(p, t);
+      __syncthreads();
+      if (p.tile_log && tid == 0) {
+        p.tile_log[2 * t] = m0 / p.mb;
+        p.tile_log[2 * t + 1] = t;
+      }
+    } else if (p.mode == MODE_ROLES) {
+      __threadfence();
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t slot = add_relaxed(&h->prod_next, 1u);
+        st_release(&p.fifo[slot], (uint32_t)t + 1u);
+        if (p.tile_log) {
+          p.tile_log[2 * t] = m0 / p.mb;
+          p.tile_log[2 * t + 1] = (int32_t)slot;
+        }
+      }
+    }
+  }
+}
+
+template <class G>
+__device__ __forceinline__ void rs_reduce_role(const RsParams& p, WsHeader* h, uint32_t* sb) {
+  const int tid = threadIdx.x;
+  for (;;) {
+    const uint32_t i = wg_bcast(tid == 0 ? add_relaxed(&h->red_next, 1u) : 0u, sb);
+    if (i >= (uint32_t)p.n_tiles) break;
+    uint32_t t = i;
+    if (p.mode == MODE_ROLES) {
+      uint32_t v = 0;
+      if (tid == 0) v = wait_geq(&p.fifo[i], 1u, h, p.spin_limit) ? ld_relaxed(&p.fifo[i]) : 0u;
+      v = wg_bcast(v, sb);
+      if (v == 0) continue;                      // watchdog expired
+      t = v - 1u;
+    }
+    reduce_tile<G::BM, G::BN>(p, (int)t);
+    if (p.mode == MODE_REDUCE && p.tile_log && tid == 0) {
+      const int tm = (int)t / p.tiles_n;
+      p.tile_log[2 * t] = tm * G::BM / p.mb;
+      p.tile_log[2 * t + 1] = (int32_t)t;
+    }
+  }
+}
+
+__device__ __forceinline__ void rs_finish(const RsParams& p, WsHeader* h, uint32_t* sb) {
+  __syncthreads();
+  uint32_t last = 0;
+  if (threadIdx.x == 0) {
+    fence_release();
+    last = add_relaxed(&h->done, 1u) == gridDim.x - 1;
+    if (last) fence_acquire();
+  }
+  last = wg_bcast(last, sb);
+  if (!last) return;
+  if (p.mode == MODE_ROLES)
+    for (int i = threadIdx.x; i < p.n_tiles; i += blockDim.x) st_relaxed(&p.fifo[i], 0u);
+  if (threadIdx.x == 0) {
+    st_relaxed(&h->ticket, 0u);
+    st_relaxed(&h->tile_next, 0u);
+    st_relaxed(&h->red_next, 0u);
+    st_relaxed(&h->prod_next, 0u);
+    st_relaxed(&h->abort, 0u);
+    st_relaxed(&h->done, 0u);
+  }
+}
+
+template <class G>
+__global__ __launch_bounds__(G::NT) void rs_kernel(const RsParams p) {
+  __shared__ u32x4 lds[G::LDS_U4];
+  __shared__ uint32_t sb[2];
+  WsHeader* h = p.hdr;
+  const uint32_t ticket = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->ticket, 1u) : 0u, sb);
+  const bool reducer = p.mode == MODE_REDUCE || (p.mode == MODE_ROLES && ticket >= (uint32_t)p.n_compute);
+  if (!reducer) rs_compute_role<G>(p, h, lds, sb);
+  if (p.mode == MODE_ROLES || p.mode == MODE_REDUCE) rs_reduce_role<G>(p, h, sb);
+  rs_finish(p, h, sb);
+}
+
+inline int rs_tile(int64_t M, int64_t N, int64_t K, int mb) {
+  int t = mk_default_tile(M, N, K);
+  // Tiles must not straddle owners.
+  if ((t == TILE_256x256 || t == TILE_256x128) && mb % 256) t = (N >= 256) ? TILE_128x256 : TILE_128x128;
+  return t;
+}
+
+inline int tile_bm(int t) { return (t == TILE_256x256 || t == TILE_256x128) ? 256 : 128; }
+
+}  // namespace
+
+extern "C" size_t mk_gemm_rs_workspace(int64_t M, int64_t K, int64_t N, int R, int out_dtype) {
+  (void)K; (void)R;
+  if (M <= 0 || N <= 0) return sizeof(WsHeader);
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  size_t bytes = sizeof(WsHeader) + (size_t)tiles * 4;
+  bytes = (bytes + 255) & ~(size_t)255;
+  if (out_dtype == MK_BF16) bytes += (size_t)M * N * 4;   // fp32 staging for the reduce role
+  return bytes;
+}
+
+template <class G>
+static int run_rs(RsParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStream_t st, bool can_stage) {
+  p.tiles_m = (p.M + G::BM - 1) / G::BM;
+  p.tiles_n = (p.N + G::BN - 1) / G::BN;
+  p.n_tiles = p.tiles_m * p.tiles_n;
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, rs_kernel<G>, G::NT, 0);
+  if (e != hipSuccess) return mkh::hip_fail(e, "occupancy query");
+  if (occ < 1) return mkh::fail(MK_ERR_UNSUPPORTED, "kernel does not fit on a CU");
+  const int full = d->n_cu * occ;
+  const int grid = o.grid > 0 ? std::min(o.grid, full) : full;
+  if (!can_stage) return mkh::fail(MK_ERR_WORKSPACE, "bf16 output needs the fp32 staging workspace");
+  if (o.mode == 1) {   // unfused baseline: GEMM to fp32 staging, then a reduce-scatter kernel
+    if (!can_stage) return mkh::fail(MK_ERR_WORKSPACE, "bf16 output needs the fp32 staging workspace");
+    p.mode = MODE_GEMM;
+    hipLaunchKernelGGL(rs_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "gemm kernel launch");
+    p.mode = MODE_REDUCE;
+    hipLaunchKernelGGL(rs_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "reduce kernel launch");
+    return MK_OK;
+  }
+  const int n_reduce = o.n_reduce;   // 0 = default (epilogue reduction), -1 = epilogue
+  if (n_reduce > 0) {
+    if (!can_stage) return mkh::fail(MK_ERR_WORKSPACE, "bf16 output needs the fp32 staging workspace");
+    if (n_reduce >= grid) return mkh::fail(MK_ERR_INVALID, "n_reduce %d leaves no compute workgroup", n_reduce);
+    p.mode = MODE_ROLES;
+    p.n_compute = grid - n_reduce;
+  } else {
+    p.mode = MODE_EPI;
+    p.n_compute = grid;
+  }
+  hipLaunchKernelGGL(rs_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "fused kernel launch");
+  return MK_OK;
+}
+
+extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
+                          const float* const* partials, int R, void* const* out_owner, int out_dtype,
+                          const mk_launch* launch, void* workspace, size_t workspace_bytes, void* stream) {
+  using mkh::fail;
+  if (!A || !B || !out_owner) return fail(MK_ERR_INVALID, "A, B and out_owner must be non-NULL");
+  if (R < 1 || R > MK_MAX_RANKS) return fail(MK_ERR_UNSUPPORTED, "R=%d outside [1,%d]", R, MK_MAX_RANKS);
+  if (M < 1 || K < 8 || N < 8) return fail(MK_ERR_INVALID, "empty or too small shape");
+  if (K % 8 || N % 8) return fail(MK_ERR_UNSUPPORTED, "K and N must be multiples of 8");
+  if (M % R) return fail(MK_ERR_INVALID, "M (%lld) not divisible by R (%d)", (long long)M, R);
+  if (M > (1 << 30) || K > (1 << 20) || N > (1 << 30) || K * N * 2 >= (1ll << 31) || M * N * 4 >= (1ll << 40))
+    return fail(MK_ERR_UNSUPPORTED, "dimension too large");
+  if (R > 1 && !partials) return fail(MK_ERR_INVALID, "partials is NULL");
+  if (out_dtype != MK_BF16 && out_dtype != MK_F32) return fail(MK_ERR_INVALID, "out_dtype %d", out_dtype);
+  for (int r = 0; r + 1 < R; ++r)
+    if (!partials[r] || !mkh::aligned16(partials[r])) return fail(MK_ERR_INVALID, "partial %d NULL or misaligned", r);
+  for (int r = 0; r < R; ++r)
+    if (!out_owner[r] || !mkh::aligned16(out_owner[r])) return fail(MK_ERR_INVALID, "owner %d NULL or misaligned", r);
+  if (!mkh::aligned16(A) || !mkh::aligned16(B)) return fail(MK_ERR_INVALID, "A and B must be 16-byte aligned");
+  const int mb = (int)(M / R);
+  const mk_launch o = mkh::launch_opts(launch);
+  if (o.mode != 0 && o.mode != 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
+  if (o.grid < 0 || o.n_reduce < -1) return fail(MK_ERR_INVALID, "bad grid or n_reduce");
+  const int tile = o.tile ? o.tile : rs_tile(M, N, K, mb);
+  if (tile <= 0 || tile >= TILE_COUNT) return fail(MK_ERR_INVALID, "tile id %d", tile);
+  if (mb % tile_bm(tile)) return fail(MK_ERR_UNSUPPORTED, "rows per owner (%d) must be a multiple of the tile height %d",
+                                      mb, tile_bm(tile));
+  if (!workspace) return fail(MK_ERR_WORKSPACE, "workspace is NULL");
+  const size_t need_min = mk_gemm_rs_workspace(M, K, N, R, MK_F32);
+  if (workspace_bytes < need_min) return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need_min);
+  const size_t need_stage = need_min + (size_t)M * N * 4;
+  const bool have_stage = workspace_bytes >= need_stage;
+  const mkh::DevInfo* d = mkh::dev_info();
+  if (!d) return MK_ERR_HIP;
+
+  RsParams p;
+  memset(&p, 0, sizeof p);
+  p.A = (const uint16_t*)A;
+  p.B = (const uint16_t*)B;
+  for (int r = 0; r + 1 < R; ++r) p.P[r] = partials[r];
+  for (int r = 0; r < R; ++r) p.out[r] = out_owner[r];
+  p.hdr = (WsHeader*)workspace;
+  p.fifo = (uint32_t*)((char*)workspace + sizeof(WsHeader));
+  // fp32 output can be staged in place in the owner blocks.
+  p.stage = out_dtype == MK_F32 ? nullptr : (have_stage ? (float*)((char*)workspace + need_min) : nullptr);
+  const bool can_stage = out_dtype == MK_F32 || have_stage;
+  p.tile_log = o.tile_log;
+  p.spin_limit = mkh::spin_ticks(o, d);
+  p.M = (int)M; p.K = (int)K; p.N = (int)N; p.R = R; p.mb = mb;
+  p.out_bf16 = out_dtype == MK_BF16;
+  const hipStream_t st = (hipStream_t)stream;
+  switch (tile) {
+    case TILE_256x256: return run_rs<TileGemm<256, 256, 2, 2>>(p, o, d, st, can_stage);
+    case TILE_128x128: return run_rs<TileGemm<128, 128, 2, 2>>(p, o, d, st, can_stage);
+    case TILE_256x128: return run_rs<TileGemm<256, 128, 2, 2>>(p, o, d, st, can_stage);
+    case TILE_128x256: return run_rs<TileGemm<128, 256, 2, 2>>(p, o, d, st, can_stage);
+    default: return fail(MK_ERR_INVALID, "tile id %d", tile);
+  }
+}

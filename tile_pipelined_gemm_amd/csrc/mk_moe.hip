@@ -1,0 +1,460 @@
+// MoE dispatch -> grouped GEMM.
+//
+// [P1] "Los cinco núcleos fusionados", row Envío MoE + GEMM: tokens are routed
+// to the ranks of their experts (all-to-all) and the per-expert grouped GEMM
+// runs in the same kernel on the tokens as they land, with no staging round
+// trip.  Here the landing buffer Xs is the one copy of each routed token row
+// and the grouped GEMM reads it tile by tile as rows arrive.
+//
+// Kernels, in stream order:
+//   route_kernel   one wave per token: top-k of the fp32 logits by k rounds of
+//                  a wave-wide arg-max (ties to the lower expert id); then, per
+//                  block of 64 tokens, each expert's count and each pair's rank
+//                  among the block's pairs for that expert (token order).
+//   scan_kernel    one workgroup: per expert, exclusive prefix of the block
+//                  counts (token order), totals, the exclusive expert prefix
+//                  (offsets) and the grouped-GEMM M-tile table of the local
+//                  experts.  Everything is integer and deterministic.
+//   moe_kernel     persistent.  copy role: source blocks in arrival order; for
+//                  each (token, slot) write perm and, for local experts, copy
+//                  the token row into its landing row, then count the row into
+//                  its M-tile's arrival counter (release).  compute role:
+//                  grouped-GEMM tiles, each started once its M-tile's counter
+//                  equals the tile's row count (acquire).
+#include <string.h>
+
+#include <algorithm>
+
+#include "mk_device.h"
+#include "mk_host.h"
+#include "mk_tiles.h"
+
+using namespace mk;
+
+namespace {
+
+constexpr int RB = 64;          // tokens per routing block
+constexpr int ROUTE_NT = 256;   // 4 waves, 16 tokens each
+
+struct MoeWs {                  // device workspace layout (offsets in bytes)
+  size_t block_cnt, rank, tile_base, tile_cnt, total;
+};
+
+inline MoeWs moe_ws_layout(int64_t T, int E, int k, int L) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  MoeWs w;
+  const int64_t nrb = (T + RB - 1) / RB;
+  const int64_t rows = T * std::min(k, L);
+  const int64_t max_tiles = rows / 128 + L + 1;
+  w.block_cnt = sizeof(WsHeader);
+  w.rank = up(w.block_cnt + (size_t)nrb * E * 4);
+  w.tile_base = up(w.rank + (size_t)T * k * 4);
+  w.tile_cnt = up(w.tile_base + (size_t)(L + 1) * 4 + 4);
+  w.total = up(w.tile_cnt + (size_t)max_tiles * 4);
+  return w;
+}
+
+// ------------------------------------------------------------------ routing
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__global__ __launch_bounds__(ROUTE_NT) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int32_t* __restrict__ topk, int32_t* __restrict__ block_cnt,
+                                                         int32_t* __restrict__ rank) {
+  __shared__ int16_t s_top[RB * MK_MAX_TOPK];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t_blk = blockIdx.x * RB;
+  const int per_lane = (E + 63) / 64;            // <= 16
+  for (int i = 0; i < RB / 4; ++i) {
+    const int tl = w * (RB / 4) + i;
+    const int t = t_blk + tl;
+    if (t >= T) break;                           // uniform per wave
+    float v[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int e = lane + 64 * s;
+      const float x = (s < per_lane && e < E) ? logits[(int64_t)t * E + e] : -__builtin_inff();
+      v[s] = x == x ? x : -__builtin_inff();   // NaN ranks below every number
+    }
+    uint32_t taken = 0;
+    for (int j = 0; j < k; ++j) {
+      float bv = -__builtin_inff();
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int e = lane + 64 * s;
+        if (s < per_lane && e < E && !((taken >> s) & 1u) && better(v[s], e, bv, bi)) {
+          bv = v[s];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == 0) {
+        topk[(int64_t)t * k + j] = bi;
+        s_top[tl * MK_MAX_TOPK + j] = (int16_t)bi;
+      }
+    }
+  }
+  __syncthreads();
+  // Per expert: count within this routing block and rank of each pair.
+  const int nt = min(RB, T - t_blk);
+  for (int e = threadIdx.x; e < E; e += ROUTE_NT) {
+    int c = 0;
+    for (int tl = 0; tl < nt; ++tl)
+      for (int j = 0; j < k; ++j)
+        if (s_top[tl * MK_MAX_TOPK + j] == e) {
+          rank[(int64_t)(t_blk + tl) * k + j] = c;
+          ++c;
+        }
+    block_cnt[(int64_t)blockIdx.x * E + e] = c;
+  }
+}
+
+// One workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ block_cnt, int nrb, int E,
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ n_local, int eb, int L, int BM,
+                                                    int32_t* __restrict__ tile_base) {
+  __shared__ int32_t s[1024];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E) {
+    for (int b = 0; b < nrb; ++b) {
+      const int c = block_cnt[(int64_t)b * E + e];
+      block_cnt[(int64_t)b * E + e] = tot;       // becomes the block offset within expert e
+      tot += c;
+    }
+    counts[e] = tot;
+  }
+  s[e] = e < E ? tot : 0;
+  __syncthreads();
+  // Inclusive Hillis-Steele scan over experts.
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = e >= off ? s[e - off] : 0;
+    __syncthreads();
+    s[e] += add;
+    __syncthreads();
+  }
+  if (e < E) offsets[e + 1] = s[e];
+  if (e == 0) offsets[0] = 0;
+  __syncthreads();
+  if (e == 0) {
+    const int base = eb > 0 ? s[eb - 1] : 0;
+    n_local[0] = s[eb + L - 1] - base;
+    int acc = 0;
+    for (int l = 0; l < L; ++l) {
+      tile_base[l] = acc;
+      const int c = s[eb + l] - (eb + l > 0 ? s[eb + l - 1] : 0);
+      acc += (c + BM - 1) / BM;
+    }
+    tile_base[L] = acc;
+  }
+}
+
+// ------------------------------------------------------ dispatch + grouped GEMM
+enum { MODE_FUSED = 0, MODE_COPY = 1, MODE_GEMM = 2 };
+
+struct MoeParams {
+  const uint16_t* X;
+  const uint16_t* W[MK_MAX_LOCAL];
+  uint16_t* Xs;
+  void* Y;
+  const int32_t* topk;
+  const int32_t* block_off;     // [nrb x E]
+  const int32_t* rank;          // [T x k]
+  const int32_t* counts;
+  const int32_t* offsets;
+  int32_t* perm;
+  const int32_t* tile_base;     // [L+1]
+  uint32_t* tile_cnt;           // [tiles] rows landed per M-tile
+  WsHeader* hdr;
+  int32_t* tile_log;
+  uint64_t spin_limit;
+  int T, H, E, k, L, F, eb, y_bf16;
+  int n_blocks, block_tokens, part_tokens, parts;
+  int mode, n_copy, tiles_n, withhold;
+  uint16_t order[MK_MAX_UNITS];
+  uint32_t delay_ticks[MK_MAX_UNITS];
+};
+
+constexpr int MAX_PAIRS = 8 * MK_MAX_TOPK;   // part_tokens (<= 8) x k
+
+__device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, uint32_t* sb, int BM) {
+  __shared__ int32_t s_src[MAX_PAIRS], s_dst[MAX_PAIRS], s_tile[MAX_PAIRS];
+  __shared__ int32_t s_n;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  uint64_t t0 = 0;
+  if (tid == 0) {
+    const uint64_t now = now_ticks();
+    const uint64_t old = atomicCAS((unsigned long long*)&h->t0, 0ull, (unsigned long long)now);
+    t0 = old ? old : now;
+  }
+  const uint32_t n_work = (uint32_t)p.n_blocks * p.parts;
+  const int base_local = p.offsets[p.eb];
+  const int cpr = p.H / 8;
+  for (;;) {
+    const uint32_t w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
+    if (w >= n_work) break;
+    const int j = w / p.parts, part = w % p.parts;
+    const int blk = p.order[j];
+    if (blk == p.withhold) continue;
+    if (tid == 0) {
+      wait_until(t0 + p.delay_ticks[blk], p.spin_limit);
+      s_n = 0;
+    }
+    __syncthreads();
+    const int t0k = blk * p.block_tokens + part * p.part_tokens;
+    const int npair = min(p.part_tokens, p.T - t0k) * p.k;
+    // Positions of this part's pairs; perm for all of them, landing rows for local ones.
+    if (tid < npair) {
+      const int t = t0k + tid / p.k, jj = tid % p.k;
+      const int e = p.topk[(int64_t)t * p.k + jj];
+      const int pos = p.offsets[e] + p.block_off[(int64_t)(t / RB) * p.E + e] + p.rank[(int64_t)t * p.k + jj];
+      p.perm[pos] = t * p.k + jj;
+      const int l = e - p.eb;
+      if (l >= 0 && l < p.L) {
+        const int slot = atomicAdd(&s_n, 1);
+        s_src[slot] = t;
+        s_dst[slot] = pos - base_local;
+        s_tile[slot] = p.tile_base[l] + (pos - p.offsets[e]) / BM;
+      }
+    }
+    __syncthreads();
+    const int n = s_n;
+    const int64_t total = (int64_t)n * cpr;
+    for (int64_t base = 0; base < total; base += (int64_t)nt * 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = base + (int64_t)u * nt + tid;
+        if (i < total) v[u] = ((const u32x4*)(p.X + (int64_t)s_src[i / cpr] * p.H))[i % cpr];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = base + (int64_t)u * nt + tid;
+        if (i < total) ((u32x4*)(p.Xs + (int64_t)s_dst[i / cpr] * p.H))[i % cpr] = v[u];
+      }
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid < 64) {
+      fence_release();
+      for (int q = tid; q < n; q += 64) add_relaxed(&p.tile_cnt[s_tile[q]], 1u);
+    }
+    __syncthreads();
+  }
+}
+
+template <class G>
+__device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h, u32x4* lds, uint32_t* sb) {
+  const int tid = threadIdx.x;
+  const int n_mt = p.tile_base[p.L];
+  const uint32_t n_tiles = (uint32_t)n_mt * p.tiles_n;
+  const int base_local = p.offsets[p.eb];
+  G g;
+  int l = 0;
+  for (;;) {
+    const uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+    if (q >= n_tiles) break;
+    const int mt = (int)(q / p.tiles_n), tn = (int)(q % p.tiles_n);
+    while (l + 1 < p.L && p.tile_base[l + 1] <= mt) ++l;        // queue is expert-ordered
+    while (l > 0 && p.tile_base[l] > mt) --l;
+    const int e = p.eb + l;
+    const int r0 = (mt - p.tile_base[l]) * G::BM;              // expert-relative first row
+    const int rows = min(G::BM, p.counts[e] - r0);
+    if (p.mode == MODE_FUSED) {
+      uint32_t ok = 1;
+      if (tid == 0) ok = wait_geq(&p.tile_cnt[mt], (uint32_t)rows, h, p.spin_limit);
+      if (!wg_bcast(ok, sb)) continue;
+    }
+    const int q0 = p.offsets[e] - base_local + r0;              // landing row of the tile
+    const int n0 = tn * G::BN;
+    g.bind(p.Xs + (int64_t)q0 * p.H, p.H, rows, p.W[l] + n0, p.F, p.F - n0, p.W[l] + (int64_t)p.H * p.F, p.H);
+    g.run(lds);
+    if (p.y_bf16) {
+      uint16_t* Y = (uint16_t*)p.Y;
+      g.for_each([&](int r, int c, float v) {
+        if (r < rows && n0 + c < p.F) Y[(int64_t)(q0 + r) * p.F + n0 + c] = f2bf(v);
+      });
+    } else {
+      float* Y = (float*)p.Y;
+      g.for_each([&](int r, int c, float v) {
+        if (r < rows && n0 + c < p.F) Y[(int64_t)(q0 + r) * p.F + n0 + c] = v;
+      });
+    }
+    if (p.tile_log && tid == 0 && tn == 0) {
+      int32_t* L4 = p.tile_log + 4 * (int64_t)mt;
+      L4[0] = l; L4[1] = r0; L4[2] = rows;
+      L4[3] = p.mode == MODE_FUSED ? (int32_t)ld_relaxed(&p.tile_cnt[mt]) : rows;
+    }
+  }
+}
+
+__device__ __forceinline__ void moe_finish(const MoeParams& p, WsHeader* h, uint32_t* sb) {
+  __syncthreads();
+  uint32_t last = 0;
+  if (threadIdx.x == 0) {
+    fence_release();
+    last = add_relaxed(&h->done, 1u) == gridDim.x - 1;
+    if (last) fence_acquire();
+  }
+  last = wg_bcast(last, sb);
+  if (!last) return;
+  const int n_mt = p.tile_base[p.L];
+  for (int i = threadIdx.x; i < n_mt; i += blockDim.x) st_relaxed(&p.tile_cnt[i], 0u);
+  if (threadIdx.x == 0) {
+    st_relaxed(&h->ticket, 0u);
+    st_relaxed(&h->tile_next, 0u);
+    st_relaxed(&h->copy_next, 0u);
+    st_relaxed(&h->abort, 0u);
+    __hip_atomic_store(&h->t0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_relaxed(&h->done, 0u);
+  }
+}
+
+template <class G>
+__global__ __launch_bounds__(G::NT) void moe_kernel(const MoeParams p) {
+  __shared__ u32x4 lds[G::LDS_U4];
+  __shared__ uint32_t sb[2];
+  WsHeader* h = p.hdr;
+  const uint32_t ticket = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->ticket, 1u) : 0u, sb);
+  if (p.mode == MODE_COPY || (p.mode == MODE_FUSED && ticket < (uint32_t)p.n_copy)) moe_copy_role(p, h, sb, G::BM);
+  if (p.mode != MODE_COPY) moe_compute_role<G>(p, h, lds, sb);
+  moe_finish(p, h, sb);
+}
+
+template <class G>
+int run_moe(MoeParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStream_t st, int32_t* counts,
+            int32_t* offsets, int32_t* n_local, int32_t* block_cnt, int nrb) {
+  hipError_t e;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, block_cnt, nrb, p.E, counts, offsets, n_local,
+                     p.eb, p.L, G::BM, const_cast<int32_t*>(p.tile_base));
+  if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "scan kernel launch");
+  p.tiles_n = (p.F + G::BN - 1) / G::BN;
+  int occ = 0;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, moe_kernel<G>, G::NT, 0)) != hipSuccess)
+    return mkh::hip_fail(e, "occupancy query");
+  if (occ < 1) return mkh::fail(MK_ERR_UNSUPPORTED, "kernel does not fit on a CU");
+  const int full = d->n_cu * occ;
+  const int grid = o.grid > 0 ? std::min(o.grid, full) : full;
+  const int n_work = p.n_blocks * p.parts;
+  if (o.mode == 1) {   // unfused baseline: permute kernel, then grouped GEMM kernel
+    p.mode = MODE_COPY;
+    p.n_copy = grid;
+    hipLaunchKernelGGL(moe_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "permute kernel launch");
+    p.mode = MODE_GEMM;
+    p.n_copy = 0;
+    hipLaunchKernelGGL(moe_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "grouped gemm kernel launch");
+    return MK_OK;
+  }
+  p.mode = MODE_FUSED;
+  int n_copy = o.n_copy > 0 ? o.n_copy : std::max(1, grid / 4);
+  p.n_copy = std::min(std::min(n_copy, grid), n_work);
+  hipLaunchKernelGGL(moe_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "fused kernel launch");
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" size_t mk_moe_dispatch_gemm_workspace(int64_t T, int64_t H, int E, int k, int L, int64_t F) {
+  (void)H; (void)F;
+  if (T <= 0 || E <= 0 || k <= 0 || L <= 0) return sizeof(WsHeader);
+  return moe_ws_layout(T, E, k, L).total;
+}
+
+extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t T, int64_t H, int E, int k,
+                                    const void* const* W, int expert_begin, int L, int64_t F,
+                                    int32_t* topk_idx, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                    int32_t* n_local_rows, void* Xs, void* Y, int y_dtype,
+                                    const mk_arrival* arrival, const mk_launch* launch,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  using mkh::fail;
+  if (!X || !logits || !W || !topk_idx || !counts || !offsets || !perm || !n_local_rows || !Xs || !Y)
+    return fail(MK_ERR_INVALID, "NULL pointer argument");
+  if (T < 1 || H < 8 || F < 8) return fail(MK_ERR_INVALID, "empty or too small shape");
+  if (H % 8 || F % 8) return fail(MK_ERR_UNSUPPORTED, "H and F must be multiples of 8");
+  if (E < 1 || E > MK_MAX_EXPERTS) return fail(MK_ERR_UNSUPPORTED, "E=%d outside [1,%d]", E, MK_MAX_EXPERTS);
+  if (k < 1 || k > MK_MAX_TOPK || k > E) return fail(MK_ERR_INVALID, "k=%d outside [1,min(E,%d)]", k, MK_MAX_TOPK);
+  if (L < 1 || L > MK_MAX_LOCAL) return fail(MK_ERR_UNSUPPORTED, "L=%d outside [1,%d]", L, MK_MAX_LOCAL);
+  if (expert_begin < 0 || expert_begin + L > E) return fail(MK_ERR_INVALID, "local experts outside [0,E)");
+  if (y_dtype != MK_BF16 && y_dtype != MK_F32) return fail(MK_ERR_INVALID, "y_dtype %d", y_dtype);
+  const int64_t cap = T * std::min(k, L);
+  if (T * k > (1 << 30) || cap * H * 2 >= (1ll << 40) || H * F * 2 >= (1ll << 31) || (int64_t)128 * H * 2 >= (1ll << 31))
+    return fail(MK_ERR_UNSUPPORTED, "dimension too large");
+  for (int l = 0; l < L; ++l)
+    if (!W[l] || !mkh::aligned16(W[l])) return fail(MK_ERR_INVALID, "W[%d] NULL or misaligned", l);
+  if (!mkh::aligned16(X) || !mkh::aligned16(Xs) || !mkh::aligned16(Y))
+    return fail(MK_ERR_INVALID, "X, Xs and Y must be 16-byte aligned");
+  mkh::Schedule s;
+  int rc = mkh::make_schedule(arrival, T, 1, &s);
+  if (rc) return rc;
+  if (!workspace) return fail(MK_ERR_WORKSPACE, "workspace is NULL");
+  const MoeWs lay = moe_ws_layout(T, E, k, L);
+  if (workspace_bytes < lay.total) return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, lay.total);
+  const mk_launch o = mkh::launch_opts(launch);
+  if (o.mode != 0 && o.mode != 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
+  if (o.grid < 0 || o.n_copy < 0) return fail(MK_ERR_INVALID, "negative grid or n_copy");
+  const mkh::DevInfo* d = mkh::dev_info();
+  if (!d) return MK_ERR_HIP;
+  const hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int32_t* block_cnt = (int32_t*)(ws + lay.block_cnt);
+  int32_t* rank = (int32_t*)(ws + lay.rank);
+  const int nrb = (int)((T + RB - 1) / RB);
+
+  hipLaunchKernelGGL(route_kernel, dim3(nrb), dim3(ROUTE_NT), 0, st, logits, (int)T, E, k, topk_idx, block_cnt, rank);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return mkh::hip_fail(e, "route kernel launch");
+
+  MoeParams p;
+  memset(&p, 0, sizeof p);
+  p.X = (const uint16_t*)X;
+  for (int l = 0; l < L; ++l) p.W[l] = (const uint16_t*)W[l];
+  p.Xs = (uint16_t*)Xs;
+  p.Y = Y;
+  p.topk = topk_idx;
+  p.block_off = block_cnt;
+  p.rank = rank;
+  p.counts = counts;
+  p.offsets = offsets;
+  p.perm = perm;
+  p.tile_base = (const int32_t*)(ws + lay.tile_base);
+  p.tile_cnt = (uint32_t*)(ws + lay.tile_cnt);
+  p.hdr = (WsHeader*)workspace;
+  p.tile_log = o.tile_log;
+  p.spin_limit = mkh::spin_ticks(o, d);
+  p.T = (int)T; p.H = (int)H; p.E = E; p.k = k; p.L = L; p.F = (int)F; p.eb = expert_begin;
+  p.y_bf16 = y_dtype == MK_BF16;
+  p.n_blocks = s.n_units;
+  p.block_tokens = s.unit_rows;
+  p.part_tokens = std::min(8, s.unit_rows);
+  while (s.unit_rows % p.part_tokens) --p.part_tokens;
+  p.parts = s.unit_rows / p.part_tokens;
+  p.withhold = s.withhold;
+  for (int j = 0; j < s.n_units; ++j) {
+    p.order[j] = (uint16_t)s.order[j];
+    p.delay_ticks[j] = (uint32_t)mkh::ns_to_ticks(s.delay_ns[j], d->wall_khz);
+  }
+  int tile = o.tile ? o.tile : TILE_256x256;
+  if (F < 256 && tile == TILE_256x256) tile = TILE_128x128;
+  switch (tile) {
+    case TILE_256x256: return run_moe<TileGemm<256, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
+    case TILE_128x128: return run_moe<TileGemm<128, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
+    case TILE_256x128: return run_moe<TileGemm<256, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
+    case TILE_128x256: return run_moe<TileGemm<128, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
+    default: return fail(MK_ERR_INVALID, "tile id %d", tile);
+  }
+}

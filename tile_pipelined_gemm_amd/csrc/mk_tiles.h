@@ -1,0 +1,23 @@
+// Tile configurations shared by the entry points and the per-shape defaults.
+#pragma once
+
+#include <stdint.h>
+
+enum MkTile {
+  TILE_AUTO = 0,
+  TILE_256x256 = 1,  // 4 waves, 128x128 per wave: highest MFMA density, 1 workgroup per CU
+  TILE_128x128 = 2,  // 4 waves, 64x64 per wave: small or ragged problems
+  TILE_256x128 = 3,  // 4 waves, 128x64 per wave
+  TILE_128x256 = 4,  // 4 waves, 64x128 per wave
+  TILE_COUNT
+};
+
+// Per-shape default: the largest tile that still gives every CU work.
+inline int mk_default_tile(int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (M >= 256 && N >= 256 && t256 >= 256) return TILE_256x256;
+  const int64_t t128x256 = ((M + 127) / 128) * ((N + 255) / 256);
+  if (N >= 256 && t128x256 >= 256) return TILE_128x256;
+  return TILE_128x128;
+}

@@ -1,0 +1,227 @@
+"""Thin ctypes binding of libmk.so (declared in include/mk.h).
+
+Every function here only marshals arguments -- torch tensors become device
+pointers, Python lists become host pointer arrays, the current torch stream
+becomes the hipStream_t -- and calls the C entry point of the same name.  All
+computation runs in the HIP kernels of libmk.so; there is no fallback: if the
+library is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmk.so")
+
+MK_BF16, MK_F32 = 0, 1
+MK_OK, MK_ERR_INVALID, MK_ERR_UNSUPPORTED, MK_ERR_WORKSPACE, MK_ERR_HIP, MK_ERR_TIMEOUT, MK_ERR_SCHEDULE = \
+    0, -1, -2, -3, -4, -5, -6
+MK_MAX_UNITS = 256
+
+# Symbols declared in include/mk.h (checked by the CPU tests).
+EXPORTS = [
+    "mk_ag_gemm_workspace", "mk_ag_gemm", "mk_gemm_rs_workspace", "mk_gemm_rs",
+    "mk_moe_dispatch_gemm_workspace", "mk_moe_dispatch_gemm", "mk_workspace_init",
+    "mk_poll_status", "mk_status_string", "mk_last_error", "mk_tile_name", "mk_version",
+]
+
+
+class MkError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mk error {code}: {msg}")
+        self.code = code
+
+
+class mk_arrival(C.Structure):
+    _fields_ = [("order", C.POINTER(C.c_int32)), ("delay_ns", C.POINTER(C.c_uint32)),
+                ("n_units", C.c_int32), ("unit_rows", C.c_int32), ("withhold", C.c_int32)]
+
+
+class mk_launch(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("grid", C.c_int32), ("n_copy", C.c_int32),
+                ("n_reduce", C.c_int32), ("tile", C.c_int32), ("spin_limit_us", C.c_uint32),
+                ("tile_log", C.c_void_p), ("reserved", C.c_int32 * 4)]
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load libmk.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run `python -m tile_pipelined_gemm_amd.build`")
+    lib = C.CDLL(path)
+    vp, i32, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+    pp = C.POINTER(C.c_void_p)
+    lib.mk_ag_gemm_workspace.restype = sz
+    lib.mk_ag_gemm_workspace.argtypes = [i32, i64, i64, i64, C.c_int32]
+    lib.mk_ag_gemm.restype = i32
+    lib.mk_ag_gemm.argtypes = [pp, i32, i64, i64, vp, i64, vp, i32, vp,
+                               C.POINTER(mk_arrival), C.POINTER(mk_launch), vp, sz, vp]
+    lib.mk_gemm_rs_workspace.restype = sz
+    lib.mk_gemm_rs_workspace.argtypes = [i64, i64, i64, i32, i32]
+    lib.mk_gemm_rs.restype = i32
+    lib.mk_gemm_rs.argtypes = [vp, vp, i64, i64, i64, pp, i32, pp, i32,
+                               C.POINTER(mk_launch), vp, sz, vp]
+    lib.mk_moe_dispatch_gemm_workspace.restype = sz
+    lib.mk_moe_dispatch_gemm_workspace.argtypes = [i64, i64, i32, i32, i32, i64]
+    lib.mk_moe_dispatch_gemm.restype = i32
+    lib.mk_moe_dispatch_gemm.argtypes = [vp, vp, i64, i64, i32, i32, pp, i32, i32, i64,
+                                         vp, vp, vp, vp, vp, vp, vp, i32,
+                                         C.POINTER(mk_arrival), C.POINTER(mk_launch), vp, sz, vp]
+    lib.mk_workspace_init.restype = i32
+    lib.mk_workspace_init.argtypes = [vp, sz, vp]
+    lib.mk_poll_status.restype = i32
+    lib.mk_poll_status.argtypes = [vp, vp]
+    lib.mk_status_string.restype = C.c_char_p
+    lib.mk_status_string.argtypes = [i32]
+    lib.mk_last_error.restype = C.c_char_p
+    lib.mk_last_error.argtypes = []
+    lib.mk_tile_name.restype = C.c_char_p
+    lib.mk_tile_name.argtypes = [i32]
+    lib.mk_version.restype = i32
+    lib.mk_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != MK_OK:
+        raise MkError(rc, _lib.mk_last_error().decode())
+    return rc
+
+
+# ---------------------------------------------------------------- marshalling
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _ptr_array(ts: Sequence) -> C.Array:
+    return (C.c_void_p * max(1, len(ts)))(*[_ptr(t) for t in ts])
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MK_BF16
+    if t.dtype == torch.float32:
+        return MK_F32
+    raise ValueError(f"unsupported output dtype {t.dtype}")
+
+
+def make_arrival(order=None, delay_ns=None, unit_rows=0, withhold=-1):
+    """Build an mk_arrival from Python sequences (None when order is None)."""
+    if order is None:
+        return None, ()
+    order = list(int(x) for x in order)
+    o = (C.c_int32 * len(order))(*order)
+    d = None
+    if delay_ns is not None:
+        d = (C.c_uint32 * len(order))(*[int(x) for x in delay_ns])
+    a = mk_arrival(C.cast(o, C.POINTER(C.c_int32)),
+                   C.cast(d, C.POINTER(C.c_uint32)) if d is not None else None,
+                   len(order), int(unit_rows), int(withhold))
+    return a, (o, d)
+
+
+def make_launch(mode=0, grid=0, n_copy=0, n_reduce=0, tile=0, spin_limit_us=0, tile_log=None):
+    return mk_launch(mode, grid, n_copy, n_reduce, tile, spin_limit_us, _ptr(tile_log), (C.c_int32 * 4)())
+
+
+# ---------------------------------------------------------------- entry points
+def mk_ag_gemm_workspace(R, m_shard, K, N, unit_rows=0) -> int:
+    return load().mk_ag_gemm_workspace(R, m_shard, K, N, unit_rows)
+
+
+def mk_gemm_rs_workspace(M, K, N, R, out_dtype=MK_F32) -> int:
+    return load().mk_gemm_rs_workspace(M, K, N, R, out_dtype)
+
+
+def mk_moe_dispatch_gemm_workspace(T, H, E, k, L, F) -> int:
+    return load().mk_moe_dispatch_gemm_workspace(T, H, E, k, L, F)
+
+
+def mk_workspace_init(ws, stream=None):
+    return _check(load().mk_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mk_poll_status(ws, stream=None) -> int:
+    """Synchronise and return the sticky device status (MK_OK or MK_ERR_TIMEOUT)."""
+    return load().mk_poll_status(_ptr(ws), _stream(stream))
+
+
+def mk_ag_gemm(shards, B, C_out, a_gathered, ws, *, order=None, delay_ns=None, unit_rows=0,
+               withhold=-1, launch=None, stream=None, check=True) -> int:
+    lib = load()
+    R = len(shards)
+    m_shard, K = shards[0].shape
+    N = B.shape[1]
+    arr, keep = make_arrival(order, delay_ns, unit_rows or m_shard, withhold)
+    lau = launch if launch is not None else make_launch()
+    rc = lib.mk_ag_gemm(_ptr_array(shards), R, m_shard, K, _ptr(B), N, _ptr(C_out), _dtype_code(C_out),
+                        _ptr(a_gathered), C.byref(arr) if arr is not None else None, C.byref(lau),
+                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    del keep
+    return _check(rc) if check else rc
+
+
+def mk_gemm_rs(A, B, partials, out_owner, ws, *, launch=None, stream=None, check=True) -> int:
+    lib = load()
+    M, K = A.shape
+    N = B.shape[1]
+    R = len(out_owner)
+    lau = launch if launch is not None else make_launch()
+    rc = lib.mk_gemm_rs(_ptr(A), _ptr(B), M, K, N, _ptr_array(partials), R, _ptr_array(out_owner),
+                        _dtype_code(out_owner[0]), C.byref(lau), _ptr(ws), ws.numel() * ws.element_size(),
+                        _stream(stream))
+    return _check(rc) if check else rc
+
+
+def mk_moe_dispatch_gemm(X, logits, W, k, expert_begin, topk_idx, counts, offsets, perm, n_local_rows,
+                         Xs, Y, ws, *, order=None, delay_ns=None, block_tokens=0, withhold=-1,
+                         launch=None, stream=None, check=True) -> int:
+    lib = load()
+    T, H = X.shape
+    E = logits.shape[1]
+    L = len(W)
+    F = W[0].shape[1]
+    arr, keep = make_arrival(order, delay_ns, block_tokens, withhold)
+    lau = launch if launch is not None else make_launch()
+    rc = lib.mk_moe_dispatch_gemm(_ptr(X), _ptr(logits), T, H, E, k, _ptr_array(W), expert_begin, L, F,
+                                  _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(n_local_rows),
+                                  _ptr(Xs), _ptr(Y), _dtype_code(Y),
+                                  C.byref(arr) if arr is not None else None, C.byref(lau),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    del keep
+    return _check(rc) if check else rc
+
+
+def mk_tile_name(i: int):
+    r = load().mk_tile_name(i)
+    return r.decode() if r is not None else None
+
+
+def workspace(nbytes: int, device="cuda"):
+    """A zero-filled workspace tensor (bytes rounded up to 256)."""
+    import torch
+    nbytes = (int(nbytes) + 255) // 256 * 256
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
