@@ -102,6 +102,8 @@ def test_rs_validation(lib):
     assert _rs(lib, out_dtype=5) == mk.MK_ERR_INVALID
     assert _rs(lib, partials=False) == mk.MK_ERR_INVALID
     assert _rs(lib, M=4 * 96) == mk.MK_ERR_UNSUPPORTED       # 96 rows per owner: not a tile multiple
+    lau = mk.make_launch(tile=1)
+    assert _rs(lib, lau=C.byref(lau)) == mk.MK_ERR_UNSUPPORTED   # only the 128x128 tile is enabled
     assert _rs(lib, ws_bytes=64) == mk.MK_ERR_WORKSPACE
     lau = mk.make_launch(n_reduce=-5)
     assert _rs(lib, lau=C.byref(lau)) == mk.MK_ERR_INVALID

@@ -93,11 +93,14 @@ __device__ inline void wait_until(uint64_t deadline, uint64_t limit_ticks) {
     __builtin_amdgcn_s_sleep(8);
 }
 
-// Value of thread 0 broadcast to the workgroup (uses one LDS word).
+// Value of thread 0 broadcast to the workgroup (uses one LDS word).  The
+// result is made wave-uniform (readfirstlane), so everything derived from it
+// -- tile coordinates, buffer descriptors, loop exits -- lives in scalar
+// registers and branches are uniform.
 __device__ __forceinline__ uint32_t wg_bcast(uint32_t v, uint32_t* slot) {
   if (threadIdx.x == 0) *slot = v;
   __syncthreads();
-  uint32_t r = *slot;
+  const uint32_t r = __builtin_amdgcn_readfirstlane(*slot);
   __syncthreads();
   return r;
 }
@@ -126,6 +129,18 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 constexpr uint32_t OOB = 0x80000000u;   // a voffset that is always past the end
+
+// Values the caller knows to be the same in every lane, moved to scalar
+// registers (buffer descriptors must live there).
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <class T>
+__device__ __forceinline__ const T* uni(const T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint64_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint64_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(lo | (hi << 32));
+}
 
 // ------------------------------------------------------------ block tile GEMM
 // BM x BN output tile per workgroup, WM x WN waves, each wave owning a
@@ -170,14 +185,15 @@ struct TileGemm {
   __device__ __forceinline__ void bind(const uint16_t* A, int64_t lda, int mrows,
                                        const uint16_t* B, int64_t ldb, int ncols_, const uint16_t* B_end,
                                        int K_) {
+    // Every argument is uniform across the workgroup.
     const int tid = threadIdx.x;
-    K = K_;
-    ncols = ncols_;
-    ldaB = (uint32_t)(lda * 2);
-    ldbB = (uint32_t)(ldb * 2);
+    K = uni(K_);
+    ncols = uni(ncols_);
+    ldaB = uni((uint32_t)(lda * 2));
+    ldbB = uni((uint32_t)(ldb * 2));
     const int rows = mrows < BM ? mrows : BM;
-    rsA = make_rsrc(A, (uint32_t)(rows > 0 ? rows : 0) * ldaB);
-    rsB = make_rsrc(B, (uint32_t)((B_end - B) * 2));
+    rsA = make_rsrc(uni(A), uni((uint32_t)(rows > 0 ? rows : 0) * ldaB));
+    rsB = make_rsrc(uni(B), uni((uint32_t)((B_end - B) * 2)));
     voA = (uint32_t)(tid >> 3) * ldaB + (uint32_t)(tid & 7) * 16u;
     const int kb = tid / B_NB, nb = tid % B_NB;
     voB = (nb * 8 < ncols) ? (uint32_t)(kb * 8) * ldbB + (uint32_t)nb * 16u : OOB;
