@@ -100,7 +100,7 @@ __device__ inline void wait_until(uint64_t deadline, uint64_t limit_ticks) {
 __device__ __forceinline__ uint32_t wg_bcast(uint32_t v, uint32_t* slot) {
   if (threadIdx.x == 0) *slot = v;
   __syncthreads();
-  const uint32_t r = __builtin_amdgcn_readfirstlane(*slot);
+  const uint32_t r = (uint32_t)__builtin_amdgcn_readfirstlane((int)*slot);
   __syncthreads();
   return r;
 }
@@ -131,14 +131,18 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 constexpr uint32_t OOB = 0x80000000u;   // a voffset that is always past the end
 
 // Values the caller knows to be the same in every lane, moved to scalar
-// registers (buffer descriptors must live there).
-__device__ __forceinline__ uint32_t uni(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+// registers (buffer descriptors must live there).  The builtin works on int:
+// each 32-bit half is taken back as uint32_t before widening, so a low half
+// with bit 31 set is not sign-extended into the high half of a pointer.
+__device__ __forceinline__ uint32_t uni(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 template <class T>
 __device__ __forceinline__ const T* uni(const T* p) {
   const uint64_t v = (uint64_t)p;
-  const uint64_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint64_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint64_t lo = uni((uint32_t)v);
+  const uint64_t hi = uni((uint32_t)(v >> 32));
   return (const T*)(lo | (hi << 32));
 }
 
