@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the unfused and library yardsticks")
     ap.add_argument("--copies", type=int, default=0, help="rotated input copies (0 = auto)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -168,7 +170,7 @@ def bench_moe(args, stream, extra=True):
 
 
 def cpu_baseline(seed):
-    """The oracle (numpy float64) on a bounded row sample of the AG workload."""
+    """The oracle (numpy float64) timed on whole calls of the AG workload."""
     import numpy as np
     import oracle.ag_gemm as og
     import workloads as wl
@@ -178,14 +180,17 @@ def cpu_baseline(seed):
     except Exception:
         cores = os.cpu_count()
     w = wl.CONFIGS["ag"]["make"](seed)
-    rows = np.arange(0, w.M, 4)            # every 4th row: 2048 x 8192 x 3584
-    t0 = time.perf_counter()
-    og.ag_gemm_rows(w.shards, w.B, rows)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * len(rows) * w.K * w.N
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"float64 rows of C = gather(A) @ B: {len(rows)} of {w.M} rows (every 4th), "
-                       f"K={w.K}, N={w.N}; {dt:.1f} s")
+    flops = 2.0 * w.M * w.K * w.N
+    reps, t0 = 0, time.perf_counter()
+    while True:                     # whole oracle calls, about 10 s in total
+        og.ag_gemm(w.shards, w.B, w.out_dtype, order=w.order, delay_ns=w.delay_ns, unit_rows=w.unit_rows)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or reps >= 50:
+            break
+    return dict(value=flops * reps / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"{reps} full oracle calls of the AG workload (gather, float64 GEMM "
+                       f"{w.M}x{w.K}x{w.N}, bf16 rounding) in {dt:.1f} s")
 
 
 def main():
@@ -199,6 +204,13 @@ def main():
     mk.load()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.copy_calib:
+        n = args.copy_calib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        wall, kern = timed(lambda i: dst.copy_(src), args.steps, args.warmup, stream)
+        print(json.dumps({"copy_bytes": n, "kernel_ms": kern, "gbs": 2 * n / kern / 1e6}), flush=True)
+        return
     only = set(x for x in args.only.split(",") if x)
 
     def want(x):
