@@ -93,6 +93,13 @@ def bench_ag(name, args, stream, extra=True):
         uw, uk = timed(unfused, max(3, args.steps // 2), 2, stream)
         r["unfused_ms"] = uk
         r["speedup_vs_unfused"] = uk / kern
+        # role split and scheduling variants of the fused kernel
+        for tag, kw in [("n_copy16", dict(n_copy=16)), ("n_copy128", dict(n_copy=128)),
+                        ("global_queue", dict(flags=mk.MK_FLAG_GLOBAL_QUEUE)),
+                        ("no_steal", dict(flags=mk.MK_FLAG_NO_STEAL))]:
+            lv = mk.make_launch(**kw)
+            _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 5, 2, stream)
+            r[f"variant_{tag}_ms"] = vk
         # hipBLASLt yardstick on the already gathered A (not the target)
         Ag = [p.Ag for p in probs]
         Bs = [p.B for p in probs]

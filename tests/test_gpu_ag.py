@@ -64,6 +64,8 @@ def test_output_independent_of_schedule_and_roles(gpu):
             dict(order=w.order, delay_ns=w.delay_ns),
             dict(order=w.order, launch=gpu.make_launch(n_copy=1)),
             dict(order=w.order, launch=gpu.make_launch(n_copy=64, grid=80)),
+            dict(order=w.order, delay_ns=w.delay_ns, launch=gpu.make_launch(flags=gpu.MK_FLAG_GLOBAL_QUEUE)),
+            dict(order=w.order, delay_ns=w.delay_ns, launch=gpu.make_launch(flags=gpu.MK_FLAG_NO_STEAL)),
             dict(launch=gpu.make_launch(mode=1))]
     outs = []
     for kw in runs:
@@ -85,13 +87,12 @@ def test_tile_log_records_chunk_dependencies(gpu):
     prob.run(launch=gpu.make_launch(tile=1, tile_log=log))
     torch.cuda.synchronize()
     L = log.cpu().numpy().reshape(-1, 4)
-    n_tiles = (w.M // 256) * (w.N // 256)
-    seen = set()
-    for q in range(n_tiles):
-        tm, tn, u0, u1 = L[q]
+    tiles_n = w.N // 256
+    n_tiles = (w.M // 256) * tiles_n
+    for t in range(n_tiles):                      # one record per output tile id
+        tm, tn, u0, u1 = L[t]
+        assert (tm, tn) == (t // tiles_n, t % tiles_n)
         assert (u0, u1) == og.tile_units(tm, 256, w.unit_rows, w.M)
-        seen.add((tm, tn))
-    assert len(seen) == n_tiles
     assert np.all(L[n_tiles:] == -1)
 
 
