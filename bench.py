@@ -95,8 +95,8 @@ def bench_ag(name, args, stream, extra=True):
         r["speedup_vs_unfused"] = uk / kern
         # role split and scheduling variants of the fused kernel
         for tag, kw in [("n_copy16", dict(n_copy=16)), ("n_copy128", dict(n_copy=128)),
-                        ("global_queue", dict(flags=mk.MK_FLAG_GLOBAL_QUEUE)),
-                        ("no_steal", dict(flags=mk.MK_FLAG_NO_STEAL))]:
+                        ("tile_dma", dict(tile=mk.TILE_256x256_DMA)),
+                        ("tile_dma_n_copy16", dict(tile=mk.TILE_256x256_DMA, n_copy=16))]:
             lv = mk.make_launch(**kw)
             _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 5, 2, stream)
             r[f"variant_{tag}_ms"] = vk

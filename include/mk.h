@@ -97,13 +97,8 @@ typedef struct mk_launch {
   int32_t tile;           /* tile configuration id; 0 = default (see mk_tile_name) */
   uint32_t spin_limit_us; /* watchdog for every wait; 0 = 2,000,000 us */
   int32_t* tile_log;      /* device int32 or NULL: per-tile record, see each op */
-  int32_t flags;          /* MK_FLAG_* bits; 0 = all scheduling optimisations on */
-  int32_t reserved[3];
+  int32_t reserved[4];     /* must be zero */
 } mk_launch;
-
-/* mk_launch.flags */
-#define MK_FLAG_GLOBAL_QUEUE 1  /* one global tile queue instead of one queue per XCD (L2) */
-#define MK_FLAG_NO_STEAL 2      /* compute workgroups spin instead of taking pending copy work */
 
 /* ---------------------------------------------------------------------------
  * AllGather -> GEMM  ([P1] "Los cinco núcleos fusionados", row AllGather + GEMM)
@@ -116,8 +111,8 @@ typedef struct mk_launch {
  * nearest-even for bf16), starting each output tile as soon as the units
  * covering its rows have landed.
  *   arrival NULL = one unit per shard, issued in rank order, no delay.
- *   tile_log (optional): per output tile id (tile_row*tiles_n + tile_col),
- *   4 int32 {tile_row, tile_col, first unit, last unit}.
+ *   tile_log (optional): per tile in queue order, 4 int32 {tile_row,
+ *   tile_col, first unit, last unit}.
  * ------------------------------------------------------------------------- */
 size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_t N, int32_t unit_rows);
 int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K,

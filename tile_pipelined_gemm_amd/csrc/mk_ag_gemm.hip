@@ -22,6 +22,7 @@
 #include <algorithm>
 
 #include "mk_device.h"
+#include "mk_gemm_dma.h"
 #include "mk_host.h"
 #include "mk_tiles.h"
 
@@ -30,8 +31,6 @@ using namespace mk;
 namespace {
 
 enum { MODE_FUSED = 0, MODE_COPY = 1, MODE_GEMM = 2 };
-constexpr int NXCD = 8;              // XCDs; workgroup i runs on XCD i % 8
-constexpr uint32_t NONE = 0xffffffffu;
 
 struct AgParams {
   const uint16_t* shard[MK_MAX_RANKS];
@@ -44,167 +43,92 @@ struct AgParams {
   uint64_t spin_limit;
   int R, m_shard, M, K, N, c_bf16;
   int n_units, unit_rows, parts, part_rows;
-  int mode, n_copy, tiles_m, tiles_n, n_tiles, withhold, flags;
+  int mode, n_copy, tiles_m, tiles_n, n_tiles, withhold;
   uint16_t order[MK_MAX_UNITS];
-  uint16_t rb_order[MK_MAX_UNITS];   // tile rows in landing order (global queue)
-  uint16_t xrb[MK_MAX_UNITS];        // tile rows per XCD queue, each in landing order
-  uint16_t xoff[NXCD + 1];           // XCD x owns xrb[xoff[x] .. xoff[x+1])
+  uint16_t rb_order[MK_MAX_UNITS];   // tile rows in landing order
   uint32_t delay_ticks[MK_MAX_UNITS];
 };
 
-// Header words used by this op.
-__device__ __forceinline__ uint32_t* landed_total(WsHeader* h) { return &h->aux[0]; }
-__device__ __forceinline__ uint32_t* xcd_head(WsHeader* h, int x) { return &h->aux[8 + x]; }
-
-// Kernel start time shared by every workgroup that copies (thread 0 only).
-__device__ __forceinline__ uint64_t shared_t0(WsHeader* h) {
-  const uint64_t now = now_ticks();
-  const uint64_t old = atomicCAS((unsigned long long*)&h->t0, 0ull, (unsigned long long)now);
-  return old ? old : now;
-}
-
-constexpr int COPY_BATCH = 16;       // 16-byte loads in flight per thread (64 KiB per workgroup)
-
-// Copy work item w (unit order[w / parts], part w % parts): a contiguous run
-// of part_rows rows inside one shard.  Published with ONE agent-scope release
-// (every wave first waits for its own stores, then thread 0 writes back L2 and
-// bumps the counters).
-__device__ __forceinline__ void ag_copy_item(const AgParams& p, WsHeader* h, uint32_t w, uint64_t t0) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int j = w / p.parts, part = w % p.parts;
-  const int c = p.order[j];
-  if (c == p.withhold) return;                   // never delivered (failure tests)
-  if (tid == 0) wait_until(t0 + p.delay_ticks[c], p.spin_limit);
-  __syncthreads();
-  const int row0 = c * p.unit_rows + part * p.part_rows;
-  const u32x4* __restrict__ src =
-      (const u32x4*)(p.shard[row0 / p.m_shard] + (int64_t)(row0 % p.m_shard) * p.K);
-  u32x4* __restrict__ dst = (u32x4*)(p.Ag + (int64_t)row0 * p.K);
-  const int n16 = p.part_rows * (p.K / 8);
-  for (int base = 0; base < n16; base += nt * COPY_BATCH) {
-    u32x4 v[COPY_BATCH];
-#pragma unroll
-    for (int u = 0; u < COPY_BATCH; ++u) {
-      const int i = base + u * nt + tid;
-      if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
-    }
-#pragma unroll
-    for (int u = 0; u < COPY_BATCH; ++u) {
-      const int i = base + u * nt + tid;
-      if (i < n16) dst[i] = v[u];
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);                 // this wave's stores have reached L2
-  __syncthreads();
-  if (tid == 0) {
-    fence_release();                             // write back L2 once for the whole item
-    add_relaxed(&p.unit_cnt[c], 1u);
-    add_relaxed(landed_total(h), 1u);
-  }
-}
+constexpr int COPY_UNROLL = 8;
 
 __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uint32_t* sb) {
-  const uint32_t n_work = (uint32_t)p.n_units * p.parts;
+  const int tid = threadIdx.x, nt = blockDim.x;
   uint64_t t0 = 0;
-  if (threadIdx.x == 0) t0 = shared_t0(h);
-  for (;;) {
-    const uint32_t w = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
-    if (w >= n_work) break;
-    ag_copy_item(p, h, w, t0);
-  }
-}
-
-// Thread 0: next output tile as (tm << 16 | tn), or NONE.  Default: one queue
-// per XCD (each owns a set of tile rows, so its L2 holds only those rows of
-// A), stealing from the other XCDs' queues once its own is empty.
-__device__ inline uint32_t ag_next_tile(const AgParams& p, WsHeader* h) {
-  if (p.flags & MK_FLAG_GLOBAL_QUEUE) {
-    const uint32_t q = add_relaxed(&h->tile_next, 1u);
-    if (q >= (uint32_t)p.n_tiles) return NONE;
-    return ((uint32_t)p.rb_order[q / p.tiles_n] << 16) | (q % p.tiles_n);
-  }
-  const int x = blockIdx.x % NXCD;
-  for (int s = 0; s < NXCD; ++s) {
-    const int y = (x + s) % NXCD;
-    const uint32_t nq = (uint32_t)(p.xoff[y + 1] - p.xoff[y]) * p.tiles_n;
-    if (nq == 0 || ld_relaxed(xcd_head(h, y)) >= nq) continue;
-    const uint32_t q = add_relaxed(xcd_head(h, y), 1u);
-    if (q < nq) return ((uint32_t)p.xrb[p.xoff[y] + q / p.tiles_n] << 16) | (q % p.tiles_n);
-  }
-  return NONE;
-}
-
-// Thread 0: wait until units u0..u1 have landed.  Returns 1 when they have
-// (after an acquire), 2 + w when the workgroup should copy item w first
-// (work it would otherwise spend spinning), 0 on watchdog expiry / abort.
-__device__ inline uint32_t ag_wait_or_steal(const AgParams& p, WsHeader* h, int u0, int u1) {
-  const uint32_t n_work = (uint32_t)p.n_units * p.parts;
-  const bool steal = !(p.flags & MK_FLAG_NO_STEAL);
-  uint64_t t_begin = 0;
-  for (;;) {
-    bool ready = true;
-    for (int u = u0; u <= u1 && ready; ++u) ready = ld_relaxed(&p.unit_cnt[u]) >= (uint32_t)p.parts;
-    if (ready) {
-      fence_acquire();
-      return 1u;
-    }
-    if (steal && ld_relaxed(&h->copy_next) < n_work) {
-      const uint32_t w = add_relaxed(&h->copy_next, 1u);
-      if (w < n_work) return 2u + w;
-    }
-    if (ld_relaxed(&h->abort)) return 0u;
+  if (tid == 0) {
     const uint64_t now = now_ticks();
-    if (t_begin == 0) t_begin = now;
-    if (now - t_begin > p.spin_limit) {
-      st_relaxed(&h->status, ST_TIMEOUT);
-      st_relaxed(&h->abort, 1u);
-      return 0u;
+    const uint64_t old = atomicCAS((unsigned long long*)&h->t0, 0ull, (unsigned long long)now);
+    t0 = old ? old : now;
+  }
+  const uint32_t n_work = (uint32_t)p.n_units * p.parts;
+  const int cpr = p.K / 8;                         // 16-byte chunks per row
+  const int64_t n16 = (int64_t)p.part_rows * cpr;
+  for (;;) {
+    const uint32_t w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
+    if (w >= n_work) break;
+    const int j = w / p.parts, part = w % p.parts;
+    const int c = p.order[j];
+    if (c == p.withhold) continue;               // never delivered (failure tests)
+    if (tid == 0) wait_until(t0 + p.delay_ticks[c], p.spin_limit);
+    __syncthreads();
+    const int row0 = c * p.unit_rows + part * p.part_rows;
+    for (int64_t base = 0; base < n16; base += (int64_t)nt * COPY_UNROLL) {
+      u32x4 v[COPY_UNROLL];
+#pragma unroll
+      for (int u = 0; u < COPY_UNROLL; ++u) {
+        const int64_t i = base + (int64_t)u * nt + tid;
+        if (i < n16) {
+          const int row = row0 + (int)(i / cpr), c16 = (int)(i % cpr);
+          const u32x4* src = (const u32x4*)(p.shard[row / p.m_shard] + (int64_t)(row % p.m_shard) * p.K);
+          v[u] = src[c16];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < COPY_UNROLL; ++u) {
+        const int64_t i = base + (int64_t)u * nt + tid;
+        if (i < n16) {
+          const int row = row0 + (int)(i / cpr), c16 = (int)(i % cpr);
+          ((u32x4*)(p.Ag + (int64_t)row * p.K))[c16] = v[u];
+        }
+      }
     }
-    __builtin_amdgcn_s_sleep(1);
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      add_release(&p.unit_cnt[c], 1u);
+      add_release(&h->aux[0], 1u);                 // parts landed in total
+    }
   }
 }
 
-template <class G>
-__device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, u32x4* lds, uint32_t* sb) {
+template <class G, class SM>
+__device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, SM sm, uint32_t* sb) {
   const int tid = threadIdx.x;
   const uint32_t all_parts = (uint32_t)p.n_units * p.parts;
   bool all_landed = (p.mode == MODE_GEMM);
-  uint64_t t0 = 0;
   G g;
   for (;;) {
-    const uint32_t code = wg_bcast(tid == 0 ? ag_next_tile(p, h) : 0u, sb);
-    if (code == NONE) break;
-    const int tm = (int)(code >> 16), tn = (int)(code & 0xffffu);
+    const uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+    if (q >= (uint32_t)p.n_tiles) break;
+    const int tm = p.rb_order[q / p.tiles_n], tn = q % p.tiles_n;
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int u0 = m0 / p.unit_rows, u1 = (min(p.M, m0 + G::BM) - 1) / p.unit_rows;
-    bool ok = true;
-    while (!all_landed) {
-      uint32_t st = 0;
+    if (!all_landed) {
+      uint32_t ok = 1, all = 0;
       if (tid == 0) {
-        st = ag_wait_or_steal(p, h, u0, u1);
-        // Once every part has landed (and an acquire followed), no later
-        // tile of this workgroup needs to wait.
-        if (st == 1u && ld_relaxed(landed_total(h)) >= all_parts) {
+        for (int u = u0; u <= u1 && ok; ++u) ok = wait_geq(&p.unit_cnt[u], p.parts, h, p.spin_limit);
+        // Once every part has landed (and one acquire has been taken after
+        // that), no later tile of this workgroup needs to wait.
+        if (ok && ld_relaxed(&h->aux[0]) >= all_parts) {
           fence_acquire();
-          st = 3u << 30;
+          all = 1;
         }
-        if (st >= 2u && st < (3u << 30) && t0 == 0) t0 = shared_t0(h);
       }
-      st = wg_bcast(st, sb);
-      if (st == 1u) break;
-      if (st == (3u << 30)) {
-        all_landed = true;
-        break;
-      }
-      if (st == 0u) {
-        ok = false;
-        break;
-      }
-      ag_copy_item(p, h, st - 2u, t0);
+      const uint32_t v = wg_bcast(ok | (all << 1), sb);
+      if (!(v & 1u)) continue;
+      all_landed = (v >> 1) & 1u;
     }
-    if (!ok) continue;
     g.bind(p.Ag + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
-    g.run(lds);
+    g.run(sm);
     if (p.c_bf16) {
       uint16_t* C = (uint16_t*)p.C;
       g.for_each([&](int r, int c, float v) {
@@ -219,7 +143,7 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, 
       });
     }
     if (p.tile_log && tid == 0) {
-      int32_t* L = p.tile_log + 4 * ((int64_t)tm * p.tiles_n + tn);
+      int32_t* L = p.tile_log + 4 * (int64_t)q;
       L[0] = tm; L[1] = tn; L[2] = u0; L[3] = u1;
     }
   }
@@ -237,27 +161,37 @@ __device__ __forceinline__ void ag_finish(const AgParams& p, WsHeader* h, uint32
   last = wg_bcast(last, sb);
   if (!last) return;
   for (int i = threadIdx.x; i < p.n_units; i += blockDim.x) st_relaxed(&p.unit_cnt[i], 0u);
-  if (threadIdx.x < NXCD) st_relaxed(xcd_head(h, threadIdx.x), 0u);
   if (threadIdx.x == 0) {
     st_relaxed(&h->ticket, 0u);
     st_relaxed(&h->tile_next, 0u);
     st_relaxed(&h->copy_next, 0u);
     st_relaxed(&h->abort, 0u);
-    st_relaxed(landed_total(h), 0u);
+    st_relaxed(&h->aux[0], 0u);
     __hip_atomic_store(&h->t0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     st_relaxed(&h->done, 0u);
   }
 }
 
-template <class G>
-__global__ __launch_bounds__(G::NT) void ag_kernel(const AgParams p) {
-  __shared__ u32x4 lds[G::LDS_U4];
-  __shared__ uint32_t sb[2];
+template <class G, class SM>
+__device__ __forceinline__ void ag_body(const AgParams& p, SM sm, uint32_t* sb) {
   WsHeader* h = p.hdr;
   const uint32_t ticket = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->ticket, 1u) : 0u, sb);
   if (p.mode == MODE_COPY || (p.mode == MODE_FUSED && ticket < (uint32_t)p.n_copy)) ag_copy_role(p, h, sb);
-  if (p.mode != MODE_COPY) ag_compute_role<G>(p, h, lds, sb);
+  if (p.mode != MODE_COPY) ag_compute_role<G>(p, h, sm, sb);
   ag_finish(p, h, sb);
+}
+
+template <class G>
+__global__ __launch_bounds__(G::NT) void ag_kernel(const AgParams p) {
+  __shared__ uint32_t sb[2];
+  if constexpr (G::STAGES == 4) {
+    __shared__ u32x4 a0[G::SA_U4], a1[G::SA_U4], a2[G::SA_U4], a3[G::SA_U4];
+    __shared__ u32x4 b0[G::SB_U4], b1[G::SB_U4], b2[G::SB_U4], b3[G::SB_U4];
+    ag_body<G>(p, Smem4{{a0, a1, a2, a3}, {b0, b1, b2, b3}}, sb);
+  } else {
+    __shared__ u32x4 lds[G::LDS_U4];
+    ag_body<G>(p, Smem1{lds}, sb);
+  }
 }
 
 }  // namespace
@@ -285,14 +219,6 @@ static int run_ag(AgParams& p, const mk_launch& o, const mkh::Schedule& s, const
   }
   std::stable_sort(rb.begin(), rb.end(), [&](int a, int b) { return key[a] < key[b]; });
   for (int t = 0; t < p.tiles_m; ++t) p.rb_order[t] = (uint16_t)rb[t];
-  // Per-XCD queues: tile row t belongs to XCD t % 8; each list in landing order.
-  int n = 0;
-  for (int x = 0; x < NXCD; ++x) {
-    p.xoff[x] = (uint16_t)n;
-    for (int t = 0; t < p.tiles_m; ++t)
-      if (rb[t] % NXCD == x) p.xrb[n++] = (uint16_t)rb[t];
-  }
-  p.xoff[NXCD] = (uint16_t)n;
 
   int occ = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ag_kernel<G>, G::NT, 0);
@@ -369,14 +295,10 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   p.n_units = s.n_units;
   p.unit_rows = s.unit_rows;
   p.withhold = s.withhold;
-  p.flags = o.flags;
-  // Split each unit into parts of about 256 KiB so several copy workgroups
-  // share it; a part never crosses a shard boundary (it is one contiguous copy).
+  // Split each unit into parts of about 256 KiB so several copy workgroups share it.
   const int64_t row_bytes = K * 2;
-  int g = s.unit_rows, b = (int)m_shard;
-  while (b) { const int t = g % b; g = b; b = t; }   // gcd(unit_rows, m_shard)
-  int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(g, (256 << 10) / row_bytes));
-  while (g % part_rows) --part_rows;
+  int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(s.unit_rows, (256 << 10) / row_bytes));
+  while (s.unit_rows % part_rows) --part_rows;
   p.part_rows = part_rows;
   p.parts = s.unit_rows / part_rows;
   for (int j = 0; j < s.n_units; ++j) {
@@ -390,6 +312,9 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
     case TILE_128x128: return run_ag<TileGemm<128, 128, 2, 2>>(p, o, s, d, st);
     case TILE_256x128: return run_ag<TileGemm<256, 128, 2, 2>>(p, o, s, d, st);
     case TILE_128x256: return run_ag<TileGemm<128, 256, 2, 2>>(p, o, s, d, st);
+    case TILE_256x256_DMA:
+      if (!TileGemmD<256, 256>::supports_k((int)K)) return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
+      return run_ag<TileGemmD<256, 256>>(p, o, s, d, st);
     default: return fail(MK_ERR_INVALID, "tile id %d", tile);
   }
 }

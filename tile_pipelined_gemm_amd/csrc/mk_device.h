@@ -151,9 +151,15 @@ __device__ __forceinline__ const T* uni(const T* p) {
 // (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA blocks; K advances 64 at a
 // time.  Rows past `mrows`, columns past `ncols` and k past K read as zero,
 // so ragged edges need no special path (K and N are multiples of 8).
+// LDS handed to a tile engine: one array (register-staged engine) or four
+// stages of A and B as separate objects (direct-to-LDS engine).
+struct Smem1 { u32x4* lds; };
+struct Smem4 { u32x4* a[4]; u32x4* b[4]; };
+
 template <int BM_, int BN_, int WM_, int WN_>
 struct TileGemm {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 64;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 64, STAGES = 2;
+  static __host__ __device__ constexpr bool supports_k(int) { return true; }
   static constexpr int NT = 64 * WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
@@ -280,7 +286,8 @@ struct TileGemm {
   }
 
   // Full K loop for the bound tile.  Ends with a barrier so LDS may be reused.
-  __device__ __forceinline__ void run(u32x4* __restrict__ lds) {
+  __device__ __forceinline__ void run(Smem1 m) {
+    u32x4* __restrict__ lds = m.lds;
     zero_acc();
     const int nk = (K + BK - 1) / BK;
     load(0);

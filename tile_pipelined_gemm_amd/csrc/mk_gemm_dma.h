@@ -1,0 +1,238 @@
+// Direct-to-LDS variant of the block tile GEMM (gfx950).
+//
+// Operands go HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR staging)
+// through a 4-stage ring of 32-deep K slices.  A is stored [row][k] and read
+// with ds_read_b128; B stays row-major [k][n] in LDS and each MFMA B fragment
+// is assembled by two ds_read_b64_tr_b16 (the gfx950 LDS transpose read:
+// within each group of 16 lanes, lane i receives element i%4 of the 64-bit
+// rows addressed by lanes 4r + (i%16)/4, r = 0..3; pointing lane L at row
+// k0 + (L%16)/4, column nb + 4(L%4) therefore hands lane i the four k-values
+// of column nb + i%16).  Both layouts are XOR-swizzled in 16-byte units so the
+// fragment reads are free of bank conflicts; the swizzle is applied on the
+// global side of each copy, because every wave instruction fills 1 KiB of LDS
+// linearly.
+//
+// Pipeline, per K slice kt (stage kt%4):
+//   MFMAs of substep 0 (fragments read during the previous slice)
+//   wait for this wave's DMA of slice kt+1, barrier   (slice kt+1 visible to
+//        all waves; every wave is done reading stage kt-1)
+//   DMA of slice kt+3 into stage (kt+3)%4 == (kt-1)%4
+//   read substep-1 fragments of slice kt and substep-0 fragments of kt+1
+//   MFMAs of substep 1
+// The DMA is issued through inline asm so the compiler does not add its own
+// (conservative) waits on it; the explicit vmcnt waits and the barrier are
+// one asm statement with a memory clobber, so no LDS access moves across them.
+#pragma once
+
+#include "mk_device.h"
+
+namespace mk {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Buffer descriptor as four scalars: base, stride 0, num_records = bytes,
+// raw 32-bit data format.
+__device__ __forceinline__ u32x4 buf_desc(const void* p, uint32_t bytes) {
+  const uint64_t b = (uint64_t)p;
+  u32x4 d;
+  d[0] = uni((uint32_t)b);
+  d[1] = uni((uint32_t)(b >> 32)) & 0xffffu;
+  d[2] = uni(bytes);
+  d[3] = 0x00020000u;
+  return d;
+}
+
+// One 16-byte-per-lane DMA: lane i's 16 bytes land at LDS byte lds + 16*i.
+// M0 is saved and restored around it.
+__device__ __forceinline__ void dma16(u32x4 desc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(voff), "s"(desc), "s"(soff)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N == 0 || N == 8 || N == 16, "vmcnt");
+  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int BM_ = 256, int BN_ = 256>
+struct TileGemmD {
+  static constexpr int BM = BM_, BN = BN_, WM = 2, WN = 2, BK = 32, STAGES = 4;
+  static constexpr int NT = 256;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;   // per stage
+  static constexpr int A_INS = A_BYTES / 1024 / 4, B_INS = B_BYTES / 1024 / 4;  // DMA per wave per slice
+  static constexpr int SA_U4 = A_BYTES / 16, SB_U4 = B_BYTES / 16;
+  static constexpr int LDS_U4 = STAGES * (SA_U4 + SB_U4);
+  static_assert(A_INS + B_INS == 8, "the vmcnt immediates assume 8 DMA instructions per slice");
+  static_assert(BM == 256 && BN == 256, "fragment addressing assumes a 256x256 tile");
+
+  f32x16 acc[FM][FN];
+  u32x4 dA, dB;
+  uint32_t ldaB, ldbB, voA, voB;
+  int nk;
+
+  static __host__ __device__ constexpr bool supports_k(int K) { return K % (STAGES * BK) == 0; }
+
+  __device__ __forceinline__ void bind(const uint16_t* A, int64_t lda, int mrows, const uint16_t* B,
+                                       int64_t ldb, int ncols, const uint16_t* B_end, int K) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    ldaB = uni((uint32_t)(lda * 2));
+    ldbB = uni((uint32_t)(ldb * 2));
+    const int rows = mrows < BM ? mrows : BM;
+    dA = buf_desc(A, uni((uint32_t)(rows > 0 ? rows : 0) * ldaB));
+    dB = buf_desc(B, uni((uint32_t)((B_end - B) * 2)));
+    nk = uni(K) / BK;
+    // A: LDS unit p = blk*64 + lane holds tile row p/4 and physical chunk p%4,
+    // which is logical k-chunk (p%4) ^ ((row>>1)&3).
+    voA = (uint32_t)(lane >> 2) * ldaB + (uint32_t)((lane & 3) ^ ((lane >> 3) & 3)) * 16u;
+    // B: LDS unit p holds k-row p/32; physical chunk p%32 = logical ^ ((row&3)<<1).
+    const int brow = (2 * w + (lane >> 5)) & 3;
+    const int lchunk = (lane & 31) ^ (brow << 1);
+    voB = (lchunk * 8 < ncols) ? (uint32_t)(lane >> 5) * ldbB + (uint32_t)lchunk * 16u : OOB;
+  }
+
+  // DMA of K slice kt into stage buffers (sa, sb): each wave fills 4 KiB of
+  // A (16-row blocks) and 4 KiB of B (2-row blocks).
+  __device__ __forceinline__ void issue(u32x4* sa, u32x4* sb, int kt) {
+    const int w = uni((int)(threadIdx.x >> 6));   // wave index: the same in every lane
+    const uint32_t la = uni(lds_addr(sa)), lb = uni(lds_addr(sb));
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+      const int blk = i * 4 + w;
+      dma16(dA, uni(la + blk * 1024), voA, uni((uint32_t)(blk * 16) * ldaB + (uint32_t)(kt * BK * 2)));
+    }
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+      const int blk = i * 4 + w;
+      dma16(dB, uni(lb + blk * 1024), voB, uni((uint32_t)(kt * BK + blk * 2) * ldbB));
+    }
+  }
+
+  __device__ __forceinline__ void zero_acc() {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  }
+
+  // Per-lane fragment byte offsets inside a stage.
+  struct FragOfs { int a[2]; int b[2]; };
+  __device__ __forceinline__ FragOfs frag_offsets() const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w % WM, wn = w / WM;
+    const int hi = lane >> 5, g = lane >> 4, Lg = lane & 15;
+    FragOfs f;
+    const int arow = wm * TM + (lane & 31);
+    const int as = ((lane & 31) >> 1) & 3;
+    f.a[0] = arow * 64 + ((0 + hi) ^ as) * 16;
+    f.a[1] = arow * 64 + ((2 + hi) ^ as) * 16;
+    const int brow = (g >> 1) * 8 + (Lg >> 2);
+    const int sw = (Lg >> 2) << 1;
+    const int u = 2 * (g & 1) + ((Lg & 3) >> 1);
+    f.b[0] = brow * (BN * 2) + (wn * 16 + ((0 + u) ^ sw)) * 16 + (Lg & 1) * 8;   // even j
+    f.b[1] = brow * (BN * 2) + (wn * 16 + ((4 + u) ^ sw)) * 16 + (Lg & 1) * 8;   // odd j
+    return f;
+  }
+
+  __device__ __forceinline__ void read_frags(const u32x4* sa, const u32x4* sb, const FragOfs& f, int ks,
+                                             bf16x8 (&af)[FM], bf16x8 (&bfr)[FN]) const {
+    const char* pa = (const char*)sa;
+    const char* pb = (const char*)sb;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pa + f.a[ks] + i * 32 * 64));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int base = f.b[j & 1] + (j >> 1) * 128 + ks * 16 * (BN * 2);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pb + base));
+      const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pb + base + 4 * (BN * 2)));
+      bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+
+  __device__ __forceinline__ void mfmas(const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+
+  // One K slice.  f0/b0 hold substep-0 fragments of slice kt on entry and
+  // substep-0 fragments of slice kt+1 on exit.
+  __device__ __forceinline__ void step(int kt, const FragOfs& fo, const u32x4* sa, const u32x4* sb,
+                                       const u32x4* na, const u32x4* nb, u32x4* fa, u32x4* fb,
+                                       bf16x8 (&a0)[FM], bf16x8 (&b0)[FN]) {
+    bf16x8 a1[FM], b1[FN];
+    read_frags(sa, sb, fo, 1, a1, b1);
+    mfmas(a0, b0);
+    const int later = nk - 2 - kt;          // slices after kt+1 already in flight (0..1)
+    if (kt + 1 < nk) {
+      if (later >= 1) wait_vm_barrier<8>();
+      else wait_vm_barrier<0>();
+      if (kt + 3 < nk) issue(fa, fb, kt + 3);
+      read_frags(na, nb, fo, 0, a0, b0);
+    }
+    mfmas(a1, b1);
+  }
+
+  // Full K loop; the four stages are distinct LDS objects.
+  __device__ __forceinline__ void run(Smem4 m) {
+    u32x4 *A0 = m.a[0], *A1 = m.a[1], *A2 = m.a[2], *A3 = m.a[3];
+    u32x4 *B0 = m.b[0], *B1 = m.b[1], *B2 = m.b[2], *B3 = m.b[3];
+    const FragOfs fo = frag_offsets();
+    zero_acc();
+    issue(A0, B0, 0);
+    if (nk > 1) issue(A1, B1, 1);
+    if (nk > 2) issue(A2, B2, 2);
+    // slice 0 must be visible before its first fragments are read
+    if (nk > 2) wait_vm_barrier<16>();
+    else if (nk > 1) wait_vm_barrier<8>();
+    else wait_vm_barrier<0>();
+    bf16x8 a0[FM], b0[FN];
+    read_frags(A0, B0, fo, 0, a0, b0);
+    for (int kt = 0; kt < nk; kt += 4) {
+      step(kt + 0, fo, A0, B0, A1, B1, A3, B3, a0, b0);
+      step(kt + 1, fo, A1, B1, A2, B2, A0, B0, a0, b0);
+      step(kt + 2, fo, A2, B2, A3, B3, A1, B1, a0, b0);
+      step(kt + 3, fo, A3, B3, A0, B0, A2, B2, a0, b0);
+    }
+    __syncthreads();                        // LDS free for the next tile
+  }
+
+  template <class Fn>
+  __device__ __forceinline__ void for_each(Fn&& f) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w % WM, wn = w / WM;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = wn * TN + j * 32 + (lane & 31);
+          f(row, col, acc[i][j][r]);
+        }
+  }
+};
+
+}  // namespace mk

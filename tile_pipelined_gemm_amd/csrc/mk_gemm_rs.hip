@@ -97,7 +97,7 @@ __device__ __forceinline__ void reduce_tile(const RsParams& p, int t) {
 }
 
 template <class G>
-__device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, u32x4* lds, uint32_t* sb) {
+__device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, Smem1 sm, uint32_t* sb) {
   const int tid = threadIdx.x;
   G g;
   for (;;) {
@@ -107,7 +107,7 @@ __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, 
     const int tm = t / p.tiles_n, tn = t % p.tiles_n;
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     g.bind(p.A + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
-    g.run(lds);
+    g.run(sm);
     // Stage the fp32 tile (in the owner block for fp32 output, else in the
     // workspace staging area).
     float* __restrict__ S = p.stage ? p.stage + (int64_t)m0 * p.N
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(G::NT) void rs_kernel(const RsParams p) {
   WsHeader* h = p.hdr;
   const uint32_t ticket = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->ticket, 1u) : 0u, sb);
   const bool reducer = p.mode == MODE_REDUCE || (p.mode == MODE_ROLES && ticket >= (uint32_t)p.n_compute);
-  if (!reducer) rs_compute_role<G>(p, h, lds, sb);
+  if (!reducer) rs_compute_role<G>(p, h, Smem1{lds}, sb);
   if (p.mode == MODE_ROLES || p.mode == MODE_REDUCE) rs_reduce_role<G>(p, h, sb);
   rs_finish(p, h, sb);
 }

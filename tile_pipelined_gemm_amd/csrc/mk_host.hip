@@ -165,6 +165,6 @@ extern "C" int mk_version(void) { return 1; }
 #include "mk_tiles.h"
 
 extern "C" const char* mk_tile_name(int id) {
-  static const char* names[TILE_COUNT] = {"auto", "256x256", "128x128", "256x128", "128x256"};
+  static const char* names[TILE_COUNT] = {"auto", "256x256", "128x128", "256x128", "128x256", "256x256dma"};
   return (id >= 0 && id < TILE_COUNT) ? names[id] : nullptr;
 }

@@ -256,7 +256,7 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
 }
 
 template <class G>
-__device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h, u32x4* lds, uint32_t* sb) {
+__device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h, Smem1 sm, uint32_t* sb) {
   const int tid = threadIdx.x;
   const int n_mt = p.tile_base[p.L];
   const uint32_t n_tiles = (uint32_t)n_mt * p.tiles_n;
@@ -280,7 +280,7 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
     const int q0 = p.offsets[e] - base_local + r0;              // landing row of the tile
     const int n0 = tn * G::BN;
     g.bind(p.Xs + (int64_t)q0 * p.H, p.H, rows, p.W[l] + n0, p.F, p.F - n0, p.W[l] + (int64_t)p.H * p.F, p.H);
-    g.run(lds);
+    g.run(sm);
     if (p.y_bf16) {
       uint16_t* Y = (uint16_t*)p.Y;
       g.for_each([&](int r, int c, float v) {
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(G::NT) void moe_kernel(const MoeParams p) {
   WsHeader* h = p.hdr;
   const uint32_t ticket = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->ticket, 1u) : 0u, sb);
   if (p.mode == MODE_COPY || (p.mode == MODE_FUSED && ticket < (uint32_t)p.n_copy)) moe_copy_role(p, h, sb, G::BM);
-  if (p.mode != MODE_COPY) moe_compute_role<G>(p, h, lds, sb);
+  if (p.mode != MODE_COPY) moe_compute_role<G>(p, h, Smem1{lds}, sb);
   moe_finish(p, h, sb);
 }
 

@@ -9,6 +9,7 @@ enum MkTile {
   TILE_128x128 = 2,  // 4 waves, 64x64 per wave: small or ragged problems
   TILE_256x128 = 3,  // 4 waves, 128x64 per wave
   TILE_128x256 = 4,  // 4 waves, 64x128 per wave
+  TILE_256x256_DMA = 5,  // 256x256, direct-to-LDS operand loads, 4-stage ring (K % 128 == 0)
   TILE_COUNT
 };
 

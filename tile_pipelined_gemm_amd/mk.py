@@ -19,7 +19,7 @@ MK_BF16, MK_F32 = 0, 1
 MK_OK, MK_ERR_INVALID, MK_ERR_UNSUPPORTED, MK_ERR_WORKSPACE, MK_ERR_HIP, MK_ERR_TIMEOUT, MK_ERR_SCHEDULE = \
     0, -1, -2, -3, -4, -5, -6
 MK_MAX_UNITS = 256
-MK_FLAG_GLOBAL_QUEUE, MK_FLAG_NO_STEAL = 1, 2
+TILE_256x256, TILE_128x128, TILE_256x128, TILE_128x256, TILE_256x256_DMA = 1, 2, 3, 4, 5
 
 # Symbols declared in include/mk.h (checked by the CPU tests).
 EXPORTS = [
@@ -43,7 +43,7 @@ class mk_arrival(C.Structure):
 class mk_launch(C.Structure):
     _fields_ = [("mode", C.c_int32), ("grid", C.c_int32), ("n_copy", C.c_int32),
                 ("n_reduce", C.c_int32), ("tile", C.c_int32), ("spin_limit_us", C.c_uint32),
-                ("tile_log", C.c_void_p), ("flags", C.c_int32), ("reserved", C.c_int32 * 3)]
+                ("tile_log", C.c_void_p), ("reserved", C.c_int32 * 4)]
 
 
 _lib = None
@@ -144,8 +144,8 @@ def make_arrival(order=None, delay_ns=None, unit_rows=0, withhold=-1):
     return a, (o, d)
 
 
-def make_launch(mode=0, grid=0, n_copy=0, n_reduce=0, tile=0, spin_limit_us=0, tile_log=None, flags=0):
-    return mk_launch(mode, grid, n_copy, n_reduce, tile, spin_limit_us, _ptr(tile_log), flags, (C.c_int32 * 3)())
+def make_launch(mode=0, grid=0, n_copy=0, n_reduce=0, tile=0, spin_limit_us=0, tile_log=None):
+    return mk_launch(mode, grid, n_copy, n_reduce, tile, spin_limit_us, _ptr(tile_log), (C.c_int32 * 4)())
 
 
 # ---------------------------------------------------------------- entry points
