@@ -94,9 +94,10 @@ def bench_ag(name, args, stream, extra=True):
         r["unfused_ms"] = uk
         r["speedup_vs_unfused"] = uk / kern
         # role split and scheduling variants of the fused kernel
-        for tag, kw in [("n_copy16", dict(n_copy=16)), ("n_copy128", dict(n_copy=128)),
-                        ("tile_dma", dict(tile=mk.TILE_256x256_DMA)),
-                        ("tile_dma_n_copy16", dict(tile=mk.TILE_256x256_DMA, n_copy=16))]:
+        for tag, kw in [("n_copy32", dict(n_copy=32)), ("n_copy128", dict(n_copy=128)),
+                        ("n_copy256", dict(n_copy=256)),
+                        ("tile_reg", dict(tile=mk.TILE_256x256)),
+                        ("unfused_tile_reg", dict(mode=1, tile=mk.TILE_256x256))]:
             lv = mk.make_launch(**kw)
             _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 5, 2, stream)
             r[f"variant_{tag}_ms"] = vk

@@ -49,7 +49,7 @@ struct AgParams {
   uint32_t delay_ticks[MK_MAX_UNITS];
 };
 
-constexpr int COPY_UNROLL = 8;
+constexpr int COPY_UNROLL = 16;   // 16-byte loads in flight per thread (64 KiB per workgroup)
 
 __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uint32_t* sb) {
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -60,8 +60,7 @@ __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uin
     t0 = old ? old : now;
   }
   const uint32_t n_work = (uint32_t)p.n_units * p.parts;
-  const int cpr = p.K / 8;                         // 16-byte chunks per row
-  const int64_t n16 = (int64_t)p.part_rows * cpr;
+  const int n16 = p.part_rows * (p.K / 8);       // 16-byte chunks per part
   for (;;) {
     const uint32_t w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
     if (w >= n_work) break;
@@ -70,25 +69,22 @@ __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uin
     if (c == p.withhold) continue;               // never delivered (failure tests)
     if (tid == 0) wait_until(t0 + p.delay_ticks[c], p.spin_limit);
     __syncthreads();
+    // A part lies inside one shard, so it is one contiguous block on both sides.
     const int row0 = c * p.unit_rows + part * p.part_rows;
-    for (int64_t base = 0; base < n16; base += (int64_t)nt * COPY_UNROLL) {
+    const u32x4* __restrict__ src =
+        (const u32x4*)(p.shard[row0 / p.m_shard] + (int64_t)(row0 % p.m_shard) * p.K);
+    u32x4* __restrict__ dst = (u32x4*)(p.Ag + (int64_t)row0 * p.K);
+    for (int base = 0; base < n16; base += nt * COPY_UNROLL) {
       u32x4 v[COPY_UNROLL];
 #pragma unroll
       for (int u = 0; u < COPY_UNROLL; ++u) {
-        const int64_t i = base + (int64_t)u * nt + tid;
-        if (i < n16) {
-          const int row = row0 + (int)(i / cpr), c16 = (int)(i % cpr);
-          const u32x4* src = (const u32x4*)(p.shard[row / p.m_shard] + (int64_t)(row % p.m_shard) * p.K);
-          v[u] = src[c16];
-        }
+        const int i = base + u * nt + tid;
+        if (i < n16) v[u] = src[i];
       }
 #pragma unroll
       for (int u = 0; u < COPY_UNROLL; ++u) {
-        const int64_t i = base + (int64_t)u * nt + tid;
-        if (i < n16) {
-          const int row = row0 + (int)(i / cpr), c16 = (int)(i % cpr);
-          ((u32x4*)(p.Ag + (int64_t)row * p.K))[c16] = v[u];
-        }
+        const int i = base + u * nt + tid;
+        if (i < n16) dst[i] = v[u];
       }
     }
     __threadfence();
@@ -295,10 +291,13 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   p.n_units = s.n_units;
   p.unit_rows = s.unit_rows;
   p.withhold = s.withhold;
-  // Split each unit into parts of about 256 KiB so several copy workgroups share it.
+  // Split each unit into parts of about 256 KiB so several copy workgroups
+  // share it; a part never crosses a shard boundary (one contiguous copy).
   const int64_t row_bytes = K * 2;
-  int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(s.unit_rows, (256 << 10) / row_bytes));
-  while (s.unit_rows % part_rows) --part_rows;
+  int g = s.unit_rows, b = (int)m_shard;
+  while (b) { const int t = g % b; g = b; b = t; }   // gcd(unit_rows, m_shard)
+  int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(g, (256 << 10) / row_bytes));
+  while (g % part_rows) --part_rows;
   p.part_rows = part_rows;
   p.parts = s.unit_rows / part_rows;
   for (int j = 0; j < s.n_units; ++j) {
@@ -306,7 +305,8 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
     p.delay_ticks[j] = (uint32_t)mkh::ns_to_ticks(s.delay_ns[j], d->wall_khz);
   }
   const hipStream_t st = (hipStream_t)stream;
-  const int tile = o.tile ? o.tile : mk_default_tile(M, N, K);
+  int tile = o.tile ? o.tile : mk_default_tile(M, N, K);
+  if (!o.tile && tile == TILE_256x256 && TileGemmD<256, 256>::supports_k((int)K)) tile = TILE_256x256_DMA;
   switch (tile) {
     case TILE_256x256: return run_ag<TileGemm<256, 256, 2, 2>>(p, o, s, d, st);
     case TILE_128x128: return run_ag<TileGemm<128, 128, 2, 2>>(p, o, s, d, st);
