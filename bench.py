@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the unfused and library yardsticks")
     ap.add_argument("--copies", type=int, default=0, help="rotated input copies (0 = auto)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--ag-launch", default="",
+                    help="launch options for the primary AG timing, e.g. mode=1,tile=5,n_copy=64,copy_kib=256")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -75,8 +77,11 @@ def bench_ag(name, args, stream, extra=True):
     # algorithmic bytes: gather (read+write A), GEMM reads A and B once, writes C once
     abytes = 2 * w.M * w.K * 2 + w.M * w.K * 2 + w.K * w.N * 2 + w.M * w.N * (2 if w.out_dtype == "bf16" else 4)
 
+    opts = dict(kv.split("=") for kv in args.ag_launch.split(",") if kv) if name == "ag" else {}
+    lau0 = mk.make_launch(**{k: int(v) for k, v in opts.items()})
+
     def fused(i):
-        probs[i % copies].run(stream=stream, check=False)
+        probs[i % copies].run(launch=lau0, stream=stream, check=False)
 
     wall, kern = timed(fused, args.steps, args.warmup, stream)
     for p in probs:
@@ -94,10 +99,10 @@ def bench_ag(name, args, stream, extra=True):
         r["unfused_ms"] = uk
         r["speedup_vs_unfused"] = uk / kern
         # role split and scheduling variants of the fused kernel
-        for tag, kw in [("n_copy32", dict(n_copy=32)), ("n_copy128", dict(n_copy=128)),
-                        ("n_copy256", dict(n_copy=256)),
-                        ("tile_reg", dict(tile=mk.TILE_256x256)),
-                        ("unfused_tile_reg", dict(mode=1, tile=mk.TILE_256x256))]:
+        for tag, kw in [("n_copy64", dict(n_copy=64)), ("copy_kib256", dict(copy_kib=256)),
+                        ("copy_kib512", dict(copy_kib=512)), ("copy_kib1024", dict(copy_kib=1024)),
+                        ("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
+                        ("tile_reg", dict(tile=mk.TILE_256x256))]:
             lv = mk.make_launch(**kw)
             _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 5, 2, stream)
             r[f"variant_{tag}_ms"] = vk

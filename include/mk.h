@@ -89,7 +89,10 @@ typedef struct mk_arrival {
 /* Launch options.  A zero-filled struct (or NULL) selects per-shape defaults. */
 typedef struct mk_launch {
   int32_t mode;           /* 0 fused persistent kernel; 1 unfused baseline:
-                             the same steps as separate kernels in stream order */
+                             the same steps as separate kernels in stream order;
+                             AG only, for measurement: 2 = the baseline's copy
+                             kernel alone, 3 = its GEMM kernel alone (reads
+                             a_gathered as it is) */
   int32_t grid;           /* persistent workgroups; 0 = CUs x occupancy */
   int32_t n_copy;         /* copy-role workgroups (AG, MoE); 0 = default */
   int32_t n_reduce;       /* GEMM+RS: reduce-role workgroups; 0 = default;
@@ -97,7 +100,9 @@ typedef struct mk_launch {
   int32_t tile;           /* tile configuration id; 0 = default (see mk_tile_name) */
   uint32_t spin_limit_us; /* watchdog for every wait; 0 = 2,000,000 us */
   int32_t* tile_log;      /* device int32 or NULL: per-tile record, see each op */
-  int32_t reserved[4];     /* must be zero */
+  int32_t copy_kib;       /* AG: bytes per copy work item in KiB (one release each);
+                             0 = 2048; rounded to whole rows inside one unit and shard */
+  int32_t reserved[3];    /* must be zero */
 } mk_launch;
 
 /* ---------------------------------------------------------------------------

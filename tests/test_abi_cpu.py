@@ -74,7 +74,9 @@ def test_ag_too_many_units(lib):
 
 
 def test_ag_bad_launch_options(lib):
-    lau = mk.make_launch(mode=3)
+    lau = mk.make_launch(mode=4)
+    assert _ag(lib, launch=C.byref(lau)) == mk.MK_ERR_INVALID
+    lau = mk.make_launch(copy_kib=-1)
     assert _ag(lib, launch=C.byref(lau)) == mk.MK_ERR_INVALID
     lau = mk.make_launch(tile=42)
     rc = _ag(lib, launch=C.byref(lau))

@@ -64,6 +64,8 @@ def test_output_independent_of_schedule_and_roles(gpu):
             dict(order=w.order, delay_ns=w.delay_ns),
             dict(order=w.order, launch=gpu.make_launch(n_copy=1)),
             dict(order=w.order, launch=gpu.make_launch(n_copy=64, grid=80)),
+            dict(order=w.order, delay_ns=w.delay_ns, launch=gpu.make_launch(copy_kib=16)),
+            dict(order=w.order, delay_ns=w.delay_ns, launch=gpu.make_launch(copy_kib=4096, n_copy=3)),
             dict(launch=gpu.make_launch(mode=1))]
     outs = []
     for kw in runs:
@@ -75,6 +77,24 @@ def test_output_independent_of_schedule_and_roles(gpu):
         outs.append(prob.output())
     for i, o in enumerate(outs[1:], 1):
         assert np.array_equal(outs[0], o), f"run {i} differs"
+
+
+def test_copy_only_then_gemm_only_equals_fused(gpu):
+    from tile_pipelined_gemm_amd.harness import AgProblem, to_numpy
+    w = wl.make_ag(4, 128, 512, 384, seed=16, unit_rows=64, max_delay_ns=2000)
+    prob = AgProblem(w)
+    prob.run()
+    torch.cuda.synchronize()
+    fused = prob.output().copy()
+    prob.Ag.fill_(float("nan"))
+    prob.C.zero_()
+    prob.run(launch=gpu.make_launch(mode=2))           # the baseline's copy kernel alone
+    torch.cuda.synchronize()
+    assert np.array_equal(to_numpy(prob.Ag), og.gather(w.shards))
+    prob.run(launch=gpu.make_launch(mode=3))           # its GEMM kernel alone
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+    assert np.array_equal(prob.output(), fused)
 
 
 def test_tile_log_records_chunk_dependencies(gpu):

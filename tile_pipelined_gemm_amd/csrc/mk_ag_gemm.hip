@@ -224,19 +224,25 @@ static int run_ag(AgParams& p, const mk_launch& o, const mkh::Schedule& s, const
   const int grid = o.grid > 0 ? std::min(o.grid, full) : full;
   const uint32_t n_work = (uint32_t)p.n_units * p.parts;
 
-  if (o.mode == 1) {   // unfused baseline: copy kernel, then GEMM kernel
-    p.mode = MODE_COPY;
-    p.n_copy = grid;
-    hipLaunchKernelGGL(ag_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
-    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "copy kernel launch");
-    p.mode = MODE_GEMM;
-    p.n_copy = 0;
-    hipLaunchKernelGGL(ag_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
-    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "gemm kernel launch");
+  if (o.mode >= 1) {   // unfused baseline: copy kernel, then GEMM kernel (modes 2/3: one of them)
+    if (o.mode != 3) {
+      p.mode = MODE_COPY;
+      p.n_copy = grid;
+      hipLaunchKernelGGL(ag_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+      if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "copy kernel launch");
+    }
+    if (o.mode != 2) {
+      p.mode = MODE_GEMM;
+      p.n_copy = 0;
+      hipLaunchKernelGGL(ag_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+      if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "gemm kernel launch");
+    }
     return MK_OK;
   }
   p.mode = MODE_FUSED;
-  int n_copy = o.n_copy > 0 ? o.n_copy : std::max(1, grid / 4);
+  // Default split: every workgroup starts as a copy workgroup while copy work
+  // remains (the copy is short and bandwidth-bound), then computes.
+  int n_copy = o.n_copy > 0 ? o.n_copy : grid;
   n_copy = std::min<int>(n_copy, (int)std::min<uint32_t>(n_work, (uint32_t)grid));
   p.n_copy = n_copy;
   hipLaunchKernelGGL(ag_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
@@ -271,8 +277,8 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
     return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes,
                 mk_ag_gemm_workspace(R, m_shard, K, N, s.unit_rows));
   const mk_launch o = mkh::launch_opts(launch);
-  if (o.mode != 0 && o.mode != 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
-  if (o.grid < 0 || o.n_copy < 0) return fail(MK_ERR_INVALID, "negative grid or n_copy");
+  if (o.mode < 0 || o.mode > 3) return fail(MK_ERR_INVALID, "mode %d", o.mode);
+  if (o.grid < 0 || o.n_copy < 0 || o.copy_kib < 0) return fail(MK_ERR_INVALID, "negative grid, n_copy or copy_kib");
   const mkh::DevInfo* d = mkh::dev_info();
   if (!d) return MK_ERR_HIP;
 
@@ -291,12 +297,15 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   p.n_units = s.n_units;
   p.unit_rows = s.unit_rows;
   p.withhold = s.withhold;
-  // Split each unit into parts of about 256 KiB so several copy workgroups
-  // share it; a part never crosses a shard boundary (one contiguous copy).
+  // Copy work items ("parts") of about copy_kib KiB: each is published with
+  // one release, which writes back the XCD's L2, so fewer larger items cost
+  // fewer write-backs.  A part never crosses a unit or shard boundary (one
+  // contiguous copy).
   const int64_t row_bytes = K * 2;
   int g = s.unit_rows, b = (int)m_shard;
   while (b) { const int t = g % b; g = b; b = t; }   // gcd(unit_rows, m_shard)
-  int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(g, (256 << 10) / row_bytes));
+  const int64_t item_bytes = (int64_t)(o.copy_kib > 0 ? o.copy_kib : 2048) << 10;
+  int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(g, item_bytes / row_bytes));
   while (g % part_rows) --part_rows;
   p.part_rows = part_rows;
   p.parts = s.unit_rows / part_rows;

@@ -43,7 +43,7 @@ class mk_arrival(C.Structure):
 class mk_launch(C.Structure):
     _fields_ = [("mode", C.c_int32), ("grid", C.c_int32), ("n_copy", C.c_int32),
                 ("n_reduce", C.c_int32), ("tile", C.c_int32), ("spin_limit_us", C.c_uint32),
-                ("tile_log", C.c_void_p), ("reserved", C.c_int32 * 4)]
+                ("tile_log", C.c_void_p), ("copy_kib", C.c_int32), ("reserved", C.c_int32 * 3)]
 
 
 _lib = None
@@ -144,8 +144,9 @@ def make_arrival(order=None, delay_ns=None, unit_rows=0, withhold=-1):
     return a, (o, d)
 
 
-def make_launch(mode=0, grid=0, n_copy=0, n_reduce=0, tile=0, spin_limit_us=0, tile_log=None):
-    return mk_launch(mode, grid, n_copy, n_reduce, tile, spin_limit_us, _ptr(tile_log), (C.c_int32 * 4)())
+def make_launch(mode=0, grid=0, n_copy=0, n_reduce=0, tile=0, spin_limit_us=0, tile_log=None, copy_kib=0):
+    return mk_launch(mode, grid, n_copy, n_reduce, tile, spin_limit_us, _ptr(tile_log), copy_kib,
+                     (C.c_int32 * 3)())
 
 
 # ---------------------------------------------------------------- entry points
