@@ -29,6 +29,33 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+AG_KERNEL_SOURCES = ["mk_ag_gemm.hip", "mk_device.h", "mk_gemm_dma.h", "mk_host.h", "mk_host.hip", "mk_tiles.h"]
+AG_COUNTERS = os.path.join(ROOT, "profiles", "ag_gemm_8192x8192x3584_counters.md")
+
+
+def counter_traffic(sources, summary, csrc=os.path.join(ROOT, "tile_pipelined_gemm_amd", "csrc")):
+    """HBM bytes per launch from a committed rocprofv3 counter summary:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) times the factors a plain copy
+    of known size gave.  None unless the kernel sources still hash to the
+    value the counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    try:
+        with open(summary) as fh:
+            kv = dict(ln.split(":", 1) for ln in fh.read().splitlines()
+                      if ":" in ln and ln.split(":", 1)[0] in
+                      ("source-sha256", "fetch-scale", "write-scale", "FETCH_SIZE_KiB", "WRITE_SIZE_KiB"))
+    except OSError:
+        return None
+    if len(kv) != 5 or kv["source-sha256"].strip() != h.hexdigest():
+        return None
+    return int(1024 * (float(kv["FETCH_SIZE_KiB"]) * float(kv["fetch-scale"]) +
+                       float(kv["WRITE_SIZE_KiB"]) * float(kv["write-scale"])))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,7 +236,7 @@ def cpu_baseline(seed):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the kernels compute one GPU share and there is no multi-GPU launcher.",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -252,6 +279,9 @@ def main():
     if primary is None:
         primary = next(iter(configs.values()))
     value = primary["flops"] / primary["ms"] / 1e9
+    # counters were taken on the default launch of the AG workload only
+    traffic = counter_traffic(AG_KERNEL_SOURCES, AG_COUNTERS) \
+        if primary is configs.get("ag") and not args.ag_launch else None
     out = {
         "metric": "fused AG+GEMM / GEMM+RS TFLOP/s at 1 MI355X; % of bf16 MFMA peak",
         "value": round(value, 2),
@@ -271,7 +301,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(primary["flops"] / primary["kernel_ms"] / 1e9, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(primary["flops"] / primary["kernel_ms"] / 1e9 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic},
         "cpu_baseline": cpu,
         "configs": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in configs.items()},

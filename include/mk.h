@@ -51,14 +51,14 @@ typedef enum mk_dtype { MK_BF16 = 0, MK_F32 = 1 } mk_dtype;
 typedef enum mk_status {
   MK_OK = 0,
   MK_ERR_INVALID = -1,      /* bad pointer, shape, dtype or option */
-  MK_ERR_UNSUPPORTED = -2,  /* valid request outside this build's limits */
+  MK_ERR_UNSUPPORTED = -2,  /* valid request outside this library's limits */
   MK_ERR_WORKSPACE = -3,    /* workspace missing or too small */
   MK_ERR_HIP = -4,          /* a HIP runtime call failed */
   MK_ERR_TIMEOUT = -5,      /* a kernel wait exceeded its watchdog */
   MK_ERR_SCHEDULE = -6      /* arrival schedule is not a permutation / bad delays */
 } mk_status;
 
-/* Limits of this build. */
+/* Limits of this library. */
 #define MK_MAX_RANKS 64     /* R: shards, partial-sum contributors, owners */
 #define MK_MAX_UNITS 256    /* delivery units in one schedule */
 #define MK_MAX_EXPERTS 1024 /* E */
@@ -101,7 +101,7 @@ typedef struct mk_launch {
   uint32_t spin_limit_us; /* watchdog for every wait; 0 = 2,000,000 us */
   int32_t* tile_log;      /* device int32 or NULL: per-tile record, see each op */
   int32_t copy_kib;       /* AG: bytes per copy work item in KiB (one release each);
-                             0 = 2048; rounded to whole rows inside one unit and shard */
+                             0 = 1024; rounded to whole rows inside one unit and shard */
   int32_t reserved[3];    /* must be zero */
 } mk_launch;
 

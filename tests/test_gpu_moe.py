@@ -71,7 +71,8 @@ def test_schedule_roles_and_baseline_bitwise_identical(gpu):
     outs = []
     for kw in [dict(), dict(order=np.arange(nb)[::-1].copy()), dict(delay_ns=np.full(nb, 5000)),
                dict(launch=gpu.make_launch(n_copy=1)), dict(launch=gpu.make_launch(mode=1)),
-               dict(launch=gpu.make_launch(tile=2))]:
+               dict(launch=gpu.make_launch(tile=2)), dict(launch=gpu.make_launch(tile=gpu.TILE_256x256)),
+               dict(launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA))]:
         prob.Xs.fill_(float("nan"))
         prob.Y.zero_()
         prob.run(**kw)
@@ -81,6 +82,24 @@ def test_schedule_roles_and_baseline_bitwise_identical(gpu):
         outs.append(np.concatenate([o["perm"].view(np.uint32), o["Y"].ravel().astype(np.uint32)]))
     for i, o in enumerate(outs[1:], 1):
         assert np.array_equal(outs[0], o), f"variant {i} differs"
+
+
+def test_dma_tile_ragged_experts_integer_exact(gpu):
+    # H = 384 (a multiple of 128) takes the direct-to-LDS engine; F = 200 is ragged
+    # in N and the per-expert row counts are ragged in M.
+    w = wl.make_moe(600, 384, 24, 3, 12, 200, seed=36, dist="int", block_tokens=64, out_dtype="f32",
+                    expert_begin=6)
+    prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA))
+    ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 6, "f32")
+    got = _check_exact(prob, ref)
+    assert np.array_equal(got["Y"], ref["Y"])
+
+
+def test_dma_tile_rejects_h_not_multiple_of_128(gpu):
+    from tile_pipelined_gemm_amd.harness import MoeProblem
+    w = wl.make_moe(128, 136, 16, 2, 8, 64, seed=37, block_tokens=64)
+    prob = MoeProblem(w)
+    assert prob.run(launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA), check=False) == gpu.MK_ERR_UNSUPPORTED
 
 
 def test_withheld_block_times_out(gpu):

@@ -304,7 +304,7 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   const int64_t row_bytes = K * 2;
   int g = s.unit_rows, b = (int)m_shard;
   while (b) { const int t = g % b; g = b; b = t; }   // gcd(unit_rows, m_shard)
-  const int64_t item_bytes = (int64_t)(o.copy_kib > 0 ? o.copy_kib : 2048) << 10;
+  const int64_t item_bytes = (int64_t)(o.copy_kib > 0 ? o.copy_kib : 1024) << 10;
   int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(g, item_bytes / row_bytes));
   while (g % part_rows) --part_rows;
   p.part_rows = part_rows;

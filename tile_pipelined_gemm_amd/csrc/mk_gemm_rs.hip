@@ -200,7 +200,7 @@ __global__ __launch_bounds__(G::NT) void rs_kernel(const RsParams p) {
 
 // GEMM+RS runs with the 128x128 tile (two workgroups per CU, so one can stream
 // its reduction while the other runs MFMAs).  The larger tiles are not enabled
-// for this operation in this build: a 256x256 run with dedicated reducers did
+// for this operation: a 256x256 run with dedicated reducers did
 // not finish, and its cause is not yet established.
 inline int rs_tile(int64_t, int64_t, int64_t, int) { return TILE_128x128; }
 inline bool rs_tile_enabled(int t) { return t == TILE_128x128; }

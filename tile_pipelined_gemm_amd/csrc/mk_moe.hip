@@ -26,6 +26,7 @@
 #include <algorithm>
 
 #include "mk_device.h"
+#include "mk_gemm_dma.h"
 #include "mk_host.h"
 #include "mk_tiles.h"
 
@@ -255,8 +256,8 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
   }
 }
 
-template <class G>
-__device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h, Smem1 sm, uint32_t* sb) {
+template <class G, class SM>
+__device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h, SM sm, uint32_t* sb) {
   const int tid = threadIdx.x;
   const int n_mt = p.tile_base[p.L];
   const uint32_t n_tiles = (uint32_t)n_mt * p.tiles_n;
@@ -322,15 +323,26 @@ __device__ __forceinline__ void moe_finish(const MoeParams& p, WsHeader* h, uint
   }
 }
 
-template <class G>
-__global__ __launch_bounds__(G::NT) void moe_kernel(const MoeParams p) {
-  __shared__ u32x4 lds[G::LDS_U4];
-  __shared__ uint32_t sb[2];
+template <class G, class SM>
+__device__ __forceinline__ void moe_body(const MoeParams& p, SM sm, uint32_t* sb) {
   WsHeader* h = p.hdr;
   const uint32_t ticket = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->ticket, 1u) : 0u, sb);
   if (p.mode == MODE_COPY || (p.mode == MODE_FUSED && ticket < (uint32_t)p.n_copy)) moe_copy_role(p, h, sb, G::BM);
-  if (p.mode != MODE_COPY) moe_compute_role<G>(p, h, Smem1{lds}, sb);
+  if (p.mode != MODE_COPY) moe_compute_role<G>(p, h, sm, sb);
   moe_finish(p, h, sb);
+}
+
+template <class G>
+__global__ __launch_bounds__(G::NT) void moe_kernel(const MoeParams p) {
+  __shared__ uint32_t sb[2];
+  if constexpr (G::STAGES == 4) {
+    __shared__ u32x4 a0[G::SA_U4], a1[G::SA_U4], a2[G::SA_U4], a3[G::SA_U4];
+    __shared__ u32x4 b0[G::SB_U4], b1[G::SB_U4], b2[G::SB_U4], b3[G::SB_U4];
+    moe_body<G>(p, Smem4{{a0, a1, a2, a3}, {b0, b1, b2, b3}}, sb);
+  } else {
+    __shared__ u32x4 lds[G::LDS_U4];
+    moe_body<G>(p, Smem1{lds}, sb);
+  }
 }
 
 template <class G>
@@ -450,11 +462,15 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   }
   int tile = o.tile ? o.tile : TILE_256x256;
   if (F < 256 && tile == TILE_256x256) tile = TILE_128x128;
+  if (!o.tile && tile == TILE_256x256 && TileGemmD<256, 256>::supports_k((int)H)) tile = TILE_256x256_DMA;
   switch (tile) {
     case TILE_256x256: return run_moe<TileGemm<256, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
     case TILE_128x128: return run_moe<TileGemm<128, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
     case TILE_256x128: return run_moe<TileGemm<256, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
     case TILE_128x256: return run_moe<TileGemm<128, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
+    case TILE_256x256_DMA:
+      if (!TileGemmD<256, 256>::supports_k((int)H)) return fail(MK_ERR_UNSUPPORTED, "tile %d needs H %% 128 == 0", tile);
+      return run_moe<TileGemmD<256, 256>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
     default: return fail(MK_ERR_INVALID, "tile id %d", tile);
   }
 }
