@@ -87,7 +87,7 @@ def test_schedule_roles_and_baseline_bitwise_identical(gpu):
 def test_dma_tile_ragged_experts_integer_exact(gpu):
     # H = 384 (a multiple of 128) takes the direct-to-LDS engine; F = 200 is ragged
     # in N and the per-expert row counts are ragged in M.
-    w = wl.make_moe(600, 384, 24, 3, 12, 200, seed=36, dist="int", block_tokens=64, out_dtype="f32",
+    w = wl.make_moe(640, 384, 24, 3, 12, 200, seed=36, dist="int", block_tokens=64, out_dtype="f32",
                     expert_begin=6)
     prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA))
     ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 6, "f32")

@@ -1,0 +1,85 @@
+"""The build-time check for barrier loops with per-lane exits."""
+import glob
+import os
+
+import pytest
+
+from tile_pipelined_gemm_amd import isa_check
+
+HEAD = "_Z1kv:\n\ts_mov_b32 s0, 0\n"
+
+# A loop holding a barrier whose exit is a scalar (uniform) branch.
+UNIFORM = HEAD + """.LBB0_1:
+\ts_barrier
+\ts_add_u32 s0, s0, 1
+\ts_cmp_lt_u32 s0, 8
+\ts_cbranch_scc1 .LBB0_1
+\ts_endpgm
+"""
+
+# The same loop left one lane at a time: exec shrinks, exit when empty.
+PER_LANE = HEAD + """.LBB0_1:
+\ts_barrier
+\tv_cmp_le_u32_e32 vcc, 8, v1
+\ts_or_b64 s[4:5], vcc, s[4:5]
+\ts_andn2_b64 exec, exec, s[4:5]
+\ts_cbranch_execz .LBB0_2
+\ts_branch .LBB0_1
+.LBB0_2:
+\ts_endpgm
+"""
+
+# A divergent if inside a uniform barrier loop (the usual `if (tid == 0)`).
+IF_INSIDE = HEAD + """.LBB0_1:
+\ts_and_saveexec_b64 s[6:7], s[2:3]
+\ts_cbranch_execz .LBB0_3
+\tglobal_atomic_add v2, v3, s[8:9]
+.LBB0_3:
+\ts_or_b64 exec, exec, s[6:7]
+\ts_barrier
+\ts_add_u32 s0, s0, 1
+\ts_cmp_lt_u32 s0, 8
+\ts_cbranch_scc1 .LBB0_1
+\ts_endpgm
+"""
+
+# A per-lane spin loop without a barrier inside a uniform barrier loop.
+SPIN_INSIDE = HEAD + """.LBB0_1:
+\ts_barrier
+.LBB0_2:
+\ts_sleep 8
+\ts_andn2_b64 exec, exec, s[12:13]
+\ts_cbranch_execnz .LBB0_2
+\ts_or_b64 exec, exec, s[14:15]
+\ts_add_u32 s0, s0, 1
+\ts_cmp_lt_u32 s0, 8
+\ts_cbranch_scc1 .LBB0_1
+\ts_endpgm
+"""
+
+
+def _check(text):
+    (name, lines), = list(isa_check.kernels(text))
+    return isa_check.divergent_barrier_loops(lines)
+
+
+def test_uniform_exit_passes():
+    assert _check(UNIFORM) == []
+
+
+def test_per_lane_exit_of_barrier_loop_is_found():
+    assert _check(PER_LANE) == [(".LBB0_1", "s_cbranch_execz .LBB0_2")]
+
+
+def test_divergent_if_and_spin_inside_uniform_loop_pass():
+    assert _check(IF_INSIDE) == []
+    assert _check(SPIN_INSIDE) == []
+
+
+def test_built_kernels_are_clean():
+    from tile_pipelined_gemm_amd import build
+    files = glob.glob(os.path.join(build.BUILD, "*-hip-amdgcn-amd-amdhsa-*.s"))
+    if not files:
+        pytest.skip("library not built in this tree")
+    for f in files:
+        assert isa_check.check_file(f) == {}, f

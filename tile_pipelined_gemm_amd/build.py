@@ -8,6 +8,11 @@ import shutil
 import subprocess
 import sys
 
+try:
+    from . import isa_check
+except ImportError:                      # run as a script
+    import isa_check
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
@@ -31,12 +36,24 @@ def flags():
             "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 
+def device_asm(src):
+    """Path of the gfx950 assembly the compile of src leaves in _build."""
+    return os.path.join(BUILD, f"{os.path.splitext(src)[0]}-hip-amdgcn-amd-amdhsa-{ARCH}.s")
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    # -save-temps=obj keeps the device assembly next to the object for the
+    # barrier-loop check below
+    cmd = [hipcc(), *flags(), "-save-temps=obj", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
+    found = isa_check.check_file(device_asm(src))
+    if found:
+        lines = [f"  {k}: {v[:3]}" for k, v in found.items()]
+        raise RuntimeError(f"{src}: barrier loop with a per-lane exit (kernel could spin for ever):\n"
+                           + "\n".join(lines))
     return obj
 
 

@@ -241,7 +241,9 @@ static int run_ag(AgParams& p, const mk_launch& o, const mkh::Schedule& s, const
   }
   p.mode = MODE_FUSED;
   // Default split: every workgroup starts as a copy workgroup while copy work
-  // remains (the copy is short and bandwidth-bound), then computes.
+  // remains, then computes.  (Copying with only the workgroups left over by
+  // whole compute rounds measured slower: one workgroup's copy rate is bound
+  // by load latency, so a few copiers cannot keep ahead of the tiles.)
   int n_copy = o.n_copy > 0 ? o.n_copy : grid;
   n_copy = std::min<int>(n_copy, (int)std::min<uint32_t>(n_work, (uint32_t)grid));
   p.n_copy = n_copy;

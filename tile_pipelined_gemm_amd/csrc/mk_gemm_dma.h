@@ -7,21 +7,29 @@
 // within each group of 16 lanes, lane i receives element i%4 of the 64-bit
 // rows addressed by lanes 4r + (i%16)/4, r = 0..3; pointing lane L at row
 // k0 + (L%16)/4, column nb + 4(L%4) therefore hands lane i the four k-values
-// of column nb + i%16).  Both layouts are XOR-swizzled in 16-byte units so the
-// fragment reads are free of bank conflicts; the swizzle is applied on the
-// global side of each copy, because every wave instruction fills 1 KiB of LDS
-// linearly.
+// of column nb + i%16).
 //
-// Pipeline, per K slice kt (stage kt%4):
-//   MFMAs of substep 0 (fragments read during the previous slice)
-//   wait for this wave's DMA of slice kt+1, barrier   (slice kt+1 visible to
-//        all waves; every wave is done reading stage kt-1)
-//   DMA of slice kt+3 into stage (kt+3)%4 == (kt-1)%4
-//   read substep-1 fragments of slice kt and substep-0 fragments of kt+1
-//   MFMAs of substep 1
-// The DMA is issued through inline asm so the compiler does not add its own
-// (conservative) waits on it; the explicit vmcnt waits and the barrier are
-// one asm statement with a memory clobber, so no LDS access moves across them.
+// gfx950 LDS has 64 four-byte banks (256 bytes per clock).  Both layouts are
+// XOR-swizzled in 16-byte units so that every fragment read is free of bank
+// conflicts at that width: A (64-byte rows) swaps chunk c of row r with
+// c ^ ((r >> 2) & 3), so 16 consecutive rows cover all 64 banks; B (512-byte
+// rows) swaps chunk c of k-row r with c ^ ((r & 3) << 2), so the four k-rows a
+// transpose read touches fall on four different 64-byte bank groups.  The
+// swizzle is applied on the global side of each copy, because every DMA
+// instruction fills 1 KiB of LDS linearly.
+//
+// Schedule, per K slice kt (stage kt%4), every branch free of LDS reads so the
+// compiler's own LDS waits stay exact:
+//   wait for this wave's DMA of slice kt+1 and for its own fragment reads of
+//        slice kt, barrier   (slice kt+1 visible to all waves; no wave reads
+//        stage kt%4 any more)
+//   DMA of slice kt+4 into stage kt%4
+//   read all fragments of slice kt+1 (both 16-deep substeps)
+//   32 MFMAs of slice kt from the fragments read one slice earlier
+// so three slices are in flight while a slice is multiplied.  The DMA is
+// issued through inline asm so the compiler does not add its own
+// (conservative) waits on it; the explicit waits and the barrier are one asm
+// statement with a memory clobber, so no LDS access moves across them.
 #pragma once
 
 #include "mk_device.h"
@@ -62,12 +70,15 @@ __device__ __forceinline__ void dma16(u32x4 desc, uint32_t lds, uint32_t voff, u
       : "memory");
 }
 
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and all its LDS reads have returned, then barrier.
 template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  static_assert(N == 0 || N == 8 || N == 16, "vmcnt");
-  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N == 0 || N == 8 || N == 16 || N == 24, "vmcnt");
+  if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int BM_ = 256, int BN_ = 256>
@@ -99,12 +110,12 @@ struct TileGemmD {
     dA = buf_desc(A, uni((uint32_t)(rows > 0 ? rows : 0) * ldaB));
     dB = buf_desc(B, uni((uint32_t)((B_end - B) * 2)));
     nk = uni(K) / BK;
-    // A: LDS unit p = blk*64 + lane holds tile row p/4 and physical chunk p%4,
-    // which is logical k-chunk (p%4) ^ ((row>>1)&3).
-    voA = (uint32_t)(lane >> 2) * ldaB + (uint32_t)((lane & 3) ^ ((lane >> 3) & 3)) * 16u;
-    // B: LDS unit p holds k-row p/32; physical chunk p%32 = logical ^ ((row&3)<<1).
+    // A: LDS unit p = blk*64 + lane holds tile row p/4 = blk*16 + lane/4 and
+    // physical chunk p%4, which is logical k-chunk (p%4) ^ ((row>>2)&3).
+    voA = (uint32_t)(lane >> 2) * ldaB + (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
+    // B: LDS unit p holds k-row p/32; physical chunk p%32 = logical ^ ((row&3)<<2).
     const int brow = (2 * w + (lane >> 5)) & 3;
-    const int lchunk = (lane & 31) ^ (brow << 1);
+    const int lchunk = (lane & 31) ^ (brow << 2);
     voB = (lchunk * 8 < ncols) ? (uint32_t)(lane >> 5) * ldbB + (uint32_t)lchunk * 16u : OOB;
   }
 
@@ -135,21 +146,21 @@ struct TileGemmD {
   }
 
   // Per-lane fragment byte offsets inside a stage.
-  struct FragOfs { int a[2]; int b[2]; };
+  struct FragOfs { int a[2]; int b[FN]; };
   __device__ __forceinline__ FragOfs frag_offsets() const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w % WM, wn = w / WM;
     const int hi = lane >> 5, g = lane >> 4, Lg = lane & 15;
     FragOfs f;
     const int arow = wm * TM + (lane & 31);
-    const int as = ((lane & 31) >> 1) & 3;
+    const int as = ((lane & 31) >> 2) & 3;
     f.a[0] = arow * 64 + ((0 + hi) ^ as) * 16;
     f.a[1] = arow * 64 + ((2 + hi) ^ as) * 16;
     const int brow = (g >> 1) * 8 + (Lg >> 2);
-    const int sw = (Lg >> 2) << 1;
     const int u = 2 * (g & 1) + ((Lg & 3) >> 1);
-    f.b[0] = brow * (BN * 2) + (wn * 16 + ((0 + u) ^ sw)) * 16 + (Lg & 1) * 8;   // even j
-    f.b[1] = brow * (BN * 2) + (wn * 16 + ((4 + u) ^ sw)) * 16 + (Lg & 1) * 8;   // odd j
+    // fragment j covers logical chunks wn*16 + 4j + (0..3); k-row & 3 == Lg >> 2
+#pragma unroll
+    for (int j = 0; j < FN; ++j) f.b[j] = brow * (BN * 2) + (wn * 16 + 4 * (j ^ (Lg >> 2)) + u) * 16 + (Lg & 1) * 8;
     return f;
   }
 
@@ -161,7 +172,7 @@ struct TileGemmD {
     for (int i = 0; i < FM; ++i) af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pa + f.a[ks] + i * 32 * 64));
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int base = f.b[j & 1] + (j >> 1) * 128 + ks * 16 * (BN * 2);
+      const int base = f.b[j] + ks * 16 * (BN * 2);
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pb + base));
       const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pb + base + 4 * (BN * 2)));
       bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -176,22 +187,23 @@ struct TileGemmD {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   }
 
-  // One K slice.  f0/b0 hold substep-0 fragments of slice kt on entry and
-  // substep-0 fragments of slice kt+1 on exit.
-  __device__ __forceinline__ void step(int kt, const FragOfs& fo, const u32x4* sa, const u32x4* sb,
-                                       const u32x4* na, const u32x4* nb, u32x4* fa, u32x4* fb,
-                                       bf16x8 (&a0)[FM], bf16x8 (&b0)[FN]) {
-    bf16x8 a1[FM], b1[FN];
-    read_frags(sa, sb, fo, 1, a1, b1);
-    mfmas(a0, b0);
-    const int later = nk - 2 - kt;          // slices after kt+1 already in flight (0..1)
-    if (kt + 1 < nk) {
-      if (later >= 1) wait_vm_barrier<8>();
-      else wait_vm_barrier<0>();
-      if (kt + 3 < nk) issue(fa, fb, kt + 3);
-      read_frags(na, nb, fo, 0, a0, b0);
-    }
-    mfmas(a1, b1);
+  struct Frags { bf16x8 a[2][FM]; bf16x8 b[2][FN]; };
+
+  // One K slice: cur holds the fragments of slice kt, nxt receives those of
+  // slice kt+1 (na/nb); slice kt+4 is loaded into stage kt%4 (fa/fb).
+  __device__ __forceinline__ void step(int kt, const FragOfs& fo, const u32x4* na, const u32x4* nb,
+                                       u32x4* fa, u32x4* fb, Frags& cur, Frags& nxt) {
+    const int later = nk - 2 - kt;          // slices after kt+1 already issued (at most 2 count)
+    if (later >= 2) wait_barrier<16>();
+    else if (later == 1) wait_barrier<8>();
+    else wait_barrier<0>();
+    if (kt + 4 < nk) issue(fa, fb, kt + 4);
+    // on the last slice these read a stage nobody uses; it keeps the branch
+    // above free of LDS reads
+    read_frags(na, nb, fo, 0, nxt.a[0], nxt.b[0]);
+    read_frags(na, nb, fo, 1, nxt.a[1], nxt.b[1]);
+    mfmas(cur.a[0], cur.b[0]);
+    mfmas(cur.a[1], cur.b[1]);
   }
 
   // Full K loop; the four stages are distinct LDS objects.
@@ -200,20 +212,21 @@ struct TileGemmD {
     u32x4 *B0 = m.b[0], *B1 = m.b[1], *B2 = m.b[2], *B3 = m.b[3];
     const FragOfs fo = frag_offsets();
     zero_acc();
+    if (nk == 0) return;
+    // nk is a multiple of 4 (supports_k), so all four stages start loaded
     issue(A0, B0, 0);
-    if (nk > 1) issue(A1, B1, 1);
-    if (nk > 2) issue(A2, B2, 2);
-    // slice 0 must be visible before its first fragments are read
-    if (nk > 2) wait_vm_barrier<16>();
-    else if (nk > 1) wait_vm_barrier<8>();
-    else wait_vm_barrier<0>();
-    bf16x8 a0[FM], b0[FN];
-    read_frags(A0, B0, fo, 0, a0, b0);
+    issue(A1, B1, 1);
+    issue(A2, B2, 2);
+    issue(A3, B3, 3);
+    wait_barrier<24>();
+    Frags r0, r1;
+    read_frags(A0, B0, fo, 0, r0.a[0], r0.b[0]);
+    read_frags(A0, B0, fo, 1, r0.a[1], r0.b[1]);
     for (int kt = 0; kt < nk; kt += 4) {
-      step(kt + 0, fo, A0, B0, A1, B1, A3, B3, a0, b0);
-      step(kt + 1, fo, A1, B1, A2, B2, A0, B0, a0, b0);
-      step(kt + 2, fo, A2, B2, A3, B3, A1, B1, a0, b0);
-      step(kt + 3, fo, A3, B3, A0, B0, A2, B2, a0, b0);
+      step(kt + 0, fo, A1, B1, A0, B0, r0, r1);
+      step(kt + 1, fo, A2, B2, A1, B1, r1, r0);
+      step(kt + 2, fo, A3, B3, A2, B2, r0, r1);
+      step(kt + 3, fo, A0, B0, A3, B3, r1, r0);
     }
     __syncthreads();                        // LDS free for the next tile
   }

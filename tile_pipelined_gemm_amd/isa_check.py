@@ -1,0 +1,147 @@
+"""Build-time check of the gfx950 assembly of every kernel: no loop that
+holds a workgroup barrier may be left on an exec-mask branch.
+
+A persistent kernel's role loops contain s_barrier and end in a
+`if (threadIdx.x == 0) { ... }` block (queue atomics, releases).  When the
+compiler cannot prove a loop's exit uniform it may lower the loop with a
+per-lane exit (the lanes of a wave leave one by one, under exec masks) and
+move such a block onto the exit path.  The waves then keep executing the
+barriers without the work that block does for them: the kernel spins for
+ever.  Uniform exits (scalar branches on values made wave-uniform with
+readfirstlane) never take that form, so the check is structural: in the
+control-flow graph of each kernel, a strongly connected region that
+contains s_barrier must not have an s_cbranch_execz/execnz edge leading out
+of it.
+"""
+import re
+import sys
+
+_BRANCH = re.compile(r"(s_branch|s_cbranch_\w+)\s+(\.LBB\w+)")
+
+
+def kernels(asm_text):
+    """Yield (symbol, [instruction lines]) for each function in the file."""
+    name, body = None, []
+    for ln in asm_text.splitlines():
+        m = re.match(r"^(_Z\w+):", ln)
+        if m:
+            name, body = m.group(1), []
+            continue
+        if name is None:
+            continue
+        body.append(ln)
+        if "s_endpgm" in ln:
+            yield name, body
+            name, body = None, []
+
+
+def _blocks(lines):
+    """Split into basic blocks: (label or None, [instructions])."""
+    out, cur, lab = [], [], ".entry"
+    for raw in lines:
+        m = re.match(r"^(\.LBB\w+):", raw)
+        if m:
+            if cur or lab:
+                out.append((lab, cur))
+            lab, cur = m.group(1), []
+            continue
+        ins = raw.split(";")[0].strip()
+        if not ins or ins.startswith("."):
+            continue
+        cur.append(ins)
+        if _BRANCH.match(ins) or ins.startswith("s_endpgm") or ins.startswith("s_setpc"):
+            out.append((lab, cur))
+            lab, cur = None, []
+    if cur:
+        out.append((lab, cur))
+    return out
+
+
+def divergent_barrier_loops(lines):
+    """Return [(block label, branch)] for exec-mask exits of barrier loops."""
+    bl = _blocks(lines)
+    index_of = {lab: i for i, (lab, _) in enumerate(bl) if lab}
+    succ, exec_branch = [], []
+    for i, (_, ins) in enumerate(bl):
+        s, eb = [], False
+        last = ins[-1] if ins else ""
+        m = _BRANCH.match(last)
+        if m:
+            if m.group(2) in index_of:
+                s.append(index_of[m.group(2)])
+            if m.group(1) != "s_branch" and i + 1 < len(bl):
+                s.append(i + 1)
+            eb = m.group(1) in ("s_cbranch_execz", "s_cbranch_execnz")
+        elif not last.startswith("s_endpgm") and i + 1 < len(bl):
+            s.append(i + 1)
+        succ.append(s)
+        exec_branch.append(eb)
+
+    # strongly connected components (iterative Tarjan)
+    n = len(bl)
+    index, low, on_stack, stack, comp = [-1] * n, [0] * n, [False] * n, [], [-1] * n
+    counter = 0
+    for root in range(n):
+        if index[root] >= 0:
+            continue
+        work = [(root, 0)]
+        while work:
+            v, k = work.pop()
+            if k == 0:
+                index[v] = low[v] = counter
+                counter += 1
+                stack.append(v)
+                on_stack[v] = True
+            if k < len(succ[v]):
+                work.append((v, k + 1))
+                w = succ[v][k]
+                if index[w] < 0:
+                    work.append((w, 0))
+                elif on_stack[w]:
+                    low[v] = min(low[v], index[w])
+                continue
+            for w in succ[v]:
+                if on_stack[w] and comp[w] < 0:
+                    low[v] = min(low[v], low[w])
+            if low[v] == index[v]:
+                while True:
+                    w = stack.pop()
+                    on_stack[w] = False
+                    comp[w] = v
+                    if w == v:
+                        break
+    groups = {}
+    for v in range(n):
+        groups.setdefault(comp[v], []).append(v)
+    bad = []
+    for members in groups.values():
+        ms = set(members)
+        if len(members) == 1 and members[0] not in succ[members[0]]:
+            continue                                   # not a loop
+        if not any(ins.startswith("s_barrier") for v in members for ins in bl[v][1]):
+            continue
+        for v in members:
+            if exec_branch[v] and any(w not in ms for w in succ[v]):
+                bad.append((bl[v][0], bl[v][1][-1]))
+    return bad
+
+
+def check_file(path):
+    """Return {kernel symbol: findings} for kernels with findings."""
+    with open(path) as f:
+        text = f.read()
+    found = {}
+    for name, lines in kernels(text):
+        b = divergent_barrier_loops(lines)
+        if b:
+            found[name] = b
+    return found
+
+
+if __name__ == "__main__":
+    rc = 0
+    for p in sys.argv[1:]:
+        for k, v in check_file(p).items():
+            print(f"{p}: {k}: {v[:3]}")
+            rc = 1
+    sys.exit(rc)
