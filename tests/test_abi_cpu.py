@@ -105,7 +105,9 @@ def test_rs_validation(lib):
     assert _rs(lib, partials=False) == mk.MK_ERR_INVALID
     assert _rs(lib, M=4 * 96) == mk.MK_ERR_UNSUPPORTED       # 96 rows per owner: not a tile multiple
     lau = mk.make_launch(tile=1)
-    assert _rs(lib, lau=C.byref(lau)) == mk.MK_ERR_UNSUPPORTED   # only the 128x128 tile is enabled
+    assert _rs(lib, lau=C.byref(lau)) == mk.MK_ERR_UNSUPPORTED   # 128 rows per owner: not a 256-row tile multiple
+    lau = mk.make_launch(tile=5)
+    assert _rs(lib, M=1024, K=136, lau=C.byref(lau)) == mk.MK_ERR_UNSUPPORTED   # direct-to-LDS tile needs K % 128 == 0
     assert _rs(lib, ws_bytes=64) == mk.MK_ERR_WORKSPACE
     lau = mk.make_launch(n_reduce=-5)
     assert _rs(lib, lau=C.byref(lau)) == mk.MK_ERR_INVALID

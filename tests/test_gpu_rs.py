@@ -38,30 +38,44 @@ def test_integer_inputs_bit_exact(gpu):
     assert np.array_equal(prob.output(), np.vstack(outs))
 
 
+def test_dma_tile_integer_inputs_bit_exact(gpu):
+    # K = 256 and 256 rows per owner take the direct-to-LDS 256x256 tile with the
+    # reduction done from the accumulators; N = 264 is ragged.
+    w = wl.make_rs(1024, 256, 264, 4, seed=26, dist="int")
+    prob = _run(gpu, w)
+    _, _, outs = orc.gemm_rs(w.A, w.B, w.partials, w.R, "f32")
+    assert np.array_equal(prob.output(), np.vstack(outs))
+
+
 def test_roles_and_baseline_bitwise_identical(gpu):
     w = wl.make_rs(1024, 512, 512, 4, seed=23)
     outs = []
     # the fp32 sum order (local, P_1, ..., P_{R-1}) and the K-loop order do not
     # depend on the role split, the tile shape or fusion, so the bits must agree
     for lau in [dict(), dict(n_reduce=-1), dict(n_reduce=16), dict(n_reduce=64, grid=96), dict(mode=1),
-                dict(tile=2), dict(tile=2, n_reduce=32)]:
+                dict(tile=2), dict(tile=2, n_reduce=32), dict(tile=5, n_reduce=8), dict(tile=5, mode=1),
+                dict(tile=1), dict(tile=3), dict(tile=4)]:
         prob = _run(gpu, w, gpu.make_launch(**lau))
         outs.append(prob.output())
     for i, o in enumerate(outs[1:], 1):
         assert np.array_equal(outs[0], o), f"variant {i} differs"
 
 
-DISABLED = pytest.mark.skip(reason="GEMM+RS larger tiles are disabled: a 256x256 run with dedicated "
-                                   "reducers did not finish on the GPU and its cause is not established")
-
-
-@pytest.mark.parametrize("tile", [pytest.param(1, marks=DISABLED), 2, pytest.param(3, marks=DISABLED),
-                                  pytest.param(4, marks=DISABLED)])
-def test_every_tile_config(gpu, tile):
-    w = wl.make_rs(1024, 136, 392, 4, seed=24)
-    prob = _run(gpu, w, gpu.make_launch(tile=tile, n_reduce=8))
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("n_reduce", [8, -1])
+def test_every_tile_config(gpu, tile, n_reduce):
+    # ragged N; K = 136 (K = 256 for the direct-to-LDS tile, which needs K % 128 == 0)
+    w = wl.make_rs(1024, 256 if tile == 5 else 136, 392, 4, seed=24)
+    prob = _run(gpu, w, gpu.make_launch(tile=tile, n_reduce=n_reduce))
     S, _, _ = orc.gemm_rs(w.A, w.B, w.partials, w.R)
     assert_close(out_to_f64(prob.output(), "f32"), S, "f32", f"RS tile {tile}")
+
+
+def test_dma_tile_rejects_k_not_multiple_of_128(gpu):
+    from tile_pipelined_gemm_amd.harness import RsProblem
+    w = wl.make_rs(1024, 136, 256, 4, seed=27)
+    prob = RsProblem(w)
+    assert prob.run(launch=gpu.make_launch(tile=5), check=False) == gpu.MK_ERR_UNSUPPORTED
 
 
 def test_owner_map_in_tile_log(gpu):
@@ -77,6 +91,20 @@ def test_owner_map_in_tile_log(gpu):
         tm = t // 4
         assert L[t, 0] == orc.tile_owner(tm, 128, w.M, w.R)
     assert sorted(L[:, 1].tolist()) == list(range(n_tiles))     # each production slot used once
+
+
+def test_owner_map_in_tile_log_dma_tile(gpu):
+    from tile_pipelined_gemm_amd.harness import RsProblem
+    w = wl.make_rs(2048, 256, 512, 8, seed=28)
+    prob = RsProblem(w)
+    n_tiles = (2048 // 256) * (512 // 256)
+    log = torch.full((2 * n_tiles,), -1, dtype=torch.int32, device="cuda")
+    prob.run(launch=gpu.make_launch(tile=5, tile_log=log))
+    torch.cuda.synchronize()
+    L = log.cpu().numpy().reshape(-1, 2)
+    for t in range(n_tiles):
+        assert L[t, 0] == orc.tile_owner(t // 2, 256, w.M, w.R)
+        assert L[t, 1] == t
 
 
 def test_full_size_rs_config_sampled(gpu):

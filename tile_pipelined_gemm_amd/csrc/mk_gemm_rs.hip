@@ -11,8 +11,10 @@
 //            workgroups present, a finished fp32 tile is staged, published
 //            (release) and its id appended to a produced-tile FIFO; a compute
 //            workgroup whose queue is empty turns into a reduce workgroup.
-//            Without them (n_reduce <= 0) the compute workgroup stages the
-//            tile and reduces it itself right away.
+//            Without them (n_reduce <= 0) the compute workgroup reduces the
+//            tile itself, straight from its accumulator registers: it loads
+//            the partial sums for the elements it holds, adds them and
+//            stores the owner's rows (no fp32 staging).
 //   reduce   tickets [n_compute, grid): pop produced tiles in production order,
 //            acquire, sum local + P_1 + ... + P_{R-1} in that fixed fp32 order
 //            (so every role split and schedule gives identical bits) and
@@ -22,6 +24,7 @@
 #include <algorithm>
 
 #include "mk_device.h"
+#include "mk_gemm_dma.h"
 #include "mk_host.h"
 #include "mk_tiles.h"
 
@@ -96,71 +99,129 @@ __device__ __forceinline__ void reduce_tile(const RsParams& p, int t) {
   }
 }
 
+// out = acc + P_1 + ... + P_{R-1} for the elements this thread holds, in that
+// order (the same fp32 order as reduce_tile, so every mode gives the same
+// bits).  In a 32x32 accumulator block a lane holds 16 rows of one column, so
+// each wave access covers two 128-byte row segments.  The partial values of
+// four partial sums (64 loads per lane) are in flight before any is added.
 template <class G>
-__device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, Smem1 sm, uint32_t* sb) {
+__device__ __forceinline__ void reduce_from_acc(const G& g, const RsParams& p, int m0, int n0) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w % G::WM, wn = w / G::WM;
+  const int o = m0 / p.mb;                       // a tile never straddles two owners
+  const int nq = p.R - 1;
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      const int col = n0 + wn * G::TN + j * 32 + (lane & 31);
+      const int rb = m0 + wm * G::TM + i * 32 + (lane >> 5) * 4;
+      const bool colok = col < p.N;
+      f32x16 v = g.acc[i][j];
+      for (int q0 = 0; q0 < nq; q0 += 4) {
+        float t[4][16];
+#pragma unroll
+        for (int dq = 0; dq < 4; ++dq) {
+          const int q = q0 + dq < nq ? q0 + dq : nq - 1;
+          const float* __restrict__ P = p.P[q] + col;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rb + (r >> 2) * 8 + (r & 3);
+            t[dq][r] = (colok && row < p.M) ? P[(int64_t)row * p.N] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int dq = 0; dq < 4; ++dq)
+          if (q0 + dq < nq) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v[r] += t[dq][r];
+          }
+      }
+      if (!colok) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rb + (r >> 2) * 8 + (r & 3);
+        if (row >= p.M) continue;
+        const int64_t e = (int64_t)(row - o * p.mb) * p.N + col;
+        if (p.out_bf16) ((uint16_t*)p.out[o])[e] = f2bf(v[r]);
+        else ((float*)p.out[o])[e] = v[r];
+      }
+    }
+  }
+}
+
+// The role loops take their next work index at the bottom of the body and
+// test it at the top, with no `continue`: one uniform exit and one latch, so
+// the compiler keeps every barrier in wave-uniform control flow.
+template <class G, class SM>
+__device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, SM sm, uint32_t* sb) {
   const int tid = threadIdx.x;
   G g;
-  for (;;) {
-    const uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
-    if (q >= (uint32_t)p.n_tiles) break;
+  uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+  while (q < (uint32_t)p.n_tiles) {
     const int t = (int)q;
     const int tm = t / p.tiles_n, tn = t % p.tiles_n;
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     g.bind(p.A + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
     g.run(sm);
-    // Stage the fp32 tile (in the owner block for fp32 output, else in the
-    // workspace staging area).
-    float* __restrict__ S = p.stage ? p.stage + (int64_t)m0 * p.N
-                                    : (float*)p.out[m0 / p.mb] + (int64_t)(m0 % p.mb) * p.N;
-    g.for_each([&](int r, int c, float v) __attribute__((always_inline)) {
-      const int gr = m0 + r, gc = n0 + c;
-      if (gr < p.M && gc < p.N) S[(int64_t)r * p.N + gc] = v;
-    });
     if (p.mode == MODE_EPI) {
-      // This workgroup reduces its own tile right away (its staged writes are
-      // visible to its own waves after the barrier).
-      __syncthreads();
-      reduce_tile<G::BM, G::BN>(p, t);
-      __syncthreads();
-      if (p.tile_log && tid == 0) {
-        p.tile_log[2 * t] = m0 / p.mb;
-        p.tile_log[2 * t + 1] = t;
+      reduce_from_acc(g, p, m0, n0);
+    } else {
+      // Stage the fp32 tile (in the owner block for fp32 output, else in the
+      // workspace staging area) for the reduce role or the reduce kernel.
+      float* __restrict__ S = p.stage ? p.stage + (int64_t)m0 * p.N
+                                      : (float*)p.out[m0 / p.mb] + (int64_t)(m0 % p.mb) * p.N;
+      g.for_each([&](int r, int c, float v) __attribute__((always_inline)) {
+        const int gr = m0 + r, gc = n0 + c;
+        if (gr < p.M && gc < p.N) S[(int64_t)r * p.N + gc] = v;
+      });
+      if (p.mode == MODE_ROLES) {
+        __threadfence();
+        __syncthreads();
       }
-    } else if (p.mode == MODE_ROLES) {
-      __threadfence();
-      __syncthreads();
-      if (tid == 0) {
+    }
+    uint32_t next = 0;
+    if (tid == 0) {
+      if (p.mode == MODE_ROLES) {
         const uint32_t slot = add_relaxed(&h->prod_next, 1u);
         st_release(&p.fifo[slot], (uint32_t)t + 1u);
         if (p.tile_log) {
           p.tile_log[2 * t] = m0 / p.mb;
           p.tile_log[2 * t + 1] = (int32_t)slot;
         }
+      } else if (p.mode == MODE_EPI && p.tile_log) {
+        p.tile_log[2 * t] = m0 / p.mb;
+        p.tile_log[2 * t + 1] = t;
       }
+      next = add_relaxed(&h->tile_next, 1u);
     }
+    q = wg_bcast(next, sb);
   }
 }
 
 template <class G>
 __device__ __forceinline__ void rs_reduce_role(const RsParams& p, WsHeader* h, uint32_t* sb) {
   const int tid = threadIdx.x;
-  for (;;) {
-    const uint32_t i = wg_bcast(tid == 0 ? add_relaxed(&h->red_next, 1u) : 0u, sb);
-    if (i >= (uint32_t)p.n_tiles) break;
+  uint32_t i = wg_bcast(tid == 0 ? add_relaxed(&h->red_next, 1u) : 0u, sb);
+  while (i < (uint32_t)p.n_tiles) {
     uint32_t t = i;
     if (p.mode == MODE_ROLES) {
       uint32_t v = 0;
       if (tid == 0) v = wait_geq(&p.fifo[i], 1u, h, p.spin_limit) ? ld_relaxed(&p.fifo[i]) : 0u;
       v = wg_bcast(v, sb);
-      if (v == 0) continue;                      // watchdog expired
-      t = v - 1u;
+      t = v - 1u;                                // v == 0: watchdog expired, nothing to reduce
     }
-    reduce_tile<G::BM, G::BN>(p, (int)t);
-    if (p.mode == MODE_REDUCE && p.tile_log && tid == 0) {
-      const int tm = (int)t / p.tiles_n;
-      p.tile_log[2 * t] = tm * G::BM / p.mb;
-      p.tile_log[2 * t + 1] = (int32_t)t;
+    if (t < (uint32_t)p.n_tiles) reduce_tile<G::BM, G::BN>(p, (int)t);
+    uint32_t next = 0;
+    if (tid == 0) {
+      if (p.mode == MODE_REDUCE && p.tile_log) {
+        const int tm = (int)t / p.tiles_n;
+        p.tile_log[2 * t] = tm * G::BM / p.mb;
+        p.tile_log[2 * t + 1] = (int32_t)t;
+      }
+      next = add_relaxed(&h->red_next, 1u);
     }
+    i = wg_bcast(next, sb);
   }
 }
 
@@ -186,26 +247,37 @@ __device__ __forceinline__ void rs_finish(const RsParams& p, WsHeader* h, uint32
   }
 }
 
-template <class G>
-__global__ __launch_bounds__(G::NT) void rs_kernel(const RsParams p) {
-  __shared__ u32x4 lds[G::LDS_U4];
-  __shared__ uint32_t sb[2];
+template <class G, class SM>
+__device__ __forceinline__ void rs_body(const RsParams& p, SM sm, uint32_t* sb) {
   WsHeader* h = p.hdr;
   const uint32_t ticket = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->ticket, 1u) : 0u, sb);
   const bool reducer = p.mode == MODE_REDUCE || (p.mode == MODE_ROLES && ticket >= (uint32_t)p.n_compute);
-  if (!reducer) rs_compute_role<G>(p, h, Smem1{lds}, sb);
+  if (!reducer) rs_compute_role<G>(p, h, sm, sb);
   if (p.mode == MODE_ROLES || p.mode == MODE_REDUCE) rs_reduce_role<G>(p, h, sb);
   rs_finish(p, h, sb);
 }
 
-// GEMM+RS runs with the 128x128 tile (two workgroups per CU, so one can stream
-// its reduction while the other runs MFMAs).  The larger tiles are not enabled
-// for this operation: a 256x256 run with dedicated reducers did
-// not finish, and its cause is not yet established.
-inline int rs_tile(int64_t, int64_t, int64_t, int) { return TILE_128x128; }
-inline bool rs_tile_enabled(int t) { return t == TILE_128x128; }
+template <class G>
+__global__ __launch_bounds__(G::NT) void rs_kernel(const RsParams p) {
+  __shared__ uint32_t sb[2];
+  if constexpr (G::STAGES == 4) {
+    __shared__ u32x4 a0[G::SA_U4], a1[G::SA_U4], a2[G::SA_U4], a3[G::SA_U4];
+    __shared__ u32x4 b0[G::SB_U4], b1[G::SB_U4], b2[G::SB_U4], b3[G::SB_U4];
+    rs_body<G>(p, Smem4{{a0, a1, a2, a3}, {b0, b1, b2, b3}}, sb);
+  } else {
+    __shared__ u32x4 lds[G::LDS_U4];
+    rs_body<G>(p, Smem1{lds}, sb);
+  }
+}
 
-inline int tile_bm(int t) { return (t == TILE_256x256 || t == TILE_256x128) ? 256 : 128; }
+// Default: the direct-to-LDS 256x256 tile when K is a multiple of 128 and
+// the owner blocks hold whole tile rows, else 128x128.
+inline int tile_bm(int t) {
+  return (t == TILE_256x256 || t == TILE_256x128 || t == TILE_256x256_DMA) ? 256 : 128;
+}
+inline int rs_tile(int64_t, int64_t, int64_t K, int mb) {
+  return (TileGemmD<256, 256>::supports_k((int)K) && mb % 256 == 0) ? TILE_256x256_DMA : TILE_128x128;
+}
 
 }  // namespace
 
@@ -280,7 +352,8 @@ extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, in
   if (o.grid < 0 || o.n_reduce < -1) return fail(MK_ERR_INVALID, "bad grid or n_reduce");
   const int tile = o.tile ? o.tile : rs_tile(M, N, K, mb);
   if (tile <= 0 || tile >= TILE_COUNT) return fail(MK_ERR_INVALID, "tile id %d", tile);
-  if (!rs_tile_enabled(tile)) return fail(MK_ERR_UNSUPPORTED, "tile %d is not enabled for GEMM+RS", tile);
+  if (tile == TILE_256x256_DMA && !TileGemmD<256, 256>::supports_k((int)K))
+    return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
   if (mb % tile_bm(tile)) return fail(MK_ERR_UNSUPPORTED, "rows per owner (%d) must be a multiple of the tile height %d",
                                       mb, tile_bm(tile));
   if (!workspace) return fail(MK_ERR_WORKSPACE, "workspace is NULL");
@@ -307,5 +380,12 @@ extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, in
   p.M = (int)M; p.K = (int)K; p.N = (int)N; p.R = R; p.mb = mb;
   p.out_bf16 = out_dtype == MK_BF16;
   const hipStream_t st = (hipStream_t)stream;
-  return run_rs<TileGemm<128, 128, 2, 2>>(p, o, d, st, can_stage);
+  switch (tile) {
+    case TILE_256x256: return run_rs<TileGemm<256, 256, 2, 2>>(p, o, d, st, can_stage);
+    case TILE_128x128: return run_rs<TileGemm<128, 128, 2, 2>>(p, o, d, st, can_stage);
+    case TILE_256x128: return run_rs<TileGemm<256, 128, 2, 2>>(p, o, d, st, can_stage);
+    case TILE_128x256: return run_rs<TileGemm<128, 256, 2, 2>>(p, o, d, st, can_stage);
+    case TILE_256x256_DMA: return run_rs<TileGemmD<256, 256>>(p, o, d, st, can_stage);
+  }
+  return fail(MK_ERR_INVALID, "tile id %d", tile);
 }
