@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--ag-launch", default="",
                     help="launch options for the primary AG timing, e.g. mode=1,tile=5,n_copy=64,copy_kib=256")
+    ap.add_argument("--ag-timeline", default="",
+                    help="only run the AG workload once per launch spec (';'-separated) with the "
+                         "tile and copy logs and print each timeline summary as JSON")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -127,7 +130,7 @@ def bench_ag(name, args, stream, extra=True):
         r["speedup_vs_unfused"] = uk / kern
         # role split and scheduling variants of the fused kernel
         for tag, kw in [("n_copy32", dict(n_copy=32)), ("n_copy64", dict(n_copy=64)),
-                        ("copy_kib512", dict(copy_kib=512)), ("copy_kib2048", dict(copy_kib=2048)),
+                        ("copy_kib256", dict(copy_kib=256)), ("copy_kib1024", dict(copy_kib=1024)),
                         ("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
                         ("tile_reg", dict(tile=mk.TILE_256x256))]:
             lv = mk.make_launch(**kw)
@@ -244,6 +247,17 @@ def main():
     mk.load()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.ag_timeline:
+        import workloads as wl
+        from tile_pipelined_gemm_amd.harness import AgProblem, ag_timeline
+        prob = AgProblem(wl.CONFIGS["ag"]["make"](seed=args.seed))
+        for spec in args.ag_timeline.split(";"):
+            kw = {k: int(v) for k, v in (kv.split("=") for kv in spec.split(",") if kv)}
+            for _ in range(3):                       # warm up
+                prob.run(launch=mk.make_launch(**kw))
+            torch.cuda.synchronize()
+            print(json.dumps({"launch": spec, **ag_timeline(prob, **kw)}), flush=True)
+        return
     if args.copy_calib:
         n = args.copy_calib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")

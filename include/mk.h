@@ -102,8 +102,12 @@ typedef struct mk_launch {
   uint32_t spin_limit_us; /* watchdog for every wait; 0 = 2,000,000 us */
   int32_t* tile_log;      /* device int32 or NULL: per-tile record, see each op */
   int32_t copy_kib;       /* AG: bytes per copy work item in KiB (one release each);
-                             0 = 1024; rounded to whole rows inside one unit and shard */
-  int32_t reserved[3];    /* must be zero */
+                             0 = 512; rounded to whole rows inside one unit and shard */
+  int32_t reserved0;      /* must be zero */
+  int32_t* copy_log;      /* AG: device int32 or NULL: per copy work item (in
+                             queue order), 8 int32 {unit, part, workgroup,
+                             t_start, t_end, 0, 0, 0}; times are the low 32 bits
+                             of the device wall clock (mk_wall_clock_khz) */
 } mk_launch;
 
 /* ---------------------------------------------------------------------------
@@ -117,8 +121,10 @@ typedef struct mk_launch {
  * nearest-even for bf16), starting each output tile as soon as the units
  * covering its rows have landed.
  *   arrival NULL = one unit per shard, issued in rank order, no delay.
- *   tile_log (optional): per tile in queue order, 4 int32 {tile_row,
- *   tile_col, first unit, last unit}.
+ *   tile_log (optional): per tile in queue order, 8 int32 {tile_row,
+ *   tile_col, first unit, last unit, workgroup, t_take, t_ready, t_done}:
+ *   when the tile was taken from the queue, when its units had landed, and
+ *   when its stores were issued (low 32 bits of the device wall clock).
  * ------------------------------------------------------------------------- */
 size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_t N, int32_t unit_rows);
 int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
@@ -181,6 +187,10 @@ int mk_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  * previous call on this workspace hit its watchdog, else MK_OK. */
 int mk_poll_status(void* workspace, void* stream);
 const char* mk_status_string(int status);
+
+/* Rate of the device wall clock that stamps the logs, in kHz (100000 on
+ * gfx950), for the current HIP device; negative mk_status on failure. */
+int mk_wall_clock_khz(void);
 const char* mk_last_error(void);
 /* Name of tile configuration `id` (NULL if out of range); id 0 is "auto". */
 const char* mk_tile_name(int id);

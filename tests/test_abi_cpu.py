@@ -104,8 +104,10 @@ def test_rs_validation(lib):
     assert _rs(lib, out_dtype=5) == mk.MK_ERR_INVALID
     assert _rs(lib, partials=False) == mk.MK_ERR_INVALID
     assert _rs(lib, M=4 * 96) == mk.MK_ERR_UNSUPPORTED       # 96 rows per owner: not a tile multiple
-    lau = mk.make_launch(tile=1)
+    lau = mk.make_launch(tile=3)
     assert _rs(lib, lau=C.byref(lau)) == mk.MK_ERR_UNSUPPORTED   # 128 rows per owner: not a 256-row tile multiple
+    lau = mk.make_launch(tile=1)
+    assert _rs(lib, M=1024, lau=C.byref(lau)) == mk.MK_ERR_UNSUPPORTED   # register 256x256 tile not built for RS
     lau = mk.make_launch(tile=5)
     assert _rs(lib, M=1024, K=136, lau=C.byref(lau)) == mk.MK_ERR_UNSUPPORTED   # direct-to-LDS tile needs K % 128 == 0
     assert _rs(lib, ws_bytes=64) == mk.MK_ERR_WORKSPACE

@@ -99,20 +99,41 @@ def test_copy_only_then_gemm_only_equals_fused(gpu):
 
 def test_tile_log_records_chunk_dependencies(gpu):
     from tile_pipelined_gemm_amd.harness import AgProblem
-    w = wl.make_ag(4, 256, 256, 512, seed=14, unit_rows=64)
+    w = wl.make_ag(4, 256, 256, 512, seed=14, unit_rows=64, max_delay_ns=5000)
     prob = AgProblem(w)
-    log = torch.full((4 * 64,), -1, dtype=torch.int32, device="cuda")
-    prob.run(launch=gpu.make_launch(tile=1, tile_log=log))
+    log = torch.full((8 * 64,), -1, dtype=torch.int32, device="cuda")
+    clog = torch.full((8 * 64,), -1, dtype=torch.int32, device="cuda")
+    prob.run(launch=gpu.make_launch(tile=1, tile_log=log, copy_log=clog, copy_kib=16))
     torch.cuda.synchronize()
-    L = log.cpu().numpy().reshape(-1, 4)
+    L = log.cpu().numpy().reshape(-1, 8).astype(np.int64)
+    CL = clog.cpu().numpy().reshape(-1, 8).astype(np.int64)
     n_tiles = (w.M // 256) * (w.N // 256)
+    parts = 64 * 256 * 2 // (16 * 1024)              # 16 KiB copy items: 2 per 64-row unit
+    n_items = (w.M // 64) * parts
     seen = set()
     for q in range(n_tiles):                      # one record per tile, in queue order
-        tm, tn, u0, u1 = L[q]
+        tm, tn, u0, u1 = L[q, :4]
         assert (u0, u1) == og.tile_units(tm, 256, w.unit_rows, w.M)
         seen.add((tm, tn))
     assert len(seen) == n_tiles
     assert np.all(L[n_tiles:] == -1)
+    # copy log: every (unit, part) copied once, in arrival order of units
+    items = CL[:n_items]
+    assert sorted(map(tuple, items[:, :2].tolist())) == [(u, p) for u in range(w.M // 64) for p in range(parts)]
+    assert [int(items[i * parts, 0]) for i in range(w.M // 64)] == [int(c) for c in w.order]
+    assert np.all(CL[n_items:] == -1)
+    # timestamps (wall clock, 32-bit): each tile became ready after every copy of
+    # its units had started, and take <= ready <= done; copies start <= end
+    wrap = lambda x: x & 0xffffffff
+    base = int(min(L[:n_tiles, 5].min(), items[:, 3].min()))
+    rel = lambda x: (wrap(x - base))
+    for q in range(n_tiles):
+        tm, tn, u0, u1, wg, tt, tr, td = L[q]
+        assert rel(tt) <= rel(tr) <= rel(td)
+        starts = [rel(t) for (u, pt, _, t) in items[:, :4] if u0 <= u <= u1]
+        assert rel(tr) >= max(starts)
+    assert np.all([rel(a) <= rel(b) for a, b in items[:, 3:5]])
+    assert gpu.mk_wall_clock_khz() > 0
 
 
 def test_withheld_chunk_times_out_and_kernel_exits(gpu):

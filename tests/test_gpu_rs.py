@@ -54,14 +54,14 @@ def test_roles_and_baseline_bitwise_identical(gpu):
     # depend on the role split, the tile shape or fusion, so the bits must agree
     for lau in [dict(), dict(n_reduce=-1), dict(n_reduce=16), dict(n_reduce=64, grid=96), dict(mode=1),
                 dict(tile=2), dict(tile=2, n_reduce=32), dict(tile=5, n_reduce=8), dict(tile=5, mode=1),
-                dict(tile=1), dict(tile=3), dict(tile=4)]:
+                dict(tile=3), dict(tile=4)]:
         prob = _run(gpu, w, gpu.make_launch(**lau))
         outs.append(prob.output())
     for i, o in enumerate(outs[1:], 1):
         assert np.array_equal(outs[0], o), f"variant {i} differs"
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile", [2, 3, 4, 5])
 @pytest.mark.parametrize("n_reduce", [8, -1])
 def test_every_tile_config(gpu, tile, n_reduce):
     # ragged N; K = 136 (K = 256 for the direct-to-LDS tile, which needs K % 128 == 0)

@@ -83,3 +83,13 @@ def test_built_kernels_are_clean():
         pytest.skip("library not built in this tree")
     for f in files:
         assert isa_check.check_file(f) == {}, f
+
+
+def test_spill_between_mfmas_is_found():
+    mf = "\tv_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]\n"
+    text = HEAD + mf * 3 + "\tscratch_load_dword v9, off, off offset:8\n" + mf * 3 + "\ts_endpgm\n"
+    (name, lines), = list(isa_check.kernels(text))
+    assert isa_check.spills_among_mfma(lines) == ["scratch_load_dword v9, off, off offset:8"]
+    far = HEAD + mf + "\ts_nop 0\n" * 12 + "\tscratch_store_dword off, v1, off\n" + "\ts_endpgm\n"
+    (name, lines), = list(isa_check.kernels(far))
+    assert isa_check.spills_among_mfma(lines) == []

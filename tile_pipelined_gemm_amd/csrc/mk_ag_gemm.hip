@@ -40,9 +40,11 @@ struct AgParams {
   WsHeader* hdr;
   uint32_t* unit_cnt;   // [n_units] parts landed
   int32_t* tile_log;
+  int32_t* copy_log;
   uint64_t spin_limit;
   int R, m_shard, M, K, N, c_bf16;
   int n_units, unit_rows, parts, part_rows;
+  uint32_t part_bytes;
   int mode, n_copy, tiles_m, tiles_n, n_tiles, withhold;
   uint16_t order[MK_MAX_UNITS];
   uint16_t rb_order[MK_MAX_UNITS];   // tile rows in landing order
@@ -51,6 +53,9 @@ struct AgParams {
 
 constexpr int COPY_UNROLL = 16;   // 16-byte loads in flight per thread (64 KiB per workgroup)
 
+// Role loops take their next work index at the bottom of the body and test it
+// at the top (no `continue`), so every barrier stays in wave-uniform control
+// flow.  Log timestamps are the low 32 bits of the 100 MHz wall clock.
 __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uint32_t* sb) {
   const int tid = threadIdx.x, nt = blockDim.x;
   uint64_t t0 = 0;
@@ -61,38 +66,49 @@ __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uin
   }
   const uint32_t n_work = (uint32_t)p.n_units * p.parts;
   const int n16 = p.part_rows * (p.K / 8);       // 16-byte chunks per part
-  for (;;) {
-    const uint32_t w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
-    if (w >= n_work) break;
+  uint32_t w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
+  while (w < n_work) {
     const int j = w / p.parts, part = w % p.parts;
     const int c = p.order[j];
-    if (c == p.withhold) continue;               // never delivered (failure tests)
-    if (tid == 0) wait_until(t0 + p.delay_ticks[c], p.spin_limit);
-    __syncthreads();
-    // A part lies inside one shard, so it is one contiguous block on both sides.
-    const int row0 = c * p.unit_rows + part * p.part_rows;
-    const u32x4* __restrict__ src =
-        (const u32x4*)(p.shard[row0 / p.m_shard] + (int64_t)(row0 % p.m_shard) * p.K);
-    u32x4* __restrict__ dst = (u32x4*)(p.Ag + (int64_t)row0 * p.K);
-    for (int base = 0; base < n16; base += nt * COPY_UNROLL) {
-      u32x4 v[COPY_UNROLL];
-#pragma unroll
-      for (int u = 0; u < COPY_UNROLL; ++u) {
-        const int i = base + u * nt + tid;
-        if (i < n16) v[u] = src[i];
+    if (c != p.withhold) {                         // a withheld unit never lands (failure tests)
+      uint32_t t_start = 0;
+      if (tid == 0) {
+        wait_until(t0 + p.delay_ticks[c], p.spin_limit);
+        t_start = (uint32_t)now_ticks();
       }
+      __syncthreads();
+      // A part lies inside one shard, so it is one contiguous block on both sides.
+      const int row0 = c * p.unit_rows + part * p.part_rows;
+      // Buffer accesses bounded to the part: past its end loads return zero
+      // and stores are dropped, so the loop needs no per-element guard (a
+      // guarded store would be its own branch, and the compiler would wait for
+      // every earlier memory operation before each one).
+      const __amdgpu_buffer_rsrc_t src =
+          make_rsrc(uni(p.shard[row0 / p.m_shard] + (int64_t)(row0 % p.m_shard) * p.K), p.part_bytes);
+      const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Ag + (int64_t)row0 * p.K), p.part_bytes);
+      for (int base = 0; base < n16; base += nt * COPY_UNROLL) {
+        u32x4 v[COPY_UNROLL];
 #pragma unroll
-      for (int u = 0; u < COPY_UNROLL; ++u) {
-        const int i = base + u * nt + tid;
-        if (i < n16) dst[i] = v[u];
+        for (int u = 0; u < COPY_UNROLL; ++u) v[u] = bload(src, (uint32_t)(base + u * nt + tid) * 16u, 0);
+#pragma unroll
+        for (int u = 0; u < COPY_UNROLL; ++u) bstore(dst, (uint32_t)(base + u * nt + tid) * 16u, 0, v[u]);
+      }
+      // Release only: the copier never reads what others publish, so the
+      // acquire half of a full fence (an L2 invalidate that would also drop
+      // the lines of the GEMM tiles running on this XCD) is not needed.
+      fence_release();
+      __syncthreads();
+      if (tid == 0) {
+        add_release(&p.unit_cnt[c], 1u);
+        add_release(&h->aux[0], 1u);                 // parts landed in total
+        if (p.copy_log) {
+          int32_t* L = p.copy_log + 8 * (int64_t)w;
+          L[0] = c; L[1] = part; L[2] = (int32_t)blockIdx.x;
+          L[3] = (int32_t)t_start; L[4] = (int32_t)(uint32_t)now_ticks();
+        }
       }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      add_release(&p.unit_cnt[c], 1u);
-      add_release(&h->aux[0], 1u);                 // parts landed in total
-    }
+    w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
   }
 }
 
@@ -102,46 +118,52 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, 
   const uint32_t all_parts = (uint32_t)p.n_units * p.parts;
   bool all_landed = (p.mode == MODE_GEMM);
   G g;
-  for (;;) {
-    const uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
-    if (q >= (uint32_t)p.n_tiles) break;
+  uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+  while (q < (uint32_t)p.n_tiles) {
     const int tm = p.rb_order[q / p.tiles_n], tn = q % p.tiles_n;
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int u0 = m0 / p.unit_rows, u1 = (min(p.M, m0 + G::BM) - 1) / p.unit_rows;
+    const uint32_t t_take = (uint32_t)now_ticks();
+    uint32_t ok = 1;
     if (!all_landed) {
-      uint32_t ok = 1, all = 0;
+      uint32_t all = 0;
       if (tid == 0) {
-        for (int u = u0; u <= u1 && ok; ++u) ok = wait_geq(&p.unit_cnt[u], p.parts, h, p.spin_limit);
-        // Once every part has landed (and one acquire has been taken after
-        // that), no later tile of this workgroup needs to wait.
-        if (ok && ld_relaxed(&h->aux[0]) >= all_parts) {
-          fence_acquire();
-          all = 1;
+        for (int u = u0; u <= u1 && ok; ++u) ok = wait_geq_relaxed(&p.unit_cnt[u], p.parts, h, p.spin_limit);
+        // Once every part has landed (and the acquire below has been taken
+        // after that), no later tile of this workgroup needs to wait.
+        if (ok) {
+          all = ld_relaxed(&h->aux[0]) >= all_parts;
+          fence_acquire();                       // one acquire for all the tile's units
         }
       }
       const uint32_t v = wg_bcast(ok | (all << 1), sb);
-      if (!(v & 1u)) continue;
+      ok = v & 1u;
       all_landed = (v >> 1) & 1u;
     }
-    g.bind(p.Ag + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
-    g.run(sm);
-    if (p.c_bf16) {
-      uint16_t* C = (uint16_t*)p.C;
-      g.for_each([&](int r, int c, float v) {
-        const int gr = m0 + r, gc = n0 + c;
-        if (gr < p.M && gc < p.N) C[(int64_t)gr * p.N + gc] = f2bf(v);
-      });
-    } else {
-      float* C = (float*)p.C;
-      g.for_each([&](int r, int c, float v) {
-        const int gr = m0 + r, gc = n0 + c;
-        if (gr < p.M && gc < p.N) C[(int64_t)gr * p.N + gc] = v;
-      });
+    if (ok) {                                      // else the watchdog expired: skip the tile
+      const uint32_t t_ready = (uint32_t)now_ticks();
+      g.bind(p.Ag + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
+      g.run(sm);
+      if (p.c_bf16) {
+        uint16_t* C = (uint16_t*)p.C;
+        g.for_each([&](int r, int c, float v) {
+          const int gr = m0 + r, gc = n0 + c;
+          if (gr < p.M && gc < p.N) C[(int64_t)gr * p.N + gc] = f2bf(v);
+        });
+      } else {
+        float* C = (float*)p.C;
+        g.for_each([&](int r, int c, float v) {
+          const int gr = m0 + r, gc = n0 + c;
+          if (gr < p.M && gc < p.N) C[(int64_t)gr * p.N + gc] = v;
+        });
+      }
+      if (p.tile_log && tid == 0) {
+        int32_t* L = p.tile_log + 8 * (int64_t)q;
+        L[0] = tm; L[1] = tn; L[2] = u0; L[3] = u1; L[4] = (int32_t)blockIdx.x;
+        L[5] = (int32_t)t_take; L[6] = (int32_t)t_ready; L[7] = (int32_t)(uint32_t)now_ticks();
+      }
     }
-    if (p.tile_log && tid == 0) {
-      int32_t* L = p.tile_log + 4 * (int64_t)q;
-      L[0] = tm; L[1] = tn; L[2] = u0; L[3] = u1;
-    }
+    q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
   }
 }
 
@@ -293,6 +315,7 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   p.hdr = (WsHeader*)workspace;
   p.unit_cnt = (uint32_t*)((char*)workspace + sizeof(WsHeader));
   p.tile_log = o.tile_log;
+  p.copy_log = o.copy_log;
   p.spin_limit = mkh::spin_ticks(o, d);
   p.R = R; p.m_shard = (int)m_shard; p.M = (int)M; p.K = (int)K; p.N = (int)N;
   p.c_bf16 = c_dtype == MK_BF16;
@@ -306,10 +329,13 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   const int64_t row_bytes = K * 2;
   int g = s.unit_rows, b = (int)m_shard;
   while (b) { const int t = g % b; g = b; b = t; }   // gcd(unit_rows, m_shard)
-  const int64_t item_bytes = (int64_t)(o.copy_kib > 0 ? o.copy_kib : 1024) << 10;
+  const int64_t item_bytes = (int64_t)(o.copy_kib > 0 ? o.copy_kib : 512) << 10;
   int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(g, item_bytes / row_bytes));
-  while (g % part_rows) --part_rows;
+  // whole rows that divide the unit and the shard; at most 1 GiB per part so
+  // 32-bit buffer offsets cover it
+  while (part_rows > 1 && (g % part_rows || (int64_t)part_rows * row_bytes > (1ll << 30))) --part_rows;
   p.part_rows = part_rows;
+  p.part_bytes = (uint32_t)(part_rows * row_bytes);
   p.parts = s.unit_rows / part_rows;
   for (int j = 0; j < s.n_units; ++j) {
     p.order[j] = (uint16_t)s.order[j];

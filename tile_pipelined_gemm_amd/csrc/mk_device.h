@@ -63,26 +63,34 @@ __device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMI
 // Constant-rate (100 MHz on MI300-class parts) wall clock shared by all CUs.
 __device__ __forceinline__ uint64_t now_ticks() { return wall_clock64(); }
 
-// Thread-0 helper: spin until *p >= target.  Returns false if the watchdog
-// expired (status and abort are then set) or another wait already aborted.
-__device__ inline bool wait_geq(const uint32_t* p, uint32_t target, WsHeader* h,
-                                uint64_t limit_ticks) {
-  if (ld_relaxed(p) >= target) {
-    fence_acquire();
-    return true;
-  }
+// Thread-0 helper: spin until *p >= target, with relaxed loads only (the
+// caller takes one acquire fence after all its waits).  Polls back off to
+// about 1 us apart: hundreds of workgroups polling a few flag lines every
+// few cycles would take memory bandwidth from the copies they wait for.
+// Returns false if the watchdog expired (status and abort are then set) or
+// another wait already aborted.
+__device__ inline bool wait_geq_relaxed(const uint32_t* p, uint32_t target, WsHeader* h,
+                                        uint64_t limit_ticks) {
+  if (ld_relaxed(p) >= target) return true;
   const uint64_t t_begin = now_ticks();
-  while (ld_relaxed(p) < target) {
-    if (ld_relaxed(&h->abort)) return false;
+  for (uint32_t it = 0; ld_relaxed(p) < target; ++it) {
+    if ((it & 15u) == 15u && ld_relaxed(&h->abort)) return false;
     if (now_ticks() - t_begin > limit_ticks) {
       st_relaxed(&h->status, ST_TIMEOUT);
       st_relaxed(&h->abort, 1u);
       return false;
     }
-    __builtin_amdgcn_s_sleep(2);
+    if (it < 8) __builtin_amdgcn_s_sleep(4);
+    else __builtin_amdgcn_s_sleep(32);
   }
-  fence_acquire();
   return true;
+}
+
+// As wait_geq_relaxed, then an agent-scope acquire.
+__device__ inline bool wait_geq(const uint32_t* p, uint32_t target, WsHeader* h, uint64_t limit_ticks) {
+  const bool ok = wait_geq_relaxed(p, target, h, limit_ticks);
+  if (ok) fence_acquire();
+  return ok;
 }
 
 // Thread-0 helper: wait until the wall clock reaches `deadline`, but never
@@ -127,6 +135,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 }
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+// A store past the descriptor's range is dropped by the hardware.
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
 }
 constexpr uint32_t OOB = 0x80000000u;   // a voffset that is always past the end
 

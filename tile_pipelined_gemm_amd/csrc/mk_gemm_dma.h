@@ -24,8 +24,8 @@
 //        slice kt, barrier   (slice kt+1 visible to all waves; no wave reads
 //        stage kt%4 any more)
 //   DMA of slice kt+4 into stage kt%4
-//   read all fragments of slice kt+1 (both 16-deep substeps)
-//   32 MFMAs of slice kt from the fragments read one slice earlier
+//   read all fragments of slice kt+1 (both 16-deep substeps), interleaved
+//        with the 32 MFMAs of slice kt (fragments read one slice earlier)
 // so three slices are in flight while a slice is multiplied.  The DMA is
 // issued through inline asm so the compiler does not add its own
 // (conservative) waits on it; the explicit waits and the barrier are one asm
@@ -81,7 +81,10 @@ __device__ __forceinline__ void wait_barrier() {
   else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int BM_ = 256, int BN_ = 256>
+// INTERLEAVE pins one LDS read after each of the first 24 MFMAs of a slice.
+// It helps when registers are to spare; a kernel that keeps more state live
+// across the K loop (GEMM+RS) turns it off to keep the loop free of spills.
+template <int BM_ = 256, int BN_ = 256, bool INTERLEAVE = true>
 struct TileGemmD {
   static constexpr int BM = BM_, BN = BN_, WM = 2, WN = 2, BK = 32, STAGES = 4;
   static constexpr int NT = 256;
@@ -204,6 +207,17 @@ struct TileGemmD {
     read_frags(na, nb, fo, 1, nxt.a[1], nxt.b[1]);
     mfmas(cur.a[0], cur.b[0]);
     mfmas(cur.a[1], cur.b[1]);
+    // Interleave: one LDS read after each of the first 24 MFMAs (the reads
+    // then overlap the matrix pipeline instead of bunching up in front of it).
+    static_assert(2 * (FM + 2 * FN) == 24 && 2 * FM * FN == 32, "schedule assumes 24 reads, 32 MFMAs");
+    if constexpr (INTERLEAVE) {
+#pragma unroll
+      for (int i = 0; i < 24; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
   }
 
   // Full K loop; the four stages are distinct LDS objects.

@@ -352,6 +352,10 @@ extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, in
   if (o.grid < 0 || o.n_reduce < -1) return fail(MK_ERR_INVALID, "bad grid or n_reduce");
   const int tile = o.tile ? o.tile : rs_tile(M, N, K, mb);
   if (tile <= 0 || tile >= TILE_COUNT) return fail(MK_ERR_INVALID, "tile id %d", tile);
+  // The register-staged 256x256 tile is not built for this operation: with
+  // the partial sums added from its accumulators its K loop spills.
+  if (tile == TILE_256x256)
+    return fail(MK_ERR_UNSUPPORTED, "tile %d is not available for GEMM+RS (use tile %d)", tile, TILE_256x256_DMA);
   if (tile == TILE_256x256_DMA && !TileGemmD<256, 256>::supports_k((int)K))
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
   if (mb % tile_bm(tile)) return fail(MK_ERR_UNSUPPORTED, "rows per owner (%d) must be a multiple of the tile height %d",
@@ -381,11 +385,10 @@ extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, in
   p.out_bf16 = out_dtype == MK_BF16;
   const hipStream_t st = (hipStream_t)stream;
   switch (tile) {
-    case TILE_256x256: return run_rs<TileGemm<256, 256, 2, 2>>(p, o, d, st, can_stage);
     case TILE_128x128: return run_rs<TileGemm<128, 128, 2, 2>>(p, o, d, st, can_stage);
     case TILE_256x128: return run_rs<TileGemm<256, 128, 2, 2>>(p, o, d, st, can_stage);
     case TILE_128x256: return run_rs<TileGemm<128, 256, 2, 2>>(p, o, d, st, can_stage);
-    case TILE_256x256_DMA: return run_rs<TileGemmD<256, 256>>(p, o, d, st, can_stage);
+    case TILE_256x256_DMA: return run_rs<TileGemmD<256, 256, false>>(p, o, d, st, can_stage);
   }
   return fail(MK_ERR_INVALID, "tile id %d", tile);
 }

@@ -162,6 +162,11 @@ extern "C" const char* mk_last_error(void) { return mkh::g_err.c_str(); }
 
 extern "C" int mk_version(void) { return 1; }
 
+extern "C" int mk_wall_clock_khz(void) {
+  const mkh::DevInfo* d = mkh::dev_info();
+  return d ? d->wall_khz : MK_ERR_HIP;
+}
+
 #include "mk_tiles.h"
 
 extern "C" const char* mk_tile_name(int id) {

@@ -202,57 +202,69 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
   }
   const uint32_t n_work = (uint32_t)p.n_blocks * p.parts;
   const int base_local = p.offsets[p.eb];
-  const int cpr = p.H / 8;
-  for (;;) {
-    const uint32_t w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
-    if (w >= n_work) break;
+  const int cpr = p.H / 8;                        // 16-byte chunks per row
+  const uint32_t row_bytes = (uint32_t)p.H * 2u;
+  // One uniform exit at the top, next item taken at the bottom: every barrier
+  // stays in wave-uniform control flow.
+  uint32_t w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
+  while (w < n_work) {
     const int j = w / p.parts, part = w % p.parts;
     const int blk = p.order[j];
-    if (blk == p.withhold) continue;
-    if (tid == 0) {
-      wait_until(t0 + p.delay_ticks[blk], p.spin_limit);
-      s_n = 0;
-    }
-    __syncthreads();
-    const int t0k = blk * p.block_tokens + part * p.part_tokens;
-    const int npair = min(p.part_tokens, p.T - t0k) * p.k;
-    // Positions of this part's pairs; perm for all of them, landing rows for local ones.
-    if (tid < npair) {
-      const int t = t0k + tid / p.k, jj = tid % p.k;
-      const int e = p.topk[(int64_t)t * p.k + jj];
-      const int pos = p.offsets[e] + p.block_off[(int64_t)(t / RB) * p.E + e] + p.rank[(int64_t)t * p.k + jj];
-      p.perm[pos] = t * p.k + jj;
-      const int l = e - p.eb;
-      if (l >= 0 && l < p.L) {
-        const int slot = atomicAdd(&s_n, 1);
-        s_src[slot] = t;
-        s_dst[slot] = pos - base_local;
-        s_tile[slot] = p.tile_base[l] + (pos - p.offsets[e]) / BM;
+    if (blk != p.withhold) {                       // a withheld block never lands (failure tests)
+      if (tid == 0) {
+        wait_until(t0 + p.delay_ticks[blk], p.spin_limit);
+        s_n = 0;
       }
-    }
-    __syncthreads();
-    const int n = s_n;
-    const int64_t total = (int64_t)n * cpr;
-    for (int64_t base = 0; base < total; base += (int64_t)nt * 8) {
-      u32x4 v[8];
+      __syncthreads();
+      const int t0k = blk * p.block_tokens + part * p.part_tokens;
+      const int npair = min(p.part_tokens, p.T - t0k) * p.k;
+      // Positions of this part's pairs; perm for all of them, landing rows for local ones.
+      if (tid < npair) {
+        const int t = t0k + tid / p.k, jj = tid % p.k;
+        const int e = p.topk[(int64_t)t * p.k + jj];
+        const int pos = p.offsets[e] + p.block_off[(int64_t)(t / RB) * p.E + e] + p.rank[(int64_t)t * p.k + jj];
+        p.perm[pos] = t * p.k + jj;
+        const int l = e - p.eb;
+        if (l >= 0 && l < p.L) {
+          const int slot = atomicAdd(&s_n, 1);
+          s_src[slot] = t;
+          s_dst[slot] = pos - base_local;
+          s_tile[slot] = p.tile_base[l] + (pos - p.offsets[e]) / BM;
+        }
+      }
+      __syncthreads();
+      const int n = (int)uni((uint32_t)s_n);
+      // Rows four at a time, each through a descriptor bounded to its row:
+      // chunks past the row end load zero and their stores are dropped, so no
+      // per-element guard; a short last group repeats its last row.
+      for (int r0 = 0; r0 < n; r0 += 4) {
+        for (int c0 = 0; c0 < cpr; c0 += 4 * nt) {
+          u32x4 v[4][4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t i = base + (int64_t)u * nt + tid;
-        if (i < total) v[u] = ((const u32x4*)(p.X + (int64_t)s_src[i / cpr] * p.H))[i % cpr];
-      }
+          for (int rr = 0; rr < 4; ++rr) {
+            const int r = min(r0 + rr, n - 1);
+            const __amdgpu_buffer_rsrc_t src = make_rsrc(uni(p.X + (int64_t)uni((uint32_t)s_src[r]) * p.H), row_bytes);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t i = base + (int64_t)u * nt + tid;
-        if (i < total) ((u32x4*)(p.Xs + (int64_t)s_dst[i / cpr] * p.H))[i % cpr] = v[u];
+            for (int cc = 0; cc < 4; ++cc) v[rr][cc] = bload(src, (uint32_t)(c0 + cc * nt + tid) * 16u, 0);
+          }
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int r = min(r0 + rr, n - 1);
+            const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Xs + (int64_t)uni((uint32_t)s_dst[r]) * p.H), row_bytes);
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) bstore(dst, (uint32_t)(c0 + cc * nt + tid) * 16u, 0, v[rr][cc]);
+          }
+        }
       }
+      __threadfence();
+      __syncthreads();
+      if (tid < 64) {
+        fence_release();
+        for (int q = tid; q < n; q += 64) add_relaxed(&p.tile_cnt[s_tile[q]], 1u);
+      }
+      __syncthreads();
     }
-    __threadfence();
-    __syncthreads();
-    if (tid < 64) {
-      fence_release();
-      for (int q = tid; q < n; q += 64) add_relaxed(&p.tile_cnt[s_tile[q]], 1u);
-    }
-    __syncthreads();
+    w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
   }
 }
 

@@ -113,3 +113,39 @@ class MoeProblem:
         n = self.local_rows()
         return dict(topk=to_numpy(self.topk), counts=to_numpy(self.counts), offsets=to_numpy(self.offsets),
                     perm=to_numpy(self.perm), n_local=n, Y=to_numpy(self.Y[:n]))
+
+
+def ag_timeline(prob, **launch_kw):
+    """Run one AG+GEMM call with the tile and copy logs on and summarise its
+    timeline (microseconds from the first logged event)."""
+    import numpy as np
+    n_rec = 8 * max(4096, 2 * mk.MK_MAX_UNITS * 64)
+    tlog = torch.full((n_rec,), -1, dtype=torch.int32, device="cuda")
+    clog = torch.full((n_rec,), -1, dtype=torch.int32, device="cuda")
+    prob.run(launch=mk.make_launch(tile_log=tlog, copy_log=clog, **launch_kw))
+    torch.cuda.synchronize()
+    khz = mk.load().mk_wall_clock_khz()
+    T = tlog.cpu().numpy().reshape(-1, 8).astype(np.int64)
+    Cl = clog.cpu().numpy().reshape(-1, 8).astype(np.int64)
+    T = T[T[:, 0] >= 0]
+    Cl = Cl[Cl[:, 0] >= 0]
+    stamps = np.concatenate([T[:, 5:8].ravel(), Cl[:, 3:5].ravel()]) & 0xffffffff
+    base = int(stamps.min())
+    us = lambda x: ((np.asarray(x) - base) & 0xffffffff) * 1000.0 / khz
+    out = {"tiles": int(len(T)), "copy_items": int(len(Cl))}
+    if len(Cl):
+        land = {}
+        for u, _, _, _, te in Cl[:, :5]:
+            land[int(u)] = max(land.get(int(u), 0.0), float(us(te)))
+        out.update(copy_first_start_us=float(us(Cl[:, 3]).min()), copy_last_end_us=float(us(Cl[:, 4]).max()),
+                   copy_item_mean_us=float((us(Cl[:, 4]) - us(Cl[:, 3])).mean()),
+                   copy_workgroups=int(len(set(Cl[:, 2].tolist()))),
+                   unit_land_us=[round(land[u], 2) for u in sorted(land)])
+    if len(T):
+        wait = us(T[:, 6]) - us(T[:, 5])
+        comp = us(T[:, 7]) - us(T[:, 6])
+        out.update(first_tile_ready_us=float(us(T[:, 6]).min()), last_tile_done_us=float(us(T[:, 7]).max()),
+                   tile_wait_mean_us=float(wait.mean()), tile_wait_max_us=float(wait.max()),
+                   tile_compute_mean_us=float(comp.mean()), tile_compute_max_us=float(comp.max()),
+                   compute_workgroups=int(len(set(T[:, 4].tolist()))))
+    return out

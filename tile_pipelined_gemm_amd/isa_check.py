@@ -1,5 +1,6 @@
-"""Build-time check of the gfx950 assembly of every kernel: no loop that
-holds a workgroup barrier may be left on an exec-mask branch.
+"""Build-time checks of the gfx950 assembly of every kernel: no loop that
+holds a workgroup barrier may be left on an exec-mask branch, and no
+register spill may sit among the MFMAs of a K loop.
 
 A persistent kernel's role loops contain s_barrier and end in a
 `if (threadIdx.x == 0) { ... }` block (queue atomics, releases).  When the
@@ -126,6 +127,25 @@ def divergent_barrier_loops(lines):
     return bad
 
 
+def spills_among_mfma(lines, window=8):
+    """Return the scratch (register spill) instructions that sit between matrix
+    instructions -- within `window` instructions of an MFMA on both sides,
+    i.e. inside an MFMA loop body, where a spill costs a memory round trip
+    per K step."""
+    ins = [ln.split(";")[0].strip() for ln in lines]
+    ins = [x for x in ins if x and not x.startswith(".") and not x.endswith(":")]
+    mf = [i for i, x in enumerate(ins) if x.startswith("v_mfma")]
+    bad = []
+    for i, x in enumerate(ins):
+        if not x.startswith("scratch_"):
+            continue
+        before = any(i - window <= j < i for j in mf)
+        after = any(i < j <= i + window for j in mf)
+        if before and after:
+            bad.append(x)
+    return bad
+
+
 def check_file(path):
     """Return {kernel symbol: findings} for kernels with findings."""
     with open(path) as f:
@@ -133,6 +153,9 @@ def check_file(path):
     found = {}
     for name, lines in kernels(text):
         b = divergent_barrier_loops(lines)
+        sp = spills_among_mfma(lines)
+        if sp:
+            b = b + [("spill among MFMAs", x) for x in sp[:3]]
         if b:
             found[name] = b
     return found

@@ -26,6 +26,7 @@ EXPORTS = [
     "mk_ag_gemm_workspace", "mk_ag_gemm", "mk_gemm_rs_workspace", "mk_gemm_rs",
     "mk_moe_dispatch_gemm_workspace", "mk_moe_dispatch_gemm", "mk_workspace_init",
     "mk_poll_status", "mk_status_string", "mk_last_error", "mk_tile_name", "mk_version",
+    "mk_wall_clock_khz",
 ]
 
 
@@ -43,7 +44,8 @@ class mk_arrival(C.Structure):
 class mk_launch(C.Structure):
     _fields_ = [("mode", C.c_int32), ("grid", C.c_int32), ("n_copy", C.c_int32),
                 ("n_reduce", C.c_int32), ("tile", C.c_int32), ("spin_limit_us", C.c_uint32),
-                ("tile_log", C.c_void_p), ("copy_kib", C.c_int32), ("reserved", C.c_int32 * 3)]
+                ("tile_log", C.c_void_p), ("copy_kib", C.c_int32), ("reserved0", C.c_int32),
+                ("copy_log", C.c_void_p)]
 
 
 _lib = None
@@ -88,6 +90,8 @@ def load(path: Optional[str] = None):
     lib.mk_tile_name.argtypes = [i32]
     lib.mk_version.restype = i32
     lib.mk_version.argtypes = []
+    lib.mk_wall_clock_khz.restype = i32
+    lib.mk_wall_clock_khz.argtypes = []
     _lib = lib
     return lib
 
@@ -144,9 +148,21 @@ def make_arrival(order=None, delay_ns=None, unit_rows=0, withhold=-1):
     return a, (o, d)
 
 
-def make_launch(mode=0, grid=0, n_copy=0, n_reduce=0, tile=0, spin_limit_us=0, tile_log=None, copy_kib=0):
-    return mk_launch(mode, grid, n_copy, n_reduce, tile, spin_limit_us, _ptr(tile_log), copy_kib,
-                     (C.c_int32 * 3)())
+def mk_wall_clock_khz() -> int:
+    """Rate of the device wall clock that stamps the tile and copy logs (kHz)."""
+    return _check_pos(load().mk_wall_clock_khz())
+
+
+def _check_pos(v: int) -> int:
+    if v < 0:
+        raise MkError(v, load().mk_last_error().decode())
+    return v
+
+
+def make_launch(mode=0, grid=0, n_copy=0, n_reduce=0, tile=0, spin_limit_us=0, tile_log=None, copy_kib=0,
+                copy_log=None):
+    return mk_launch(mode, grid, n_copy, n_reduce, tile, spin_limit_us, _ptr(tile_log), copy_kib, 0,
+                     _ptr(copy_log))
 
 
 # ---------------------------------------------------------------- entry points
