@@ -76,8 +76,15 @@ def parse():
     return ap.parse_args()
 
 
+class Timing(tuple):
+    """(wall ms/step, mean event ms/launch) with the median and minimum of the
+    per-launch event times as attributes."""
+    median = 0.0
+    min = 0.0
+
+
 def timed(fn, steps, warmup, stream):
-    """Run fn warmup+steps times; return (wall ms/step, mean event ms/launch)."""
+    """Run fn warmup+steps times; return Timing(wall ms/step, mean event ms/launch)."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -90,8 +97,11 @@ def timed(fn, steps, warmup, stream):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    kern = sum(a.elapsed_time(b) for a, b in ev) / steps
-    return wall, kern
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    t = Timing((wall, sum(per) / steps))
+    t.median = per[steps // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] + per[steps // 2])
+    t.min = per[0]
+    return t
 
 
 def bench_ag(name, args, stream, extra=True):
@@ -113,12 +123,13 @@ def bench_ag(name, args, stream, extra=True):
     def fused(i):
         probs[i % copies].run(launch=lau0, stream=stream, check=False)
 
-    wall, kern = timed(fused, args.steps, args.warmup, stream)
+    tm = timed(fused, args.steps, args.warmup, stream)
+    wall, kern = tm
     for p in probs:
         assert mk.mk_poll_status(p.ws, stream) == mk.MK_OK
     r = dict(workload=wl.CONFIGS[name]["desc"], M=w.M, K=w.K, N=w.N, R=w.R, chunk_rows=w.unit_rows,
-             copies=copies, ms=wall, kernel_ms=kern, tflops=flops / kern / 1e9,
-             gbs=abytes / kern / 1e6, flops=flops, alg_bytes=abytes)
+             copies=copies, ms=wall, kernel_ms=kern, kernel_ms_median=tm.median, kernel_ms_min=tm.min,
+             tflops=flops / kern / 1e9, gbs=abytes / kern / 1e6, flops=flops, alg_bytes=abytes)
     if extra:
         lau = mk.make_launch(mode=1)
 
@@ -134,8 +145,11 @@ def bench_ag(name, args, stream, extra=True):
                         ("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
                         ("tile_reg", dict(tile=mk.TILE_256x256))]:
             lv = mk.make_launch(**kw)
-            _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 5, 2, stream)
+            _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 10, 3, stream)
             r[f"variant_{tag}_ms"] = vk
+        # overlap efficiency: the share of the shorter phase hidden by fusion
+        tc, tg = r["variant_copy_only_ms"], r["variant_gemm_only_ms"]
+        r["overlap_eff"] = (tc + tg - kern) / min(tc, tg)
         # hipBLASLt yardstick on the already gathered A (not the target)
         Ag = [p.Ag for p in probs]
         Bs = [p.B for p in probs]
