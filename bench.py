@@ -157,7 +157,7 @@ def bench_ag(name, args, stream, extra=True):
         r["speedup_vs_unfused"] = uk / kern
         # role split and scheduling variants of the fused kernel
         for tag, kw in [("n_copy32", dict(n_copy=32)), ("n_copy64", dict(n_copy=64)),
-                        ("copy_kib256", dict(copy_kib=256)), ("copy_kib1024", dict(copy_kib=1024)),
+                        ("copy_kib512", dict(copy_kib=512)), ("copy_writeback", dict(copy_policy=1)),
                         ("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
                         ("tile_reg", dict(tile=mk.TILE_256x256))]:
             lv = mk.make_launch(**kw)

@@ -102,8 +102,10 @@ typedef struct mk_launch {
   uint32_t spin_limit_us; /* watchdog for every wait; 0 = 2,000,000 us */
   int32_t* tile_log;      /* device int32 or NULL: per-tile record, see each op */
   int32_t copy_kib;       /* AG: bytes per copy work item in KiB (one release each);
-                             0 = 512; rounded to whole rows inside one unit and shard */
-  int32_t reserved0;      /* must be zero */
+                             0 = 1024; rounded to whole rows inside one unit and shard */
+  int32_t copy_policy;    /* AG copy stores: 0 = default (2), 1 = write-back
+                             through the XCD L2, 2 = write-through (sc1): the
+                             release after each item then has little to write back */
   int32_t* copy_log;      /* AG: device int32 or NULL: per copy work item (in
                              queue order), 8 int32 {unit, part, workgroup,
                              t_start, t_end, 0, 0, 0}; times are the low 32 bits

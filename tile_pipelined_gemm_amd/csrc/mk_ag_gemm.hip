@@ -45,6 +45,7 @@ struct AgParams {
   int R, m_shard, M, K, N, c_bf16;
   int n_units, unit_rows, parts, part_rows;
   uint32_t part_bytes;
+  int copy_wt;          // copy stores written through the L2
   int mode, n_copy, tiles_m, tiles_n, n_tiles, withhold;
   uint16_t order[MK_MAX_UNITS];
   uint16_t rb_order[MK_MAX_UNITS];   // tile rows in landing order
@@ -52,6 +53,18 @@ struct AgParams {
 };
 
 constexpr int COPY_UNROLL = 16;   // 16-byte loads in flight per thread (64 KiB per workgroup)
+
+template <int POLICY>
+__device__ __forceinline__ void copy_part(__amdgpu_buffer_rsrc_t src, __amdgpu_buffer_rsrc_t dst, int n16, int tid,
+                                          int nt) {
+  for (int base = 0; base < n16; base += nt * COPY_UNROLL) {
+    u32x4 v[COPY_UNROLL];
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) v[u] = bload(src, (uint32_t)(base + u * nt + tid) * 16u, 0);
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) bstore<POLICY>(dst, (uint32_t)(base + u * nt + tid) * 16u, 0, v[u]);
+  }
+}
 
 // Role loops take their next work index at the bottom of the body and test it
 // at the top (no `continue`), so every barrier stays in wave-uniform control
@@ -86,13 +99,8 @@ __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uin
       const __amdgpu_buffer_rsrc_t src =
           make_rsrc(uni(p.shard[row0 / p.m_shard] + (int64_t)(row0 % p.m_shard) * p.K), p.part_bytes);
       const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Ag + (int64_t)row0 * p.K), p.part_bytes);
-      for (int base = 0; base < n16; base += nt * COPY_UNROLL) {
-        u32x4 v[COPY_UNROLL];
-#pragma unroll
-        for (int u = 0; u < COPY_UNROLL; ++u) v[u] = bload(src, (uint32_t)(base + u * nt + tid) * 16u, 0);
-#pragma unroll
-        for (int u = 0; u < COPY_UNROLL; ++u) bstore(dst, (uint32_t)(base + u * nt + tid) * 16u, 0, v[u]);
-      }
+      if (p.copy_wt) copy_part<16>(src, dst, n16, tid, nt);
+      else copy_part<0>(src, dst, n16, tid, nt);
       // Release only: the copier never reads what others publish, so the
       // acquire half of a full fence (an L2 invalidate that would also drop
       // the lines of the GEMM tiles running on this XCD) is not needed.
@@ -303,6 +311,7 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   const mk_launch o = mkh::launch_opts(launch);
   if (o.mode < 0 || o.mode > 3) return fail(MK_ERR_INVALID, "mode %d", o.mode);
   if (o.grid < 0 || o.n_copy < 0 || o.copy_kib < 0) return fail(MK_ERR_INVALID, "negative grid, n_copy or copy_kib");
+  if (o.copy_policy < 0 || o.copy_policy > 2) return fail(MK_ERR_INVALID, "copy_policy %d", o.copy_policy);
   const mkh::DevInfo* d = mkh::dev_info();
   if (!d) return MK_ERR_HIP;
 
@@ -316,6 +325,7 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   p.unit_cnt = (uint32_t*)((char*)workspace + sizeof(WsHeader));
   p.tile_log = o.tile_log;
   p.copy_log = o.copy_log;
+  p.copy_wt = o.copy_policy != 1;              // default: written through
   p.spin_limit = mkh::spin_ticks(o, d);
   p.R = R; p.m_shard = (int)m_shard; p.M = (int)M; p.K = (int)K; p.N = (int)N;
   p.c_bf16 = c_dtype == MK_BF16;
@@ -329,7 +339,7 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   const int64_t row_bytes = K * 2;
   int g = s.unit_rows, b = (int)m_shard;
   while (b) { const int t = g % b; g = b; b = t; }   // gcd(unit_rows, m_shard)
-  const int64_t item_bytes = (int64_t)(o.copy_kib > 0 ? o.copy_kib : 512) << 10;
+  const int64_t item_bytes = (int64_t)(o.copy_kib > 0 ? o.copy_kib : 1024) << 10;
   int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(g, item_bytes / row_bytes));
   // whole rows that divide the unit and the shard; at most 1 GiB per part so
   // 32-bit buffer offsets cover it

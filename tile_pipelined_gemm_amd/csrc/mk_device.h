@@ -113,6 +113,34 @@ __device__ __forceinline__ uint32_t wg_bcast(uint32_t v, uint32_t* slot) {
   return r;
 }
 
+// Transpose the 4x4 blocks held by each quad of lanes: on entry lane j of a
+// quad holds v[k] = element (row k, column j) of the block, on exit (row j,
+// column k).  Two butterfly stages over DPP quad permutations (lane ^ 1, then
+// lane ^ 2); in each, the lane with the bit clear sends element k|m and keeps
+// element k, its partner sends k and keeps k|m.
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 v) {
+  const bool b0 = threadIdx.x & 1, b1 = threadIdx.x & 2;
+#pragma unroll
+  for (int k = 0; k < 4; k += 2) {                    // stage 1: pairs (k, k+1) across lane ^ 1
+    const float r = dpp_xor1(b0 ? v[k] : v[k + 1]);
+    if (b0) v[k] = r;
+    else v[k + 1] = r;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {                       // stage 2: pairs (k, k+2) across lane ^ 2
+    const float r = dpp_xor2(b1 ? v[k] : v[k + 2]);
+    if (b1) v[k] = r;
+    else v[k + 2] = r;
+  }
+  return v;
+}
+
 // fp32 -> bf16 bits, round to nearest even (hardware conversion on gfx950).
 __device__ __forceinline__ uint16_t f2bf(float x) {
   __bf16 b = (__bf16)x;
@@ -136,9 +164,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
-// A store past the descriptor's range is dropped by the hardware.
+// A store past the descriptor's range is dropped by the hardware.  POLICY is
+// the instruction's cache-policy field: 0 default (write-back L2), 16 = sc1
+// (written through the L2 at device scope).
+template <int POLICY = 0>
 __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, POLICY);
 }
 constexpr uint32_t OOB = 0x80000000u;   // a voffset that is always past the end
 

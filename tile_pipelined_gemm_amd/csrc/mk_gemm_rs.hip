@@ -101,50 +101,74 @@ __device__ __forceinline__ void reduce_tile(const RsParams& p, int t) {
 
 // out = acc + P_1 + ... + P_{R-1} for the elements this thread holds, in that
 // order (the same fp32 order as reduce_tile, so every mode gives the same
-// bits).  In a 32x32 accumulator block a lane holds 16 rows of one column, so
-// each wave access covers two 128-byte row segments.  The partial values of
-// four partial sums (64 loads per lane) are in flight before any is added.
+// bits).  In a 32x32 accumulator block each quad of lanes holds 4 columns x
+// 16 rows; a quad transpose (DPP) turns every 4x4 piece into one 4-column row
+// run per lane, so the partial sums are read and the outputs written with
+// 16-byte accesses.  All accesses go through buffer descriptors bounded to
+// the tile's rows, and a column past N gets an out-of-range offset: such a
+// load returns zero and such a store is dropped, so no memory operation sits
+// behind a branch (a guarded store would wait for every earlier access).
 template <class G>
 __device__ __forceinline__ void reduce_from_acc(const G& g, const RsParams& p, int m0, int n0) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
   const int wm = w % G::WM, wn = w / G::WM;
   const int o = m0 / p.mb;                       // a tile never straddles two owners
   const int nq = p.R - 1;
+  const int rows = min(G::BM, p.M - m0);
+  const uint32_t esz = p.out_bf16 ? 2u : 4u;
+  const uint32_t rb4 = (uint32_t)p.N * 4u, rbo = (uint32_t)p.N * esz;   // row bytes in / out
+  const uint32_t in_bytes = uni((uint32_t)rows * rb4);
+  const __amdgpu_buffer_rsrc_t dout =
+      make_rsrc(uni((const char*)p.out[o] + ((int64_t)(m0 - o * p.mb) * p.N) * esz), uni((uint32_t)rows * rbo));
+  // Per-lane part of every offset (the lane's row in a 4-row group and its
+  // 4-column run); the block and group parts are scalar offsets.
+  const int lrow = (lane >> 5) * 4 + (lane & 3), lcol = (lane & 31) & ~3;
+  const uint32_t lin = (uint32_t)lrow * rb4 + (uint32_t)lcol * 4u;
+  const uint32_t lout = (uint32_t)lrow * rbo + (uint32_t)lcol * esz;
 #pragma unroll
   for (int i = 0; i < G::FM; ++i) {
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
-      const int col = n0 + wn * G::TN + j * 32 + (lane & 31);
-      const int rb = m0 + wm * G::TM + i * 32 + (lane >> 5) * 4;
-      const bool colok = col < p.N;
-      f32x16 v = g.acc[i][j];
+      // keep the blocks in order: otherwise the scheduler hoists every
+      // block's transpose ahead of the loads and runs out of registers
+      __builtin_amdgcn_sched_barrier(0);
+      const int cb = n0 + wn * G::TN + j * 32;                 // first column of the block
+      const bool colok = cb + lcol < p.N;
+      const uint32_t vin = colok ? lin : OOB, vout = colok ? lout : OOB;
+      const int rb = wm * G::TM + i * 32;                      // first row of the block in the tile
+      f32x4 v[4];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        v[gq] = quad_transpose(f32x4{g.acc[i][j][4 * gq], g.acc[i][j][4 * gq + 1], g.acc[i][j][4 * gq + 2],
+                                     g.acc[i][j][4 * gq + 3]});
       for (int q0 = 0; q0 < nq; q0 += 4) {
-        float t[4][16];
+        f32x4 t[4][4];
 #pragma unroll
         for (int dq = 0; dq < 4; ++dq) {
           const int q = q0 + dq < nq ? q0 + dq : nq - 1;
-          const float* __restrict__ P = p.P[q] + col;
+          const __amdgpu_buffer_rsrc_t dp = make_rsrc(uni(p.P[q] + (int64_t)m0 * p.N), in_bytes);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = rb + (r >> 2) * 8 + (r & 3);
-            t[dq][r] = (colok && row < p.M) ? P[(int64_t)row * p.N] : 0.f;
-          }
+          for (int gq = 0; gq < 4; ++gq)
+            t[dq][gq] = __builtin_bit_cast(f32x4, bload(dp, vin, uni((uint32_t)(rb + 8 * gq) * rb4 + (uint32_t)cb * 4u)));
         }
 #pragma unroll
         for (int dq = 0; dq < 4; ++dq)
           if (q0 + dq < nq) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) v[r] += t[dq][r];
+            for (int gq = 0; gq < 4; ++gq) v[gq] += t[dq][gq];
           }
       }
-      if (!colok) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rb + (r >> 2) * 8 + (r & 3);
-        if (row >= p.M) continue;
-        const int64_t e = (int64_t)(row - o * p.mb) * p.N + col;
-        if (p.out_bf16) ((uint16_t*)p.out[o])[e] = f2bf(v[r]);
-        else ((float*)p.out[o])[e] = v[r];
+      for (int gq = 0; gq < 4; ++gq) {
+        const uint32_t so = uni((uint32_t)(rb + 8 * gq) * rbo + (uint32_t)cb * esz);
+        if (p.out_bf16) {
+          u32x2 b;
+          b[0] = (uint32_t)f2bf(v[gq][0]) | ((uint32_t)f2bf(v[gq][1]) << 16);
+          b[1] = (uint32_t)f2bf(v[gq][2]) | ((uint32_t)f2bf(v[gq][3]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(b, dout, vout, so, 0);
+        } else {
+          bstore(dout, vout, so, __builtin_bit_cast(u32x4, v[gq]));
+        }
       }
     }
   }

@@ -44,7 +44,7 @@ class mk_arrival(C.Structure):
 class mk_launch(C.Structure):
     _fields_ = [("mode", C.c_int32), ("grid", C.c_int32), ("n_copy", C.c_int32),
                 ("n_reduce", C.c_int32), ("tile", C.c_int32), ("spin_limit_us", C.c_uint32),
-                ("tile_log", C.c_void_p), ("copy_kib", C.c_int32), ("reserved0", C.c_int32),
+                ("tile_log", C.c_void_p), ("copy_kib", C.c_int32), ("copy_policy", C.c_int32),
                 ("copy_log", C.c_void_p)]
 
 
@@ -160,8 +160,8 @@ def _check_pos(v: int) -> int:
 
 
 def make_launch(mode=0, grid=0, n_copy=0, n_reduce=0, tile=0, spin_limit_us=0, tile_log=None, copy_kib=0,
-                copy_log=None):
-    return mk_launch(mode, grid, n_copy, n_reduce, tile, spin_limit_us, _ptr(tile_log), copy_kib, 0,
+                copy_log=None, copy_policy=0):
+    return mk_launch(mode, grid, n_copy, n_reduce, tile, spin_limit_us, _ptr(tile_log), copy_kib, copy_policy,
                      _ptr(copy_log))
 
 
