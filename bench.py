@@ -238,9 +238,14 @@ def bench_moe(args, stream, extra=True):
              flops=flops, alg_bytes=abytes)
     if extra:
         lau = mk.make_launch(mode=1)
-        _, uk = timed(lambda i: probs[i % copies].run(launch=lau, stream=stream, check=False), 3, 1, stream)
+        _, uk = timed(lambda i: probs[i % copies].run(launch=lau, stream=stream, check=False), 5, 2, stream)
         r["unfused_ms"] = uk
         r["speedup_vs_unfused"] = uk / kern
+        for tag, kw in [("n_copy32", dict(n_copy=32)), ("n_copy128", dict(n_copy=128)),
+                        ("n_copy64", dict(n_copy=64)), ("tile_reg", dict(tile=mk.TILE_256x256))]:
+            lv = mk.make_launch(**kw)
+            _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 5, 2, stream)
+            r[f"variant_{tag}_ms"] = vk
     return r
 
 
