@@ -94,8 +94,8 @@ typedef struct mk_launch {
                              kernel alone, 3 = its GEMM kernel alone (reads
                              a_gathered as it is) */
   int32_t grid;           /* persistent workgroups; 0 = CUs x occupancy */
-  int32_t n_copy;         /* copy-role workgroups (AG, MoE); 0 = default (AG:
-                             every workgroup copies first, then computes) */
+  int32_t n_copy;         /* copy-role workgroups (AG, MoE); 0 = default
+                             (every workgroup copies first, then computes) */
   int32_t n_reduce;       /* GEMM+RS: reduce-role workgroups; 0 = default;
                              -1 = each compute workgroup reduces its own tiles */
   int32_t tile;           /* tile configuration id; 0 = default (see mk_tile_name) */
