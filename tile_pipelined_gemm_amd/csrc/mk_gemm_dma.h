@@ -220,8 +220,10 @@ struct TileGemmD {
     }
   }
 
-  // Full K loop; the four stages are distinct LDS objects.
-  __device__ __forceinline__ void run(Smem4 m) {
+  // Full K loop; the four stages are distinct LDS objects.  If `mark` is
+  // given, thread 0 sets *mark once three quarters of the K slices are done
+  // (a workgroup that wants to start later than this one can wait for it).
+  __device__ __forceinline__ void run(Smem4 m, uint32_t* mark = nullptr) {
     u32x4 *A0 = m.a[0], *A1 = m.a[1], *A2 = m.a[2], *A3 = m.a[3];
     u32x4 *B0 = m.b[0], *B1 = m.b[1], *B2 = m.b[2], *B3 = m.b[3];
     const FragOfs fo = frag_offsets();
@@ -236,7 +238,9 @@ struct TileGemmD {
     Frags r0, r1;
     read_frags(A0, B0, fo, 0, r0.a[0], r0.b[0]);
     read_frags(A0, B0, fo, 1, r0.a[1], r0.b[1]);
+    const int mark_kt = (nk * 3 / 4) & ~3;
     for (int kt = 0; kt < nk; kt += 4) {
+      if (mark && kt == mark_kt && threadIdx.x == 0) st_relaxed(mark, 1u);
       step(kt + 0, fo, A1, B1, A0, B0, r0, r1);
       step(kt + 1, fo, A2, B2, A1, B1, r1, r0);
       step(kt + 2, fo, A3, B3, A2, B2, r0, r1);

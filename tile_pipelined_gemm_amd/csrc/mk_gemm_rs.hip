@@ -174,6 +174,81 @@ __device__ __forceinline__ void reduce_from_acc(const G& g, const RsParams& p, i
   }
 }
 
+// The same reduction for the direct-to-LDS engine, with the partial sums
+// brought in by LDS DMA instead of register loads: after the K loop the
+// engine's four stages (128 KiB) are free, so each wave owns 32 KiB = 32
+// slots of 1 KiB.  For one 32x32 block a wave issues one DMA per (row group,
+// partial) -- lane L's 16 bytes land at slot + 16 L, exactly the 4-column run
+// it holds after the quad transpose -- so up to 28 KiB per wave are in flight
+// without holding a register; then it waits once, reads its own slots back
+// and adds in the fixed order.  Columns past N get an out-of-range offset
+// (the DMA writes zero).  Used when R - 1 <= 7.
+template <class G>
+__device__ __forceinline__ void reduce_from_acc_lds(const G& g, const RsParams& p, int m0, int n0, Smem4 sm) {
+  const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
+  const int wm = w % G::WM, wn = w / G::WM;
+  const int o = m0 / p.mb;
+  const int nq = p.R - 1;
+  const int rows = min(G::BM, p.M - m0);
+  const uint32_t esz = p.out_bf16 ? 2u : 4u;
+  const uint32_t rb4 = (uint32_t)p.N * 4u, rbo = (uint32_t)p.N * esz;
+  const uint32_t in_bytes = uni((uint32_t)rows * rb4);
+  const __amdgpu_buffer_rsrc_t dout =
+      make_rsrc(uni((const char*)p.out[o] + ((int64_t)(m0 - o * p.mb) * p.N) * esz), uni((uint32_t)rows * rbo));
+  const int lrow = (lane >> 5) * 4 + (lane & 3), lcol = (lane & 31) & ~3;
+  const uint32_t lin = (uint32_t)lrow * rb4 + (uint32_t)lcol * 4u;
+  const uint32_t lout = (uint32_t)lrow * rbo + (uint32_t)lcol * esz;
+  // this wave's 32 slots: 16 in stage a[w], 16 in stage b[w]
+  const uint32_t la = uni(lds_addr(w == 0 ? sm.a[0] : w == 1 ? sm.a[1] : w == 2 ? sm.a[2] : sm.a[3]));
+  const uint32_t lb = uni(lds_addr(w == 0 ? sm.b[0] : w == 1 ? sm.b[1] : w == 2 ? sm.b[2] : sm.b[3]));
+  const char* pa = (const char*)(w == 0 ? sm.a[0] : w == 1 ? sm.a[1] : w == 2 ? sm.a[2] : sm.a[3]);
+  const char* pb = (const char*)(w == 0 ? sm.b[0] : w == 1 ? sm.b[1] : w == 2 ? sm.b[2] : sm.b[3]);
+  u32x4 dp[7];
+#pragma unroll
+  for (int q = 0; q < 7; ++q) dp[q] = buf_desc(p.P[q < nq ? q : 0] + (int64_t)m0 * p.N, q < nq ? in_bytes : 0u);
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      const int cb = n0 + wn * G::TN + j * 32;
+      const bool colok = cb + lcol < p.N;
+      const uint32_t vin = colok ? lin : OOB, vout = colok ? lout : OOB;
+      const int rb = wm * G::TM + i * 32;
+      // slot of (row group gq, partial q) = 7 gq + q
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+        for (int q = 0; q < 7; ++q)
+          if (q < nq) {
+            const int sl = 7 * gq + q;
+            dma16(dp[q], uni(sl < 16 ? la + sl * 1024 : lb + (sl - 16) * 1024), vin,
+                  uni((uint32_t)(rb + 8 * gq) * rb4 + (uint32_t)cb * 4u));
+          }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        f32x4 v = quad_transpose(f32x4{g.acc[i][j][4 * gq], g.acc[i][j][4 * gq + 1], g.acc[i][j][4 * gq + 2],
+                                       g.acc[i][j][4 * gq + 3]});
+#pragma unroll
+        for (int q = 0; q < 7; ++q)
+          if (q < nq) {
+            const int sl = 7 * gq + q;
+            v += *(const f32x4*)((sl < 16 ? pa + sl * 1024 : pb + (sl - 16) * 1024) + 16 * lane);
+          }
+        const uint32_t so = uni((uint32_t)(rb + 8 * gq) * rbo + (uint32_t)cb * esz);
+        if (p.out_bf16) {
+          u32x2 b;
+          b[0] = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+          b[1] = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(b, dout, vout, so, 0);
+        } else {
+          bstore(dout, vout, so, __builtin_bit_cast(u32x4, v));
+        }
+      }
+    }
+  }
+}
+
 // The role loops take their next work index at the bottom of the body and
 // test it at the top, with no `continue`: one uniform exit and one latch, so
 // the compiler keeps every barrier in wave-uniform control flow.
@@ -181,15 +256,44 @@ template <class G, class SM>
 __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, SM sm, uint32_t* sb) {
   const int tid = threadIdx.x;
   G g;
+  // Phase offset (fused epilogue): every workgroup alternates an MFMA-bound K
+  // loop with an HBM-bound reduction, so if all start together all reduce
+  // together.  Odd workgroups therefore start their first tile only when
+  // the first even one is three quarters through its first K loop (aux[1];
+  // measured best among fixed offsets of 0 to 1.3 K loops); from then on the
+  // two halves of the grid are out of phase.  Even workgroups wait on
+  // nothing, so the wait always ends.
+  const bool offset = p.mode == MODE_EPI && p.n_tiles > (int)gridDim.x / 2;
+  if (offset && (blockIdx.x & 1)) {
+    if (tid == 0) wait_geq_relaxed(&h->aux[1], 1u, h, p.spin_limit);
+    __syncthreads();
+  }
+  bool first = true;
   uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
   while (q < (uint32_t)p.n_tiles) {
     const int t = (int)q;
     const int tm = t / p.tiles_n, tn = t % p.tiles_n;
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     g.bind(p.A + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
-    g.run(sm);
+    uint32_t* mark = offset && first && !(blockIdx.x & 1) ? &h->aux[1] : nullptr;
+    if constexpr (G::STAGES == 4) {
+      g.run(sm, mark);                             // raised three quarters into the K loop
+    } else {
+      g.run(sm);
+      if (mark && tid == 0) st_relaxed(mark, 1u);
+    }
+    first = false;
     if (p.mode == MODE_EPI) {
-      reduce_from_acc(g, p, m0, n0);
+      if constexpr (G::STAGES == 4) {
+        if (p.R <= 8) {
+          reduce_from_acc_lds(g, p, m0, n0, sm);
+          __syncthreads();                         // LDS back to the K loop of the next tile
+        } else {
+          reduce_from_acc(g, p, m0, n0);
+        }
+      } else {
+        reduce_from_acc(g, p, m0, n0);
+      }
     } else {
       // Stage the fp32 tile (in the owner block for fp32 output, else in the
       // workspace staging area) for the reduce role or the reduce kernel.
@@ -266,6 +370,7 @@ __device__ __forceinline__ void rs_finish(const RsParams& p, WsHeader* h, uint32
     st_relaxed(&h->tile_next, 0u);
     st_relaxed(&h->red_next, 0u);
     st_relaxed(&h->prod_next, 0u);
+    st_relaxed(&h->aux[1], 0u);
     st_relaxed(&h->abort, 0u);
     st_relaxed(&h->done, 0u);
   }
