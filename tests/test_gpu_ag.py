@@ -191,6 +191,25 @@ def test_dma_tile_matches_register_tile_bitwise(gpu):
     assert np.array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("dma,reg", [(6, 2), (7, 3), (8, 4)])
+def test_smaller_dma_tiles_match_register_tiles(gpu, dma, reg):
+    # 128- and 256-wide direct-to-LDS tiles: ragged M and N, K a multiple of 128
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = wl.make_ag(3, 100, 384, 392, seed=44, unit_rows=20, max_delay_ns=5000)
+    prob = AgProblem(w)
+    outs = []
+    for tile in (reg, dma):
+        prob.Ag.fill_(float("nan"))
+        prob.C.zero_()
+        prob.run(launch=gpu.make_launch(tile=tile))
+        torch.cuda.synchronize()
+        assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+        outs.append(prob.output())
+    C64, _ = og.ag_gemm(w.shards, w.B, "bf16")
+    assert_close(out_to_f64(outs[1], "bf16"), C64, "bf16", f"dma tile {dma}")
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_dma_tile_integer_inputs_bit_exact(gpu):
     w = wl.make_ag(2, 160, 512, 264, seed=42, dist="int", unit_rows=32, out_dtype="f32")
     prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA))

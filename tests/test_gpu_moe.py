@@ -72,7 +72,10 @@ def test_schedule_roles_and_baseline_bitwise_identical(gpu):
     for kw in [dict(), dict(order=np.arange(nb)[::-1].copy()), dict(delay_ns=np.full(nb, 5000)),
                dict(launch=gpu.make_launch(n_copy=1)), dict(launch=gpu.make_launch(mode=1)),
                dict(launch=gpu.make_launch(tile=2)), dict(launch=gpu.make_launch(tile=gpu.TILE_256x256)),
-               dict(launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA))]:
+               dict(launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA)),
+               dict(launch=gpu.make_launch(tile=gpu.TILE_128x128_DMA)),
+               dict(launch=gpu.make_launch(tile=gpu.TILE_256x128_DMA)),
+               dict(launch=gpu.make_launch(tile=gpu.TILE_128x256_DMA))]:
         prob.Xs.fill_(float("nan"))
         prob.Y.zero_()
         prob.run(**kw)

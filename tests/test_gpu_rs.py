@@ -54,18 +54,18 @@ def test_roles_and_baseline_bitwise_identical(gpu):
     # depend on the role split, the tile shape or fusion, so the bits must agree
     for lau in [dict(), dict(n_reduce=-1), dict(n_reduce=16), dict(n_reduce=64, grid=96), dict(mode=1),
                 dict(tile=2), dict(tile=2, n_reduce=32), dict(tile=5, n_reduce=8), dict(tile=5, mode=1),
-                dict(tile=3), dict(tile=4)]:
+                dict(tile=3), dict(tile=4), dict(tile=6), dict(tile=7), dict(tile=8)]:
         prob = _run(gpu, w, gpu.make_launch(**lau))
         outs.append(prob.output())
     for i, o in enumerate(outs[1:], 1):
         assert np.array_equal(outs[0], o), f"variant {i} differs"
 
 
-@pytest.mark.parametrize("tile", [2, 3, 4, 5])
+@pytest.mark.parametrize("tile", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("n_reduce", [8, -1])
 def test_every_tile_config(gpu, tile, n_reduce):
-    # ragged N; K = 136 (K = 256 for the direct-to-LDS tile, which needs K % 128 == 0)
-    w = wl.make_rs(1024, 256 if tile == 5 else 136, 392, 4, seed=24)
+    # ragged N; K = 136 (K = 256 for the direct-to-LDS tiles, which need K % 128 == 0)
+    w = wl.make_rs(1024, 256 if tile >= 5 else 136, 392, 4, seed=24)
     prob = _run(gpu, w, gpu.make_launch(tile=tile, n_reduce=n_reduce))
     S, _, _ = orc.gemm_rs(w.A, w.B, w.partials, w.R)
     assert_close(out_to_f64(prob.output(), "f32"), S, "f32", f"RS tile {tile}")

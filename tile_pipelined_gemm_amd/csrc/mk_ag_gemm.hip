@@ -353,15 +353,20 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   }
   const hipStream_t st = (hipStream_t)stream;
   int tile = o.tile ? o.tile : mk_default_tile(M, N, K);
+  // Only the 256x256 tile switches to the direct-to-LDS engine by default: at
+  // 128 rows the register-staged engine measured faster (skinny shapes).
   if (!o.tile && tile == TILE_256x256 && TileGemmD<256, 256>::supports_k((int)K)) tile = TILE_256x256_DMA;
+  if (mk_is_dma_tile(tile) && !TileGemmD<256, 256>::supports_k((int)K))
+    return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
   switch (tile) {
     case TILE_256x256: return run_ag<TileGemm<256, 256, 2, 2>>(p, o, s, d, st);
     case TILE_128x128: return run_ag<TileGemm<128, 128, 2, 2>>(p, o, s, d, st);
     case TILE_256x128: return run_ag<TileGemm<256, 128, 2, 2>>(p, o, s, d, st);
     case TILE_128x256: return run_ag<TileGemm<128, 256, 2, 2>>(p, o, s, d, st);
-    case TILE_256x256_DMA:
-      if (!TileGemmD<256, 256>::supports_k((int)K)) return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
-      return run_ag<TileGemmD<256, 256>>(p, o, s, d, st);
+    case TILE_256x256_DMA: return run_ag<TileGemmD<256, 256>>(p, o, s, d, st);
+    case TILE_128x128_DMA: return run_ag<TileGemmD<128, 128>>(p, o, s, d, st);
+    case TILE_256x128_DMA: return run_ag<TileGemmD<256, 128>>(p, o, s, d, st);
+    case TILE_128x256_DMA: return run_ag<TileGemmD<128, 256>>(p, o, s, d, st);
     default: return fail(MK_ERR_INVALID, "tile id %d", tile);
   }
 }

@@ -74,14 +74,16 @@ __device__ __forceinline__ void dma16(u32x4 desc, uint32_t lds, uint32_t voff, u
 // outstanding and all its LDS reads have returned, then barrier.
 template <int N>
 __device__ __forceinline__ void wait_barrier() {
-  static_assert(N == 0 || N == 8 || N == 16 || N == 24, "vmcnt");
-  if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// INTERLEAVE pins one LDS read after each of the first 24 MFMAs of a slice.
+// Tiles of 128 or 256 rows by 128 or 256 columns, 4 waves (2x2), each wave a
+// (BM/2)x(BN/2) block of 32x32 MFMA tiles.  Per 32-deep K slice and per wave
+// the DMA moves BM/64 KiB of A (16 rows per instruction) and BN/64 KiB of B
+// (1024 / (2*BN) k-rows per instruction).
+//
+// INTERLEAVE pins one LDS read after each MFMA of a slice (256x256 only).
 // It helps when registers are to spare; a kernel that keeps more state live
 // across the K loop (GEMM+RS) turns it off to keep the loop free of spills.
 template <int BM_ = 256, int BN_ = 256, bool INTERLEAVE = true>
@@ -92,10 +94,12 @@ struct TileGemmD {
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;   // per stage
   static constexpr int A_INS = A_BYTES / 1024 / 4, B_INS = B_BYTES / 1024 / 4;  // DMA per wave per slice
+  static constexpr int D = A_INS + B_INS;                              // vm operations per slice
+  static constexpr int B_ROWS = 1024 / (2 * BN);                       // k-rows per B instruction
   static constexpr int SA_U4 = A_BYTES / 16, SB_U4 = B_BYTES / 16;
   static constexpr int LDS_U4 = STAGES * (SA_U4 + SB_U4);
-  static_assert(A_INS + B_INS == 8, "the vmcnt immediates assume 8 DMA instructions per slice");
-  static_assert(BM == 256 && BN == 256, "fragment addressing assumes a 256x256 tile");
+  static constexpr int READS = 2 * (FM + 2 * FN), MFMAS = 2 * FM * FN;  // per slice and wave
+  static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile shape");
 
   f32x16 acc[FM][FN];
   u32x4 dA, dB;
@@ -106,7 +110,7 @@ struct TileGemmD {
 
   __device__ __forceinline__ void bind(const uint16_t* A, int64_t lda, int mrows, const uint16_t* B,
                                        int64_t ldb, int ncols, const uint16_t* B_end, int K) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     ldaB = uni((uint32_t)(lda * 2));
     ldbB = uni((uint32_t)(ldb * 2));
     const int rows = mrows < BM ? mrows : BM;
@@ -116,14 +120,18 @@ struct TileGemmD {
     // A: LDS unit p = blk*64 + lane holds tile row p/4 = blk*16 + lane/4 and
     // physical chunk p%4, which is logical k-chunk (p%4) ^ ((row>>2)&3).
     voA = (uint32_t)(lane >> 2) * ldaB + (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
-    // B: LDS unit p holds k-row p/32; physical chunk p%32 = logical ^ ((row&3)<<2).
-    const int brow = (2 * w + (lane >> 5)) & 3;
-    const int lchunk = (lane & 31) ^ (brow << 2);
-    voB = (lchunk * 8 < ncols) ? (uint32_t)(lane >> 5) * ldbB + (uint32_t)lchunk * 16u : OOB;
+    // B: an instruction covers B_ROWS k-rows of BN/8 chunks; physical chunk
+    // = logical ^ ((k-row & 3) << 2).  Block blk = i*4 + w starts at k-row
+    // blk*B_ROWS, so k-row & 3 = (w*B_ROWS + lane / (BN/8)) & 3.
+    const int w = threadIdx.x >> 6;
+    const int rin = lane / (BN / 8);
+    const int brow = (w * B_ROWS + rin) & 3;
+    const int lchunk = (lane % (BN / 8)) ^ (brow << 2);
+    voB = (lchunk * 8 < ncols) ? (uint32_t)rin * ldbB + (uint32_t)lchunk * 16u : OOB;
   }
 
-  // DMA of K slice kt into stage buffers (sa, sb): each wave fills 4 KiB of
-  // A (16-row blocks) and 4 KiB of B (2-row blocks).
+  // DMA of K slice kt into stage buffers (sa, sb): each wave fills A_INS KiB
+  // of A (16-row blocks) and B_INS KiB of B (B_ROWS-row blocks).
   __device__ __forceinline__ void issue(u32x4* sa, u32x4* sb, int kt) {
     const int w = uni((int)(threadIdx.x >> 6));   // wave index: the same in every lane
     const uint32_t la = uni(lds_addr(sa)), lb = uni(lds_addr(sb));
@@ -135,7 +143,7 @@ struct TileGemmD {
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
       const int blk = i * 4 + w;
-      dma16(dB, uni(lb + blk * 1024), voB, uni((uint32_t)(kt * BK + blk * 2) * ldbB));
+      dma16(dB, uni(lb + blk * 1024), voB, uni((uint32_t)(kt * BK + blk * B_ROWS) * ldbB));
     }
   }
 
@@ -161,9 +169,11 @@ struct TileGemmD {
     f.a[1] = arow * 64 + ((2 + hi) ^ as) * 16;
     const int brow = (g >> 1) * 8 + (Lg >> 2);
     const int u = 2 * (g & 1) + ((Lg & 3) >> 1);
-    // fragment j covers logical chunks wn*16 + 4j + (0..3); k-row & 3 == Lg >> 2
+    // fragment j covers logical chunks 4c + (0..3), c = (wn*TN + 32j) / 32;
+    // its k-rows have (row & 3) == Lg >> 2, so the group c is XORed with it
 #pragma unroll
-    for (int j = 0; j < FN; ++j) f.b[j] = brow * (BN * 2) + (wn * 16 + 4 * (j ^ (Lg >> 2)) + u) * 16 + (Lg & 1) * 8;
+    for (int j = 0; j < FN; ++j)
+      f.b[j] = brow * (BN * 2) + (4 * ((wn * FN + j) ^ (Lg >> 2)) + u) * 16 + (Lg & 1) * 8;
     return f;
   }
 
@@ -197,8 +207,8 @@ struct TileGemmD {
   __device__ __forceinline__ void step(int kt, const FragOfs& fo, const u32x4* na, const u32x4* nb,
                                        u32x4* fa, u32x4* fb, Frags& cur, Frags& nxt) {
     const int later = nk - 2 - kt;          // slices after kt+1 already issued (at most 2 count)
-    if (later >= 2) wait_barrier<16>();
-    else if (later == 1) wait_barrier<8>();
+    if (later >= 2) wait_barrier<2 * D>();
+    else if (later == 1) wait_barrier<D>();
     else wait_barrier<0>();
     if (kt + 4 < nk) issue(fa, fb, kt + 4);
     // on the last slice these read a stage nobody uses; it keeps the branch
@@ -207,16 +217,15 @@ struct TileGemmD {
     read_frags(na, nb, fo, 1, nxt.a[1], nxt.b[1]);
     mfmas(cur.a[0], cur.b[0]);
     mfmas(cur.a[1], cur.b[1]);
-    // Interleave: one LDS read after each of the first 24 MFMAs (the reads
-    // then overlap the matrix pipeline instead of bunching up in front of it).
-    static_assert(2 * (FM + 2 * FN) == 24 && 2 * FM * FN == 32, "schedule assumes 24 reads, 32 MFMAs");
-    if constexpr (INTERLEAVE) {
+    // Interleave: one LDS read after each MFMA (the reads then overlap the
+    // matrix pipeline instead of bunching up in front of it).
+    if constexpr (INTERLEAVE && READS <= MFMAS) {
 #pragma unroll
-      for (int i = 0; i < 24; ++i) {
+      for (int i = 0; i < READS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      if constexpr (MFMAS > READS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
     }
   }
 
@@ -234,7 +243,7 @@ struct TileGemmD {
     issue(A1, B1, 1);
     issue(A2, B2, 2);
     issue(A3, B3, 3);
-    wait_barrier<24>();
+    wait_barrier<3 * D>();
     Frags r0, r1;
     read_frags(A0, B0, fo, 0, r0.a[0], r0.b[0]);
     read_frags(A0, B0, fo, 1, r0.a[1], r0.b[1]);

@@ -182,9 +182,11 @@ __device__ __forceinline__ void reduce_from_acc(const G& g, const RsParams& p, i
 // it holds after the quad transpose -- so up to 28 KiB per wave are in flight
 // without holding a register; then it waits once, reads its own slots back
 // and adds in the fixed order.  Columns past N get an out-of-range offset
-// (the DMA writes zero).  Used when R - 1 <= 7.
+// (the DMA writes zero).  Used with the 256x256 tile (16 KiB per stage and
+// operand, so a[w] and b[w] hold 32 slots) when R - 1 <= 7.
 template <class G>
 __device__ __forceinline__ void reduce_from_acc_lds(const G& g, const RsParams& p, int m0, int n0, Smem4 sm) {
+  static_assert(G::SA_U4 * 16 >= 16384 && G::SB_U4 * 16 >= 16384, "32 slots of 1 KiB per wave");
   const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
   const int wm = w % G::WM, wn = w / G::WM;
   const int o = m0 / p.mb;
@@ -284,7 +286,8 @@ __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, 
     }
     first = false;
     if (p.mode == MODE_EPI) {
-      if constexpr (G::STAGES == 4) {
+      // the LDS path needs 32 KiB of stage buffers per wave: 256x256 tile only
+      if constexpr (G::STAGES == 4 && G::BM == 256 && G::BN == 256) {
         if (p.R <= 8) {
           reduce_from_acc_lds(g, p, m0, n0, sm);
           __syncthreads();                         // LDS back to the K loop of the next tile
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(G::NT) void rs_kernel(const RsParams p) {
 // Default: the direct-to-LDS 256x256 tile when K is a multiple of 128 and
 // the owner blocks hold whole tile rows, else 128x128.
 inline int tile_bm(int t) {
-  return (t == TILE_256x256 || t == TILE_256x128 || t == TILE_256x256_DMA) ? 256 : 128;
+  return (t == TILE_256x256 || t == TILE_256x128 || t == TILE_256x256_DMA || t == TILE_256x128_DMA) ? 256 : 128;
 }
 inline int rs_tile(int64_t, int64_t, int64_t K, int mb) {
   return (TileGemmD<256, 256>::supports_k((int)K) && mb % 256 == 0) ? TILE_256x256_DMA : TILE_128x128;
@@ -485,7 +488,7 @@ extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, in
   // the partial sums added from its accumulators its K loop spills.
   if (tile == TILE_256x256)
     return fail(MK_ERR_UNSUPPORTED, "tile %d is not available for GEMM+RS (use tile %d)", tile, TILE_256x256_DMA);
-  if (tile == TILE_256x256_DMA && !TileGemmD<256, 256>::supports_k((int)K))
+  if (mk_is_dma_tile(tile) && !TileGemmD<256, 256>::supports_k((int)K))
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
   if (mb % tile_bm(tile)) return fail(MK_ERR_UNSUPPORTED, "rows per owner (%d) must be a multiple of the tile height %d",
                                       mb, tile_bm(tile));
@@ -518,6 +521,9 @@ extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, in
     case TILE_256x128: return run_rs<TileGemm<256, 128, 2, 2>>(p, o, d, st, can_stage);
     case TILE_128x256: return run_rs<TileGemm<128, 256, 2, 2>>(p, o, d, st, can_stage);
     case TILE_256x256_DMA: return run_rs<TileGemmD<256, 256, false>>(p, o, d, st, can_stage);
+    case TILE_128x128_DMA: return run_rs<TileGemmD<128, 128, false>>(p, o, d, st, can_stage);
+    case TILE_256x128_DMA: return run_rs<TileGemmD<256, 128, false>>(p, o, d, st, can_stage);
+    case TILE_128x256_DMA: return run_rs<TileGemmD<128, 256, false>>(p, o, d, st, can_stage);
   }
   return fail(MK_ERR_INVALID, "tile id %d", tile);
 }

@@ -476,15 +476,20 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   }
   int tile = o.tile ? o.tile : TILE_256x256;
   if (F < 256 && tile == TILE_256x256) tile = TILE_128x128;
+  // Only the 256x256 tile switches to the direct-to-LDS engine by default: at
+  // 128 rows the register-staged engine measured faster (skinny shapes).
   if (!o.tile && tile == TILE_256x256 && TileGemmD<256, 256>::supports_k((int)H)) tile = TILE_256x256_DMA;
+  if (mk_is_dma_tile(tile) && !TileGemmD<256, 256>::supports_k((int)H))
+    return fail(MK_ERR_UNSUPPORTED, "tile %d needs H %% 128 == 0", tile);
   switch (tile) {
     case TILE_256x256: return run_moe<TileGemm<256, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
     case TILE_128x128: return run_moe<TileGemm<128, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
     case TILE_256x128: return run_moe<TileGemm<256, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
     case TILE_128x256: return run_moe<TileGemm<128, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
-    case TILE_256x256_DMA:
-      if (!TileGemmD<256, 256>::supports_k((int)H)) return fail(MK_ERR_UNSUPPORTED, "tile %d needs H %% 128 == 0", tile);
-      return run_moe<TileGemmD<256, 256>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
+    case TILE_256x256_DMA: return run_moe<TileGemmD<256, 256>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
+    case TILE_128x128_DMA: return run_moe<TileGemmD<128, 128>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
+    case TILE_256x128_DMA: return run_moe<TileGemmD<256, 128>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
+    case TILE_128x256_DMA: return run_moe<TileGemmD<128, 256>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
     default: return fail(MK_ERR_INVALID, "tile id %d", tile);
   }
 }

@@ -10,8 +10,23 @@ enum MkTile {
   TILE_256x128 = 3,  // 4 waves, 128x64 per wave
   TILE_128x256 = 4,  // 4 waves, 64x128 per wave
   TILE_256x256_DMA = 5,  // 256x256, direct-to-LDS operand loads, 4-stage ring (K % 128 == 0)
+  TILE_128x128_DMA = 6,  // the same engine at 128x128 (64 KiB LDS, 2 workgroups per CU)
+  TILE_256x128_DMA = 7,
+  TILE_128x256_DMA = 8,
   TILE_COUNT
 };
+
+// The direct-to-LDS version of a register-staged tile shape (K % 128 == 0).
+inline int mk_dma_tile(int t) {
+  switch (t) {
+    case TILE_256x256: return TILE_256x256_DMA;
+    case TILE_128x128: return TILE_128x128_DMA;
+    case TILE_256x128: return TILE_256x128_DMA;
+    case TILE_128x256: return TILE_128x256_DMA;
+    default: return t;
+  }
+}
+inline bool mk_is_dma_tile(int t) { return t >= TILE_256x256_DMA && t <= TILE_128x256_DMA; }
 
 // Per-shape default: the largest tile that still gives every CU work.
 inline int mk_default_tile(int64_t M, int64_t N, int64_t K) {
