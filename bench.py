@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--ag-launch", default="",
                     help="launch options for the primary AG timing, e.g. mode=1,tile=5,n_copy=64,copy_kib=256")
+    ap.add_argument("--moe-timeline", default="",
+                    help="only run the MoE workload once per launch spec (';'-separated) with the "
+                         "tile and copy logs and print each timeline summary as JSON")
     ap.add_argument("--ag-timeline", default="",
                     help="only run the AG workload once per launch spec (';'-separated) with the "
                          "tile and copy logs and print each timeline summary as JSON")
@@ -156,9 +159,10 @@ def bench_ag(name, args, stream, extra=True):
         r["unfused_ms"] = uk
         r["speedup_vs_unfused"] = uk / kern
         # role split and scheduling variants of the fused kernel
-        for tag, kw in [("n_copy32", dict(n_copy=32)), ("n_copy64", dict(n_copy=64)),
-                        ("copy_kib512", dict(copy_kib=512)), ("copy_writeback", dict(copy_policy=1)),
+        for tag, kw in [("n_copy64", dict(n_copy=64)), ("copy_writeback", dict(copy_policy=1)),
+                        ("xcd_queues", dict(queue_mode=1)),
                         ("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
+                        ("gemm_only_xcd_queues", dict(mode=3, queue_mode=1)),
                         ("tile_reg", dict(tile=mk.TILE_256x256))]:
             lv = mk.make_launch(**kw)
             _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 10, 3, stream)
@@ -241,8 +245,10 @@ def bench_moe(args, stream, extra=True):
         _, uk = timed(lambda i: probs[i % copies].run(launch=lau, stream=stream, check=False), 5, 2, stream)
         r["unfused_ms"] = uk
         r["speedup_vs_unfused"] = uk / kern
-        for tag, kw in [("n_copy32", dict(n_copy=32)), ("n_copy128", dict(n_copy=128)),
-                        ("n_copy64", dict(n_copy=64)), ("tile_reg", dict(tile=mk.TILE_256x256))]:
+        for tag, kw in [("n_copy64", dict(n_copy=64)), ("tile_reg", dict(tile=mk.TILE_256x256)),
+                        ("tile_128x256dma", dict(tile=mk.TILE_128x256_DMA)),
+                        ("tile_256x128dma", dict(tile=mk.TILE_256x128_DMA)),
+                        ("tile_128x128dma", dict(tile=mk.TILE_128x128_DMA))]:
             lv = mk.make_launch(**kw)
             _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 5, 2, stream)
             r[f"variant_{tag}_ms"] = vk
@@ -294,6 +300,17 @@ def main():
                 prob.run(launch=mk.make_launch(**kw))
             torch.cuda.synchronize()
             print(json.dumps({"launch": spec, **ag_timeline(prob, **kw)}), flush=True)
+        return
+    if args.moe_timeline:
+        import workloads as wl
+        from tile_pipelined_gemm_amd.harness import MoeProblem, moe_timeline
+        prob = MoeProblem(wl.CONFIGS["moe"]["make"](seed=args.seed))
+        for spec in args.moe_timeline.split(";"):
+            kw = {k: int(v) for k, v in (kv.split("=") for kv in spec.split(",") if kv)}
+            for _ in range(3):                       # warm up
+                prob.run(launch=mk.make_launch(**kw))
+            torch.cuda.synchronize()
+            print(json.dumps({"launch": spec, **moe_timeline(prob, **kw)}), flush=True)
         return
     if args.copy_calib:
         n = args.copy_calib << 20

@@ -64,6 +64,8 @@ typedef enum mk_status {
 #define MK_MAX_EXPERTS 1024 /* E */
 #define MK_MAX_TOPK 16      /* k */
 #define MK_MAX_LOCAL 64     /* L: local experts */
+#define MK_MAX_COLS (1 << 22) /* N (AG, GEMM+RS) and F (MoE): a 256-row output
+                                 tile must span less than 4 GiB */
 
 /*
  * Arrival schedule (host memory).  Unit c becomes available to copy no
@@ -106,10 +108,14 @@ typedef struct mk_launch {
   int32_t copy_policy;    /* AG copy stores: 0 = default (2), 1 = write-back
                              through the XCD L2, 2 = write-through (sc1): the
                              release after each item then has little to write back */
-  int32_t* copy_log;      /* AG: device int32 or NULL: per copy work item (in
-                             queue order), 8 int32 {unit, part, workgroup,
-                             t_start, t_end, 0, 0, 0}; times are the low 32 bits
-                             of the device wall clock (mk_wall_clock_khz) */
+  int32_t* copy_log;      /* AG, MoE: device int32 or NULL: per copy work item
+                             (in queue order), 8 int32, see each op; times are
+                             the low 32 bits of the device wall clock
+                             (mk_wall_clock_khz) */
+  int32_t queue_mode;     /* AG: 0 = default: one tile queue in landing order;
+                             1 = 8 per-XCD queues (the tiles that share an A
+                             row block run on one XCD and share its L2; a
+                             drained queue's workgroups help the others) */
 } mk_launch;
 
 /* ---------------------------------------------------------------------------
@@ -127,6 +133,8 @@ typedef struct mk_launch {
  *   tile_col, first unit, last unit, workgroup, t_take, t_ready, t_done}:
  *   when the tile was taken from the queue, when its units had landed, and
  *   when its stores were issued (low 32 bits of the device wall clock).
+ *   copy_log (optional): per copy work item (in queue order), 8 int32
+ *   {unit, part, workgroup, t_start, t_end, 0, 0, 0}.
  * ------------------------------------------------------------------------- */
 size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_t N, int32_t unit_rows);
 int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
@@ -169,8 +177,14 @@ int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
  * local expert e, Y rows of e = Xs rows of e @ W[e] (W[e] [H x F] bf16),
  * each M-tile starting once all of its rows have landed.
  *   Xs has room for T*min(k, L) rows [x H] bf16, Y for T*min(k, L) rows [x F].
- *   tile_log (optional): per grouped-GEMM M-tile id, 4 int32 {local expert,
- *   first row (expert-relative), rows, landed count seen}.
+ *   tile_log (optional): per output tile q = m_tile*ceil(F/BN) + tile_col
+ *   (BN the tile width of the chosen tile), 8 int32 {local expert, first row
+ *   (expert-relative), rows, landed count seen, workgroup, t_take, t_ready,
+ *   t_done} (times as in the AG tile log).
+ *   copy_log (optional): per copy work item (source block x part of 8 or
+ *   fewer tokens, in queue order), 8 int32 {block, part, workgroup, t_start,
+ *   t_end, local rows copied, t_indexed, t_copied}: t_indexed when the
+ *   item's landing rows were known, t_copied when its stores were issued.
  * ------------------------------------------------------------------------- */
 size_t mk_moe_dispatch_gemm_workspace(int64_t T, int64_t H, int E, int k, int L, int64_t F);
 int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t T, int64_t H, int E, int k,

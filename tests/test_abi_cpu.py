@@ -79,6 +79,8 @@ def test_ag_bad_launch_options(lib):
     assert _ag(lib, launch=C.byref(lau)) == mk.MK_ERR_INVALID
     lau = mk.make_launch(copy_kib=-1)
     assert _ag(lib, launch=C.byref(lau)) == mk.MK_ERR_INVALID
+    lau = mk.make_launch(queue_mode=2)
+    assert _ag(lib, launch=C.byref(lau)) == mk.MK_ERR_INVALID
     lau = mk.make_launch(tile=42)
     rc = _ag(lib, launch=C.byref(lau))
     assert rc in (mk.MK_ERR_INVALID, mk.MK_ERR_HIP)   # device query may come first without a GPU

@@ -66,7 +66,10 @@ def test_output_independent_of_schedule_and_roles(gpu):
             dict(order=w.order, launch=gpu.make_launch(n_copy=64, grid=80)),
             dict(order=w.order, delay_ns=w.delay_ns, launch=gpu.make_launch(copy_kib=16)),
             dict(order=w.order, delay_ns=w.delay_ns, launch=gpu.make_launch(copy_kib=4096, n_copy=3)),
-            dict(launch=gpu.make_launch(mode=1))]
+            dict(order=w.order, launch=gpu.make_launch(queue_mode=1)),
+            dict(order=w.order, launch=gpu.make_launch(queue_mode=1, grid=80)),
+            dict(launch=gpu.make_launch(mode=1)),
+            dict(launch=gpu.make_launch(mode=1, queue_mode=1))]
     outs = []
     for kw in runs:
         prob.Ag.fill_(float("nan"))
@@ -170,6 +173,40 @@ def test_full_size_skinny_config_sampled(gpu):
     w = wl.CONFIGS["skinny_ag"]["make"]()
     prob = _run(gpu, w)
     _sampled_rows(w, prob, 24, 1, "skinny AG 128x8192x28672")
+
+
+# ---- more tiles than workgroups with a partial last round: 272 tiles of
+# 256x256 on 256 workgroups ----
+def _round_workload(dist, out_dtype):
+    # M = 4096, N = 4352: 16 x 17 = 272 tiles; K = 512: 4 K units per tile
+    return wl.make_ag(8, 512, 512, 4352, seed=46, dist=dist, unit_rows=128, max_delay_ns=5000,
+                      out_dtype=out_dtype)
+
+
+def test_partial_round_integer_inputs_bit_exact(gpu):
+    w = _round_workload("int", "f32")
+    prob = _run(gpu, w)
+    _, C = og.ag_gemm(w.shards, w.B, "f32")
+    assert np.array_equal(prob.output(), C)
+
+
+def test_partial_round_output_independent_of_grid_mode_and_engine(gpu):
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = _round_workload("normal", "bf16")
+    prob = AgProblem(w)
+    outs = []
+    for kw in [dict(), dict(grid=80), dict(grid=1), dict(mode=1), dict(queue_mode=1), dict(n_copy=5),
+               dict(tile=gpu.TILE_256x256)]:
+        prob.Ag.fill_(float("nan"))
+        prob.C.zero_()
+        prob.run(launch=gpu.make_launch(**kw))
+        torch.cuda.synchronize()
+        assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK, kw
+        outs.append(prob.output())
+    C64, _ = og.ag_gemm(w.shards, w.B, "bf16")
+    assert_close(out_to_f64(outs[0], "bf16"), C64, "bf16", "AG, 272 tiles")
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(outs[0], o), f"run {i} differs"
 
 
 # ---- the direct-to-LDS tile engine (tile 5) ----

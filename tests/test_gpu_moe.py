@@ -105,6 +105,35 @@ def test_dma_tile_rejects_h_not_multiple_of_128(gpu):
     assert prob.run(launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA), check=False) == gpu.MK_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("tile,bm,bn", [(0, 128, 128), (5, 256, 256)])
+def test_tile_and_copy_logs(gpu, tile, bm, bn):
+    # Every grouped-GEMM tile is logged once with its expert, first row and row
+    # count; in the fused mode each tile saw all of its rows landed.  Every
+    # (block, part) copy item is logged once and the items copy every local row.
+    from tile_pipelined_gemm_amd.harness import MoeProblem
+    w = wl.make_moe(640, 384, 24, 3, 12, 200, seed=38, block_tokens=64, expert_begin=6)
+    prob = MoeProblem(w)
+    tiles_n = -(-w.F // bn)
+    n_tiles = (w.T * min(w.k, w.L) // 128 + w.L + 1) * tiles_n
+    tlog = torch.full((8 * n_tiles,), -1, dtype=torch.int32, device="cuda")
+    clog = torch.full((8 * 2 * w.T,), -1, dtype=torch.int32, device="cuda")
+    prob.run(launch=gpu.make_launch(tile=tile, tile_log=tlog, copy_log=clog))
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+    counts = prob.outputs()["counts"][6:18]
+    want = [(l, r0, min(bm, int(c) - r0)) for l, c in enumerate(counts) for r0 in range(0, int(c), bm)
+            for _ in range(tiles_n)]
+    T = tlog.cpu().numpy().reshape(-1, 8)
+    T = T[T[:, 0] >= 0]
+    assert [tuple(int(x) for x in r[:3]) for r in T] == want
+    assert np.array_equal(T[:, 3], T[:, 2])
+    C = clog.cpu().numpy().reshape(-1, 8)
+    C = C[C[:, 0] >= 0]
+    parts = 64 // 8
+    assert sorted((int(b), int(q)) for b, q in C[:, :2]) == [(b, q) for b in range(w.T // 64) for q in range(parts)]
+    assert int(C[:, 5].sum()) == prob.local_rows()
+
+
 def test_withheld_block_times_out(gpu):
     from tile_pipelined_gemm_amd.harness import MoeProblem
     w = wl.make_moe(512, 64, 32, 4, 8, 64, seed=35, block_tokens=64)

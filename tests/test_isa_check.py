@@ -93,3 +93,44 @@ def test_spill_between_mfmas_is_found():
     far = HEAD + mf + "\ts_nop 0\n" * 12 + "\tscratch_store_dword off, v1, off\n" + "\ts_endpgm\n"
     (name, lines), = list(isa_check.kernels(far))
     assert isa_check.spills_among_mfma(lines) == []
+
+
+def test_wide_store_data_rewritten_right_after_is_flagged():
+    body = """
+        buffer_store_dwordx4 v[36:39], v34, s[60:63], s3 offen
+        v_cndmask_b32_e32 v36, v51, v50, vcc
+        s_endpgm
+    """.splitlines()
+    assert len(isa_check.wide_store_data_overwrites(body)) == 1
+
+
+def test_wide_store_data_rewritten_after_enough_wait_states_passes():
+    ok_nop = """
+        buffer_store_dwordx4 v[36:39], v34, s[60:63], s3 offen
+        s_nop 1
+        v_mov_b32_e32 v36, 0
+    """.splitlines()
+    ok_gap = """
+        buffer_store_dwordx4 v[36:39], v34, s[60:63], s3 offen
+        s_add_i32 s3, s3, 16
+        v_add_u32_e32 v40, s3, v34
+        v_mov_b32_e32 v37, 0
+    """.splitlines()
+    ok_other = """
+        buffer_store_dwordx4 v[36:39], v34, s[60:63], s3 offen
+        v_mov_b32_e32 v40, 0
+    """.splitlines()
+    ok_narrow = """
+        buffer_store_dwordx2 v[36:37], v34, s[60:63], s3 offen
+        v_mov_b32_e32 v36, 0
+    """.splitlines()
+    for body in (ok_nop, ok_gap, ok_other, ok_narrow):
+        assert isa_check.wide_store_data_overwrites(body) == []
+
+
+def test_wide_store_register_range_overlap():
+    body = """
+        buffer_store_dwordx3 v[10:12], v0, s[0:3], s4 offen
+        v_pk_mov_b32 v[12:13], v[0:1], v[0:1] op_sel:[0,1]
+    """.splitlines()
+    assert len(isa_check.wide_store_data_overwrites(body)) == 1

@@ -52,8 +52,9 @@ def _compile(src):
     found = isa_check.check_file(device_asm(src))
     if found:
         lines = [f"  {k}: {v[:3]}" for k, v in found.items()]
-        raise RuntimeError(f"{src}: barrier loop with a per-lane exit (kernel could spin for ever) "
-                           "or register spills inside an MFMA loop:\n" + "\n".join(lines))
+        raise RuntimeError(f"{src}: barrier loop with a per-lane exit (kernel could spin for ever), "
+                           "register spills inside an MFMA loop, or a wide store whose data is "
+                           "rewritten right after it:\n" + "\n".join(lines))
     return obj
 
 

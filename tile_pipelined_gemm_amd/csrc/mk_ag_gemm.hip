@@ -47,6 +47,7 @@ struct AgParams {
   uint32_t part_bytes;
   int copy_wt;          // copy stores written through the L2
   int mode, n_copy, tiles_m, tiles_n, n_tiles, withhold;
+  int xcd_queues;       // tiles from per-XCD queues (else one queue in landing order)
   uint16_t order[MK_MAX_UNITS];
   uint16_t rb_order[MK_MAX_UNITS];   // tile rows in landing order
   uint32_t delay_ticks[MK_MAX_UNITS];
@@ -126,7 +127,27 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, 
   const uint32_t all_parts = (uint32_t)p.n_units * p.parts;
   bool all_landed = (p.mode == MODE_GEMM);
   G g;
-  uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+  // Tile q covers tile row rb_order[q / tiles_n] (tile rows in landing
+  // order) and tile column q % tiles_n.  Per-XCD queues: queue x holds the
+  // tile rows at landing positions x, x + XQ, x + 2*XQ, ..., each with all
+  // its columns, so the tiles that share an A row block run on one XCD.
+  XcdQueues xq(&h->aux[XQ_AUX]);
+  const int tm_n = p.tiles_m, tn_n = p.tiles_n;
+  auto qlen = [tm_n, tn_n](int x) -> uint32_t { return x < tm_n ? (uint32_t)((tm_n - 1 - x) / XQ + 1) * tn_n : 0u; };
+  auto next_tile = [&]() -> uint32_t {
+    uint32_t q = (uint32_t)p.n_tiles;
+    if (tid == 0) {
+      if (!p.xcd_queues) {
+        q = add_relaxed(&h->tile_next, 1u);
+      } else {
+        int x;
+        uint32_t j;
+        if (xq.take(qlen, x, j)) q = (uint32_t)(x + XQ * (int)(j / tn_n)) * tn_n + j % tn_n;
+      }
+    }
+    return wg_bcast(q, sb);
+  };
+  uint32_t q = next_tile();
   while (q < (uint32_t)p.n_tiles) {
     const int tm = p.rb_order[q / p.tiles_n], tn = q % p.tiles_n;
     const int m0 = tm * G::BM, n0 = tn * G::BN;
@@ -152,26 +173,15 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, 
       const uint32_t t_ready = (uint32_t)now_ticks();
       g.bind(p.Ag + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
       g.run(sm);
-      if (p.c_bf16) {
-        uint16_t* C = (uint16_t*)p.C;
-        g.for_each([&](int r, int c, float v) {
-          const int gr = m0 + r, gc = n0 + c;
-          if (gr < p.M && gc < p.N) C[(int64_t)gr * p.N + gc] = f2bf(v);
-        });
-      } else {
-        float* C = (float*)p.C;
-        g.for_each([&](int r, int c, float v) {
-          const int gr = m0 + r, gc = n0 + c;
-          if (gr < p.M && gc < p.N) C[(int64_t)gr * p.N + gc] = v;
-        });
-      }
+      const int64_t esz = p.c_bf16 ? 2 : 4;
+      store_tile(g, (char*)p.C + ((int64_t)m0 * p.N + n0) * esz, p.N, p.M - m0, p.N - n0, p.c_bf16);
       if (p.tile_log && tid == 0) {
         int32_t* L = p.tile_log + 8 * (int64_t)q;
         L[0] = tm; L[1] = tn; L[2] = u0; L[3] = u1; L[4] = (int32_t)blockIdx.x;
         L[5] = (int32_t)t_take; L[6] = (int32_t)t_ready; L[7] = (int32_t)(uint32_t)now_ticks();
       }
     }
-    q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+    q = next_tile();
   }
 }
 
@@ -193,6 +203,7 @@ __device__ __forceinline__ void ag_finish(const AgParams& p, WsHeader* h, uint32
     st_relaxed(&h->copy_next, 0u);
     st_relaxed(&h->abort, 0u);
     st_relaxed(&h->aux[0], 0u);
+    for (int i = 0; i < XQ; ++i) st_relaxed(&h->aux[XQ_AUX + i], 0u);
     __hip_atomic_store(&h->t0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     st_relaxed(&h->done, 0u);
   }
@@ -293,7 +304,7 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   if (K % 8 || N % 8) return fail(MK_ERR_UNSUPPORTED, "K (%lld) and N (%lld) must be multiples of 8",
                                   (long long)K, (long long)N);
   const int64_t M = (int64_t)R * m_shard;
-  if (M > (1 << 30) || K > (1 << 20) || N > (1 << 30) || K * N * 2 >= (1ll << 31))
+  if (M > (1 << 30) || K > (1 << 20) || N > MK_MAX_COLS || K * N * 2 >= (1ll << 31))
     return fail(MK_ERR_UNSUPPORTED, "dimension too large");
   if (!B || !C || !a_gathered) return fail(MK_ERR_INVALID, "B, C and a_gathered must be non-NULL");
   if (c_dtype != MK_BF16 && c_dtype != MK_F32) return fail(MK_ERR_INVALID, "c_dtype %d", c_dtype);
@@ -312,6 +323,7 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   if (o.mode < 0 || o.mode > 3) return fail(MK_ERR_INVALID, "mode %d", o.mode);
   if (o.grid < 0 || o.n_copy < 0 || o.copy_kib < 0) return fail(MK_ERR_INVALID, "negative grid, n_copy or copy_kib");
   if (o.copy_policy < 0 || o.copy_policy > 2) return fail(MK_ERR_INVALID, "copy_policy %d", o.copy_policy);
+  if (o.queue_mode < 0 || o.queue_mode > 1) return fail(MK_ERR_INVALID, "queue_mode %d", o.queue_mode);
   const mkh::DevInfo* d = mkh::dev_info();
   if (!d) return MK_ERR_HIP;
 
@@ -326,6 +338,7 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   p.tile_log = o.tile_log;
   p.copy_log = o.copy_log;
   p.copy_wt = o.copy_policy != 1;              // default: written through
+  p.xcd_queues = o.queue_mode == 1;            // default: one queue in landing order
   p.spin_limit = mkh::spin_ticks(o, d);
   p.R = R; p.m_shard = (int)m_shard; p.M = (int)M; p.K = (int)K; p.N = (int)N;
   p.c_bf16 = c_dtype == MK_BF16;

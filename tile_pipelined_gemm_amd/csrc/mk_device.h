@@ -113,6 +113,39 @@ __device__ __forceinline__ uint32_t wg_bcast(uint32_t v, uint32_t* slot) {
   return r;
 }
 
+// Per-XCD work queues.  MI355X has 8 XCDs of 32 CUs, each with its own L2:
+// tiles that share an operand block reuse it from L2 only when they run on
+// the same XCD, so work is split into XQ queues, one per XCD, and a
+// workgroup drains its own XCD's queue before it helps with the others.
+constexpr int XQ = 8;
+constexpr int XQ_AUX = 16;   // WsHeader::aux[XQ_AUX .. XQ_AUX + XQ) are the queue heads
+
+// The XCD this wave runs on (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ int xcd_id() {
+  return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (XQ - 1);
+}
+
+// Thread-0 state of one workgroup walking the queues: its home queue first,
+// then the others in order; a drained queue is never visited again, so every
+// workgroup stops after at most XQ failed takes.
+struct XcdQueues {
+  uint32_t* head;
+  int home, visited;
+  __device__ explicit XcdQueues(uint32_t* heads) : head(heads), home(xcd_id()), visited(0) {}
+  // Next item: true with its queue x and index j, or false once every queue
+  // is drained.  len(x) is the length of queue x.
+  template <class Len>
+  __device__ bool take(Len len, int& x, uint32_t& j) {
+    while (visited < XQ) {
+      x = (home + visited) & (XQ - 1);
+      j = __hip_atomic_fetch_add(&head[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (j < len(x)) return true;
+      ++visited;
+    }
+    return false;
+  }
+};
+
 // Transpose the 4x4 blocks held by each quad of lanes: on entry lane j of a
 // quad holds v[k] = element (row k, column j) of the block, on exit (row j,
 // column k).  Two butterfly stages over DPP quad permutations (lane ^ 1, then
@@ -161,8 +194,11 @@ __device__ __forceinline__ uint32_t lofs(uint32_t n, uint32_t c) { return n * 9 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
+// POLICY is the instruction's cache-policy field: 0 default, 16 = sc1 (a
+// device-coherent load: it sees what other XCDs wrote through their L2).
+template <int POLICY = 0>
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY);
 }
 // A store past the descriptor's range is dropped by the hardware.  POLICY is
 // the instruction's cache-policy field: 0 default (write-back L2), 16 = sc1
@@ -172,6 +208,19 @@ __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
   __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, POLICY);
 }
 constexpr uint32_t OOB = 0x80000000u;   // a voffset that is always past the end
+
+// Store 16 bytes of values just computed by vector ALU instructions, as two
+// 8-byte stores.  A 16-byte buffer store can read its data registers late
+// enough that the next ALU instruction has already overwritten them: seen on
+// gfx950 with two waves per SIMD, where the first dword of some lanes' stores
+// took the following value.  The compiler inserts no wait there, and stores
+// of at most 8 bytes are outside that hazard.  Copies (data straight from
+// loads, not rewritten by ALU instructions) keep 16-byte stores.
+__device__ __forceinline__ void bstore_alu16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, f32x4 v) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{u[0], u[1]}, r, voff, soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{u[2], u[3]}, r, voff, soff + 8u, 0);
+}
 
 // Values the caller knows to be the same in every lane, moved to scalar
 // registers (buffer descriptors must live there).  The builtin works on int:
@@ -364,5 +413,48 @@ struct TileGemm {
         }
   }
 };
+
+// Store an accumulator tile (either engine: acc[FM][FN], waves WM x WN) to a
+// row-major C at the tile's origin: ld elements per row, the first `rows` x
+// `cols` valid, fp32 or bf16 (round to nearest even).  Each lane's 4x4 blocks
+// are transposed across its quad of lanes so a lane holds 4 consecutive
+// columns of one row, then stored as one 16-byte (fp32) or 8-byte (bf16)
+// access through a descriptor bounded to the valid rows; a 4-column run past
+// `cols` gets the out-of-range offset.  No store is guarded, so none waits
+// for the ones before it.  cols is a multiple of 4 and rows*ld*esize < 2^32.
+template <class G>
+__device__ __forceinline__ void store_tile(const G& g, void* C, int64_t ld, int rows, int cols, bool bf16) {
+  const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
+  const int wm = w % G::WM, wn = w / G::WM;
+  const uint32_t esz = bf16 ? 2u : 4u;
+  const uint32_t rbo = uni((uint32_t)ld * esz);
+  rows = rows < G::BM ? rows : G::BM;
+  const __amdgpu_buffer_rsrc_t d = make_rsrc(uni(C), uni((uint32_t)(rows > 0 ? rows : 0) * rbo));
+  const int lrow = (lane >> 5) * 4 + (lane & 3), lcol = (lane & 31) & ~3;
+  const uint32_t lout = (uint32_t)lrow * rbo + (uint32_t)lcol * esz;
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      const int cb = wn * G::TN + j * 32;                  // first column of the block
+      const uint32_t vo = cb + lcol < cols ? lout : OOB;
+      const int rb = wm * G::TM + i * 32;                  // first row of the block
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x4 v = quad_transpose(f32x4{g.acc[i][j][4 * gq], g.acc[i][j][4 * gq + 1], g.acc[i][j][4 * gq + 2],
+                                             g.acc[i][j][4 * gq + 3]});
+        const uint32_t so = uni((uint32_t)(rb + 8 * gq) * rbo + (uint32_t)cb * esz);
+        if (bf16) {
+          u32x2 b;
+          b[0] = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+          b[1] = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(b, d, vo, so, 0);
+        } else {
+          bstore_alu16(d, vo, so, v);
+        }
+      }
+    }
+  }
+}
 
 }  // namespace mk

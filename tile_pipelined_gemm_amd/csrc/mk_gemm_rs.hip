@@ -167,7 +167,7 @@ __device__ __forceinline__ void reduce_from_acc(const G& g, const RsParams& p, i
           b[1] = (uint32_t)f2bf(v[gq][2]) | ((uint32_t)f2bf(v[gq][3]) << 16);
           __builtin_amdgcn_raw_buffer_store_b64(b, dout, vout, so, 0);
         } else {
-          bstore(dout, vout, so, __builtin_bit_cast(u32x4, v[gq]));
+          bstore_alu16(dout, vout, so, v[gq]);
         }
       }
     }
@@ -244,7 +244,7 @@ __device__ __forceinline__ void reduce_from_acc_lds(const G& g, const RsParams& 
           b[1] = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
           __builtin_amdgcn_raw_buffer_store_b64(b, dout, vout, so, 0);
         } else {
-          bstore(dout, vout, so, __builtin_bit_cast(u32x4, v));
+          bstore_alu16(dout, vout, so, v);
         }
       }
     }
@@ -302,10 +302,7 @@ __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, 
       // workspace staging area) for the reduce role or the reduce kernel.
       float* __restrict__ S = p.stage ? p.stage + (int64_t)m0 * p.N
                                       : (float*)p.out[m0 / p.mb] + (int64_t)(m0 % p.mb) * p.N;
-      g.for_each([&](int r, int c, float v) __attribute__((always_inline)) {
-        const int gr = m0 + r, gc = n0 + c;
-        if (gr < p.M && gc < p.N) S[(int64_t)r * p.N + gc] = v;
-      });
+      store_tile(g, S + n0, p.N, p.M - m0, p.N - n0, false);
       if (p.mode == MODE_ROLES) {
         __threadfence();
         __syncthreads();
@@ -469,7 +466,7 @@ extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, in
   if (M < 1 || K < 8 || N < 8) return fail(MK_ERR_INVALID, "empty or too small shape");
   if (K % 8 || N % 8) return fail(MK_ERR_UNSUPPORTED, "K and N must be multiples of 8");
   if (M % R) return fail(MK_ERR_INVALID, "M (%lld) not divisible by R (%d)", (long long)M, R);
-  if (M > (1 << 30) || K > (1 << 20) || N > (1 << 30) || K * N * 2 >= (1ll << 31) || M * N * 4 >= (1ll << 40))
+  if (M > (1 << 30) || K > (1 << 20) || N > MK_MAX_COLS || K * N * 2 >= (1ll << 31) || M * N * 4 >= (1ll << 40))
     return fail(MK_ERR_UNSUPPORTED, "dimension too large");
   if (R > 1 && !partials) return fail(MK_ERR_INVALID, "partials is NULL");
   if (out_dtype != MK_BF16 && out_dtype != MK_F32) return fail(MK_ERR_INVALID, "out_dtype %d", out_dtype);

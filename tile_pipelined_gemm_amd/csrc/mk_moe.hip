@@ -180,6 +180,7 @@ struct MoeParams {
   uint32_t* tile_cnt;           // [tiles] rows landed per M-tile
   WsHeader* hdr;
   int32_t* tile_log;
+  int32_t* copy_log;
   uint64_t spin_limit;
   int T, H, E, k, L, F, eb, y_bf16;
   int n_blocks, block_tokens, part_tokens, parts;
@@ -189,6 +190,8 @@ struct MoeParams {
 };
 
 constexpr int MAX_PAIRS = 8 * MK_MAX_TOPK;   // part_tokens (<= 8) x k
+constexpr int COPY_ROWS = 8;                 // rows per copy round trip (32 x 16 B loads per thread)
+constexpr int SC1 = 16;                      // cache-policy bits: write through the L2
 
 __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, uint32_t* sb, int BM) {
   __shared__ int32_t s_src[MAX_PAIRS], s_dst[MAX_PAIRS], s_tile[MAX_PAIRS];
@@ -211,8 +214,10 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
     const int j = w / p.parts, part = w % p.parts;
     const int blk = p.order[j];
     if (blk != p.withhold) {                       // a withheld block never lands (failure tests)
+      uint32_t t_start = 0;
       if (tid == 0) {
         wait_until(t0 + p.delay_ticks[blk], p.spin_limit);
+        t_start = (uint32_t)now_ticks();
         s_n = 0;
       }
       __syncthreads();
@@ -233,34 +238,47 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
         }
       }
       __syncthreads();
+      const uint32_t t_indexed = (uint32_t)now_ticks();
       const int n = (int)uni((uint32_t)s_n);
-      // Rows four at a time, each through a descriptor bounded to its row:
-      // chunks past the row end load zero and their stores are dropped, so no
-      // per-element guard; a short last group repeats its last row.
-      for (int r0 = 0; r0 < n; r0 += 4) {
+      // Rows COPY_ROWS at a time, each through a descriptor bounded to its
+      // row: chunks past the row end load zero and their stores are dropped,
+      // so no per-element guard; a short last group repeats its last row.
+      // All loads of a group are issued before its first store (loads and
+      // stores share one in-order counter, so a group is one round trip).
+      // Stores write through the L2 (sc1): the release below then has little
+      // to write back.
+      for (int r0 = 0; r0 < n; r0 += COPY_ROWS) {
         for (int c0 = 0; c0 < cpr; c0 += 4 * nt) {
-          u32x4 v[4][4];
+          u32x4 v[COPY_ROWS][4];
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
+          for (int rr = 0; rr < COPY_ROWS; ++rr) {
             const int r = min(r0 + rr, n - 1);
             const __amdgpu_buffer_rsrc_t src = make_rsrc(uni(p.X + (int64_t)uni((uint32_t)s_src[r]) * p.H), row_bytes);
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) v[rr][cc] = bload(src, (uint32_t)(c0 + cc * nt + tid) * 16u, 0);
           }
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
+          for (int rr = 0; rr < COPY_ROWS; ++rr) {
             const int r = min(r0 + rr, n - 1);
             const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Xs + (int64_t)uni((uint32_t)s_dst[r]) * p.H), row_bytes);
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) bstore(dst, (uint32_t)(c0 + cc * nt + tid) * 16u, 0, v[rr][cc]);
+            for (int cc = 0; cc < 4; ++cc) bstore<SC1>(dst, (uint32_t)(c0 + cc * nt + tid) * 16u, 0, v[rr][cc]);
           }
         }
       }
-      __threadfence();
+      const uint32_t t_copied = (uint32_t)now_ticks();
+      // Release only (no acquire: a copier reads nothing that others publish,
+      // and an L2 invalidate would drop the lines of GEMM tiles on this XCD).
+      fence_release();
       __syncthreads();
       if (tid < 64) {
-        fence_release();
         for (int q = tid; q < n; q += 64) add_relaxed(&p.tile_cnt[s_tile[q]], 1u);
+      }
+      if (tid == 0) add_relaxed(&h->aux[0], 1u);        // items landed in total
+      if (p.copy_log && tid == 0) {
+        int32_t* L = p.copy_log + 8 * (int64_t)w;
+        L[0] = blk; L[1] = part; L[2] = (int32_t)blockIdx.x; L[3] = (int32_t)t_start;
+        L[4] = (int32_t)(uint32_t)now_ticks(); L[5] = n; L[6] = (int32_t)t_indexed; L[7] = (int32_t)t_copied;
       }
       __syncthreads();
     }
@@ -274,41 +292,49 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
   const int n_mt = p.tile_base[p.L];
   const uint32_t n_tiles = (uint32_t)n_mt * p.tiles_n;
   const int base_local = p.offsets[p.eb];
+  const uint32_t all_items = (uint32_t)p.n_blocks * p.parts;   // never reached with a withheld block
+  // Once every copy item has landed and this workgroup has taken an acquire
+  // after seeing that, its later tiles need neither a wait nor an acquire
+  // (each acquire invalidates the XCD's L2 under the other tiles there).
+  bool all_landed = p.mode != MODE_FUSED;
   G g;
   int l = 0;
   for (;;) {
     const uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
     if (q >= n_tiles) break;
+    const uint32_t t_take = (uint32_t)now_ticks();
     const int mt = (int)(q / p.tiles_n), tn = (int)(q % p.tiles_n);
     while (l + 1 < p.L && p.tile_base[l + 1] <= mt) ++l;        // queue is expert-ordered
     while (l > 0 && p.tile_base[l] > mt) --l;
     const int e = p.eb + l;
     const int r0 = (mt - p.tile_base[l]) * G::BM;              // expert-relative first row
     const int rows = min(G::BM, p.counts[e] - r0);
-    if (p.mode == MODE_FUSED) {
-      uint32_t ok = 1;
-      if (tid == 0) ok = wait_geq(&p.tile_cnt[mt], (uint32_t)rows, h, p.spin_limit);
-      if (!wg_bcast(ok, sb)) continue;
+    if (!all_landed) {
+      uint32_t ok = 1, all = 0;
+      if (tid == 0) {
+        ok = wait_geq_relaxed(&p.tile_cnt[mt], (uint32_t)rows, h, p.spin_limit);
+        if (ok) {
+          all = ld_relaxed(&h->aux[0]) >= all_items;
+          fence_acquire();
+        }
+      }
+      const uint32_t v = wg_bcast(ok | (all << 1), sb);
+      all_landed = (v >> 1) & 1u;
+      if (!(v & 1u)) continue;
     }
+    const uint32_t t_ready = (uint32_t)now_ticks();
     const int q0 = p.offsets[e] - base_local + r0;              // landing row of the tile
     const int n0 = tn * G::BN;
     g.bind(p.Xs + (int64_t)q0 * p.H, p.H, rows, p.W[l] + n0, p.F, p.F - n0, p.W[l] + (int64_t)p.H * p.F, p.H);
     g.run(sm);
-    if (p.y_bf16) {
-      uint16_t* Y = (uint16_t*)p.Y;
-      g.for_each([&](int r, int c, float v) {
-        if (r < rows && n0 + c < p.F) Y[(int64_t)(q0 + r) * p.F + n0 + c] = f2bf(v);
-      });
-    } else {
-      float* Y = (float*)p.Y;
-      g.for_each([&](int r, int c, float v) {
-        if (r < rows && n0 + c < p.F) Y[(int64_t)(q0 + r) * p.F + n0 + c] = v;
-      });
-    }
-    if (p.tile_log && tid == 0 && tn == 0) {
-      int32_t* L4 = p.tile_log + 4 * (int64_t)mt;
-      L4[0] = l; L4[1] = r0; L4[2] = rows;
-      L4[3] = p.mode == MODE_FUSED ? (int32_t)ld_relaxed(&p.tile_cnt[mt]) : rows;
+    const int64_t esz = p.y_bf16 ? 2 : 4;
+    store_tile(g, (char*)p.Y + ((int64_t)q0 * p.F + n0) * esz, p.F, rows, p.F - n0, p.y_bf16);
+    if (p.tile_log && tid == 0) {
+      int32_t* L = p.tile_log + 8 * (int64_t)q;
+      L[0] = l; L[1] = r0; L[2] = rows;
+      L[3] = p.mode == MODE_FUSED ? (int32_t)ld_relaxed(&p.tile_cnt[mt]) : rows;
+      L[4] = (int32_t)blockIdx.x; L[5] = (int32_t)t_take; L[6] = (int32_t)t_ready;
+      L[7] = (int32_t)(uint32_t)now_ticks();
     }
   }
 }
@@ -329,6 +355,7 @@ __device__ __forceinline__ void moe_finish(const MoeParams& p, WsHeader* h, uint
     st_relaxed(&h->ticket, 0u);
     st_relaxed(&h->tile_next, 0u);
     st_relaxed(&h->copy_next, 0u);
+    st_relaxed(&h->aux[0], 0u);
     st_relaxed(&h->abort, 0u);
     __hip_atomic_store(&h->t0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     st_relaxed(&h->done, 0u);
@@ -418,7 +445,8 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   if (expert_begin < 0 || expert_begin + L > E) return fail(MK_ERR_INVALID, "local experts outside [0,E)");
   if (y_dtype != MK_BF16 && y_dtype != MK_F32) return fail(MK_ERR_INVALID, "y_dtype %d", y_dtype);
   const int64_t cap = T * std::min(k, L);
-  if (T * k > (1 << 30) || cap * H * 2 >= (1ll << 40) || H * F * 2 >= (1ll << 31) || (int64_t)128 * H * 2 >= (1ll << 31))
+  if (T * k > (1 << 30) || cap * H * 2 >= (1ll << 40) || H * F * 2 >= (1ll << 31) || (int64_t)128 * H * 2 >= (1ll << 31) ||
+      F > MK_MAX_COLS)
     return fail(MK_ERR_UNSUPPORTED, "dimension too large");
   for (int l = 0; l < L; ++l)
     if (!W[l] || !mkh::aligned16(W[l])) return fail(MK_ERR_INVALID, "W[%d] NULL or misaligned", l);
@@ -461,6 +489,7 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   p.tile_cnt = (uint32_t*)(ws + lay.tile_cnt);
   p.hdr = (WsHeader*)workspace;
   p.tile_log = o.tile_log;
+  p.copy_log = o.copy_log;
   p.spin_limit = mkh::spin_ticks(o, d);
   p.T = (int)T; p.H = (int)H; p.E = E; p.k = k; p.L = L; p.F = (int)F; p.eb = expert_begin;
   p.y_bf16 = y_dtype == MK_BF16;

@@ -149,3 +149,49 @@ def ag_timeline(prob, **launch_kw):
                    tile_compute_mean_us=float(comp.mean()), tile_compute_max_us=float(comp.max()),
                    compute_workgroups=int(len(set(T[:, 4].tolist()))))
     return out
+
+
+def moe_timeline(prob, **launch_kw):
+    """Run one MoE dispatch + grouped GEMM call with the tile and copy logs on
+    and summarise its timeline (microseconds from the first logged event)."""
+    import numpy as np
+    w = prob.w
+    n_tiles = (w.T * min(w.k, w.L) // 128 + w.L + 1) * ((w.F + 127) // 128)
+    n_items = w.T + w.block_tokens
+    tlog = torch.full((8 * n_tiles,), -1, dtype=torch.int32, device="cuda")
+    clog = torch.full((8 * n_items,), -1, dtype=torch.int32, device="cuda")
+    prob.run(launch=mk.make_launch(tile_log=tlog, copy_log=clog, **launch_kw))
+    torch.cuda.synchronize()
+    khz = mk.load().mk_wall_clock_khz()
+    T = tlog.cpu().numpy().reshape(-1, 8).astype(np.int64)
+    Cl = clog.cpu().numpy().reshape(-1, 8).astype(np.int64)
+    T = T[T[:, 0] >= 0]
+    Cl = Cl[Cl[:, 0] >= 0]
+    stamps = np.concatenate([T[:, 5:8].ravel(), Cl[:, 3:5].ravel()]) & 0xffffffff
+    base = int(stamps.min())
+    us = lambda x: ((np.asarray(x) - base) & 0xffffffff) * 1000.0 / khz
+    out = {"tiles": int(len(T)), "copy_items": int(len(Cl))}
+    if len(Cl):
+        out.update(copy_first_start_us=float(us(Cl[:, 3]).min()), copy_last_end_us=float(us(Cl[:, 4]).max()),
+                   copy_item_mean_us=float((us(Cl[:, 4]) - us(Cl[:, 3])).mean()),
+                   copy_index_mean_us=float((us(Cl[:, 6]) - us(Cl[:, 3])).mean()),
+                   copy_rows_mean_us=float((us(Cl[:, 7]) - us(Cl[:, 6])).mean()),
+                   copy_release_mean_us=float((us(Cl[:, 4]) - us(Cl[:, 7])).mean()),
+                   copy_rows_per_item=float(Cl[:, 5].mean()),
+                   copy_workgroups=int(len(set(Cl[:, 2].tolist()))))
+    if len(T):
+        take, ready, done = us(T[:, 5]), us(T[:, 6]), us(T[:, 7])
+        comp = done - ready
+        per_wg = {}
+        for wg, d in zip(T[:, 4].tolist(), done.tolist()):
+            per_wg[wg] = max(per_wg.get(wg, 0.0), d)
+        ends = np.array(sorted(per_wg.values()))
+        out.update(first_tile_ready_us=float(ready.min()), last_tile_done_us=float(done.max()),
+                   tile_wait_mean_us=float((ready - take).mean()), tile_wait_max_us=float((ready - take).max()),
+                   tile_compute_mean_us=float(comp.mean()), tile_compute_p10_us=float(np.percentile(comp, 10)),
+                   tile_compute_p90_us=float(np.percentile(comp, 90)),
+                   tiles_per_workgroup_max=int(np.bincount(T[:, 4]).max()),
+                   compute_workgroups=int(len(per_wg)),
+                   workgroup_end_p10_us=float(np.percentile(ends, 10)),
+                   workgroup_end_p50_us=float(np.percentile(ends, 50)))
+    return out

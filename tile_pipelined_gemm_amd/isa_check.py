@@ -1,6 +1,7 @@
 """Build-time checks of the gfx950 assembly of every kernel: no loop that
-holds a workgroup barrier may be left on an exec-mask branch, and no
-register spill may sit among the MFMAs of a K loop.
+holds a workgroup barrier may be left on an exec-mask branch, no register
+spill may sit among the MFMAs of a K loop, and no 12/16-byte buffer store may
+have its data registers rewritten right after it.
 
 A persistent kernel's role loops contain s_barrier and end in a
 `if (threadIdx.x == 0) { ... }` block (queue atomics, releases).  When the
@@ -146,6 +147,40 @@ def spills_among_mfma(lines, window=8):
     return bad
 
 
+_STORE_WIDE = re.compile(r"^buffer_store_dwordx[34]\s+v\[(\d+):(\d+)\]")
+_VDST = re.compile(r"^v_\w+\s+(?:v(\d+)|v\[(\d+):(\d+)\])")
+
+
+def wide_store_data_overwrites(lines, wait_states=2):
+    """Return the 12/16-byte buffer stores whose data registers an ALU
+    instruction rewrites within `wait_states` wait states.  Such a store can
+    read its data late enough to pick up the new value (observed on gfx950),
+    and the compiler inserts no wait for buffer stores with a register
+    soffset, so the code must not produce the pattern."""
+    ins = [ln.split(";")[0].strip() for ln in lines]
+    ins = [x for x in ins if x and not x.startswith(".") and not x.endswith(":")]
+    bad = []
+    for i, x in enumerate(ins):
+        m = _STORE_WIDE.match(x)
+        if not m:
+            continue
+        lo, hi = int(m.group(1)), int(m.group(2))
+        ws, j = 0, i + 1
+        while ws < wait_states and j < len(ins):
+            y = ins[j]
+            d = _VDST.match(y)
+            if d:
+                a = int(d.group(1) or d.group(2))
+                b = int(d.group(1) or d.group(3))
+                if a <= hi and b >= lo:
+                    bad.append(f"{x} | {y}")
+                    break
+            n = re.match(r"^s_nop\s+(\d+)", y)
+            ws += int(n.group(1)) + 1 if n else 1
+            j += 1
+    return bad
+
+
 def check_file(path):
     """Return {kernel symbol: findings} for kernels with findings."""
     with open(path) as f:
@@ -156,6 +191,9 @@ def check_file(path):
         sp = spills_among_mfma(lines)
         if sp:
             b = b + [("spill among MFMAs", x) for x in sp[:3]]
+        ow = wide_store_data_overwrites(lines)
+        if ow:
+            b = b + [("store data rewritten", x) for x in ow[:3]]
         if b:
             found[name] = b
     return found

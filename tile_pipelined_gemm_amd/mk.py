@@ -46,7 +46,7 @@ class mk_launch(C.Structure):
     _fields_ = [("mode", C.c_int32), ("grid", C.c_int32), ("n_copy", C.c_int32),
                 ("n_reduce", C.c_int32), ("tile", C.c_int32), ("spin_limit_us", C.c_uint32),
                 ("tile_log", C.c_void_p), ("copy_kib", C.c_int32), ("copy_policy", C.c_int32),
-                ("copy_log", C.c_void_p)]
+                ("copy_log", C.c_void_p), ("queue_mode", C.c_int32)]
 
 
 _lib = None
@@ -161,9 +161,9 @@ def _check_pos(v: int) -> int:
 
 
 def make_launch(mode=0, grid=0, n_copy=0, n_reduce=0, tile=0, spin_limit_us=0, tile_log=None, copy_kib=0,
-                copy_log=None, copy_policy=0):
+                copy_log=None, copy_policy=0, queue_mode=0):
     return mk_launch(mode, grid, n_copy, n_reduce, tile, spin_limit_us, _ptr(tile_log), copy_kib, copy_policy,
-                     _ptr(copy_log))
+                     _ptr(copy_log), queue_mode)
 
 
 # ---------------------------------------------------------------- entry points
