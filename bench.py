@@ -159,11 +159,16 @@ def bench_ag(name, args, stream, extra=True):
         r["unfused_ms"] = uk
         r["speedup_vs_unfused"] = uk / kern
         # role split and scheduling variants of the fused kernel
-        for tag, kw in [("n_copy64", dict(n_copy=64)), ("copy_writeback", dict(copy_policy=1)),
-                        ("xcd_queues", dict(queue_mode=1)),
-                        ("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
-                        ("gemm_only_xcd_queues", dict(mode=3, queue_mode=1)),
-                        ("tile_reg", dict(tile=mk.TILE_256x256))]:
+        variants = [("n_copy64", dict(n_copy=64)), ("copy_writeback", dict(copy_policy=1)),
+                    ("xcd_queues", dict(queue_mode=1)),
+                    ("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
+                    ("gemm_only_xcd_queues", dict(mode=3, queue_mode=1))]
+        if w.M >= 256:
+            variants.append(("tile_reg", dict(tile=mk.TILE_256x256)))
+        else:                                        # skinny: the 128-row tiles
+            variants += [("tile_128x128", dict(tile=mk.TILE_128x128)),
+                         ("tile_128x256", dict(tile=mk.TILE_128x256))]
+        for tag, kw in variants:
             lv = mk.make_launch(**kw)
             _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 10, 3, stream)
             r[f"variant_{tag}_ms"] = vk

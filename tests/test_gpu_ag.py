@@ -209,6 +209,34 @@ def test_partial_round_output_independent_of_grid_mode_and_engine(gpu):
         assert np.array_equal(outs[0], o), f"run {i} differs"
 
 
+# ---- skinny shapes (M = 128, one tile row; the default tile is 128x256
+# direct-to-LDS): every tile shape and engine gives the same bits ----
+def test_skinny_integer_inputs_bit_exact(gpu):
+    w = wl.make_ag(8, 16, 2048, 8192, seed=47, dist="int", unit_rows=16, max_delay_ns=5000, out_dtype="f32")
+    prob = _run(gpu, w)
+    _, C = og.ag_gemm(w.shards, w.B, "f32")
+    assert np.array_equal(prob.output(), C)
+
+
+def test_skinny_output_independent_of_grid_mode_and_engine(gpu):
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = wl.make_ag(8, 16, 2048, 28672, seed=48, unit_rows=16, max_delay_ns=5000)
+    prob = AgProblem(w)
+    outs = []
+    for kw in [dict(), dict(grid=80), dict(grid=3), dict(mode=1), dict(n_copy=5), dict(queue_mode=1),
+               dict(tile=gpu.TILE_128x128_DMA), dict(tile=gpu.TILE_128x128), dict(tile=gpu.TILE_128x256)]:
+        prob.Ag.fill_(float("nan"))
+        prob.C.zero_()
+        prob.run(launch=gpu.make_launch(**kw))
+        torch.cuda.synchronize()
+        assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK, kw
+        outs.append(prob.output())
+    C64, _ = og.ag_gemm(w.shards, w.B, "bf16")
+    assert_close(out_to_f64(outs[0], "bf16"), C64, "bf16", "skinny AG")
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(outs[0], o), f"run {i} differs"
+
+
 # ---- the direct-to-LDS tile engine (tile 5) ----
 def test_dma_tile_matches_register_tile_bitwise(gpu):
     # M = 300 and N = 392 are ragged for a 256x256 tile; K = 1024 is a multiple of 128.
