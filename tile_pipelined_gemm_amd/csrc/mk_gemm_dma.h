@@ -18,15 +18,16 @@
 // swizzle is applied on the global side of each copy, because every DMA
 // instruction fills 1 KiB of LDS linearly.
 //
-// Schedule, per K slice kt (stage kt%4), every branch free of LDS reads so the
-// compiler's own LDS waits stay exact:
+// Schedule, per K slice kt (stage kt%4), with no branch in the loop:
 //   wait for this wave's DMA of slice kt+1 and for its own fragment reads of
 //        slice kt, barrier   (slice kt+1 visible to all waves; no wave reads
 //        stage kt%4 any more)
-//   DMA of slice kt+4 into stage kt%4
-//   read all fragments of slice kt+1 (both 16-deep substeps), interleaved
-//        with the 32 MFMAs of slice kt (fragments read one slice earlier)
-// so three slices are in flight while a slice is multiplied.  The DMA is
+//   the MFMAs of slice kt (fragments read one slice earlier) in chunks, each
+//        followed by its share of the fragment reads of slice kt+1 and of the
+//        DMA of slice kt+4 into stage kt%4
+// so three slices are in flight while a slice is multiplied, and the DMA
+// issue overlaps the matrix pipeline (issued all at once after the barrier
+// it held back each slice's first MFMA: 11% of the GEMM time).  The DMA is
 // issued through inline asm so the compiler does not add its own
 // (conservative) waits on it; the explicit waits and the barrier are one asm
 // statement with a memory clobber, so no LDS access moves across them.
@@ -83,9 +84,9 @@ __device__ __forceinline__ void wait_barrier() {
 // the DMA moves BM/64 KiB of A (16 rows per instruction) and BN/64 KiB of B
 // (1024 / (2*BN) k-rows per instruction).
 //
-// INTERLEAVE pins one LDS read after each MFMA of a slice (256x256 only).
-// It helps when registers are to spare; a kernel that keeps more state live
-// across the K loop (GEMM+RS) turns it off to keep the loop free of spills.
+// INTERLEAVE pins one LDS read after each MFMA inside a chunk.  It helps
+// when registers are to spare; a kernel that keeps more state live across
+// the K loop (GEMM+RS) turns it off to keep the loop free of spills.
 template <int BM_ = 256, int BN_ = 256, bool INTERLEAVE = true>
 struct TileGemmD {
   static constexpr int BM = BM_, BN = BN_, WM = 2, WN = 2, BK = 32, STAGES = 4;
@@ -177,55 +178,84 @@ struct TileGemmD {
     return f;
   }
 
-  __device__ __forceinline__ void read_frags(const u32x4* sa, const u32x4* sb, const FragOfs& f, int ks,
-                                             bf16x8 (&af)[FM], bf16x8 (&bfr)[FN]) const {
+  // B fragments are kept as their two transposed-read halves and joined at
+  // the MFMA (the join is register naming only).
+  struct Frags { bf16x8 a[2][FM]; i16x4 bl[2][FN]; i16x4 bu[2][FN]; };
+
+  static constexpr int CH = 2 * FM;                 // chunks per slice: (substep, A fragment)
+  static constexpr int RPC = READS / CH;            // fragment reads per chunk
+  static_assert(READS % CH == 0, "reads per chunk");
+
+  // Fragment read r (0..READS-1) of a slice: per 16-deep substep, the FM A
+  // fragments (one ds_read_b128 each), then the two halves of each of the FN
+  // B fragments (one ds_read_b64_tr_b16 each).
+  __device__ __forceinline__ void read_one(const u32x4* sa, const u32x4* sb, const FragOfs& fo, int r,
+                                           Frags& f) const {
     const char* pa = (const char*)sa;
     const char* pb = (const char*)sb;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pa + f.a[ks] + i * 32 * 64));
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int base = f.b[j] + ks * 16 * (BN * 2);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pb + base));
-      const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pb + base + 4 * (BN * 2)));
-      bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+    const int ks = r / (READS / 2), rr = r % (READS / 2);
+    if (rr < FM) {
+      f.a[ks][rr] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pa + fo.a[ks] + rr * 32 * 64));
+    } else {
+      const int j = (rr - FM) / 2, up = (rr - FM) % 2;
+      const int base = fo.b[j] + ks * 16 * (BN * 2) + up * 4 * (BN * 2);
+      const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pb + base));
+      if (up) f.bu[ks][j] = v;
+      else f.bl[ks][j] = v;
     }
   }
 
-  __device__ __forceinline__ void mfmas(const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN]) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  // DMA instruction d (0..D-1) of slice kt into stage (sa, sb): A blocks
+  // first, then B.  Past the last slice the offset is out of range, so the
+  // instruction reads nothing and every slice keeps the same wait counts.
+  __device__ __forceinline__ void issue_one(u32x4* sa, u32x4* sb, int kt, int d, bool more) {
+    const int w = uni((int)(threadIdx.x >> 6));   // wave index: the same in every lane
+    if (d < A_INS) {
+      const int blk = d * 4 + w;
+      dma16(dA, uni(lds_addr(sa) + blk * 1024), more ? voA : OOB,
+            uni((uint32_t)(blk * 16) * ldaB + (uint32_t)(kt * BK * 2)));
+    } else {
+      const int blk = (d - A_INS) * 4 + w;
+      dma16(dB, uni(lds_addr(sb) + blk * 1024), more ? voB : OOB, uni((uint32_t)(kt * BK + blk * B_ROWS) * ldbB));
+    }
   }
 
-  struct Frags { bf16x8 a[2][FM]; bf16x8 b[2][FN]; };
-
   // One K slice: cur holds the fragments of slice kt, nxt receives those of
-  // slice kt+1 (na/nb); slice kt+4 is loaded into stage kt%4 (fa/fb).
+  // slice kt+1 (na/nb); slice kt+4 is loaded into stage kt%4 (fa/fb).  The
+  // slice runs in CH chunks, chunk c = (substep c / FM, A fragment c % FM):
+  // its FN MFMAs, RPC of the next slice's fragment reads and its share of
+  // the DMA.  Each DMA is an inline-asm statement the compiler schedules
+  // around, so it ends a chunk; spread this way the DMA issue overlaps the
+  // matrix pipeline instead of holding back the slice's first MFMA.
   __device__ __forceinline__ void step(int kt, const FragOfs& fo, const u32x4* na, const u32x4* nb,
                                        u32x4* fa, u32x4* fb, Frags& cur, Frags& nxt) {
-    const int later = nk - 2 - kt;          // slices after kt+1 already issued (at most 2 count)
-    if (later >= 2) wait_barrier<2 * D>();
-    else if (later == 1) wait_barrier<D>();
-    else wait_barrier<0>();
-    if (kt + 4 < nk) issue(fa, fb, kt + 4);
-    // on the last slice these read a stage nobody uses; it keeps the branch
-    // above free of LDS reads
-    read_frags(na, nb, fo, 0, nxt.a[0], nxt.b[0]);
-    read_frags(na, nb, fo, 1, nxt.a[1], nxt.b[1]);
-    mfmas(cur.a[0], cur.b[0]);
-    mfmas(cur.a[1], cur.b[1]);
-    // Interleave: one LDS read after each MFMA (the reads then overlap the
-    // matrix pipeline instead of bunching up in front of it).
-    if constexpr (INTERLEAVE && READS <= MFMAS) {
+    wait_barrier<2 * D>();                  // slice kt+1 landed (kt+2, kt+3 may be in flight)
+    const bool more = kt + 4 < nk;
 #pragma unroll
-      for (int i = 0; i < READS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    for (int c = 0; c < CH; ++c) {
+      const int ks = c / FM, i = c % FM;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const bf16x8 bop =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(cur.bl[ks][j], cur.bu[ks][j], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[ks][i], bop, acc[i][j], 0, 0, 0);
       }
-      if constexpr (MFMAS > READS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
+      // on the last slice these read a stage nobody uses
+#pragma unroll
+      for (int r = 0; r < RPC; ++r) read_one(na, nb, fo, c * RPC + r, nxt);
+      // Interleave: one LDS read after each MFMA of the chunk.
+      if constexpr (INTERLEAVE) {
+        constexpr int PAIRS = FN < RPC ? FN : RPC;
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        if constexpr (FN > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, FN - PAIRS, 0);
+        if constexpr (RPC > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, RPC - PAIRS, 0);
+      }
+#pragma unroll
+      for (int d = c * D / CH; d < (c + 1) * D / CH; ++d) issue_one(fa, fb, kt + 4, d, more);
     }
   }
 
@@ -245,8 +275,8 @@ struct TileGemmD {
     issue(A3, B3, 3);
     wait_barrier<3 * D>();
     Frags r0, r1;
-    read_frags(A0, B0, fo, 0, r0.a[0], r0.b[0]);
-    read_frags(A0, B0, fo, 1, r0.a[1], r0.b[1]);
+#pragma unroll
+    for (int r = 0; r < READS; ++r) read_one(A0, B0, fo, r, r0);
     const int mark_kt = (nk * 3 / 4) & ~3;
     for (int kt = 0; kt < nk; kt += 4) {
       if (mark && kt == mark_kt && threadIdx.x == 0) st_relaxed(mark, 1u);
@@ -255,6 +285,9 @@ struct TileGemmD {
       step(kt + 2, fo, A3, B3, A2, B2, r0, r1);
       step(kt + 3, fo, A0, B0, A3, B3, r1, r0);
     }
+    // the out-of-range DMAs issued past the last slice must not land in LDS
+    // after the caller has started reusing it
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();                        // LDS free for the next tile
   }
 
