@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="", help="comma list of workloads to run (ag,rs,moe,skinny_ag)")
+    ap.add_argument("--only", default="", help="comma list of workloads to run (ag,skinny_ag,rs,ar,moe)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the unfused and library yardsticks")
     ap.add_argument("--copies", type=int, default=0, help="rotated input copies (0 = auto)")
@@ -222,6 +222,36 @@ def bench_rs(args, stream, extra=True):
     return r
 
 
+def bench_ar(args, stream, extra=True):
+    """GEMM -> AllReduce on the GEMM+RS inputs: every one of the R ranks'
+    outputs receives the whole reduced sum."""
+    import workloads as wl
+    from tile_pipelined_gemm_amd import mk
+    from tile_pipelined_gemm_amd.harness import ArProblem
+    w = wl.CONFIGS["rs"]["make"](args.seed)
+    prob = ArProblem(w)
+    del w.partials[:]
+    flops = prob.flops
+    M, K, N, R = w.M, w.K, w.N, w.R
+    abytes = M * K * 2 + K * N * 2 + (R - 1) * M * N * 4 + R * M * N * 4
+
+    def fused(i):
+        prob.run(stream=stream, check=False)
+
+    settle(fused, 0.3)
+    wall, kern = timed(fused, max(3, args.steps // 2), 2, stream)
+    assert mk.mk_poll_status(prob.ws, stream) == mk.MK_OK
+    r = dict(workload="GEMM+AR 8192x3584x8192, 7 fp32 partials, 8 ranks each receive the fp32 sum",
+             M=M, K=K, N=N, R=R, ms=wall, kernel_ms=kern, tflops=flops / kern / 1e9, gbs=abytes / kern / 1e6,
+             flops=flops, alg_bytes=abytes, hbm_frac=abytes / kern / 1e6 / PEAK_HBM_GBS)
+    if extra:
+        lau = mk.make_launch(mode=1)
+        _, uk = timed(lambda i: prob.run(launch=lau, stream=stream, check=False), 3, 1, stream)
+        r["unfused_ms"] = uk
+        r["speedup_vs_unfused"] = uk / kern
+    return r
+
+
 def bench_moe(args, stream, extra=True):
     import workloads as wl
     from tile_pipelined_gemm_amd import mk
@@ -342,6 +372,9 @@ def main():
     if want("rs"):
         log("bench: rs")
         configs["rs"] = bench_rs(args, stream, extra)
+    if want("ar"):
+        log("bench: ar")
+        configs["ar"] = bench_ar(args, stream, extra)
     if want("moe"):
         log("bench: moe")
         configs["moe"] = bench_moe(args, stream, extra)

@@ -162,6 +162,24 @@ int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
                const mk_launch* launch, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * GEMM -> AllReduce  ([P1] "Los cinco núcleos fusionados", row
+ * GEMM + AllReduce)
+ *
+ * The same contributions and the same fp32 sum S = A@B + P_1 + ... + P_{R-1}
+ * (in exactly that order) as mk_gemm_rs, delivered whole to every rank:
+ * out_rank[r] [M x N] of `out_dtype` receives all of S for r = 0..R-1 (the
+ * reduce-scatter followed by the all-gather of the owner blocks; on one GPU
+ * the R outputs stand for the R ranks' buffers).  Each output tile is reduced
+ * and written to every rank as soon as its GEMM tile is done.  M need not be
+ * divisible by R.  Workspace, launch options and errors as for mk_gemm_rs;
+ * tile_log records owner 0 for every tile.
+ * ------------------------------------------------------------------------- */
+size_t mk_gemm_ar_workspace(int64_t M, int64_t K, int64_t N, int R, int out_dtype);
+int mk_gemm_ar(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
+               const float* const* partials, int R, void* const* out_rank, int out_dtype,
+               const mk_launch* launch, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * MoE dispatch -> grouped GEMM  ([P1] "Los cinco núcleos fusionados", row
  * Envío MoE + GEMM)
  *

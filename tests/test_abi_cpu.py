@@ -118,6 +118,30 @@ def test_rs_validation(lib):
     assert _rs(lib, lau=C.byref(lau)) == mk.MK_ERR_INVALID
 
 
+def _ar(lib, M=510, K=64, N=64, R=4, out_dtype=mk.MK_F32, ws_bytes=1 << 24, partials=True, lau=None, outs=True):
+    P = (C.c_void_p * R)(*([FAKE] * R))
+    O = (C.c_void_p * R)(*([FAKE] * R))
+    return lib.mk_gemm_ar(FAKE, FAKE, M, K, N, P if partials else None, R, O if outs else None, out_dtype, lau,
+                          FAKE, ws_bytes, None)
+
+
+def test_ar_validation(lib):
+    # M = 510 is not a multiple of R: fine for the all-reduce (the first HIP call then fails without a GPU)
+    import torch
+    if not torch.cuda.is_available():
+        assert _ar(lib) == mk.MK_ERR_HIP
+    assert _ar(lib, K=60) == mk.MK_ERR_UNSUPPORTED
+    assert _ar(lib, R=65) == mk.MK_ERR_UNSUPPORTED
+    assert _ar(lib, out_dtype=5) == mk.MK_ERR_INVALID
+    assert _ar(lib, partials=False) == mk.MK_ERR_INVALID
+    assert _ar(lib, outs=False) == mk.MK_ERR_INVALID
+    lau = mk.make_launch(tile=1)
+    assert _ar(lib, lau=C.byref(lau)) == mk.MK_ERR_UNSUPPORTED    # register 256x256 tile not built
+    assert _ar(lib, ws_bytes=64) == mk.MK_ERR_WORKSPACE
+    assert lib.mk_gemm_ar_workspace(8192, 3584, 8192, 8, mk.MK_F32) == lib.mk_gemm_rs_workspace(
+        8192, 3584, 8192, 8, mk.MK_F32)
+
+
 def test_rs_workspace_sizes(lib):
     f32 = lib.mk_gemm_rs_workspace(8192, 3584, 8192, 8, mk.MK_F32)
     bf = lib.mk_gemm_rs_workspace(8192, 3584, 8192, 8, mk.MK_BF16)

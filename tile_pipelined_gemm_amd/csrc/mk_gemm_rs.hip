@@ -45,6 +45,7 @@ struct RsParams {
   int32_t* tile_log;
   uint64_t spin_limit;
   int M, K, N, R, out_bf16, mb;   // mb = rows per owner
+  int n_dst;                      // outputs per row block: 1 (reduce-scatter) or R (all-reduce)
   int mode, n_compute, tiles_m, tiles_n, n_tiles;
 };
 
@@ -87,13 +88,15 @@ __device__ __forceinline__ void reduce_tile(const RsParams& p, int t) {
       if (ok[u]) {
         const int o = gr[u] / p.mb;
         const int64_t i = (int64_t)(gr[u] - o * p.mb) * p.N + gc[u];
-        if (p.out_bf16) {
-          u32x2 b;
-          b[0] = (uint32_t)f2bf(v[u][0]) | ((uint32_t)f2bf(v[u][1]) << 16);
-          b[1] = (uint32_t)f2bf(v[u][2]) | ((uint32_t)f2bf(v[u][3]) << 16);
-          *(u32x2*)((uint16_t*)p.out[o] + i) = b;
-        } else {
-          *(f32x4*)((float*)p.out[o] + i) = v[u];
+        for (int d = 0; d < p.n_dst; ++d) {
+          if (p.out_bf16) {
+            u32x2 b;
+            b[0] = (uint32_t)f2bf(v[u][0]) | ((uint32_t)f2bf(v[u][1]) << 16);
+            b[1] = (uint32_t)f2bf(v[u][2]) | ((uint32_t)f2bf(v[u][3]) << 16);
+            *(u32x2*)((uint16_t*)p.out[o + d] + i) = b;
+          } else {
+            *(f32x4*)((float*)p.out[o + d] + i) = v[u];
+          }
         }
       }
   }
@@ -118,8 +121,8 @@ __device__ __forceinline__ void reduce_from_acc(const G& g, const RsParams& p, i
   const uint32_t esz = p.out_bf16 ? 2u : 4u;
   const uint32_t rb4 = (uint32_t)p.N * 4u, rbo = (uint32_t)p.N * esz;   // row bytes in / out
   const uint32_t in_bytes = uni((uint32_t)rows * rb4);
-  const __amdgpu_buffer_rsrc_t dout =
-      make_rsrc(uni((const char*)p.out[o] + ((int64_t)(m0 - o * p.mb) * p.N) * esz), uni((uint32_t)rows * rbo));
+  const int64_t dofs = ((int64_t)(m0 - o * p.mb) * p.N) * esz;   // tile origin in its row block
+  const uint32_t dbytes = uni((uint32_t)rows * rbo);
   // Per-lane part of every offset (the lane's row in a 4-row group and its
   // 4-column run); the block and group parts are scalar offsets.
   const int lrow = (lane >> 5) * 4 + (lane & 3), lcol = (lane & 31) & ~3;
@@ -158,16 +161,19 @@ __device__ __forceinline__ void reduce_from_acc(const G& g, const RsParams& p, i
             for (int gq = 0; gq < 4; ++gq) v[gq] += t[dq][gq];
           }
       }
+      for (int d = 0; d < p.n_dst; ++d) {
+        const __amdgpu_buffer_rsrc_t dout = make_rsrc(uni((const char*)p.out[o + d] + dofs), dbytes);
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const uint32_t so = uni((uint32_t)(rb + 8 * gq) * rbo + (uint32_t)cb * esz);
-        if (p.out_bf16) {
-          u32x2 b;
-          b[0] = (uint32_t)f2bf(v[gq][0]) | ((uint32_t)f2bf(v[gq][1]) << 16);
-          b[1] = (uint32_t)f2bf(v[gq][2]) | ((uint32_t)f2bf(v[gq][3]) << 16);
-          __builtin_amdgcn_raw_buffer_store_b64(b, dout, vout, so, 0);
-        } else {
-          bstore_alu16(dout, vout, so, v[gq]);
+        for (int gq = 0; gq < 4; ++gq) {
+          const uint32_t so = uni((uint32_t)(rb + 8 * gq) * rbo + (uint32_t)cb * esz);
+          if (p.out_bf16) {
+            u32x2 b;
+            b[0] = (uint32_t)f2bf(v[gq][0]) | ((uint32_t)f2bf(v[gq][1]) << 16);
+            b[1] = (uint32_t)f2bf(v[gq][2]) | ((uint32_t)f2bf(v[gq][3]) << 16);
+            __builtin_amdgcn_raw_buffer_store_b64(b, dout, vout, so, 0);
+          } else {
+            bstore_alu16(dout, vout, so, v[gq]);
+          }
         }
       }
     }
@@ -195,8 +201,8 @@ __device__ __forceinline__ void reduce_from_acc_lds(const G& g, const RsParams& 
   const uint32_t esz = p.out_bf16 ? 2u : 4u;
   const uint32_t rb4 = (uint32_t)p.N * 4u, rbo = (uint32_t)p.N * esz;
   const uint32_t in_bytes = uni((uint32_t)rows * rb4);
-  const __amdgpu_buffer_rsrc_t dout =
-      make_rsrc(uni((const char*)p.out[o] + ((int64_t)(m0 - o * p.mb) * p.N) * esz), uni((uint32_t)rows * rbo));
+  const int64_t dofs = ((int64_t)(m0 - o * p.mb) * p.N) * esz;   // tile origin in its row block
+  const uint32_t dbytes = uni((uint32_t)rows * rbo);
   const int lrow = (lane >> 5) * 4 + (lane & 3), lcol = (lane & 31) & ~3;
   const uint32_t lin = (uint32_t)lrow * rb4 + (uint32_t)lcol * 4u;
   const uint32_t lout = (uint32_t)lrow * rbo + (uint32_t)lcol * esz;
@@ -238,13 +244,16 @@ __device__ __forceinline__ void reduce_from_acc_lds(const G& g, const RsParams& 
             v += *(const f32x4*)((sl < 16 ? pa + sl * 1024 : pb + (sl - 16) * 1024) + 16 * lane);
           }
         const uint32_t so = uni((uint32_t)(rb + 8 * gq) * rbo + (uint32_t)cb * esz);
-        if (p.out_bf16) {
-          u32x2 b;
-          b[0] = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-          b[1] = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-          __builtin_amdgcn_raw_buffer_store_b64(b, dout, vout, so, 0);
-        } else {
-          bstore_alu16(dout, vout, so, v);
+        for (int d = 0; d < p.n_dst; ++d) {
+          const __amdgpu_buffer_rsrc_t dout = make_rsrc(uni((const char*)p.out[o + d] + dofs), dbytes);
+          if (p.out_bf16) {
+            u32x2 b;
+            b[0] = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+            b[1] = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+            __builtin_amdgcn_raw_buffer_store_b64(b, dout, vout, so, 0);
+          } else {
+            bstore_alu16(dout, vout, so, v);
+          }
         }
       }
     }
@@ -457,15 +466,19 @@ static int run_rs(RsParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStr
   return MK_OK;
 }
 
-extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
-                          const float* const* partials, int R, void* const* out_owner, int out_dtype,
-                          const mk_launch* launch, void* workspace, size_t workspace_bytes, void* stream) {
+// GEMM + reduce-scatter (all_reduce false: row block r of the reduced sum
+// goes to outs[r]) or GEMM + all-reduce (true: the whole reduced sum goes to
+// every outs[r]); one kernel for both, the all-reduce writing each reduced
+// tile R times.
+static int gemm_reduce(const void* A, const void* B, int64_t M, int64_t K, int64_t N, const float* const* partials,
+                       int R, void* const* outs, int out_dtype, const mk_launch* launch, void* workspace,
+                       size_t workspace_bytes, void* stream, bool all_reduce) {
   using mkh::fail;
-  if (!A || !B || !out_owner) return fail(MK_ERR_INVALID, "A, B and out_owner must be non-NULL");
+  if (!A || !B || !outs) return fail(MK_ERR_INVALID, "A, B and the outputs must be non-NULL");
   if (R < 1 || R > MK_MAX_RANKS) return fail(MK_ERR_UNSUPPORTED, "R=%d outside [1,%d]", R, MK_MAX_RANKS);
   if (M < 1 || K < 8 || N < 8) return fail(MK_ERR_INVALID, "empty or too small shape");
   if (K % 8 || N % 8) return fail(MK_ERR_UNSUPPORTED, "K and N must be multiples of 8");
-  if (M % R) return fail(MK_ERR_INVALID, "M (%lld) not divisible by R (%d)", (long long)M, R);
+  if (!all_reduce && M % R) return fail(MK_ERR_INVALID, "M (%lld) not divisible by R (%d)", (long long)M, R);
   if (M > (1 << 30) || K > (1 << 20) || N > MK_MAX_COLS || K * N * 2 >= (1ll << 31) || M * N * 4 >= (1ll << 40))
     return fail(MK_ERR_UNSUPPORTED, "dimension too large");
   if (R > 1 && !partials) return fail(MK_ERR_INVALID, "partials is NULL");
@@ -473,22 +486,25 @@ extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, in
   for (int r = 0; r + 1 < R; ++r)
     if (!partials[r] || !mkh::aligned16(partials[r])) return fail(MK_ERR_INVALID, "partial %d NULL or misaligned", r);
   for (int r = 0; r < R; ++r)
-    if (!out_owner[r] || !mkh::aligned16(out_owner[r])) return fail(MK_ERR_INVALID, "owner %d NULL or misaligned", r);
+    if (!outs[r] || !mkh::aligned16(outs[r])) return fail(MK_ERR_INVALID, "output %d NULL or misaligned", r);
   if (!mkh::aligned16(A) || !mkh::aligned16(B)) return fail(MK_ERR_INVALID, "A and B must be 16-byte aligned");
-  const int mb = (int)(M / R);
+  const int mb = all_reduce ? (int)M : (int)(M / R);   // rows per output block
   const mk_launch o = mkh::launch_opts(launch);
   if (o.mode != 0 && o.mode != 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
   if (o.grid < 0 || o.n_reduce < -1) return fail(MK_ERR_INVALID, "bad grid or n_reduce");
-  const int tile = o.tile ? o.tile : rs_tile(M, N, K, mb);
+  // Default: the direct-to-LDS 256x256 tile when K is a multiple of 128 and
+  // the output blocks hold whole tile rows (all-reduce: one block of M rows,
+  // a ragged last tile row is masked), else 128x128.
+  const int tile = o.tile ? o.tile : rs_tile(M, N, K, all_reduce ? 256 : mb);
   if (tile <= 0 || tile >= TILE_COUNT) return fail(MK_ERR_INVALID, "tile id %d", tile);
   // The register-staged 256x256 tile is not built for this operation: with
   // the partial sums added from its accumulators its K loop spills.
   if (tile == TILE_256x256)
-    return fail(MK_ERR_UNSUPPORTED, "tile %d is not available for GEMM+RS (use tile %d)", tile, TILE_256x256_DMA);
+    return fail(MK_ERR_UNSUPPORTED, "tile %d is not available for GEMM+RS/AR (use tile %d)", tile, TILE_256x256_DMA);
   if (mk_is_dma_tile(tile) && !TileGemmD<256, 256>::supports_k((int)K))
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
-  if (mb % tile_bm(tile)) return fail(MK_ERR_UNSUPPORTED, "rows per owner (%d) must be a multiple of the tile height %d",
-                                      mb, tile_bm(tile));
+  if (!all_reduce && mb % tile_bm(tile))
+    return fail(MK_ERR_UNSUPPORTED, "rows per owner (%d) must be a multiple of the tile height %d", mb, tile_bm(tile));
   if (!workspace) return fail(MK_ERR_WORKSPACE, "workspace is NULL");
   const size_t need_min = mk_gemm_rs_workspace(M, K, N, R, MK_F32);
   if (workspace_bytes < need_min) return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need_min);
@@ -502,15 +518,17 @@ extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, in
   p.A = (const uint16_t*)A;
   p.B = (const uint16_t*)B;
   for (int r = 0; r + 1 < R; ++r) p.P[r] = partials[r];
-  for (int r = 0; r < R; ++r) p.out[r] = out_owner[r];
+  for (int r = 0; r < R; ++r) p.out[r] = outs[r];
   p.hdr = (WsHeader*)workspace;
   p.fifo = (uint32_t*)((char*)workspace + sizeof(WsHeader));
-  // fp32 output can be staged in place in the owner blocks.
+  // fp32 output can be staged in place in the output blocks (all-reduce: in
+  // output 0, which the reduction then rewrites in place).
   p.stage = out_dtype == MK_F32 ? nullptr : (have_stage ? (float*)((char*)workspace + need_min) : nullptr);
   const bool can_stage = out_dtype == MK_F32 || have_stage;
   p.tile_log = o.tile_log;
   p.spin_limit = mkh::spin_ticks(o, d);
   p.M = (int)M; p.K = (int)K; p.N = (int)N; p.R = R; p.mb = mb;
+  p.n_dst = all_reduce ? R : 1;
   p.out_bf16 = out_dtype == MK_BF16;
   const hipStream_t st = (hipStream_t)stream;
   switch (tile) {
@@ -523,4 +541,22 @@ extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, in
     case TILE_128x256_DMA: return run_rs<TileGemmD<128, 256, false>>(p, o, d, st, can_stage);
   }
   return fail(MK_ERR_INVALID, "tile id %d", tile);
+}
+
+extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
+                          const float* const* partials, int R, void* const* out_owner, int out_dtype,
+                          const mk_launch* launch, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_reduce(A, B, M, K, N, partials, R, out_owner, out_dtype, launch, workspace, workspace_bytes, stream,
+                     false);
+}
+
+extern "C" size_t mk_gemm_ar_workspace(int64_t M, int64_t K, int64_t N, int R, int out_dtype) {
+  return mk_gemm_rs_workspace(M, K, N, R, out_dtype);
+}
+
+extern "C" int mk_gemm_ar(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
+                          const float* const* partials, int R, void* const* out_rank, int out_dtype,
+                          const mk_launch* launch, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_reduce(A, B, M, K, N, partials, R, out_rank, out_dtype, launch, workspace, workspace_bytes, stream,
+                     true);
 }

@@ -78,6 +78,29 @@ class RsProblem:
         return np.vstack([to_numpy(o) for o in self.out])
 
 
+class ArProblem:
+    """GEMM -> AllReduce on an RsWorkload: every rank's output is the whole S."""
+
+    def __init__(self, w, device="cuda"):
+        self.w = w
+        self.A = bf16_tensor(w.A, device)
+        self.B = bf16_tensor(w.B, device)
+        self.P = [f32_tensor(p, device) for p in w.partials]
+        self.out = [torch.empty(w.M, w.N, dtype=_out_dtype(w.out_dtype), device=device) for _ in range(w.R)]
+        code = mk.MK_BF16 if w.out_dtype == "bf16" else mk.MK_F32
+        self.ws = mk.workspace(mk.mk_gemm_ar_workspace(w.M, w.K, w.N, w.R, code), device)
+
+    @property
+    def flops(self):
+        return 2.0 * self.w.M * self.w.N * self.w.K
+
+    def run(self, launch=None, stream=None, check=True):
+        return mk.mk_gemm_ar(self.A, self.B, self.P, self.out, self.ws, launch=launch, stream=stream, check=check)
+
+    def outputs(self):
+        return [to_numpy(o) for o in self.out]
+
+
 class MoeProblem:
     def __init__(self, w, device="cuda"):
         self.w = w

@@ -25,6 +25,7 @@ TILE_128x128_DMA, TILE_256x128_DMA, TILE_128x256_DMA = 6, 7, 8
 # Symbols declared in include/mk.h (checked by the CPU tests).
 EXPORTS = [
     "mk_ag_gemm_workspace", "mk_ag_gemm", "mk_gemm_rs_workspace", "mk_gemm_rs",
+    "mk_gemm_ar_workspace", "mk_gemm_ar",
     "mk_moe_dispatch_gemm_workspace", "mk_moe_dispatch_gemm", "mk_workspace_init",
     "mk_poll_status", "mk_status_string", "mk_last_error", "mk_tile_name", "mk_version",
     "mk_wall_clock_khz",
@@ -72,6 +73,11 @@ def load(path: Optional[str] = None):
     lib.mk_gemm_rs_workspace.argtypes = [i64, i64, i64, i32, i32]
     lib.mk_gemm_rs.restype = i32
     lib.mk_gemm_rs.argtypes = [vp, vp, i64, i64, i64, pp, i32, pp, i32,
+                               C.POINTER(mk_launch), vp, sz, vp]
+    lib.mk_gemm_ar_workspace.restype = sz
+    lib.mk_gemm_ar_workspace.argtypes = [i64, i64, i64, i32, i32]
+    lib.mk_gemm_ar.restype = i32
+    lib.mk_gemm_ar.argtypes = [vp, vp, i64, i64, i64, pp, i32, pp, i32,
                                C.POINTER(mk_launch), vp, sz, vp]
     lib.mk_moe_dispatch_gemm_workspace.restype = sz
     lib.mk_moe_dispatch_gemm_workspace.argtypes = [i64, i64, i32, i32, i32, i64]
@@ -211,6 +217,22 @@ def mk_gemm_rs(A, B, partials, out_owner, ws, *, launch=None, stream=None, check
     lau = launch if launch is not None else make_launch()
     rc = lib.mk_gemm_rs(_ptr(A), _ptr(B), M, K, N, _ptr_array(partials), R, _ptr_array(out_owner),
                         _dtype_code(out_owner[0]), C.byref(lau), _ptr(ws), ws.numel() * ws.element_size(),
+                        _stream(stream))
+    return _check(rc) if check else rc
+
+
+def mk_gemm_ar_workspace(M, K, N, R, out_dtype=MK_F32) -> int:
+    return load().mk_gemm_ar_workspace(M, K, N, R, out_dtype)
+
+
+def mk_gemm_ar(A, B, partials, out_rank, ws, *, launch=None, stream=None, check=True) -> int:
+    lib = load()
+    M, K = A.shape
+    N = B.shape[1]
+    R = len(out_rank)
+    lau = launch if launch is not None else make_launch()
+    rc = lib.mk_gemm_ar(_ptr(A), _ptr(B), M, K, N, _ptr_array(partials), R, _ptr_array(out_rank),
+                        _dtype_code(out_rank[0]), C.byref(lau), _ptr(ws), ws.numel() * ws.element_size(),
                         _stream(stream))
     return _check(rc) if check else rc
 
