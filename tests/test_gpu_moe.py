@@ -134,6 +134,41 @@ def test_tile_and_copy_logs(gpu, tile, bm, bn):
     assert int(C[:, 5].sum()) == prob.local_rows()
 
 
+def _split_tail_workload(dist, out_dtype):
+    # 38 M-tiles x 8 N-tiles of 256x256 = 304 tiles: on 256 workgroups a last
+    # round of 48 tiles, which is split into 4 K parts of 256
+    return wl.make_moe(2048, 1024, 16, 4, 16, 2048, seed=71, block_tokens=256, dist=dist, out_dtype=out_dtype)
+
+
+def _in_split_regime(w):
+    topk = om.route_topk(w.logits, w.k)
+    counts, _, _ = om.dispatch(topk, w.E)
+    tiles = sum((int(c) + 255) // 256 for c in counts[:w.L]) * (w.F // 256)
+    full = torch.cuda.get_device_properties(0).multi_processor_count
+    return tiles > full and 0 < tiles % full <= full // 4
+
+
+def test_split_tail_integer_inputs_bit_exact(gpu):
+    w = _split_tail_workload("int", "f32")
+    assert _in_split_regime(w), "shape no longer exercises the split tail on this device"
+    prob = _run(gpu, w)
+    ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 0, "f32")
+    got = _check_exact(prob, ref)
+    assert np.array_equal(got["Y"], ref["Y"])
+
+
+def test_split_tail_bitwise_identical_across_launches(gpu):
+    w = _split_tail_workload("normal", "bf16")
+    outs = []
+    for kw in [dict(), dict(mode=1), dict(grid=80), dict(n_copy=5), dict(n_copy=64)]:
+        prob = _run(gpu, w, launch=gpu.make_launch(**kw))
+        outs.append(prob.outputs()["Y"])
+    ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 0, "bf16")
+    assert_close(out_to_f64(outs[0], "bf16"), ref["Y64"], "bf16", "MoE split tail")
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(outs[0], o), f"launch {i} differs"
+
+
 def test_withheld_block_times_out(gpu):
     from tile_pipelined_gemm_amd.harness import MoeProblem
     w = wl.make_moe(512, 64, 32, 4, 8, 64, seed=35, block_tokens=64)

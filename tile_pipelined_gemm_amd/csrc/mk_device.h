@@ -457,4 +457,76 @@ __device__ __forceinline__ void store_tile(const G& g, void* C, int64_t ld, int 
   }
 }
 
+// K parts of one tile (a tile split along K): each part parks its fp32
+// accumulators in its slot, in register order (chunk c of 4 floats of thread
+// t at byte 16*(c*NT + t)), written through the L2; the part that finishes
+// last reads every slot back with device-coherent loads and sums them in part
+// order, so the bits do not depend on which part finished last.
+template <class G>
+__device__ __forceinline__ void park_acc(const G& g, float* slot) {
+  constexpr int NCH = G::FM * G::FN * 4;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(uni(slot), (uint32_t)(NCH * G::NT * 16));
+  const uint32_t vo = threadIdx.x * 16u;
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int c = (i * G::FN + j) * 4 + c4;
+        const f32x16& a = g.acc[i][j];
+        bstore_alu16(rs, vo, (uint32_t)(c * G::NT * 16),
+                     f32x4{a[4 * c4], a[4 * c4 + 1], a[4 * c4 + 2], a[4 * c4 + 3]});
+      }
+}
+
+// The finishing part's output: for each 4x4 piece, the PARTS slots' values
+// are summed in part order, then transposed and stored like store_tile (the
+// accumulators themselves are left alone).
+template <class G, int PARTS>
+__device__ __forceinline__ void store_parked_sum(const float* slots, void* C, int64_t ld, int rows, int cols,
+                                                 bool bf16) {
+  constexpr int NCH = G::FM * G::FN * 4;
+  const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
+  const int wm = w % G::WM, wn = w / G::WM;
+  const uint32_t vin = threadIdx.x * 16u;
+  const uint32_t esz = bf16 ? 2u : 4u;
+  const uint32_t rbo = uni((uint32_t)ld * esz);
+  rows = rows < G::BM ? rows : G::BM;
+  const __amdgpu_buffer_rsrc_t d = make_rsrc(uni(C), uni((uint32_t)(rows > 0 ? rows : 0) * rbo));
+  const int lrow = (lane >> 5) * 4 + (lane & 3), lcol = (lane & 31) & ~3;
+  const uint32_t lout = (uint32_t)lrow * rbo + (uint32_t)lcol * esz;
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      u32x4 t[PARTS][4];
+#pragma unroll
+      for (int k = 0; k < PARTS; ++k) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(uni(slots + (int64_t)k * (G::BM * G::BN)), (uint32_t)(NCH * G::NT * 16));
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) t[k][gq] = bload<16>(rs, vin, (uint32_t)(((i * G::FN + j) * 4 + gq) * G::NT * 16));
+      }
+      const int cb = wn * G::TN + j * 32, rb = wm * G::TM + i * 32;
+      const uint32_t vo = cb + lcol < cols ? lout : OOB;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        f32x4 v = __builtin_bit_cast(f32x4, t[0][gq]);
+#pragma unroll
+        for (int k = 1; k < PARTS; ++k) v += __builtin_bit_cast(f32x4, t[k][gq]);
+        v = quad_transpose(v);
+        const uint32_t so = uni((uint32_t)(rb + 8 * gq) * rbo + (uint32_t)cb * esz);
+        if (bf16) {
+          u32x2 b;
+          b[0] = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+          b[1] = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(b, d, vo, so, 0);
+        } else {
+          bstore_alu16(d, vo, so, v);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace mk

@@ -38,10 +38,20 @@ constexpr int RB = 64;          // tokens per routing block
 constexpr int ROUTE_NT = 256;   // 4 waves, 16 tokens each
 
 struct MoeWs {                  // device workspace layout (offsets in bytes)
-  size_t block_cnt, rank, tile_base, tile_cnt, total;
+  size_t block_cnt, rank, tile_base, tile_cnt, kp_cnt, kp_slots, total;
 };
 
-inline MoeWs moe_ws_layout(int64_t T, int E, int k, int L) {
+// K parts of a tail tile.  More parts shorten the parts but lengthen the
+// finishing part's read-back of the parked sums (one workgroup reads
+// parts x BM x BN x 4 bytes); at 256x256, 4 and 8 parts come out even, and 8
+// would double the registers the read-back needs.
+constexpr int KP_MAX = 4;
+
+// The split tail (see moe_compute_role) holds at most one tile per four
+// workgroups of the full grid, cut into parts that together number at most
+// the full grid; occupancy x BM x BN <= 256 x 256 for every tile here, so the
+// parked parts fit in n_cu x 256 KiB and the counters in n_cu words.
+inline MoeWs moe_ws_layout(int64_t T, int E, int k, int L, int n_cu) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   MoeWs w;
   const int64_t nrb = (T + RB - 1) / RB;
@@ -51,7 +61,9 @@ inline MoeWs moe_ws_layout(int64_t T, int E, int k, int L) {
   w.rank = up(w.block_cnt + (size_t)nrb * E * 4);
   w.tile_base = up(w.rank + (size_t)T * k * 4);
   w.tile_cnt = up(w.tile_base + (size_t)(L + 1) * 4 + 4);
-  w.total = up(w.tile_cnt + (size_t)max_tiles * 4);
+  w.kp_cnt = up(w.tile_cnt + (size_t)max_tiles * 4);
+  w.kp_slots = up(w.kp_cnt + (size_t)n_cu * 4);
+  w.total = w.kp_slots + (size_t)n_cu * 256 * 256 * 4;
   return w;
 }
 
@@ -185,6 +197,10 @@ struct MoeParams {
   int T, H, E, k, L, F, eb, y_bf16;
   int n_blocks, block_tokens, part_tokens, parts;
   int mode, n_copy, tiles_n, withhold;
+  int full_grid;                // CUs x occupancy of this kernel (the split plan's grid)
+  int kp_len;                   // K-part counters in the workspace
+  uint32_t* kp_cnt;             // [kp_len] parts of a split tail tile finished
+  float* kp_slots;              // parked K parts
   uint16_t order[MK_MAX_UNITS];
   uint32_t delay_ticks[MK_MAX_UNITS];
 };
@@ -286,13 +302,36 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
   }
 }
 
+// Split tail: when the tiles leave a last round that fills at most a quarter
+// of the full grid, those tail tiles are cut along K into `split` parts
+// (a power of two up to KP_MAX that keeps the parts within the grid and divides
+// H into 128-deep units) so the otherwise idle workgroups share them; each
+// part parks its sums and the last part of a tile adds them in part order
+// (see park_acc / store_parked_sum).  The plan depends only on the routed
+// tile count and the device's full grid, so every launch option gives the
+// same bits.
+struct MoeSplit { uint32_t n_whole, n_items; int split; };
+__device__ __forceinline__ MoeSplit moe_split_plan(uint32_t n_tiles, int full, int H) {
+  MoeSplit sp{n_tiles, n_tiles, 1};
+  const uint32_t tail = n_tiles % (uint32_t)full;
+  if (n_tiles > (uint32_t)full && tail > 0 && tail * 4 <= (uint32_t)full && H % 128 == 0)
+    for (int s2 = 2; s2 <= KP_MAX; s2 *= 2)
+      if (tail * s2 <= (uint32_t)full && (H / 128) % s2 == 0) sp.split = s2;
+  if (sp.split > 1) {
+    sp.n_whole = n_tiles - tail;
+    sp.n_items = sp.n_whole + tail * sp.split;
+  }
+  return sp;
+}
+
 template <class G, class SM>
 __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h, SM sm, uint32_t* sb) {
   const int tid = threadIdx.x;
-  const int n_mt = p.tile_base[p.L];
+  const int n_mt = (int)uni((uint32_t)p.tile_base[p.L]);
   const uint32_t n_tiles = (uint32_t)n_mt * p.tiles_n;
   const int base_local = p.offsets[p.eb];
   const uint32_t all_items = (uint32_t)p.n_blocks * p.parts;   // never reached with a withheld block
+  const MoeSplit sp = moe_split_plan(n_tiles, p.full_grid, p.H);
   // Once every copy item has landed and this workgroup has taken an acquire
   // after seeing that, its later tiles need neither a wait nor an acquire
   // (each acquire invalidates the XCD's L2 under the other tiles there).
@@ -300,8 +339,15 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
   G g;
   int l = 0;
   for (;;) {
-    const uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
-    if (q >= n_tiles) break;
+    const uint32_t it = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+    if (it >= sp.n_items) break;
+    // work item -> tile q and K part kp (kp < 0: the whole tile)
+    uint32_t q = it;
+    int kp = -1;
+    if (it >= sp.n_whole) {
+      q = sp.n_whole + (it - sp.n_whole) / sp.split;
+      kp = (int)((it - sp.n_whole) % sp.split);
+    }
     const uint32_t t_take = (uint32_t)now_ticks();
     const int mt = (int)(q / p.tiles_n), tn = (int)(q % p.tiles_n);
     while (l + 1 < p.L && p.tile_base[l + 1] <= mt) ++l;        // queue is expert-ordered
@@ -325,11 +371,28 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
     const uint32_t t_ready = (uint32_t)now_ticks();
     const int q0 = p.offsets[e] - base_local + r0;              // landing row of the tile
     const int n0 = tn * G::BN;
-    g.bind(p.Xs + (int64_t)q0 * p.H, p.H, rows, p.W[l] + n0, p.F, p.F - n0, p.W[l] + (int64_t)p.H * p.F, p.H);
+    const int kpart = p.H / sp.split, k0 = kp < 0 ? 0 : kp * kpart;
+    g.bind(p.Xs + (int64_t)q0 * p.H + k0, p.H, rows, p.W[l] + (int64_t)k0 * p.F + n0, p.F, p.F - n0,
+           p.W[l] + (int64_t)p.H * p.F, kp < 0 ? p.H : kpart);
     g.run(sm);
     const int64_t esz = p.y_bf16 ? 2 : 4;
-    store_tile(g, (char*)p.Y + ((int64_t)q0 * p.F + n0) * esz, p.F, rows, p.F - n0, p.y_bf16);
-    if (p.tile_log && tid == 0) {
+    char* const Yt = (char*)p.Y + ((int64_t)q0 * p.F + n0) * esz;
+    uint32_t done = 1;
+    if (kp < 0) {
+      store_tile(g, Yt, p.F, rows, p.F - n0, p.y_bf16);
+    } else {
+      const uint32_t tq = q - sp.n_whole;                        // tail tile index
+      float* slots = p.kp_slots + (int64_t)tq * sp.split * (G::BM * G::BN);
+      park_acc(g, slots + (int64_t)kp * (G::BM * G::BN));
+      fence_release();
+      __syncthreads();
+      done = wg_bcast(tid == 0 ? (uint32_t)(add_relaxed(&p.kp_cnt[tq], 1u) == (uint32_t)(sp.split - 1)) : 0u, sb);
+      if (done) {
+        if (sp.split == 2) store_parked_sum<G, 2>(slots, Yt, p.F, rows, p.F - n0, p.y_bf16);
+        else store_parked_sum<G, 4>(slots, Yt, p.F, rows, p.F - n0, p.y_bf16);
+      }
+    }
+    if (done && p.tile_log && tid == 0) {
       int32_t* L = p.tile_log + 8 * (int64_t)q;
       L[0] = l; L[1] = r0; L[2] = rows;
       L[3] = p.mode == MODE_FUSED ? (int32_t)ld_relaxed(&p.tile_cnt[mt]) : rows;
@@ -351,6 +414,7 @@ __device__ __forceinline__ void moe_finish(const MoeParams& p, WsHeader* h, uint
   if (!last) return;
   const int n_mt = p.tile_base[p.L];
   for (int i = threadIdx.x; i < n_mt; i += blockDim.x) st_relaxed(&p.tile_cnt[i], 0u);
+  for (int i = threadIdx.x; i < p.kp_len; i += blockDim.x) st_relaxed(&p.kp_cnt[i], 0u);
   if (threadIdx.x == 0) {
     st_relaxed(&h->ticket, 0u);
     st_relaxed(&h->tile_next, 0u);
@@ -399,6 +463,9 @@ int run_moe(MoeParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStream_t
   const int full = d->n_cu * occ;
   const int grid = o.grid > 0 ? std::min(o.grid, full) : full;
   const int n_work = p.n_blocks * p.parts;
+  p.full_grid = full;
+  if ((int64_t)full * G::BM * G::BN > (int64_t)d->n_cu * 256 * 256)
+    return mkh::fail(MK_ERR_UNSUPPORTED, "tile slots exceed the workspace plan");
   if (o.mode == 1) {   // unfused baseline: permute kernel, then grouped GEMM kernel
     p.mode = MODE_COPY;
     p.n_copy = grid;
@@ -425,7 +492,8 @@ int run_moe(MoeParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStream_t
 extern "C" size_t mk_moe_dispatch_gemm_workspace(int64_t T, int64_t H, int E, int k, int L, int64_t F) {
   (void)H; (void)F;
   if (T <= 0 || E <= 0 || k <= 0 || L <= 0) return sizeof(WsHeader);
-  return moe_ws_layout(T, E, k, L).total;
+  const mkh::DevInfo* d = mkh::dev_info();
+  return moe_ws_layout(T, E, k, L, d ? d->n_cu : 256).total;
 }
 
 extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t T, int64_t H, int E, int k,
@@ -456,7 +524,11 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   int rc = mkh::make_schedule(arrival, T, 1, &s);
   if (rc) return rc;
   if (!workspace) return fail(MK_ERR_WORKSPACE, "workspace is NULL");
-  const MoeWs lay = moe_ws_layout(T, E, k, L);
+  const size_t need0 = moe_ws_layout(T, E, k, L, 0).total;   // before the split-tail slots
+  if (workspace_bytes < need0) return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need0);
+  const mkh::DevInfo* dv = mkh::dev_info();
+  if (!dv) return MK_ERR_HIP;
+  const MoeWs lay = moe_ws_layout(T, E, k, L, dv->n_cu);
   if (workspace_bytes < lay.total) return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, lay.total);
   const mk_launch o = mkh::launch_opts(launch);
   if (o.mode != 0 && o.mode != 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
@@ -487,6 +559,9 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   p.perm = perm;
   p.tile_base = (const int32_t*)(ws + lay.tile_base);
   p.tile_cnt = (uint32_t*)(ws + lay.tile_cnt);
+  p.kp_cnt = (uint32_t*)(ws + lay.kp_cnt);
+  p.kp_slots = (float*)(ws + lay.kp_slots);
+  p.kp_len = dv->n_cu;
   p.hdr = (WsHeader*)workspace;
   p.tile_log = o.tile_log;
   p.copy_log = o.copy_log;
