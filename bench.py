@@ -160,6 +160,7 @@ def bench_ag(name, args, stream, extra=True):
         r["speedup_vs_unfused"] = uk / kern
         # role split and scheduling variants of the fused kernel
         variants = [("n_copy64", dict(n_copy=64)), ("copy_writeback", dict(copy_policy=1)),
+                    ("copy_kib512", dict(copy_kib=512)),
                     ("xcd_queues", dict(queue_mode=1)),
                     ("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
                     ("gemm_only_xcd_queues", dict(mode=3, queue_mode=1))]

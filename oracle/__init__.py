@@ -20,7 +20,8 @@ What the pages fix: AllGather+GEMM computes C = A @ B where every rank holds a
 shard of A and the local GEMM consumes tiles as the gathered shards arrive;
 GEMM+ReduceScatter computes C = A @ B and each finished output tile is reduced
 and sent to the rank that owns it; GEMM+AllReduce computes the same sum and
-leaves all of it on every rank; MoE dispatch+GEMM routes tokens to expert
+leaves all of it on every rank; Ring Attention rotates key/value shards round
+the ring while attention consumes them; MoE dispatch+GEMM routes tokens to expert
 ranks and runs the per-expert grouped GEMM on the tokens as they land.  The
 pages give no dtypes, layouts, tie-breaks or worked numbers; every such choice
 made here is a reading, listed in each module's docstring.
@@ -31,4 +32,4 @@ one-hot operands), exact integer arithmetic, invariants (arrival-order
 independence, reduce-scatter over all owners = all-reduce, dispatch is a
 permutation whose counts sum to T*k) and library special cases.
 """
-from . import numerics, schedule, ag_gemm, gemm_rs, gemm_ar, moe  # noqa: F401
+from . import numerics, schedule, ag_gemm, gemm_rs, gemm_ar, moe, ring_attn  # noqa: F401

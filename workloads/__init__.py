@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = [
     "f32_to_bf16_bits", "AgWorkload", "RsWorkload", "MoeWorkload", "CONFIGS",
-    "make_ag", "make_rs", "make_moe", "fingerprint",
+    "make_ag", "make_rs", "make_moe", "make_ring", "fingerprint",
 ]
 
 
@@ -138,6 +138,26 @@ class MoeWorkload:
     def F(self): return self.W[0].shape[1]
 
 
+@dataclasses.dataclass
+class RingWorkload:
+    """Ring attention: rank 0's queries and every rank's key/value shard."""
+    Q: np.ndarray                   # uint16[H, S, D]
+    K: List[np.ndarray]             # R x uint16[H, S, D], rank r's keys
+    V: List[np.ndarray]             # R x uint16[H, S, D]
+    order: np.ndarray               # int32[(R-1)*H], arrival order of units (ring step s >= 1, head h): (s-1)*H + h
+    delay_ns: np.ndarray            # uint32[(R-1)*H]
+    out_dtype: str
+
+    @property
+    def H(self): return self.Q.shape[0]
+    @property
+    def S(self): return self.Q.shape[1]
+    @property
+    def D(self): return self.Q.shape[2]
+    @property
+    def R(self): return len(self.K)
+
+
 # ---------------------------------------------------------------------------
 # generators
 # ---------------------------------------------------------------------------
@@ -231,6 +251,25 @@ def make_moe(T: int, H: int, E: int, k: int, L: int, F: int, *, seed: int = 0,
                        order, delay, block_tokens, out_dtype)
 
 
+def make_ring(H: int, S: int, D: int, R: int, *, seed: int = 0, step_delay_ns: int = 0,
+              out_dtype: str = "bf16") -> RingWorkload:
+    """Ring-attention inputs.  Stream order: schedule, Q, K_0..K_{R-1}, V_0..V_{R-1}.
+
+    Q, K, V ~ N(0, 1) in bf16.  Units (ring step s = 1..R-1, head h) arrive
+    step by step (a ring delivers step s after step s-1), the heads of one
+    step in a seeded order; unit (s, h) is released (s-1)*step_delay_ns after
+    the first copy starts.
+    """
+    st = _streams(seed, 2 + 2 * R)
+    order = np.concatenate([(s - 1) * H + st[0].permutation(H) for s in range(1, R)]).astype(np.int32) \
+        if R > 1 else np.zeros(0, np.int32)
+    delay = np.array([((u // H)) * step_delay_ns for u in range((R - 1) * H)], np.uint32)
+    Q = _normal_bf16(st[1], (H, S, D), 1.0)
+    K = [_normal_bf16(st[2 + r], (H, S, D), 1.0) for r in range(R)]
+    V = [_normal_bf16(st[2 + R + r], (H, S, D), 1.0) for r in range(R)]
+    return RingWorkload(Q, K, V, order, delay, out_dtype)
+
+
 # ---------------------------------------------------------------------------
 # the five workloads (shapes of the fused kernels' single-GPU share)
 # ---------------------------------------------------------------------------
@@ -252,6 +291,10 @@ def _moe(seed=0):
                     out_dtype="bf16")
 
 
+def _ring(seed=0):
+    return make_ring(16, 4096, 128, 8, seed=seed)
+
+
 def _skinny_ag(seed=0):
     return make_ag(8, 16, 8192, 28672, seed=seed, out_dtype="bf16")
 
@@ -262,4 +305,5 @@ CONFIGS: Dict[str, dict] = {
     "rs": dict(make=_rs, op="rs", desc="GEMM+RS 8192x3584x8192, 7 fp32 partials, 8 owners"),
     "moe": dict(make=_moe, op="moe", desc="MoE T=4096 H=7168 top-8 of 256, 32 local experts, F=2048"),
     "skinny_ag": dict(make=_skinny_ag, op="ag", desc="AG+GEMM R=8 x 16x8192, N=28672"),
+    "ring": dict(make=_ring, op="ring", desc="Ring attention R=8 x 4096 tokens, 16 heads of 128, non-causal"),
 }
