@@ -291,6 +291,42 @@ def bench_moe(args, stream, extra=True):
     return r
 
 
+def bench_ring(args, stream, extra=True):
+    """Ring attention, rank 0's share: its queries against all R shards of
+    keys and values, the peers' shards moved into the receive buffers by the
+    kernel's copy workgroups."""
+    import workloads as wl
+    from tile_pipelined_gemm_amd import mk
+    from tile_pipelined_gemm_amd.harness import RingProblem
+    w = wl.CONFIGS["ring"]["make"](args.seed)
+    prob = RingProblem(w)
+    flops = prob.flops
+    H, S, D, R = w.H, w.S, w.D, w.R
+    # Q, every shard read once, O written, the R-1 peer shards written to and
+    # read back from the receive buffers
+    abytes = H * S * D * 2 * (1 + 2 * R + 1 + 2 * 2 * (R - 1))
+
+    def fused(i):
+        prob.run(stream=stream, check=False)
+
+    settle(fused, 0.3)
+    wall, kern = timed(fused, max(3, args.steps // 2), 2, stream)
+    assert mk.mk_poll_status(prob.ws, stream) == mk.MK_OK
+    r = dict(workload=wl.CONFIGS["ring"]["desc"], H=H, S=S, D=D, R=R, ms=wall, kernel_ms=kern,
+             tflops=flops / kern / 1e9, flops=flops, alg_bytes=abytes,
+             mfma_tflops=1.5 * flops / kern / 1e9)
+    if extra:
+        lau = mk.make_launch(mode=1)
+        _, uk = timed(lambda i: prob.run(launch=lau, stream=stream, check=False), 3, 1, stream)
+        r["unfused_ms"] = uk
+        r["speedup_vs_unfused"] = uk / kern
+        for tag, kw in [("n_copy64", dict(n_copy=64))]:
+            lv = mk.make_launch(**kw)
+            _, vk = timed(lambda i: prob.run(launch=lv, stream=stream, check=False), 3, 1, stream)
+            r[f"variant_{tag}_ms"] = vk
+    return r
+
+
 def cpu_baseline(seed):
     """The oracle (numpy float64) timed on whole calls of the AG workload."""
     import numpy as np
@@ -379,6 +415,9 @@ def main():
     if want("moe"):
         log("bench: moe")
         configs["moe"] = bench_moe(args, stream, extra)
+    if want("ring"):
+        log("bench: ring")
+        configs["ring"] = bench_ring(args, stream, extra)
     cpu = None
     if primary is not None and not args.no_cpu:
         log("bench: cpu baseline")

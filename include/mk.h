@@ -213,6 +213,41 @@ int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t T, int64_t 
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Ring attention  ([P1] "Los cinco núcleos fusionados", row Ring Attention)
+ *
+ * R ranks each hold S consecutive tokens of a sequence: rank r's keys and
+ * values k_shards[r], v_shards[r], each [H][S][D] bf16 (H heads, D = 128).
+ * This GPU is rank 0 with queries Q [H][S][D] bf16.  Its output is full
+ * (non-causal) attention of its queries over all R*S keys:
+ *   O[h, i] = sum_j softmax_j(Q[h, i] . K[h, j] / sqrt(D)) V[h, j]
+ * written to O [H][S][D] of `o_dtype` (fp32 arithmetic, one final rounding).
+ * The shards arrive round a ring: step s = 1..R-1 delivers rank (R-s) mod R's
+ * shard.  Copy workgroups move unit u = (s-1)*H + h (head h's keys and
+ * values of step s) from the owner's buffers into the receive buffers
+ * k_recv, v_recv [(R-1)][H][S][D] bf16 (caller-owned, overwritten), in
+ * arrival->order; the attention workgroups consume the own shard first and
+ * then step after step, each head's step s as soon as its unit has landed
+ * (online softmax in ring order).
+ *   arrival NULL = units in index order (step by step), no delay; otherwise
+ *   n_units = (R-1)*H and unit_rows = 1.  R = 1 takes no arrival and no
+ *   receive buffers (NULL allowed).
+ *   launch: mode 0 fused, 1 unfused (all copies, then attention); grid,
+ *   n_copy (default: every workgroup copies first), spin_limit_us,
+ *   tile_log, copy_log.  Other fields are ignored.
+ *   tile_log (optional): per compute item q (head_order[q / ceil(S/128)],
+ *   query block q % ceil(S/128)) 8 int32 {head, query block, R, 0,
+ *   workgroup, t_take, t_ready (last unit acquired), t_done}.
+ *   copy_log (optional): per copy item w = 2*position + part (0 keys, 1
+ *   values), 8 int32 {unit, part, workgroup, t_start, t_end, 0, 0, 0}.
+ *   Limits: D = 128, H <= 256, S <= 2^20, H*S <= 2^26, (R-1)*H <= MK_MAX_UNITS.
+ * ------------------------------------------------------------------------- */
+size_t mk_ring_attn_workspace(int H, int64_t S, int R);
+int mk_ring_attn(const void* Q, const void* const* k_shards, const void* const* v_shards, int R, int H,
+                 int64_t S, int D, void* O, int o_dtype, void* k_recv, void* v_recv,
+                 const mk_arrival* arrival, const mk_launch* launch, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Support
  * ------------------------------------------------------------------------- */
 /* Zero-fill a workspace with a fill kernel (no memset node), asynchronously. */

@@ -165,3 +165,41 @@ def test_moe_validation(lib):
     assert _moe(lib, ws_bytes=100) == mk.MK_ERR_WORKSPACE
     arr, keep = mk.make_arrival([0, 1, 1, 3], None, 64)
     assert _moe(lib, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE
+
+
+def _ring(lib, R=4, H=2, S=300, D=128, o=mk.MK_BF16, recv=True, arrival=None, lau=None, ws_bytes=1 << 20):
+    K = (C.c_void_p * R)(*([FAKE] * R))
+    V = (C.c_void_p * R)(*([FAKE] * R))
+    rv = FAKE if recv else None
+    return lib.mk_ring_attn(FAKE, K, V, R, H, S, D, FAKE, o, rv, rv, arrival, lau, FAKE, ws_bytes, None)
+
+
+def test_ring_validation(lib):
+    import torch
+    if not torch.cuda.is_available():
+        assert _ring(lib) == mk.MK_ERR_HIP                      # valid: the first HIP call fails
+        assert _ring(lib, R=1, recv=False) == mk.MK_ERR_HIP     # one rank needs no receive buffers
+    assert _ring(lib, D=64) == mk.MK_ERR_UNSUPPORTED
+    assert _ring(lib, R=0) == mk.MK_ERR_UNSUPPORTED
+    assert _ring(lib, R=65) == mk.MK_ERR_UNSUPPORTED
+    assert _ring(lib, H=0) == mk.MK_ERR_INVALID
+    assert _ring(lib, S=0) == mk.MK_ERR_INVALID
+    assert _ring(lib, H=40, R=8) == mk.MK_ERR_UNSUPPORTED    # 280 units > MK_MAX_UNITS
+    assert _ring(lib, o=7) == mk.MK_ERR_INVALID
+    assert _ring(lib, recv=False) == mk.MK_ERR_INVALID
+    assert _ring(lib, ws_bytes=64) == mk.MK_ERR_WORKSPACE
+    lau = mk.make_launch(mode=2)
+    assert _ring(lib, lau=C.byref(lau)) == mk.MK_ERR_INVALID
+    # arrival: a permutation of (R-1)*H units of one "row" each
+    arr, keep = mk.make_arrival([0, 1, 2, 3, 4, 5], None, 1)
+    if not torch.cuda.is_available():
+        assert _ring(lib, arrival=C.byref(arr)) == mk.MK_ERR_HIP
+    arr, keep = mk.make_arrival([0, 1, 2, 3, 4, 4], None, 1)
+    assert _ring(lib, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE
+    arr, keep = mk.make_arrival([0, 1, 2, 3, 4], None, 1)
+    assert _ring(lib, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE
+    arr, keep = mk.make_arrival([0, 1, 2], None, 2)
+    assert _ring(lib, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE
+    arr, keep = mk.make_arrival([0], None, 1)
+    assert _ring(lib, R=1, recv=False, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE
+    assert lib.mk_ring_attn_workspace(16, 4096, 8) >= 256 + 4 * 112

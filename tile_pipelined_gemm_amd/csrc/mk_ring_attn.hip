@@ -1,0 +1,535 @@
+// Ring attention as one persistent kernel.
+//
+// [P1] "Los cinco núcleos fusionados", row Ring Attention: the sequence is
+// split across ranks; key/value shards travel round a ring, one hop per step,
+// and each rank's local attention consumes the shard it holds while the next
+// one is in transit, transfers and compute sharing one persistent kernel.
+// [P1] "¿Qué hace mKernel?": the workgroups pick their roles themselves.
+//
+// This GPU is rank 0.  The other ranks' key/value shards are resident
+// buffers; copy workgroups move them, one (ring step, head) unit at a time in
+// the arrival order, into receive buffers, exactly where a ring transfer
+// would leave them.  Ring step s delivers the shard of rank (R - s) mod R.
+//
+// Roles (by start-order ticket):
+//   copy    tickets [0, n_copy): take (unit, K or V) items in arrival order,
+//           wait for the unit's release time, copy one head's S x 128 keys
+//           (or values) into the receive buffer with write-through stores,
+//           publish with an agent-scope release on the unit's counter.  Then
+//           compute.
+//   compute take (head, 128-query block) items; run the online softmax over
+//           the ring steps in order (own shard first), waiting at the start
+//           of each later step for that step's unit of the head.
+//
+// Compute item: 4 waves x 32 queries, head dimension 128.  Keys and values
+// stream through LDS in blocks of 64 (two stages, direct-to-LDS DMA).  Per
+// block and wave:
+//   S^T = K Q^T          16 MFMA 32x32x16; the C layout gives each lane one
+//                        query, so row statistics stay in the lane (one
+//                        cross-half exchange per block for the max)
+//   P = exp2(c (S - m))  c = log2(e)/sqrt(D); the running max m is raised only
+//                        when a row's block max exceeds it by more than 8/c
+//                        (p then stays below 2^8), so the O rescale is rare
+//   O^T += V^T P^T       P split into bf16 high and low parts, 2 x 16 MFMAs:
+//                        one bf16 rounding of P alone costs ~1.5e-3 relative
+//                        error on outputs that are themselves sums of random
+//                        terms; the split brings it to ~1e-6
+// The row sums are kept per lane half in fp32 and joined once at the end.
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "mk_device.h"
+#include "mk_gemm_dma.h"
+#include "mk_host.h"
+
+using namespace mk;
+
+namespace {
+
+enum { MODE_FUSED = 0, MODE_COPY = 1, MODE_ATTN = 2 };
+
+constexpr int HD = 128;          // head dimension
+constexpr int BQ = 128;          // queries per compute item (4 waves x 32)
+constexpr int BKV = 64;          // keys per LDS block
+constexpr int NT = 256;
+constexpr int MAX_HEADS = 256;
+constexpr int STAGE_BYTES = 2 * BKV * HD * 2;   // K block + V block
+constexpr float RESCALE_LOG2 = 8.0f;
+
+struct RingParams {
+  const uint16_t* Q;
+  const uint16_t* K[MK_MAX_RANKS];
+  const uint16_t* V[MK_MAX_RANKS];
+  uint16_t* Kr;          // receive buffers [(R-1)][H][S][HD], unit u = (s-1)*H + h
+  uint16_t* Vr;
+  void* O;
+  WsHeader* hdr;
+  uint32_t* unit_cnt;    // [n_units] parts (K, V) landed
+  int32_t* tile_log;
+  int32_t* copy_log;
+  uint64_t spin_limit;
+  float c;               // log2(e) / sqrt(HD)
+  int H, S, R, o_bf16, n_units, withhold, mode, n_copy, nqb, n_items, nkb;
+  uint32_t head_bytes;   // S * HD * 2
+  uint16_t order[MK_MAX_UNITS];
+  uint16_t head_order[MAX_HEADS];   // heads in the arrival order of their step-1 unit
+  uint32_t delay_ticks[MK_MAX_UNITS];
+};
+
+constexpr int COPY_UNROLL = 16;   // 16-byte loads in flight per thread
+
+__device__ __forceinline__ void copy_head(__amdgpu_buffer_rsrc_t src, __amdgpu_buffer_rsrc_t dst, int n16, int tid) {
+  for (int base = 0; base < n16; base += NT * COPY_UNROLL) {
+    u32x4 v[COPY_UNROLL];
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) v[u] = bload(src, (uint32_t)(base + u * NT + tid) * 16u, 0);
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) bstore<16>(dst, (uint32_t)(base + u * NT + tid) * 16u, 0, v[u]);
+  }
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bf16 (nearest even) in one instruction; a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Barrier that waits only for this wave's LDS reads (not for the DMA of the
+// next block, which stays in flight across it).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ void ring_copy_role(const RingParams& p, WsHeader* h, uint32_t* sb) {
+  const int tid = threadIdx.x;
+  uint64_t t0 = 0;
+  if (tid == 0) {
+    const uint64_t now = now_ticks();
+    const uint64_t old = atomicCAS((unsigned long long*)&h->t0, 0ull, (unsigned long long)now);
+    t0 = old ? old : now;
+  }
+  const uint32_t n_work = (uint32_t)p.n_units * 2u;
+  const int n16 = p.S * (HD / 8);
+  uint32_t w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
+  while (w < n_work) {
+    const int u = p.order[w >> 1], part = (int)(w & 1u);
+    if (u != p.withhold) {                       // a withheld unit never lands (failure tests)
+      uint32_t t_start = 0;
+      if (tid == 0) {
+        wait_until(t0 + p.delay_ticks[u], p.spin_limit);
+        t_start = (uint32_t)now_ticks();
+      }
+      __syncthreads();
+      const int s = u / p.H + 1, hd = u % p.H, r = (p.R - s) % p.R;
+      const uint16_t* src = (part ? p.V[r] : p.K[r]) + (int64_t)hd * p.S * HD;
+      uint16_t* dst = (part ? p.Vr : p.Kr) + (int64_t)u * p.S * HD;
+      copy_head(make_rsrc(uni(src), p.head_bytes), make_rsrc(uni(dst), p.head_bytes), n16, tid);
+      fence_release();
+      __syncthreads();
+      if (tid == 0) {
+        add_release(&p.unit_cnt[u], 1u);
+        add_release(&h->aux[0], 1u);              // parts landed in total
+        if (p.copy_log) {
+          int32_t* L = p.copy_log + 8 * (int64_t)w;
+          L[0] = u; L[1] = part; L[2] = (int32_t)blockIdx.x;
+          L[3] = (int32_t)t_start; L[4] = (int32_t)(uint32_t)now_ticks();
+          L[5] = 0; L[6] = 0; L[7] = 0;
+        }
+      }
+    }
+    w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
+  }
+}
+
+// Per-lane LDS offsets of one wave's fragment reads and DMA slots.
+//  K stage: key kk, 16-byte chunk cc (8 dims) at unit kk*16 + (cc ^ (kk & 15)):
+//           the 16 lanes of a ds_read_b128 (keys kk..kk+15, one chunk) hit
+//           16 distinct bank groups.
+//  V stage: key kk, chunk cc at unit kk*16 + (cc ^ 4*(kk & 3)): a transposed
+//           read takes 4 keys x 4 chunks per 32 lanes, again all distinct.
+struct LaneOfs {
+  uint32_t kdma[4];   // voffset of K DMA instruction ii (keys 16w + 4ii + lane/16)
+  uint32_t vdma;      // voffset of every V DMA instruction
+  uint32_t kread;     // byte offset of key (lane % 32) in the K stage
+  uint32_t kx;        // XOR applied to chunk indices of that key
+  uint32_t vread[4];  // transposed-read address of d-tile dt, first key group
+};
+
+__device__ __forceinline__ LaneOfs lane_offsets() {
+  const int lane = threadIdx.x & 63, c32 = lane & 31, hh = lane >> 5, g = lane >> 4, L16 = lane & 15;
+  LaneOfs o;
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int kk = 4 * ii + (lane >> 4);                        // key within the wave's 16 (mod 16)
+    o.kdma[ii] = (uint32_t)(kk * 256 + ((L16 ^ kk) & 15) * 16);
+  }
+  o.vdma = (uint32_t)((lane >> 4) * 256 + ((L16 ^ (4 * (lane >> 4))) & 15) * 16);
+  o.kread = (uint32_t)(c32 * 256);
+  o.kx = (uint32_t)(c32 & 15);
+  const int row = 4 * hh + (L16 >> 2);                          // key row within the 8-key group
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int cc = 4 * dt + 2 * (g & 1) + ((lane & 3) >> 1);
+    o.vread[dt] = (uint32_t)(row * 256 + ((cc ^ (4 * (row & 3))) & 15) * 16 + (lane & 1) * 8);
+  }
+  return o;
+}
+
+// DMA of key block kb of one (step, head) source into a stage: 4 K and 4 V
+// instructions per wave.  Keys at or past S read as zero (descriptor range).
+__device__ __forceinline__ void issue_block(const LaneOfs& lo, u32x4 dk, u32x4 dv, uint32_t stage_lds, int kb) {
+  const int w = uni((int)(threadIdx.x >> 6));
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+    dma16(dk, uni(stage_lds + (uint32_t)((4 * w + ii) * 1024)), lo.kdma[ii], uni((uint32_t)((kb * BKV + 16 * w) * 256)));
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+    dma16(dv, uni(stage_lds + 16384u + (uint32_t)((4 * w + ii) * 1024)), lo.vdma,
+          uni((uint32_t)((kb * BKV + 16 * w + 4 * ii) * 256)));
+}
+
+struct AttnState {
+  f32x16 o[4];     // O^T, d-tile dt: lane's query, dims 32dt + 8(r/4) + 4(lane/32) + r%4
+  float m, l;      // running max (raw score units) and this lane half's row sum
+};
+
+// One key block from the stage at `st`: `valid` keys (1..64) are real.
+__device__ __forceinline__ void attn_block(AttnState& a, const bf16x8 (&qf)[8], const LaneOfs& lo_ofs, const char* st,
+                                           int valid, float c) {
+  const int lane = threadIdx.x & 63, hh = lane >> 5;
+  f32x16 s[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const uint32_t off = lo_ofs.kread + ((((uint32_t)(2 * ks + hh)) ^ lo_ofs.kx) << 4);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 kf = *(const bf16x8*)(st + off + t * 32 * 256);
+      s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
+    }
+  }
+  if (valid < BKV) {                      // ragged last block of a shard
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * t + 8 * (r >> 2) + 4 * hh + (r & 3) >= valid) s[t][r] = -INFINITY;
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const bool need = (mx - a.m) * c > RESCALE_LOG2;   // always true on the first block (m = -inf)
+  if (__ballot(need)) {
+    const float alpha = need ? __builtin_amdgcn_exp2f((a.m - mx) * c) : 1.f;
+    if (need) a.m = mx;
+    a.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a.o[dt][r] *= alpha;
+  }
+  const float mc = a.m * c;
+  float sum = 0.f;
+  // k-step (t, j): slot i of lane half hh is key 32t + 16j + 8(i/4) + 4hh + i%4,
+  // the keys of registers 8j..8j+7 of S^T tile t in this lane.  Each k-step's
+  // probabilities are formed just before its 8 MFMAs, so the exponentials of
+  // the next k-step can issue while they run.
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 hi, lo;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * j + 2 * k], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * j + 2 * k + 1], c, -mc));
+        sum += p0 + p1;
+        const uint32_t u0 = __builtin_bit_cast(uint32_t, p0), u1 = __builtin_bit_cast(uint32_t, p1);
+        // high part: p truncated to bf16 (its top 16 bits); low part: the
+        // exact remainder, rounded to bf16 (relative error of p below 2^-16)
+        hi[k] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        const float l0 = p0 - __builtin_bit_cast(float, u0 & 0xffff0000u);
+        const float l1 = p1 - __builtin_bit_cast(float, u1 & 0xffff0000u);
+        lo[k] = pack_bf16(l0, l1);
+      }
+      const bf16x8 ph = __builtin_bit_cast(bf16x8, hi), pl = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const char* base = st + 16384 + lo_ofs.vread[dt] + (32 * t + 16 * j) * 256;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * 256));
+        const i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
+        a.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ph, a.o[dt], 0, 0, 0);
+        a.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl, a.o[dt], 0, 0, 0);
+      }
+    }
+  a.l += sum;
+}
+
+__device__ __forceinline__ void ring_attn_role(const RingParams& p, WsHeader* h, char* lds, uint32_t* sb) {
+  const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, hh = lane >> 5;
+  const int w = uni(tid >> 6);
+  const LaneOfs lo = lane_offsets();
+  const uint32_t lds0 = uni(lds_addr(lds));
+  const uint32_t all_parts = (uint32_t)p.n_units * 2u;
+  bool all_landed = (p.mode == MODE_ATTN) || p.n_units == 0;
+  const int total = p.R * p.nkb;
+  uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+  while (q < (uint32_t)p.n_items) {
+    const int hd = p.head_order[q / p.nqb], qb = q % p.nqb;
+    const int q0 = qb * BQ;
+    const uint32_t t_take = (uint32_t)now_ticks();
+    uint32_t t_ready = t_take;
+    // Q fragments (B operand of S^T = K Q^T): query q0 + 32w + lane%32,
+    // dims 16ks + 8(lane/32) .. +7.  Rows at or past S read as zero.
+    bf16x8 qf[8];
+    {
+      const __amdgpu_buffer_rsrc_t rq =
+          make_rsrc(uni(p.Q + ((int64_t)hd * p.S + q0) * HD), (uint32_t)(p.S - q0) * (HD * 2));
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, bload(rq, (uint32_t)((32 * w + c32) * (HD * 2) + (2 * ks + hh) * 16), 0));
+    }
+    AttnState a;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a.o[dt][r] = 0.f;
+    a.m = -INFINITY;
+    a.l = 0.f;
+
+    auto descs = [&](int s, u32x4& dk, u32x4& dv) {
+      const uint16_t* kb = s == 0 ? p.K[0] + (int64_t)hd * p.S * HD : p.Kr + ((int64_t)(s - 1) * p.H + hd) * p.S * HD;
+      const uint16_t* vb = s == 0 ? p.V[0] + (int64_t)hd * p.S * HD : p.Vr + ((int64_t)(s - 1) * p.H + hd) * p.S * HD;
+      dk = buf_desc(kb, p.head_bytes);
+      dv = buf_desc(vb, p.head_bytes);
+    };
+    u32x4 dk, dv;
+    descs(0, dk, dv);
+    issue_block(lo, dk, dv, lds0, 0);
+    uint32_t ok = 1;
+    for (int b = 0; b < total && ok; ++b) {
+      const int b1 = b + 1;
+      if (b1 < total) {
+        const int s1 = b1 / p.nkb, kb1 = b1 - s1 * p.nkb;
+        if (kb1 == 0) {
+          if (!all_landed) {                     // step s1's unit of this head must have landed
+            const int u = (s1 - 1) * p.H + hd;
+            uint32_t all = 0;
+            if (tid == 0) {
+              ok = wait_geq_relaxed(&p.unit_cnt[u], 2u, h, p.spin_limit);
+              if (ok) {
+                all = ld_relaxed(&h->aux[0]) >= all_parts;
+                fence_acquire();
+              }
+            }
+            const uint32_t v = wg_bcast(ok | (all << 1), sb);
+            ok = v & 1u;
+            all_landed = (v >> 1) & 1u;
+            t_ready = (uint32_t)now_ticks();
+            if (!ok) break;                      // watchdog expired: drop the item
+          }
+          descs(s1, dk, dv);
+        }
+        issue_block(lo, dk, dv, lds0 + (uint32_t)((b1 & 1) * STAGE_BYTES), kb1);
+        wait_barrier<8>();                       // block b landed (block b+1 in flight)
+      } else {
+        wait_barrier<0>();
+      }
+      const int kb = b % p.nkb;
+      attn_block(a, qf, lo, lds + (b & 1) * STAGE_BYTES, min(BKV, p.S - kb * BKV), p.c);
+      barrier_lds();                             // stage b&1 is refilled at the next iteration
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (ok) {
+      // O = O^T / l; lane stores its query's dims 32dt + 8(r/4) + 4hh + 0..3.
+      const float lt = a.l + __shfl_xor(a.l, 32);
+      const float inv = 1.f / lt;
+      const int64_t esz = p.o_bf16 ? 2 : 4;
+      const __amdgpu_buffer_rsrc_t ro =
+          make_rsrc(uni((char*)p.O + ((int64_t)hd * p.S + q0) * HD * esz), (uint32_t)((p.S - q0) * HD * esz));
+      const uint32_t rowoff = (uint32_t)((32 * w + c32) * HD * esz);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const uint32_t off = rowoff + (uint32_t)((32 * dt + 8 * r4 + 4 * hh) * esz);
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = a.o[dt][4 * r4 + i] * inv;
+          if (p.o_bf16) {
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, ro, off, 0, 0);
+          } else {
+            bstore_alu16(ro, off, 0, v);
+          }
+        }
+      if (p.tile_log && tid == 0) {
+        int32_t* L = p.tile_log + 8 * (int64_t)q;
+        L[0] = hd; L[1] = qb; L[2] = p.R; L[3] = 0; L[4] = (int32_t)blockIdx.x;
+        L[5] = (int32_t)t_take; L[6] = (int32_t)t_ready; L[7] = (int32_t)(uint32_t)now_ticks();
+      }
+    }
+    q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+  }
+}
+
+// Last workgroup out restores the workspace for the next call.
+__device__ __forceinline__ void ring_finish(const RingParams& p, WsHeader* h, uint32_t* sb) {
+  __syncthreads();
+  uint32_t last = 0;
+  if (threadIdx.x == 0) {
+    fence_release();
+    last = add_relaxed(&h->done, 1u) == gridDim.x - 1;
+    if (last) fence_acquire();
+  }
+  last = wg_bcast(last, sb);
+  if (!last) return;
+  for (int i = threadIdx.x; i < p.n_units; i += blockDim.x) st_relaxed(&p.unit_cnt[i], 0u);
+  if (threadIdx.x == 0) {
+    st_relaxed(&h->ticket, 0u);
+    st_relaxed(&h->tile_next, 0u);
+    st_relaxed(&h->copy_next, 0u);
+    st_relaxed(&h->abort, 0u);
+    st_relaxed(&h->aux[0], 0u);
+    __hip_atomic_store(&h->t0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_relaxed(&h->done, 0u);
+  }
+}
+
+__global__ __launch_bounds__(NT, 2) void ring_kernel(const RingParams p) {
+  __shared__ uint32_t sb[2];
+  __shared__ u32x4 lds[2 * STAGE_BYTES / 16];
+  WsHeader* h = p.hdr;
+  const uint32_t ticket = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->ticket, 1u) : 0u, sb);
+  if (p.mode == MODE_COPY || (p.mode == MODE_FUSED && ticket < (uint32_t)p.n_copy)) ring_copy_role(p, h, sb);
+  if (p.mode != MODE_COPY) ring_attn_role(p, h, (char*)lds, sb);
+  ring_finish(p, h, sb);
+}
+
+}  // namespace
+
+extern "C" size_t mk_ring_attn_workspace(int H, int64_t S, int R) {
+  (void)H; (void)S; (void)R;
+  return sizeof(WsHeader) + MK_MAX_UNITS * sizeof(uint32_t);
+}
+
+extern "C" int mk_ring_attn(const void* Q, const void* const* k_shards, const void* const* v_shards, int R, int H,
+                            int64_t S, int D, void* O, int o_dtype, void* k_recv, void* v_recv,
+                            const mk_arrival* arrival, const mk_launch* launch, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  using mkh::fail;
+  if (!Q || !k_shards || !v_shards || !O) return fail(MK_ERR_INVALID, "Q, k_shards, v_shards and O must be non-NULL");
+  if (R < 1 || R > MK_MAX_RANKS) return fail(MK_ERR_UNSUPPORTED, "R=%d outside [1,%d]", R, MK_MAX_RANKS);
+  if (H < 1 || S < 1) return fail(MK_ERR_INVALID, "empty shape (H=%d, S=%lld)", H, (long long)S);
+  if (D != HD) return fail(MK_ERR_UNSUPPORTED, "head dimension %d (only %d is built)", D, HD);
+  if (H > MAX_HEADS || S > (1 << 20) || (int64_t)H * S > (1 << 26))
+    return fail(MK_ERR_UNSUPPORTED, "H=%d, S=%lld too large", H, (long long)S);
+  if ((int64_t)(R - 1) * H > MK_MAX_UNITS)
+    return fail(MK_ERR_UNSUPPORTED, "(R-1)*H = %lld units exceed %d", (long long)(R - 1) * H, MK_MAX_UNITS);
+  if (o_dtype != MK_BF16 && o_dtype != MK_F32) return fail(MK_ERR_INVALID, "o_dtype %d", o_dtype);
+  if (!mkh::aligned16(Q) || !mkh::aligned16(O)) return fail(MK_ERR_INVALID, "Q and O must be 16-byte aligned");
+  for (int r = 0; r < R; ++r)
+    if (!k_shards[r] || !v_shards[r] || !mkh::aligned16(k_shards[r]) || !mkh::aligned16(v_shards[r]))
+      return fail(MK_ERR_INVALID, "shard %d NULL or misaligned", r);
+  if (R > 1 && (!k_recv || !v_recv || !mkh::aligned16(k_recv) || !mkh::aligned16(v_recv)))
+    return fail(MK_ERR_INVALID, "k_recv and v_recv must be non-NULL and 16-byte aligned");
+  const int n_units = (R - 1) * H;
+  mkh::Schedule s;
+  if (n_units > 0) {
+    if (arrival && arrival->unit_rows != 1)
+      return fail(MK_ERR_SCHEDULE, "ring units are one (step, head) each: unit_rows must be 1, got %d",
+                  arrival->unit_rows);
+    int rc = mkh::make_schedule(arrival, n_units, n_units, &s);
+    if (rc) return rc;
+  } else if (arrival && arrival->n_units != 0) {
+    return fail(MK_ERR_SCHEDULE, "R=1 has no units to deliver");
+  }
+  if (!workspace) return fail(MK_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < mk_ring_attn_workspace(H, S, R))
+    return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, mk_ring_attn_workspace(H, S, R));
+  const mk_launch o = mkh::launch_opts(launch);
+  if (o.mode < 0 || o.mode > 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
+  if (o.grid < 0 || o.n_copy < 0) return fail(MK_ERR_INVALID, "negative grid or n_copy");
+  const mkh::DevInfo* d = mkh::dev_info();
+  if (!d) return MK_ERR_HIP;
+
+  RingParams p;
+  memset(&p, 0, sizeof p);
+  p.Q = (const uint16_t*)Q;
+  for (int r = 0; r < R; ++r) {
+    p.K[r] = (const uint16_t*)k_shards[r];
+    p.V[r] = (const uint16_t*)v_shards[r];
+  }
+  p.Kr = (uint16_t*)k_recv;
+  p.Vr = (uint16_t*)v_recv;
+  p.O = O;
+  p.hdr = (WsHeader*)workspace;
+  p.unit_cnt = (uint32_t*)((char*)workspace + sizeof(WsHeader));
+  p.tile_log = o.tile_log;
+  p.copy_log = o.copy_log;
+  p.spin_limit = mkh::spin_ticks(o, d);
+  p.c = (float)(1.4426950408889634 / std::sqrt((double)HD));
+  p.H = H;
+  p.S = (int)S;
+  p.R = R;
+  p.o_bf16 = o_dtype == MK_BF16;
+  p.n_units = n_units;
+  p.withhold = n_units > 0 ? s.withhold : -1;
+  p.nqb = (int)((S + BQ - 1) / BQ);
+  p.n_items = H * p.nqb;
+  p.nkb = (int)((S + BKV - 1) / BKV);
+  p.head_bytes = (uint32_t)(S * HD * 2);
+  std::vector<int> heads(H), key(H);
+  for (int i = 0; i < H; ++i) {
+    heads[i] = i;
+    key[i] = n_units > 0 ? s.pos[i] : i;           // unit of (step 1, head i) is i
+  }
+  std::stable_sort(heads.begin(), heads.end(), [&](int a, int b) { return key[a] < key[b]; });
+  for (int i = 0; i < H; ++i) p.head_order[i] = (uint16_t)heads[i];
+  for (int j = 0; j < n_units; ++j) {
+    p.order[j] = (uint16_t)s.order[j];
+    p.delay_ticks[j] = (uint32_t)mkh::ns_to_ticks(s.delay_ns[j], d->wall_khz);   // indexed by unit
+  }
+
+  hipStream_t st = (hipStream_t)stream;
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ring_kernel, NT, 0);
+  if (e != hipSuccess) return mkh::hip_fail(e, "occupancy query");
+  if (occ < 1) return fail(MK_ERR_UNSUPPORTED, "kernel does not fit on a CU");
+  const int full = d->n_cu * occ;
+  const int grid = o.grid > 0 ? std::min(o.grid, full) : full;
+  const uint32_t n_work = (uint32_t)n_units * 2u;
+  if (o.mode == 1) {   // unfused baseline: all copies, then attention
+    if (n_work) {
+      p.mode = MODE_COPY;
+      p.n_copy = grid;
+      hipLaunchKernelGGL(ring_kernel, dim3(grid), dim3(NT), 0, st, p);
+      if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "copy kernel launch");
+    }
+    p.mode = MODE_ATTN;
+    p.n_copy = 0;
+    hipLaunchKernelGGL(ring_kernel, dim3(grid), dim3(NT), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "attention kernel launch");
+    return MK_OK;
+  }
+  p.mode = MODE_FUSED;
+  // Default: every workgroup copies first, then computes.  The items are few
+  // (one per workgroup at the full-size shape) and each takes the whole
+  // kernel, so a workgroup that starts its item late sets the end time; the
+  // copies themselves take a small part of it.
+  int n_copy = o.n_copy > 0 ? o.n_copy : grid;
+  n_copy = (int)std::min<uint32_t>((uint32_t)n_copy, std::min<uint32_t>(n_work, (uint32_t)grid));
+  p.n_copy = n_copy;
+  hipLaunchKernelGGL(ring_kernel, dim3(grid), dim3(NT), 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "fused kernel launch");
+  return MK_OK;
+}

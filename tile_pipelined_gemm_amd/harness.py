@@ -138,6 +138,39 @@ class MoeProblem:
                     perm=to_numpy(self.perm), n_local=n, Y=to_numpy(self.Y[:n]))
 
 
+class RingProblem:
+    """Ring attention: rank 0's queries, every rank's key/value shard and the
+    receive buffers the ring fills."""
+
+    def __init__(self, w, device="cuda"):
+        self.w = w
+        self.Q = bf16_tensor(w.Q, device)
+        self.K = [bf16_tensor(k, device) for k in w.K]
+        self.V = [bf16_tensor(v, device) for v in w.V]
+        self.O = torch.empty(w.H, w.S, w.D, dtype=_out_dtype(w.out_dtype), device=device)
+        if w.R > 1:
+            self.Kr = torch.empty(w.R - 1, w.H, w.S, w.D, dtype=torch.bfloat16, device=device)
+            self.Vr = torch.empty_like(self.Kr)
+        else:
+            self.Kr = self.Vr = None
+        self.ws = mk.workspace(mk.mk_ring_attn_workspace(w.H, w.S, w.R), device)
+
+    @property
+    def flops(self):
+        """Q K^T and P V: 4 * H * S * (R*S) * D."""
+        w = self.w
+        return 4.0 * w.H * w.S * (w.R * w.S) * w.D
+
+    def run(self, launch=None, order=None, delay_ns=None, withhold=-1, stream=None, check=True):
+        order = self.w.order if order is None else order
+        delay_ns = self.w.delay_ns if delay_ns is None else delay_ns
+        return mk.mk_ring_attn(self.Q, self.K, self.V, self.O, self.Kr, self.Vr, self.ws, order=order,
+                               delay_ns=delay_ns, withhold=withhold, launch=launch, stream=stream, check=check)
+
+    def output(self):
+        return to_numpy(self.O)
+
+
 def ag_timeline(prob, **launch_kw):
     """Run one AG+GEMM call with the tile and copy logs on and summarise its
     timeline (microseconds from the first logged event)."""

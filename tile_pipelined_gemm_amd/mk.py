@@ -26,7 +26,8 @@ TILE_128x128_DMA, TILE_256x128_DMA, TILE_128x256_DMA = 6, 7, 8
 EXPORTS = [
     "mk_ag_gemm_workspace", "mk_ag_gemm", "mk_gemm_rs_workspace", "mk_gemm_rs",
     "mk_gemm_ar_workspace", "mk_gemm_ar",
-    "mk_moe_dispatch_gemm_workspace", "mk_moe_dispatch_gemm", "mk_workspace_init",
+    "mk_moe_dispatch_gemm_workspace", "mk_moe_dispatch_gemm", "mk_ring_attn_workspace", "mk_ring_attn",
+    "mk_workspace_init",
     "mk_poll_status", "mk_status_string", "mk_last_error", "mk_tile_name", "mk_version",
     "mk_wall_clock_khz",
 ]
@@ -85,6 +86,11 @@ def load(path: Optional[str] = None):
     lib.mk_moe_dispatch_gemm.argtypes = [vp, vp, i64, i64, i32, i32, pp, i32, i32, i64,
                                          vp, vp, vp, vp, vp, vp, vp, i32,
                                          C.POINTER(mk_arrival), C.POINTER(mk_launch), vp, sz, vp]
+    lib.mk_ring_attn_workspace.restype = sz
+    lib.mk_ring_attn_workspace.argtypes = [i32, i64, i32]
+    lib.mk_ring_attn.restype = i32
+    lib.mk_ring_attn.argtypes = [vp, pp, pp, i32, i32, i64, i32, vp, i32, vp, vp,
+                                 C.POINTER(mk_arrival), C.POINTER(mk_launch), vp, sz, vp]
     lib.mk_workspace_init.restype = i32
     lib.mk_workspace_init.argtypes = [vp, sz, vp]
     lib.mk_poll_status.restype = i32
@@ -183,6 +189,28 @@ def mk_gemm_rs_workspace(M, K, N, R, out_dtype=MK_F32) -> int:
 
 def mk_moe_dispatch_gemm_workspace(T, H, E, k, L, F) -> int:
     return load().mk_moe_dispatch_gemm_workspace(T, H, E, k, L, F)
+
+
+def mk_ring_attn_workspace(H, S, R) -> int:
+    return load().mk_ring_attn_workspace(H, S, R)
+
+
+def mk_ring_attn(Q, k_shards, v_shards, O, k_recv, v_recv, ws, *, order=None, delay_ns=None, withhold=-1,
+                 launch=None, stream=None, check=True) -> int:
+    """Q, k_shards[r], v_shards[r]: [H, S, 128] bf16; O: [H, S, 128] bf16 or
+    float32; k_recv, v_recv: [(R-1), H, S, 128] bf16 receive buffers (None for
+    R = 1)."""
+    lib = load()
+    R = len(k_shards)
+    H, S, D = Q.shape
+    arr, keep = make_arrival(order if R > 1 else None, delay_ns, 1, withhold)
+    lau = launch if launch is not None else make_launch()
+    rc = lib.mk_ring_attn(_ptr(Q), _ptr_array(k_shards), _ptr_array(v_shards), R, H, S, D, _ptr(O),
+                          _dtype_code(O), _ptr(k_recv), _ptr(v_recv),
+                          C.byref(arr) if arr is not None else None, C.byref(lau),
+                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    del keep
+    return _check(rc) if check else rc
 
 
 def mk_workspace_init(ws, stream=None):
