@@ -35,7 +35,7 @@ using namespace mk;
 namespace {
 
 constexpr int RB = 64;          // tokens per routing block
-constexpr int ROUTE_NT = 256;   // 4 waves, 16 tokens each
+constexpr int ROUTE_NT = 1024;  // 16 waves, 4 tokens each
 
 struct MoeWs {                  // device workspace layout (offsets in bytes)
   size_t block_cnt, rank, tile_base, tile_cnt, kp_cnt, kp_slots, total;
@@ -76,11 +76,16 @@ __global__ __launch_bounds__(ROUTE_NT) void route_kernel(const float* __restrict
                                                          int32_t* __restrict__ topk, int32_t* __restrict__ block_cnt,
                                                          int32_t* __restrict__ rank) {
   __shared__ int16_t s_top[RB * MK_MAX_TOPK];
+  __shared__ unsigned long long s_mask[MK_MAX_EXPERTS];   // bit tl set: token tl of the block chose e
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t_blk = blockIdx.x * RB;
+  const int nt = min(RB, T - t_blk);
   const int per_lane = (E + 63) / 64;            // <= 16
-  for (int i = 0; i < RB / 4; ++i) {
-    const int tl = w * (RB / 4) + i;
+  for (int e = threadIdx.x; e < E; e += ROUTE_NT) s_mask[e] = 0ull;
+  __syncthreads();
+  constexpr int PER_WAVE = RB / (ROUTE_NT / 64);
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int tl = w * PER_WAVE + i;
     const int t = t_blk + tl;
     if (t >= T) break;                           // uniform per wave
     float v[16];
@@ -115,22 +120,20 @@ __global__ __launch_bounds__(ROUTE_NT) void route_kernel(const float* __restrict
       if (lane == 0) {
         topk[(int64_t)t * k + j] = bi;
         s_top[tl * MK_MAX_TOPK + j] = (int16_t)bi;
+        atomicOr(&s_mask[bi], 1ull << tl);
       }
     }
   }
   __syncthreads();
-  // Per expert: count within this routing block and rank of each pair.
-  const int nt = min(RB, T - t_blk);
-  for (int e = threadIdx.x; e < E; e += ROUTE_NT) {
-    int c = 0;
-    for (int tl = 0; tl < nt; ++tl)
-      for (int j = 0; j < k; ++j)
-        if (s_top[tl * MK_MAX_TOPK + j] == e) {
-          rank[(int64_t)(t_blk + tl) * k + j] = c;
-          ++c;
-        }
-    block_cnt[(int64_t)blockIdx.x * E + e] = c;
+  // Per expert: count within this routing block, and the rank of each pair
+  // (the number of earlier tokens of the block that chose the same expert; a
+  // token's k experts are distinct, so this is its position in token order).
+  for (int q = threadIdx.x; q < nt * k; q += ROUTE_NT) {
+    const int tl = q / k, j = q - (q / k) * k;
+    const int e = s_top[tl * MK_MAX_TOPK + j];
+    rank[(int64_t)(t_blk + tl) * k + j] = __popcll(s_mask[e] & ((1ull << tl) - 1ull));
   }
+  for (int e = threadIdx.x; e < E; e += ROUTE_NT) block_cnt[(int64_t)blockIdx.x * E + e] = __popcll(s_mask[e]);
 }
 
 // One workgroup of 1024 threads.
@@ -142,10 +145,17 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ block_
   const int e = threadIdx.x;
   int tot = 0;
   if (e < E) {
-    for (int b = 0; b < nrb; ++b) {
-      const int c = block_cnt[(int64_t)b * E + e];
-      block_cnt[(int64_t)b * E + e] = tot;       // becomes the block offset within expert e
-      tot += c;
+    // 16 independent loads per round trip, then the running sum over them
+    for (int b0 = 0; b0 < nrb; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = b0 + u < nrb ? block_cnt[(int64_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (b0 + u < nrb) {
+          block_cnt[(int64_t)(b0 + u) * E + e] = tot;   // becomes the block offset within expert e
+          tot += c[u];
+        }
     }
     counts[e] = tot;
   }
