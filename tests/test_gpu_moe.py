@@ -55,6 +55,17 @@ def test_ties_and_signed_zero_routing(gpu):
     assert np.all(prob.outputs()["topk"][:32] == np.arange(6))
 
 
+@pytest.mark.parametrize("E,k", [(300, 8), (1000, 16), (64, 1)])
+def test_routing_for_wide_and_narrow_expert_counts(gpu, E, k):
+    # E = 300 and 1000 take the 8- and 16-logits-per-lane routing kernels;
+    # T = 200 leaves a ragged last routing block of 8 tokens.
+    w = wl.make_moe(200, 128, E, k, 6, 128, seed=34 + E, expert_begin=E // 3, block_tokens=40)
+    prob = _run(gpu, w)
+    ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, E // 3, "bf16")
+    got = _check_exact(prob, ref)
+    assert_close(out_to_f64(got["Y"], "bf16"), ref["Y64"], "bf16", f"MoE E={E}")
+
+
 def test_integer_inputs_bit_exact_f32(gpu):
     w = wl.make_moe(512, 256, 32, 4, 8, 256, seed=33, dist="int", block_tokens=128, out_dtype="f32")
     prob = _run(gpu, w)

@@ -72,6 +72,9 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// PL = logits per lane (E <= 64*PL), a compile-time bound so the per-round
+// scan of a lane's logits has no dead slots.
+template <int PL>
 __global__ __launch_bounds__(ROUTE_NT) void route_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                          int32_t* __restrict__ topk, int32_t* __restrict__ block_cnt,
                                                          int32_t* __restrict__ rank) {
@@ -80,47 +83,61 @@ __global__ __launch_bounds__(ROUTE_NT) void route_kernel(const float* __restrict
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t_blk = blockIdx.x * RB;
   const int nt = min(RB, T - t_blk);
-  const int per_lane = (E + 63) / 64;            // <= 16
   for (int e = threadIdx.x; e < E; e += ROUTE_NT) s_mask[e] = 0ull;
   __syncthreads();
+  // A wave routes its PER_WAVE tokens together: their arg-max rounds are
+  // independent, so the shuffle chains of the tokens overlap.
   constexpr int PER_WAVE = RB / (ROUTE_NT / 64);
+  const int tl0 = w * PER_WAVE;
+  float v[PER_WAVE][PL];
+  uint32_t taken[PER_WAVE];
+#pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
-    const int tl = w * PER_WAVE + i;
-    const int t = t_blk + tl;
-    if (t >= T) break;                           // uniform per wave
-    float v[16];
+    const int t = t_blk + tl0 + i;
+    taken[i] = 0;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
+    for (int s = 0; s < PL; ++s) {
       const int e = lane + 64 * s;
-      const float x = (s < per_lane && e < E) ? logits[(int64_t)t * E + e] : -__builtin_inff();
-      v[s] = x == x ? x : -__builtin_inff();   // NaN ranks below every number
+      const float x = (t < T && e < E) ? logits[(int64_t)t * E + e] : -__builtin_inff();
+      v[i][s] = x == x ? x : -__builtin_inff();   // NaN ranks below every number
     }
-    uint32_t taken = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = -__builtin_inff();
-      int bi = 0x7fffffff;
+  }
+  for (int j = 0; j < k; ++j) {
+    float bv[PER_WAVE];
+    int bi[PER_WAVE];
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
+    for (int i = 0; i < PER_WAVE; ++i) {
+      bv[i] = -__builtin_inff();
+      bi[i] = 0x7fffffff;
+#pragma unroll
+      for (int s = 0; s < PL; ++s) {
         const int e = lane + 64 * s;
-        if (s < per_lane && e < E && !((taken >> s) & 1u) && better(v[s], e, bv, bi)) {
-          bv = v[s];
-          bi = e;
+        if (e < E && !((taken[i] >> s) & 1u) && better(v[i][s], e, bv[i], bi[i])) {
+          bv[i] = v[i][s];
+          bi[i] = e;
         }
       }
+    }
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
+    for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const float ov = __shfl_xor(bv[i], off, 64);
+        const int oi = __shfl_xor(bi[i], off, 64);
+        if (better(ov, oi, bv[i], bi[i])) {
+          bv[i] = ov;
+          bi[i] = oi;
         }
       }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == 0) {
-        topk[(int64_t)t * k + j] = bi;
-        s_top[tl * MK_MAX_TOPK + j] = (int16_t)bi;
-        atomicOr(&s_mask[bi], 1ull << tl);
+    }
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int tl = tl0 + i, t = t_blk + tl;
+      if ((bi[i] & 63) == lane) taken[i] |= 1u << (bi[i] >> 6);
+      if (lane == 0 && t < T) {
+        topk[(int64_t)t * k + j] = bi[i];
+        s_top[tl * MK_MAX_TOPK + j] = (int16_t)bi[i];
+        atomicOr(&s_mask[bi[i]], 1ull << tl);
       }
     }
   }
@@ -551,7 +568,12 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   int32_t* rank = (int32_t*)(ws + lay.rank);
   const int nrb = (int)((T + RB - 1) / RB);
 
-  hipLaunchKernelGGL(route_kernel, dim3(nrb), dim3(ROUTE_NT), 0, st, logits, (int)T, E, k, topk_idx, block_cnt, rank);
+  if (E <= 256)
+    hipLaunchKernelGGL(route_kernel<4>, dim3(nrb), dim3(ROUTE_NT), 0, st, logits, (int)T, E, k, topk_idx, block_cnt, rank);
+  else if (E <= 512)
+    hipLaunchKernelGGL(route_kernel<8>, dim3(nrb), dim3(ROUTE_NT), 0, st, logits, (int)T, E, k, topk_idx, block_cnt, rank);
+  else
+    hipLaunchKernelGGL(route_kernel<16>, dim3(nrb), dim3(ROUTE_NT), 0, st, logits, (int)T, E, k, topk_idx, block_cnt, rank);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return mkh::hip_fail(e, "route kernel launch");
 
