@@ -20,6 +20,9 @@ def fingerprints():
     m = wl.make_moe(64, 16, 32, 4, 8, 8, seed=0, block_tokens=16)
     out["moe_small"] = {"X": wl.fingerprint(m.X), "logits": wl.fingerprint(m.logits),
                         "W0": wl.fingerprint(m.W[0]), "order": m.order.tolist()}
+    g = wl.make_ring(2, 16, 128, 3, seed=0)
+    out["ring_small"] = {"Q": wl.fingerprint(g.Q), "K": [wl.fingerprint(k) for k in g.K],
+                         "V": [wl.fingerprint(v) for v in g.V], "order": g.order.tolist()}
     return out
 
 

@@ -54,3 +54,16 @@ def test_moe_blocks_and_logits():
     m = wl.make_moe(64, 16, 32, 4, 8, 8, seed=0, block_tokens=16)
     assert m.order.shape == (4,) and sorted(m.order.tolist()) == [0, 1, 2, 3]
     assert m.logits.dtype == np.float32 and np.all(np.isfinite(m.logits))
+
+
+def test_ring_schedule_is_step_major_permutation():
+    w = wl.make_ring(5, 8, 16, 4, seed=9, step_delay_ns=1500)
+    n = (w.R - 1) * w.H
+    validate(w.order, w.delay_ns, n)
+    # every unit of step s arrives before any unit of step s + 1
+    steps = w.order // w.H
+    assert np.all(np.diff(steps) >= 0)
+    assert np.array_equal(w.delay_ns, (np.arange(n) // w.H * 1500).astype(np.uint32))
+    assert (w.H, w.S, w.D, w.R) == (5, 8, 16, 4) and len(w.K) == len(w.V) == 4
+    one = wl.make_ring(2, 8, 16, 1, seed=9)
+    assert one.order.shape == (0,) and one.delay_ns.shape == (0,)
