@@ -32,4 +32,4 @@ one-hot operands), exact integer arithmetic, invariants (arrival-order
 independence, reduce-scatter over all owners = all-reduce, dispatch is a
 permutation whose counts sum to T*k) and library special cases.
 """
-from . import numerics, schedule, ag_gemm, gemm_rs, gemm_ar, moe, ring_attn  # noqa: F401
+from . import numerics, schedule, ag_gemm, gemm_rs, gemm_ar, moe, moe_combine, ring_attn  # noqa: F401

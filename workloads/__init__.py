@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = [
     "f32_to_bf16_bits", "AgWorkload", "RsWorkload", "MoeWorkload", "CONFIGS",
-    "make_ag", "make_rs", "make_moe", "make_ring", "fingerprint",
+    "make_ag", "make_rs", "make_moe", "moe_combine_inputs", "make_ring", "fingerprint",
 ]
 
 
@@ -249,6 +249,18 @@ def make_moe(T: int, H: int, E: int, k: int, L: int, F: int, *, seed: int = 0,
         raise ValueError(dist)
     return MoeWorkload(X, np.ascontiguousarray(logits, np.float32), W, k, expert_begin,
                        order, delay, block_tokens, out_dtype)
+
+
+def moe_combine_inputs(w: "MoeWorkload", *, seed: int = 0):
+    """Expert outputs for the combine step of MoE workload w: (Y_local
+    uint16[T*min(k, L), F], Y_peer uint16[T*k, F]), N(0, 1) in bf16.  Y_local
+    stands for the local grouped-GEMM output (capacity rows; the first
+    n_local are read); Y_peer for the outputs the other ranks return, one row
+    per dispatch position (rows of local positions are not read)."""
+    st = _streams(seed + 7919, 2)
+    Yl = _normal_bf16(st[0], (w.T * min(w.k, w.L), w.F), 1.0)
+    Yp = _normal_bf16(st[1], (w.T * w.k, w.F), 1.0)
+    return Yl, Yp
 
 
 def make_ring(H: int, S: int, D: int, R: int, *, seed: int = 0, step_delay_ns: int = 0,
