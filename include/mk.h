@@ -213,6 +213,31 @@ int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t T, int64_t 
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * MoE combine  (the step after [P1] "Los cinco núcleos fusionados", row
+ * Envío MoE + GEMM, which the pages do not describe)
+ *
+ * For every token t of this rank: out[t] = sum_j g[t, j] * Y_row(t, j), j in
+ * slot order, fp32 arithmetic, one final rounding to out_dtype, where
+ *   g[t, :] = softmax over logits[t, topk_idx[t, 0..k-1]] (fp32 [T x E]),
+ *   Y_row(t, j) = the expert output of pair (t, j) at its dispatch position
+ *   pos (perm[pos] = t*k + j): row pos - offsets[expert_begin] of y_local
+ *   when offsets[expert_begin] <= pos < offsets[expert_begin + L] (the
+ *   local grouped-GEMM output, bf16
+ *   [y_local_rows x F]), otherwise row pos of y_peer (the outputs the other
+ *   ranks return, bf16 [T*k x F]; rows of local positions are not read).
+ * topk_idx, offsets and perm are mk_moe_dispatch_gemm's outputs (device).
+ * out [T x F] of out_dtype.  A position outside a buffer reads zero.
+ * Workspace: mk_moe_combine_workspace(T, k) bytes (the inverse permutation;
+ * no zero fill needed).  Limits: F % 8 == 0, T*k*F*2 and y_local_rows*F*2
+ * below 2^32 bytes.
+ * ------------------------------------------------------------------------- */
+size_t mk_moe_combine_workspace(int64_t T, int k);
+int mk_moe_combine(const float* logits, int64_t T, int E, int k, const int32_t* topk_idx,
+                   const int32_t* offsets, const int32_t* perm, int expert_begin, int L,
+                   const void* y_local, int64_t y_local_rows, const void* y_peer, int64_t F,
+                   void* out, int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Ring attention  ([P1] "Los cinco núcleos fusionados", row Ring Attention)
  *
  * R ranks each hold S consecutive tokens of a sequence: rank r's keys and

@@ -203,3 +203,24 @@ def test_ring_validation(lib):
     arr, keep = mk.make_arrival([0], None, 1)
     assert _ring(lib, R=1, recv=False, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE
     assert lib.mk_ring_attn_workspace(16, 4096, 8) >= 256 + 4 * 112
+
+
+def _combine(lib, T=64, E=32, k=4, eb=0, L=8, rows=256, F=64, o=mk.MK_BF16, ws_bytes=1 << 20, yl=True):
+    return lib.mk_moe_combine(FAKE, T, E, k, FAKE, FAKE, FAKE, eb, L, FAKE if yl else None, rows, FAKE, F, FAKE, o,
+                              FAKE, ws_bytes, None)
+
+
+def test_moe_combine_validation(lib):
+    import torch
+    if not torch.cuda.is_available():
+        assert _combine(lib) == mk.MK_ERR_HIP                   # valid: the first HIP call fails
+    assert _combine(lib, yl=False) == mk.MK_ERR_INVALID
+    assert _combine(lib, T=0) == mk.MK_ERR_INVALID
+    assert _combine(lib, k=0) == mk.MK_ERR_INVALID
+    assert _combine(lib, k=17, E=64) == mk.MK_ERR_INVALID
+    assert _combine(lib, E=2000) == mk.MK_ERR_UNSUPPORTED
+    assert _combine(lib, eb=30, L=8) == mk.MK_ERR_INVALID
+    assert _combine(lib, F=60) == mk.MK_ERR_UNSUPPORTED
+    assert _combine(lib, o=9) == mk.MK_ERR_INVALID
+    assert _combine(lib, ws_bytes=16) == mk.MK_ERR_WORKSPACE
+    assert lib.mk_moe_combine_workspace(4096, 8) == 4096 * 8 * 4

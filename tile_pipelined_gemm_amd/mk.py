@@ -26,7 +26,8 @@ TILE_128x128_DMA, TILE_256x128_DMA, TILE_128x256_DMA = 6, 7, 8
 EXPORTS = [
     "mk_ag_gemm_workspace", "mk_ag_gemm", "mk_gemm_rs_workspace", "mk_gemm_rs",
     "mk_gemm_ar_workspace", "mk_gemm_ar",
-    "mk_moe_dispatch_gemm_workspace", "mk_moe_dispatch_gemm", "mk_ring_attn_workspace", "mk_ring_attn",
+    "mk_moe_dispatch_gemm_workspace", "mk_moe_dispatch_gemm", "mk_moe_combine_workspace", "mk_moe_combine",
+    "mk_ring_attn_workspace", "mk_ring_attn",
     "mk_workspace_init",
     "mk_poll_status", "mk_status_string", "mk_last_error", "mk_tile_name", "mk_version",
     "mk_wall_clock_khz",
@@ -86,6 +87,10 @@ def load(path: Optional[str] = None):
     lib.mk_moe_dispatch_gemm.argtypes = [vp, vp, i64, i64, i32, i32, pp, i32, i32, i64,
                                          vp, vp, vp, vp, vp, vp, vp, i32,
                                          C.POINTER(mk_arrival), C.POINTER(mk_launch), vp, sz, vp]
+    lib.mk_moe_combine_workspace.restype = sz
+    lib.mk_moe_combine_workspace.argtypes = [i64, i32]
+    lib.mk_moe_combine.restype = i32
+    lib.mk_moe_combine.argtypes = [vp, i64, i32, i32, vp, vp, vp, i32, i32, vp, i64, vp, i64, vp, i32, vp, sz, vp]
     lib.mk_ring_attn_workspace.restype = sz
     lib.mk_ring_attn_workspace.argtypes = [i32, i64, i32]
     lib.mk_ring_attn.restype = i32
@@ -189,6 +194,23 @@ def mk_gemm_rs_workspace(M, K, N, R, out_dtype=MK_F32) -> int:
 
 def mk_moe_dispatch_gemm_workspace(T, H, E, k, L, F) -> int:
     return load().mk_moe_dispatch_gemm_workspace(T, H, E, k, L, F)
+
+
+def mk_moe_combine_workspace(T, k) -> int:
+    return load().mk_moe_combine_workspace(T, k)
+
+
+def mk_moe_combine(logits, topk, offsets, perm, expert_begin, L, y_local, y_peer, out, ws, *, stream=None,
+                   check=True) -> int:
+    """logits [T, E] float32; topk [T, k], offsets [E+1], perm [T*k] int32 (the
+    dispatch outputs); y_local [rows, F], y_peer [T*k, F] bf16; out [T, F]."""
+    T, E = logits.shape
+    k = topk.shape[1]
+    F = out.shape[1]
+    rc = load().mk_moe_combine(_ptr(logits), T, E, k, _ptr(topk), _ptr(offsets), _ptr(perm), expert_begin, L,
+                               _ptr(y_local), y_local.shape[0], _ptr(y_peer), F, _ptr(out), _dtype_code(out),
+                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    return _check(rc) if check else rc
 
 
 def mk_ring_attn_workspace(H, S, R) -> int:
