@@ -254,6 +254,7 @@ def bench_ar(args, stream, extra=True):
 
 
 def bench_moe(args, stream, extra=True):
+    import numpy as np
     import workloads as wl
     from tile_pipelined_gemm_amd import mk
     from tile_pipelined_gemm_amd.harness import MoeProblem
@@ -281,6 +282,25 @@ def bench_moe(args, stream, extra=True):
         _, uk = timed(lambda i: probs[i % copies].run(launch=lau, stream=stream, check=False), 5, 2, stream)
         r["unfused_ms"] = uk
         r["speedup_vs_unfused"] = uk / kern
+        # the combine step after the grouped GEMM: this rank's tokens gather
+        # their k expert rows (local ones from Y, the rest from the peers'
+        # returned outputs) weighted by the top-k softmax
+        import torch
+        Yp = torch.from_numpy(wl.moe_combine_inputs(w, seed=args.seed)[1].view(np.int16)).cuda().view(torch.bfloat16)
+        cout = torch.empty(w.T, w.F, dtype=torch.bfloat16, device="cuda")
+        cws = mk.workspace(mk.mk_moe_combine_workspace(w.T, w.k))
+        p0 = probs[0]
+
+        def combine(i):
+            mk.mk_moe_combine(p0.logits, p0.topk, p0.offsets, p0.perm, w.expert_begin, w.L, p0.Y, Yp, cout, cws,
+                              stream=stream, check=False)
+
+        _, ck = timed(combine, 10, 3, stream)
+        cbytes = w.T * w.k * w.F * 2 + w.T * w.F * 2 + w.T * w.E * 4 + 3 * w.T * w.k * 4
+        r["combine_ms"] = ck
+        r["combine_gbs"] = cbytes / ck / 1e6
+        r["combine_hbm_frac"] = cbytes / ck / 1e6 / PEAK_HBM_GBS
+        del Yp
         for tag, kw in [("n_copy64", dict(n_copy=64)), ("tile_reg", dict(tile=mk.TILE_256x256)),
                         ("tile_128x256dma", dict(tile=mk.TILE_128x256_DMA)),
                         ("tile_256x128dma", dict(tile=mk.TILE_256x128_DMA)),
