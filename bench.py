@@ -168,7 +168,9 @@ def bench_ag(name, args, stream, extra=True):
             variants.append(("tile_reg", dict(tile=mk.TILE_256x256)))
         else:                                        # skinny: the 128-row tiles
             variants += [("tile_128x128", dict(tile=mk.TILE_128x128)),
-                         ("tile_128x256", dict(tile=mk.TILE_128x256))]
+                         ("tile_128x256_dma", dict(tile=mk.TILE_128x256_DMA)),
+                         ("tile_256x128_dma", dict(tile=mk.TILE_256x128_DMA)),
+                         ("gemm_only_128x256_dma", dict(mode=3, tile=mk.TILE_128x256_DMA))]
         for tag, kw in variants:
             lv = mk.make_launch(**kw)
             _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 10, 3, stream)

@@ -209,8 +209,8 @@ def test_partial_round_output_independent_of_grid_mode_and_engine(gpu):
         assert np.array_equal(outs[0], o), f"run {i} differs"
 
 
-# ---- skinny shapes (M = 128, one tile row; the default tile is 128x256
-# direct-to-LDS): every tile shape and engine gives the same bits ----
+# ---- skinny shapes (M = 128, one tile row; the default tile is the 128x128
+# direct-to-LDS tile with the 8-slice ring): every tile shape and engine gives the same bits ----
 def test_skinny_integer_inputs_bit_exact(gpu):
     w = wl.make_ag(8, 16, 2048, 8192, seed=47, dist="int", unit_rows=16, max_delay_ns=5000, out_dtype="f32")
     prob = _run(gpu, w)
@@ -224,7 +224,8 @@ def test_skinny_output_independent_of_grid_mode_and_engine(gpu):
     prob = AgProblem(w)
     outs = []
     for kw in [dict(), dict(grid=80), dict(grid=3), dict(mode=1), dict(n_copy=5), dict(queue_mode=1),
-               dict(tile=gpu.TILE_128x128_DMA), dict(tile=gpu.TILE_128x128), dict(tile=gpu.TILE_128x256)]:
+               dict(tile=gpu.TILE_128x128_DMA), dict(tile=gpu.TILE_128x128), dict(tile=gpu.TILE_128x256),
+               dict(tile=gpu.TILE_128x128_DMA8), dict(tile=gpu.TILE_256x128_DMA)]:
         prob.Ag.fill_(float("nan"))
         prob.C.zero_()
         prob.run(launch=gpu.make_launch(**kw))
@@ -273,6 +274,40 @@ def test_smaller_dma_tiles_match_register_tiles(gpu, dma, reg):
     C64, _ = og.ag_gemm(w.shards, w.B, "bf16")
     assert_close(out_to_f64(outs[1], "bf16"), C64, "bf16", f"dma tile {dma}")
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_deep_ring_dma_tile_matches_register_tile(gpu):
+    # the 8-slice ring (tile 9): ragged M and N, K = 768 = three turns of the ring
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = wl.make_ag(3, 100, 768, 392, seed=49, unit_rows=20, max_delay_ns=5000)
+    prob = AgProblem(w)
+    outs = []
+    for tile in (gpu.TILE_128x128, gpu.TILE_128x128_DMA8, gpu.TILE_128x128_DMA):
+        prob.Ag.fill_(float("nan"))
+        prob.C.zero_()
+        prob.run(launch=gpu.make_launch(tile=tile))
+        torch.cuda.synchronize()
+        assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+        outs.append(prob.output())
+    C64, _ = og.ag_gemm(w.shards, w.B, "bf16")
+    assert_close(out_to_f64(outs[1], "bf16"), C64, "bf16", "deep-ring dma tile")
+    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[2], outs[1])
+
+
+def test_deep_ring_dma_tile_integer_inputs_bit_exact(gpu):
+    w = wl.make_ag(2, 160, 512, 264, seed=50, dist="int", unit_rows=32, out_dtype="f32")
+    prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_128x128_DMA8))
+    _, C = og.ag_gemm(w.shards, w.B, "f32")
+    assert np.array_equal(prob.output(), C)
+
+
+def test_deep_ring_dma_tile_rejects_k_not_multiple_of_256(gpu):
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = wl.make_ag(2, 64, 384, 128, seed=51)
+    prob = AgProblem(w)
+    rc = prob.run(launch=gpu.make_launch(tile=gpu.TILE_128x128_DMA8), check=False)
+    assert rc == gpu.MK_ERR_UNSUPPORTED
 
 
 def test_dma_tile_integer_inputs_bit_exact(gpu):

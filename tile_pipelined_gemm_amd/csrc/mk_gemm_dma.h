@@ -80,16 +80,18 @@ __device__ __forceinline__ void wait_barrier() {
 }
 
 // Tiles of 128 or 256 rows by 128 or 256 columns, 4 waves (2x2), each wave a
-// (BM/2)x(BN/2) block of 32x32 MFMA tiles.  Per 32-deep K slice and per wave
+// (BM/2)x(BN/2) block of 32x32 MFMA tiles, with a ring of STAGES K slices
+// (4 by default; a deeper ring keeps more operand bytes in flight per CU,
+// which pays where the GEMM streams B and the tile is small).  Per 32-deep K slice and per wave
 // the DMA moves BM/64 KiB of A (16 rows per instruction) and BN/64 KiB of B
 // (1024 / (2*BN) k-rows per instruction).
 //
 // INTERLEAVE pins one LDS read after each MFMA inside a chunk.  It helps
 // when registers are to spare; a kernel that keeps more state live across
 // the K loop (GEMM+RS) turns it off to keep the loop free of spills.
-template <int BM_ = 256, int BN_ = 256, bool INTERLEAVE = true>
+template <int BM_ = 256, int BN_ = 256, bool INTERLEAVE = true, int STAGES_ = 4>
 struct TileGemmD {
-  static constexpr int BM = BM_, BN = BN_, WM = 2, WN = 2, BK = 32, STAGES = 4;
+  static constexpr int BM = BM_, BN = BN_, WM = 2, WN = 2, BK = 32, STAGES = STAGES_;
   static constexpr int NT = 256;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
@@ -101,6 +103,8 @@ struct TileGemmD {
   static constexpr int LDS_U4 = STAGES * (SA_U4 + SB_U4);
   static constexpr int READS = 2 * (FM + 2 * FN), MFMAS = 2 * FM * FN;  // per slice and wave
   static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile shape");
+  static_assert(STAGES == 4 || STAGES == 8, "ring depth");
+  static_assert((STAGES - 1) * D < 64, "vmcnt holds at most 63 outstanding operations");
 
   f32x16 acc[FM][FN];
   u32x4 dA, dB;
@@ -221,7 +225,8 @@ struct TileGemmD {
   }
 
   // One K slice: cur holds the fragments of slice kt, nxt receives those of
-  // slice kt+1 (na/nb); slice kt+4 is loaded into stage kt%4 (fa/fb).  The
+  // slice kt+1 (na/nb); slice kt+STAGES is loaded into stage kt%STAGES
+  // (fa/fb).  The
   // slice runs in CH chunks, chunk c = (substep c / FM, A fragment c % FM):
   // its FN MFMAs, RPC of the next slice's fragment reads and its share of
   // the DMA.  Each DMA is an inline-asm statement the compiler schedules
@@ -229,8 +234,8 @@ struct TileGemmD {
   // matrix pipeline instead of holding back the slice's first MFMA.
   __device__ __forceinline__ void step(int kt, const FragOfs& fo, const u32x4* na, const u32x4* nb,
                                        u32x4* fa, u32x4* fb, Frags& cur, Frags& nxt) {
-    wait_barrier<2 * D>();                  // slice kt+1 landed (kt+2, kt+3 may be in flight)
-    const bool more = kt + 4 < nk;
+    wait_barrier<(STAGES - 2) * D>();       // slice kt+1 landed (kt+2 .. kt+STAGES-1 may be in flight)
+    const bool more = kt + STAGES < nk;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int ks = c / FM, i = c % FM;
@@ -255,35 +260,49 @@ struct TileGemmD {
         if constexpr (RPC > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, RPC - PAIRS, 0);
       }
 #pragma unroll
-      for (int d = c * D / CH; d < (c + 1) * D / CH; ++d) issue_one(fa, fb, kt + 4, d, more);
+      for (int d = c * D / CH; d < (c + 1) * D / CH; ++d) issue_one(fa, fb, kt + STAGES, d, more);
     }
   }
 
-  // Full K loop; the four stages are distinct LDS objects.  If `mark` is
-  // given, thread 0 sets *mark once three quarters of the K slices are done
-  // (a workgroup that wants to start later than this one can wait for it).
+  // Full K loop.  With the default ring the four stages are distinct LDS
+  // objects; a deeper ring lives in one array, stage s at a fixed offset.  If
+  // `mark` is given, thread 0 sets *mark once three quarters of the K slices
+  // are done (a workgroup that wants to start later than this one can wait
+  // for it).
   __device__ __forceinline__ void run(Smem4 m, uint32_t* mark = nullptr) {
-    u32x4 *A0 = m.a[0], *A1 = m.a[1], *A2 = m.a[2], *A3 = m.a[3];
-    u32x4 *B0 = m.b[0], *B1 = m.b[1], *B2 = m.b[2], *B3 = m.b[3];
+    static_assert(STAGES == 4, "four stage objects");
+    run_ring(m.a, m.b, mark);
+  }
+  __device__ __forceinline__ void run(Smem1 m, uint32_t* mark = nullptr) {
+    u32x4* a[STAGES];
+    u32x4* b[STAGES];
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) {
+      a[s] = m.lds + s * (SA_U4 + SB_U4);
+      b[s] = a[s] + SA_U4;
+    }
+    run_ring(a, b, mark);
+  }
+
+  __device__ __forceinline__ void run_ring(u32x4* const* a, u32x4* const* b, uint32_t* mark) {
     const FragOfs fo = frag_offsets();
     zero_acc();
     if (nk == 0) return;
-    // nk is a multiple of 4 (supports_k), so all four stages start loaded
-    issue(A0, B0, 0);
-    issue(A1, B1, 1);
-    issue(A2, B2, 2);
-    issue(A3, B3, 3);
-    wait_barrier<3 * D>();
+    // nk is a multiple of STAGES (supports_k), so every stage starts loaded
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) issue(a[s], b[s], s);
+    wait_barrier<(STAGES - 1) * D>();
     Frags r0, r1;
 #pragma unroll
-    for (int r = 0; r < READS; ++r) read_one(A0, B0, fo, r, r0);
-    const int mark_kt = (nk * 3 / 4) & ~3;
-    for (int kt = 0; kt < nk; kt += 4) {
+    for (int r = 0; r < READS; ++r) read_one(a[0], b[0], fo, r, r0);
+    const int mark_kt = (nk * 3 / 4) & ~(STAGES - 1);
+    for (int kt = 0; kt < nk; kt += STAGES) {
       if (mark && kt == mark_kt && threadIdx.x == 0) st_relaxed(mark, 1u);
-      step(kt + 0, fo, A1, B1, A0, B0, r0, r1);
-      step(kt + 1, fo, A2, B2, A1, B1, r1, r0);
-      step(kt + 2, fo, A3, B3, A2, B2, r0, r1);
-      step(kt + 3, fo, A0, B0, A3, B3, r1, r0);
+#pragma unroll
+      for (int s = 0; s < STAGES; s += 2) {
+        step(kt + s, fo, a[(s + 1) % STAGES], b[(s + 1) % STAGES], a[s], b[s], r0, r1);
+        step(kt + s + 1, fo, a[(s + 2) % STAGES], b[(s + 2) % STAGES], a[s + 1], b[s + 1], r1, r0);
+      }
     }
     // the out-of-range DMAs issued past the last slice must not land in LDS
     // after the caller has started reusing it

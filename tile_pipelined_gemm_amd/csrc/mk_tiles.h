@@ -13,6 +13,8 @@ enum MkTile {
   TILE_128x128_DMA = 6,  // the same engine at 128x128 (64 KiB LDS, 2 workgroups per CU)
   TILE_256x128_DMA = 7,
   TILE_128x256_DMA = 8,
+  TILE_128x128_DMA8 = 9,  // 128x128 direct-to-LDS with an 8-slice ring (128 KiB LDS, 1 workgroup per CU,
+                          // K % 256 == 0): twice the operand bytes in flight, for GEMMs that stream B
   TILE_COUNT
 };
 

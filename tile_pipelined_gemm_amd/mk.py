@@ -21,6 +21,7 @@ MK_OK, MK_ERR_INVALID, MK_ERR_UNSUPPORTED, MK_ERR_WORKSPACE, MK_ERR_HIP, MK_ERR_
 MK_MAX_UNITS = 256
 TILE_256x256, TILE_128x128, TILE_256x128, TILE_128x256, TILE_256x256_DMA = 1, 2, 3, 4, 5
 TILE_128x128_DMA, TILE_256x128_DMA, TILE_128x256_DMA = 6, 7, 8
+TILE_128x128_DMA8 = 9
 
 # Symbols declared in include/mk.h (checked by the CPU tests).
 EXPORTS = [
