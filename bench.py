@@ -303,7 +303,10 @@ def bench_moe(args, stream, extra=True):
         r["combine_gbs"] = cbytes / ck / 1e6
         r["combine_hbm_frac"] = cbytes / ck / 1e6 / PEAK_HBM_GBS
         del Yp
-        for tag, kw in [("n_copy64", dict(n_copy=64)), ("tile_reg", dict(tile=mk.TILE_256x256)),
+        for tag, kw in [("n_copy64", dict(n_copy=64)), ("n_copy128", dict(n_copy=128)),
+                        ("xcd_queues", dict(queue_mode=1)), ("xcd_queues_n_copy128", dict(queue_mode=1, n_copy=128)),
+                        ("unfused_xcd_queues", dict(mode=1, queue_mode=1)),
+                        ("tile_reg", dict(tile=mk.TILE_256x256)),
                         ("tile_128x256dma", dict(tile=mk.TILE_128x256_DMA)),
                         ("tile_256x128dma", dict(tile=mk.TILE_256x128_DMA)),
                         ("tile_128x128dma", dict(tile=mk.TILE_128x128_DMA))]:

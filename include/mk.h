@@ -115,7 +115,11 @@ typedef struct mk_launch {
   int32_t queue_mode;     /* AG: 0 = default: one tile queue in landing order;
                              1 = 8 per-XCD queues (the tiles that share an A
                              row block run on one XCD and share its L2; a
-                             drained queue's workgroups help the others) */
+                             drained queue's workgroups help the others).
+                             MoE: 1 = 8 per-XCD queues keyed by tile column
+                             (when the tile columns split evenly over them:
+                             the tiles on one XCD share the same column blocks
+                             of the expert weights); 0 = one queue */
 } mk_launch;
 
 /* ---------------------------------------------------------------------------

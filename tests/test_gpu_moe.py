@@ -171,11 +171,30 @@ def test_split_tail_integer_inputs_bit_exact(gpu):
 def test_split_tail_bitwise_identical_across_launches(gpu):
     w = _split_tail_workload("normal", "bf16")
     outs = []
-    for kw in [dict(), dict(mode=1), dict(grid=80), dict(n_copy=5), dict(n_copy=64)]:
+    # queue_mode=1: per-XCD queues keyed by tile column (8 column tiles here)
+    for kw in [dict(), dict(mode=1), dict(grid=80), dict(n_copy=5), dict(n_copy=64),
+               dict(queue_mode=1), dict(queue_mode=1, n_copy=64), dict(queue_mode=1, grid=80),
+               dict(queue_mode=1, mode=1)]:
         prob = _run(gpu, w, launch=gpu.make_launch(**kw))
         outs.append(prob.outputs()["Y"])
     ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 0, "bf16")
     assert_close(out_to_f64(outs[0], "bf16"), ref["Y64"], "bf16", "MoE split tail")
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(outs[0], o), f"launch {i} differs"
+
+
+def test_xcd_queues_with_two_columns_per_queue(gpu):
+    # 128x128 tiles: 16 column tiles, two per XCD queue; another tile count, so
+    # another split tail than the 256x256 default: compared with its own
+    # single-queue launch and with the oracle
+    w = _split_tail_workload("normal", "bf16")
+    outs = []
+    for kw in [dict(tile=gpu.TILE_128x128_DMA), dict(tile=gpu.TILE_128x128_DMA, queue_mode=1),
+               dict(tile=gpu.TILE_128x128_DMA, queue_mode=1, n_copy=64)]:
+        prob = _run(gpu, w, launch=gpu.make_launch(**kw))
+        outs.append(prob.outputs()["Y"])
+    ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 0, "bf16")
+    assert_close(out_to_f64(outs[1], "bf16"), ref["Y64"], "bf16", "MoE 128x128 per-XCD queues")
     for i, o in enumerate(outs[1:], 1):
         assert np.array_equal(outs[0], o), f"launch {i} differs"
 

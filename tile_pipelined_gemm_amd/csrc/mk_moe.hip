@@ -225,6 +225,7 @@ struct MoeParams {
   int n_blocks, block_tokens, part_tokens, parts;
   int mode, n_copy, tiles_n, withhold;
   int full_grid;                // CUs x occupancy of this kernel (the split plan's grid)
+  int xcd_queues;               // whole tiles from per-XCD queues keyed by tile column
   int kp_len;                   // K-part counters in the workspace
   uint32_t* kp_cnt;             // [kp_len] parts of a split tail tile finished
   float* kp_slots;              // parked K parts
@@ -363,10 +364,35 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
   // after seeing that, its later tiles need neither a wait nor an acquire
   // (each acquire invalidates the XCD's L2 under the other tiles there).
   bool all_landed = p.mode != MODE_FUSED;
+  // Per-XCD queues (when the tile columns split evenly over the XCDs): queue
+  // x holds the whole tiles of columns x, x + XQ, ... in queue order, so the
+  // tiles on one XCD share the same column blocks of the expert weights in
+  // its L2 whichever workgroups take them; a drained queue's workgroups help
+  // the others, then all take the split tail items from the common counter.
+  const bool xq_on = p.xcd_queues && p.tiles_n % XQ == 0;
+  const int xc = p.tiles_n / XQ;                               // columns per queue and tile row
+  const uint32_t whole_rows = sp.n_whole / (uint32_t)p.tiles_n, whole_rem = sp.n_whole % (uint32_t)p.tiles_n;
+  auto qlen = [&](int x) -> uint32_t {
+    uint32_t n = whole_rows * (uint32_t)xc;
+    for (int i = 0; i < xc; ++i) n += (uint32_t)(x + XQ * i) < whole_rem ? 1u : 0u;
+    return n;
+  };
+  XcdQueues xq(&h->aux[XQ_AUX]);
+  auto next_item = [&]() -> uint32_t {
+    uint32_t it = 0;
+    if (tid == 0) {
+      int x;
+      uint32_t j;
+      if (!xq_on) it = add_relaxed(&h->tile_next, 1u);
+      else if (xq.take(qlen, x, j)) it = (j / xc) * (uint32_t)p.tiles_n + (uint32_t)(x + XQ * (int)(j % xc));
+      else it = sp.n_whole + add_relaxed(&h->tile_next, 1u);
+    }
+    return wg_bcast(it, sb);
+  };
   G g;
   int l = 0;
   for (;;) {
-    const uint32_t it = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+    const uint32_t it = next_item();
     if (it >= sp.n_items) break;
     // work item -> tile q and K part kp (kp < 0: the whole tile)
     uint32_t q = it;
@@ -447,6 +473,7 @@ __device__ __forceinline__ void moe_finish(const MoeParams& p, WsHeader* h, uint
     st_relaxed(&h->tile_next, 0u);
     st_relaxed(&h->copy_next, 0u);
     st_relaxed(&h->aux[0], 0u);
+    for (int i = 0; i < XQ; ++i) st_relaxed(&h->aux[XQ_AUX + i], 0u);
     st_relaxed(&h->abort, 0u);
     __hip_atomic_store(&h->t0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     st_relaxed(&h->done, 0u);
@@ -560,6 +587,7 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   const mk_launch o = mkh::launch_opts(launch);
   if (o.mode != 0 && o.mode != 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
   if (o.grid < 0 || o.n_copy < 0) return fail(MK_ERR_INVALID, "negative grid or n_copy");
+  if (o.queue_mode < 0 || o.queue_mode > 1) return fail(MK_ERR_INVALID, "queue_mode %d", o.queue_mode);
   const mkh::DevInfo* d = mkh::dev_info();
   if (!d) return MK_ERR_HIP;
   const hipStream_t st = (hipStream_t)stream;
@@ -598,6 +626,7 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   p.tile_log = o.tile_log;
   p.copy_log = o.copy_log;
   p.spin_limit = mkh::spin_ticks(o, d);
+  p.xcd_queues = o.queue_mode == 1;
   p.T = (int)T; p.H = (int)H; p.E = E; p.k = k; p.L = L; p.F = (int)F; p.eb = expert_begin;
   p.y_bf16 = y_dtype == MK_BF16;
   p.n_blocks = s.n_units;
