@@ -183,16 +183,25 @@ __device__ __forceinline__ void reduce_from_acc(const G& g, const RsParams& p, i
 // The same reduction for the direct-to-LDS engine, with the partial sums
 // brought in by LDS DMA instead of register loads: after the K loop the
 // engine's four stages (128 KiB) are free, so each wave owns 32 KiB = 32
-// slots of 1 KiB.  For one 32x32 block a wave issues one DMA per (row group,
-// partial) -- lane L's 16 bytes land at slot + 16 L, exactly the 4-column run
-// it holds after the quad transpose -- so up to 28 KiB per wave are in flight
-// without holding a register; then it waits once, reads its own slots back
-// and adds in the fixed order.  Columns past N get an out-of-range offset
-// (the DMA writes zero).  Used with the 256x256 tile (16 KiB per stage and
-// operand, so a[w] and b[w] hold 32 slots) when R - 1 <= 7.
+// slots of 1 KiB.  The wave walks its 32x32 blocks in pieces of one row
+// group (four rows): one DMA per partial -- lane L's 16 bytes land at slot +
+// 16 L, exactly the 4-column run it holds after the quad transpose -- into
+// one of four sets of 7 slots, so three pieces (21 KiB) are in flight while
+// a piece is added in the fixed order and stored.  Every piece issues all
+// seven partials' DMAs (a partial past R - 1 has an empty descriptor: it
+// reads nothing and writes zero, and is not added), so the wait counts are
+// constants: before piece n is read the wave waits until at most the DMAs
+// issued after piece n's are outstanding; loads complete in order, so piece
+// n has landed.  Columns past N get an out-of-range offset (the DMA writes
+// zero).  Used with the 256x256 tile (16 KiB per stage and operand, so a[w]
+// and b[w] hold 32 slots) when R - 1 <= 7.
 template <class G>
 __device__ __forceinline__ void reduce_from_acc_lds(const G& g, const RsParams& p, int m0, int n0, Smem4 sm) {
   static_assert(G::SA_U4 * 16 >= 16384 && G::SB_U4 * 16 >= 16384, "32 slots of 1 KiB per wave");
+  constexpr int NP = 7;                          // partials per piece (R - 1 <= 7)
+  constexpr int NSET = 4;                        // slot sets of NP slots
+  constexpr int LA = NSET - 1;                   // pieces in flight while one is added
+  constexpr int NPC = 4 * G::FM * G::FN;         // pieces per wave
   const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
   const int wm = w % G::WM, wn = w / G::WM;
   const int o = m0 / p.mb;
@@ -211,36 +220,53 @@ __device__ __forceinline__ void reduce_from_acc_lds(const G& g, const RsParams& 
   const uint32_t lb = uni(lds_addr(w == 0 ? sm.b[0] : w == 1 ? sm.b[1] : w == 2 ? sm.b[2] : sm.b[3]));
   const char* pa = (const char*)(w == 0 ? sm.a[0] : w == 1 ? sm.a[1] : w == 2 ? sm.a[2] : sm.a[3]);
   const char* pb = (const char*)(w == 0 ? sm.b[0] : w == 1 ? sm.b[1] : w == 2 ? sm.b[2] : sm.b[3]);
-  u32x4 dp[7];
+  u32x4 dp[NP];
 #pragma unroll
-  for (int q = 0; q < 7; ++q) dp[q] = buf_desc(p.P[q < nq ? q : 0] + (int64_t)m0 * p.N, q < nq ? in_bytes : 0u);
+  for (int q = 0; q < NP; ++q) dp[q] = buf_desc(p.P[q < nq ? q : 0] + (int64_t)m0 * p.N, q < nq ? in_bytes : 0u);
+  // piece pn: block pn / 4 = (i, j), row group pn % 4, slot set pn % NSET
+  auto issue_piece = [&](int pn) {
+    const int blk = pn >> 2, i = blk / G::FN, j = blk % G::FN, gq = pn & 3;
+    const int cb = n0 + wn * G::TN + j * 32;
+    const uint32_t vin = cb + lcol < p.N ? lin : OOB;
+    const int rb = wm * G::TM + i * 32;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int sl = (pn % NSET) * NP + q;
+      dma16(dp[q], uni(sl < 16 ? la + sl * 1024 : lb + (sl - 16) * 1024), vin,
+            uni((uint32_t)(rb + 8 * gq) * rb4 + (uint32_t)cb * 4u));
+    }
+  };
+#pragma unroll
+  for (int pn = 0; pn < LA; ++pn) issue_piece(pn);
 #pragma unroll
   for (int i = 0; i < G::FM; ++i) {
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) {
-      const int cb = n0 + wn * G::TN + j * 32;
-      const bool colok = cb + lcol < p.N;
-      const uint32_t vin = colok ? lin : OOB, vout = colok ? lout : OOB;
-      const int rb = wm * G::TM + i * 32;
-      // slot of (row group gq, partial q) = 7 gq + q
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq)
-#pragma unroll
-        for (int q = 0; q < 7; ++q)
-          if (q < nq) {
-            const int sl = 7 * gq + q;
-            dma16(dp[q], uni(sl < 16 ? la + sl * 1024 : lb + (sl - 16) * 1024), vin,
-                  uni((uint32_t)(rb + 8 * gq) * rb4 + (uint32_t)cb * 4u));
-          }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
+        const int pn = 4 * (i * G::FN + j) + gq;
+        // keep the pieces in order: otherwise the scheduler hoists later
+        // pieces' transposes and address arithmetic and runs out of registers
+        __builtin_amdgcn_sched_barrier(0);
+        if (pn + LA < NPC) {
+          issue_piece(pn + LA);
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NP * LA) : "memory");   // piece pn has landed
+        } else if (pn + 2 < NPC) {
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NP * 2) : "memory");
+        } else if (pn + 1 < NPC) {
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NP) : "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const int cb = n0 + wn * G::TN + j * 32;
+        const uint32_t vout = cb + lcol < p.N ? lout : OOB;
+        const int rb = wm * G::TM + i * 32;
         f32x4 v = quad_transpose(f32x4{g.acc[i][j][4 * gq], g.acc[i][j][4 * gq + 1], g.acc[i][j][4 * gq + 2],
                                        g.acc[i][j][4 * gq + 3]});
 #pragma unroll
-        for (int q = 0; q < 7; ++q)
+        for (int q = 0; q < NP; ++q)
           if (q < nq) {
-            const int sl = 7 * gq + q;
+            const int sl = (pn % NSET) * NP + q;
             v += *(const f32x4*)((sl < 16 ? pa + sl * 1024 : pb + (sl - 16) * 1024) + 16 * lane);
           }
         const uint32_t so = uni((uint32_t)(rb + 8 * gq) * rbo + (uint32_t)cb * esz);
