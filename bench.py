@@ -165,7 +165,9 @@ def bench_ag(name, args, stream, extra=True):
                     ("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
                     ("gemm_only_xcd_queues", dict(mode=3, queue_mode=1))]
         if w.M >= 256:
-            variants.append(("tile_reg", dict(tile=mk.TILE_256x256)))
+            variants += [("tile_reg", dict(tile=mk.TILE_256x256)),
+                         ("tile_dma_w8", dict(tile=mk.TILE_256x256_DMA_W8)),
+                         ("gemm_only_dma_w8", dict(mode=3, tile=mk.TILE_256x256_DMA_W8))]
         else:                                        # skinny: the 128-row tiles
             variants += [("tile_128x128", dict(tile=mk.TILE_128x128)),
                          ("tile_128x256_dma", dict(tile=mk.TILE_128x256_DMA)),

@@ -34,8 +34,8 @@ def test_support_functions(lib):
     assert lib.mk_version() >= 1
     assert lib.mk_status_string(mk.MK_ERR_TIMEOUT) == b"watchdog timeout"
     assert mk.mk_tile_name(0) == "auto" and mk.mk_tile_name(1) == "256x256"
-    assert [mk.mk_tile_name(i) for i in range(5, 10)] == ["256x256dma", "128x128dma", "256x128dma", "128x256dma",
-                                                         "128x128dma8"]
+    assert [mk.mk_tile_name(i) for i in range(5, 11)] == ["256x256dma", "128x128dma", "256x128dma", "128x256dma",
+                                                         "128x128dma8", "256x256dma_w8"]
     assert mk.mk_tile_name(99) is None
 
 

@@ -295,6 +295,44 @@ def test_deep_ring_dma_tile_matches_register_tile(gpu):
     assert np.array_equal(outs[2], outs[1])
 
 
+def test_eight_wave_dma_tile_matches_four_wave_and_register_tiles(gpu):
+    # tile 10: 256x256 with 8 waves (two per SIMD); ragged M and N, K = 1024
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = wl.make_ag(3, 100, 1024, 392, seed=52, unit_rows=20, max_delay_ns=5000)
+    prob = AgProblem(w)
+    outs = []
+    for kw in [dict(tile=gpu.TILE_256x256), dict(tile=gpu.TILE_256x256_DMA_W8),
+               dict(tile=gpu.TILE_256x256_DMA), dict(tile=gpu.TILE_256x256_DMA_W8, mode=1),
+               dict(tile=gpu.TILE_256x256_DMA_W8, grid=3)]:
+        prob.Ag.fill_(float("nan"))
+        prob.C.zero_()
+        prob.run(launch=gpu.make_launch(**kw))
+        torch.cuda.synchronize()
+        assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK, kw
+        outs.append(prob.output())
+    C64, _ = og.ag_gemm(w.shards, w.B, "bf16")
+    assert_close(out_to_f64(outs[1], "bf16"), C64, "bf16", "8-wave dma tile")
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(outs[0], o), f"launch {i} differs"
+
+
+def test_eight_wave_dma_tile_integer_inputs_bit_exact(gpu):
+    w = wl.make_ag(2, 160, 512, 264, seed=53, dist="int", unit_rows=32, out_dtype="f32")
+    prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA_W8))
+    _, C = og.ag_gemm(w.shards, w.B, "f32")
+    assert np.array_equal(prob.output(), C)
+
+
+def test_eight_wave_dma_tile_full_size_ag_config(gpu):
+    w = wl.CONFIGS["ag"]["make"]()
+    prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA_W8))
+    _sampled_rows(w, prob, 64, 3, "AG full, 8-wave dma tile")
+    ref = prob.output().copy()
+    prob.run(launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA))
+    torch.cuda.synchronize()
+    assert np.array_equal(prob.output(), ref)
+
+
 def test_deep_ring_dma_tile_integer_inputs_bit_exact(gpu):
     w = wl.make_ag(2, 160, 512, 264, seed=50, dist="int", unit_rows=32, out_dtype="f32")
     prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_128x128_DMA8))

@@ -383,6 +383,8 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
   if (tile == TILE_128x128_DMA8 && !TileGemmD<128, 128, true, 8>::supports_k((int)K))
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 256 == 0", tile);
+  if (tile == TILE_256x256_DMA_W8 && !TileGemmD<256, 256, true, 4, 8>::supports_k((int)K))
+    return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
   switch (tile) {
     case TILE_256x256: return run_ag<TileGemm<256, 256, 2, 2>>(p, o, s, d, st);
     case TILE_128x128: return run_ag<TileGemm<128, 128, 2, 2>>(p, o, s, d, st);
@@ -393,6 +395,7 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
     case TILE_256x128_DMA: return run_ag<TileGemmD<256, 128>>(p, o, s, d, st);
     case TILE_128x256_DMA: return run_ag<TileGemmD<128, 256>>(p, o, s, d, st);
     case TILE_128x128_DMA8: return run_ag<TileGemmD<128, 128, true, 8>>(p, o, s, d, st);
+    case TILE_256x256_DMA_W8: return run_ag<TileGemmD<256, 256, true, 4, 8>>(p, o, s, d, st);
     default: return fail(MK_ERR_INVALID, "tile id %d", tile);
   }
 }

@@ -79,24 +79,26 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Tiles of 128 or 256 rows by 128 or 256 columns, 4 waves (2x2), each wave a
-// (BM/2)x(BN/2) block of 32x32 MFMA tiles, with a ring of STAGES K slices
-// (4 by default; a deeper ring keeps more operand bytes in flight per CU,
-// which pays where the GEMM streams B and the tile is small).  Per 32-deep K slice and per wave
-// the DMA moves BM/64 KiB of A (16 rows per instruction) and BN/64 KiB of B
-// (1024 / (2*BN) k-rows per instruction).
+// Tiles of 128 or 256 rows by 128 or 256 columns, 4 waves (2x2, each wave a
+// (BM/2)x(BN/2) block of 32x32 MFMA tiles) or 8 waves (2x4, two per SIMD,
+// each wave (BM/2)x(BN/4)), with a ring of STAGES K slices (4 by default; a
+// deeper ring keeps more operand bytes in flight per CU, which pays where
+// the GEMM streams B and the tile is small).  Per 32-deep K slice the
+// workgroup's DMA moves BM/16 KiB of A (16 rows per instruction) and BN/16
+// KiB of B (1024 / (2*BN) k-rows per instruction); block blk is moved by
+// wave blk % WAVES.
 //
 // INTERLEAVE pins one LDS read after each MFMA inside a chunk.  It helps
 // when registers are to spare; a kernel that keeps more state live across
 // the K loop (GEMM+RS) turns it off to keep the loop free of spills.
-template <int BM_ = 256, int BN_ = 256, bool INTERLEAVE = true, int STAGES_ = 4>
+template <int BM_ = 256, int BN_ = 256, bool INTERLEAVE = true, int STAGES_ = 4, int WAVES_ = 4>
 struct TileGemmD {
-  static constexpr int BM = BM_, BN = BN_, WM = 2, WN = 2, BK = 32, STAGES = STAGES_;
-  static constexpr int NT = 256;
+  static constexpr int BM = BM_, BN = BN_, WAVES = WAVES_, WM = 2, WN = WAVES_ / 2, BK = 32, STAGES = STAGES_;
+  static constexpr int NT = 64 * WAVES;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;   // per stage
-  static constexpr int A_INS = A_BYTES / 1024 / 4, B_INS = B_BYTES / 1024 / 4;  // DMA per wave per slice
+  static constexpr int A_INS = A_BYTES / 1024 / WAVES, B_INS = B_BYTES / 1024 / WAVES;  // DMA per wave per slice
   static constexpr int D = A_INS + B_INS;                              // vm operations per slice
   static constexpr int B_ROWS = 1024 / (2 * BN);                       // k-rows per B instruction
   static constexpr int SA_U4 = A_BYTES / 16, SB_U4 = B_BYTES / 16;
@@ -104,6 +106,8 @@ struct TileGemmD {
   static constexpr int READS = 2 * (FM + 2 * FN), MFMAS = 2 * FM * FN;  // per slice and wave
   static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile shape");
   static_assert(STAGES == 4 || STAGES == 8, "ring depth");
+  static_assert(WAVES == 4 || WAVES == 8, "waves per workgroup");
+  static_assert(A_INS >= 1 && B_INS >= 1 && (WAVES * B_ROWS) % 4 == 0, "DMA blocks per wave; B swizzle phase");
   static_assert((STAGES - 1) * D < 64, "vmcnt holds at most 63 outstanding operations");
 
   f32x16 acc[FM][FN];
@@ -126,7 +130,7 @@ struct TileGemmD {
     // physical chunk p%4, which is logical k-chunk (p%4) ^ ((row>>2)&3).
     voA = (uint32_t)(lane >> 2) * ldaB + (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
     // B: an instruction covers B_ROWS k-rows of BN/8 chunks; physical chunk
-    // = logical ^ ((k-row & 3) << 2).  Block blk = i*4 + w starts at k-row
+    // = logical ^ ((k-row & 3) << 2).  Block blk = i*WAVES + w starts at k-row
     // blk*B_ROWS, so k-row & 3 = (w*B_ROWS + lane / (BN/8)) & 3.
     const int w = threadIdx.x >> 6;
     const int rin = lane / (BN / 8);
@@ -142,12 +146,12 @@ struct TileGemmD {
     const uint32_t la = uni(lds_addr(sa)), lb = uni(lds_addr(sb));
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-      const int blk = i * 4 + w;
+      const int blk = i * WAVES + w;
       dma16(dA, uni(la + blk * 1024), voA, uni((uint32_t)(blk * 16) * ldaB + (uint32_t)(kt * BK * 2)));
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
-      const int blk = i * 4 + w;
+      const int blk = i * WAVES + w;
       dma16(dB, uni(lb + blk * 1024), voB, uni((uint32_t)(kt * BK + blk * B_ROWS) * ldbB));
     }
   }
@@ -215,11 +219,11 @@ struct TileGemmD {
   __device__ __forceinline__ void issue_one(u32x4* sa, u32x4* sb, int kt, int d, bool more) {
     const int w = uni((int)(threadIdx.x >> 6));   // wave index: the same in every lane
     if (d < A_INS) {
-      const int blk = d * 4 + w;
+      const int blk = d * WAVES + w;
       dma16(dA, uni(lds_addr(sa) + blk * 1024), more ? voA : OOB,
             uni((uint32_t)(blk * 16) * ldaB + (uint32_t)(kt * BK * 2)));
     } else {
-      const int blk = (d - A_INS) * 4 + w;
+      const int blk = (d - A_INS) * WAVES + w;
       dma16(dB, uni(lds_addr(sb) + blk * 1024), more ? voB : OOB, uni((uint32_t)(kt * BK + blk * B_ROWS) * ldbB));
     }
   }

@@ -15,6 +15,7 @@ enum MkTile {
   TILE_128x256_DMA = 8,
   TILE_128x128_DMA8 = 9,  // 128x128 direct-to-LDS with an 8-slice ring (128 KiB LDS, 1 workgroup per CU,
                           // K % 256 == 0): twice the operand bytes in flight, for GEMMs that stream B
+  TILE_256x256_DMA_W8 = 10,  // 256x256 direct-to-LDS with 8 waves (2x4, two per SIMD; K % 128 == 0)
   TILE_COUNT
 };
 
