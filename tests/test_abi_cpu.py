@@ -149,10 +149,10 @@ def test_rs_workspace_sizes(lib):
     assert bf - f32 == 8192 * 8192 * 4
 
 
-def _moe(lib, T=256, H=128, E=64, k=4, eb=0, L=8, F=128, y=mk.MK_BF16, arrival=None, ws_bytes=1 << 24):
+def _moe(lib, T=256, H=128, E=64, k=4, eb=0, L=8, F=128, y=mk.MK_BF16, arrival=None, lau=None, ws_bytes=1 << 24):
     W = (C.c_void_p * L)(*([FAKE] * L))
     return lib.mk_moe_dispatch_gemm(FAKE, FAKE, T, H, E, k, W, eb, L, F, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                    FAKE, FAKE, y, arrival, None, FAKE, ws_bytes, None)
+                                    FAKE, FAKE, y, arrival, lau, FAKE, ws_bytes, None)
 
 
 def test_moe_validation(lib):
@@ -166,6 +166,10 @@ def test_moe_validation(lib):
     assert _moe(lib, ws_bytes=100) == mk.MK_ERR_WORKSPACE
     arr, keep = mk.make_arrival([0, 1, 1, 3], None, 64)
     assert _moe(lib, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE
+    # launch options are checked before any HIP call
+    for bad in (dict(mode=2), dict(grid=-1), dict(n_copy=-1), dict(queue_mode=2), dict(queue_mode=-1)):
+        lau = mk.make_launch(**bad)
+        assert _moe(lib, lau=C.byref(lau)) == mk.MK_ERR_INVALID, bad
 
 
 def _ring(lib, R=4, H=2, S=300, D=128, o=mk.MK_BF16, recv=True, arrival=None, lau=None, ws_bytes=1 << 20):

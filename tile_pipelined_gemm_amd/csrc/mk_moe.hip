@@ -580,16 +580,14 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   if (!workspace) return fail(MK_ERR_WORKSPACE, "workspace is NULL");
   const size_t need0 = moe_ws_layout(T, E, k, L, 0).total;   // before the split-tail slots
   if (workspace_bytes < need0) return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need0);
-  const mkh::DevInfo* dv = mkh::dev_info();
-  if (!dv) return MK_ERR_HIP;
-  const MoeWs lay = moe_ws_layout(T, E, k, L, dv->n_cu);
-  if (workspace_bytes < lay.total) return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, lay.total);
   const mk_launch o = mkh::launch_opts(launch);
   if (o.mode != 0 && o.mode != 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
   if (o.grid < 0 || o.n_copy < 0) return fail(MK_ERR_INVALID, "negative grid or n_copy");
   if (o.queue_mode < 0 || o.queue_mode > 1) return fail(MK_ERR_INVALID, "queue_mode %d", o.queue_mode);
   const mkh::DevInfo* d = mkh::dev_info();
   if (!d) return MK_ERR_HIP;
+  const MoeWs lay = moe_ws_layout(T, E, k, L, d->n_cu);
+  if (workspace_bytes < lay.total) return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, lay.total);
   const hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   int32_t* block_cnt = (int32_t*)(ws + lay.block_cnt);
@@ -621,7 +619,7 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   p.tile_cnt = (uint32_t*)(ws + lay.tile_cnt);
   p.kp_cnt = (uint32_t*)(ws + lay.kp_cnt);
   p.kp_slots = (float*)(ws + lay.kp_slots);
-  p.kp_len = dv->n_cu;
+  p.kp_len = d->n_cu;
   p.hdr = (WsHeader*)workspace;
   p.tile_log = o.tile_log;
   p.copy_log = o.copy_log;
