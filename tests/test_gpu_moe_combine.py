@@ -71,3 +71,16 @@ def test_dispatch_gemm_combine_chain(gpu):
     ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 8, "bf16")
     out, _ = oc.moe_combine(ref["Y"], Yp, w.logits, ref["topk"], ref["perm"], ref["offsets"], 8, w.L)
     assert_close(out_to_f64(got, "bf16"), out, "bf16", "dispatch + GEMM + combine")
+
+
+def test_full_size_combine_config(gpu):
+    # the benchmark's combine: T = 4096, H = 7168, top-8 of 256 experts, 32 local
+    # experts, F = 2048; every token compared with the oracle's own routing
+    w = wl.CONFIGS["moe"]["make"]()
+    prob = _dispatch(gpu, w)
+    Yl, Yp = wl.moe_combine_inputs(w, seed=0)
+    got = _combine(gpu, prob, Yl, Yp, "bf16")
+    topk = om.route_topk(w.logits, w.k)
+    _, offsets, perm = om.dispatch(topk, w.E)
+    ref, _ = oc.moe_combine(Yl, Yp, w.logits, topk, perm, offsets, w.expert_begin, w.L)
+    assert_close(out_to_f64(got, "bf16"), ref, "bf16", "combine T=4096 k=8 F=2048")
