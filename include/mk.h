@@ -100,7 +100,19 @@ typedef struct mk_launch {
                              (every workgroup copies first, then computes) */
   int32_t n_reduce;       /* GEMM+RS: reduce-role workgroups; 0 = default;
                              -1 = each compute workgroup reduces its own tiles */
-  int32_t tile;           /* tile configuration id; 0 = default (see mk_tile_name) */
+  int32_t tile;           /* tile configuration id (name: mk_tile_name); 0 = per-shape default.
+                             1 256x256, 2 128x128, 3 256x128, 4 128x256: register-staged
+                             (any K multiple of 8; 1 not for GEMM+RS/AR);
+                             5 256x256, 6 128x128, 7 256x128, 8 128x256: direct-to-LDS,
+                             4-slice ring (K % 128 == 0);
+                             9 128x128 direct-to-LDS with an 8-slice ring (AG only,
+                             K % 256 == 0; the AG default when M <= 128);
+                             10 256x256 direct-to-LDS with 8 waves (AG only, K % 128 == 0).
+                             Defaults: AG 5 (9 for a single 128-row tile row), GEMM+RS/AR
+                             5 when K % 128 == 0 and the owner blocks hold whole 256-row
+                             tiles, MoE 5 when H % 128 == 0; else a register-staged tile.
+                             An id an operation does not build returns MK_ERR_UNSUPPORTED
+                             (MK_ERR_INVALID if out of range). */
   uint32_t spin_limit_us; /* watchdog for every wait; 0 = 2,000,000 us */
   int32_t* tile_log;      /* device int32 or NULL: per-tile record, see each op */
   int32_t copy_kib;       /* AG: bytes per copy work item in KiB (one release each);
