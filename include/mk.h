@@ -108,9 +108,12 @@ typedef struct mk_launch {
                              9 128x128 direct-to-LDS with an 8-slice ring (AG only,
                              K % 256 == 0; the AG default when M <= 128);
                              10 256x256 direct-to-LDS with 8 waves (AG only, K % 128 == 0).
-                             Defaults: AG 5 (9 for a single 128-row tile row), GEMM+RS/AR
-                             5 when K % 128 == 0 and the owner blocks hold whole 256-row
-                             tiles, MoE 5 when H % 128 == 0; else a register-staged tile.
+                             Defaults: AG 5 when 256x256 tiles give every CU one
+                             (K % 128 == 0), 9 for a single 128-row tile row with N >= 256
+                             (8 if K % 256 != 0), else a register-staged tile; GEMM+RS/AR 5
+                             when K % 128 == 0 and the owner blocks hold whole 256-row tiles,
+                             else 2; MoE 5 when F >= 256 and H % 128 == 0, 2 when F < 256,
+                             else 1.
                              An id an operation does not build returns MK_ERR_UNSUPPORTED
                              (MK_ERR_INVALID if out of range). */
   uint32_t spin_limit_us; /* watchdog for every wait; 0 = 2,000,000 us */
