@@ -218,6 +218,19 @@ def test_skinny_integer_inputs_bit_exact(gpu):
     assert np.array_equal(prob.output(), C)
 
 
+@pytest.mark.parametrize("K", [256, 512])
+def test_skinny_default_tile_short_k_ragged(gpu, K):
+    # M = 40 (8 shards of 5 rows), N = 392 (ragged): the default skinny tile (the
+    # 8-slice ring; K = 256 is exactly one turn of it), integer inputs, exact
+    w = wl.make_ag(8, 5, K, 392, seed=58, dist="int", unit_rows=5, max_delay_ns=3000, out_dtype="f32")
+    prob = _run(gpu, w)
+    _, C = og.ag_gemm(w.shards, w.B, "f32")
+    assert np.array_equal(prob.output(), C)
+    prob.run(launch=gpu.make_launch(tile=gpu.TILE_128x128))
+    torch.cuda.synchronize()
+    assert np.array_equal(prob.output(), C)
+
+
 def test_skinny_output_independent_of_grid_mode_and_engine(gpu):
     from tile_pipelined_gemm_amd.harness import AgProblem
     w = wl.make_ag(8, 16, 2048, 28672, seed=48, unit_rows=16, max_delay_ns=5000)
