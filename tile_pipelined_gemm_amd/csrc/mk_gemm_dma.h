@@ -230,8 +230,8 @@ struct TileGemmD {
 
   // One K slice: cur holds the fragments of slice kt, nxt receives those of
   // slice kt+1 (na/nb); slice kt+STAGES is loaded into stage kt%STAGES
-  // (fa/fb).  The
-  // slice runs in CH chunks, chunk c = (substep c / FM, A fragment c % FM):
+  // (fa/fb).  The slice runs in CH chunks, chunk c = (substep c / FM, A
+  // fragment c % FM):
   // its FN MFMAs, RPC of the next slice's fragment reads and its share of
   // the DMA.  Each DMA is an inline-asm statement the compiler schedules
   // around, so it ends a chunk; spread this way the DMA issue overlaps the
