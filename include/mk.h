@@ -74,7 +74,8 @@ typedef enum mk_status {
  *   order     [n_units] permutation of 0..n_units-1 (issue order)
  *   delay_ns  [n_units] or NULL (= all zero); each <= 1e9
  *   n_units   number of delivery units (<= MK_MAX_UNITS)
- *   unit_rows AG: gathered rows per unit; MoE: tokens per source block
+ *   unit_rows AG: gathered rows per unit; MoE: tokens per source block;
+ *             GEMM+RS/AR: partial-sum rows per unit (one row block of one peer)
  *   withhold  -1, or one unit id that is never delivered: waits on it expire
  *             after spin_limit_us and the call reports MK_ERR_TIMEOUT.  Used
  *             to test failure handling; every kernel still exits.
@@ -96,7 +97,8 @@ typedef struct mk_launch {
                              kernel alone, 3 = its GEMM kernel alone (reads
                              a_gathered as it is) */
   int32_t grid;           /* persistent workgroups; 0 = CUs x occupancy */
-  int32_t n_copy;         /* copy-role workgroups (AG, MoE); 0 = default
+  int32_t n_copy;         /* copy-role workgroups (AG, MoE, GEMM+RS/AR with an
+                             arrival schedule); 0 = default
                              (every workgroup copies first, then computes) */
   int32_t n_reduce;       /* GEMM+RS: reduce-role workgroups; 0 = default;
                              -1 = each compute workgroup reduces its own tiles */
@@ -118,12 +120,12 @@ typedef struct mk_launch {
                              (MK_ERR_INVALID if out of range). */
   uint32_t spin_limit_us; /* watchdog for every wait; 0 = 2,000,000 us */
   int32_t* tile_log;      /* device int32 or NULL: per-tile record, see each op */
-  int32_t copy_kib;       /* AG: bytes per copy work item in KiB (one release each);
+  int32_t copy_kib;       /* AG, GEMM+RS/AR: bytes per copy work item in KiB (one release each);
                              0 = 1024; rounded to whole rows inside one unit and shard */
   int32_t copy_policy;    /* AG copy stores: 0 = default (2), 1 = write-back
                              through the XCD L2, 2 = write-through (sc1): the
                              release after each item then has little to write back */
-  int32_t* copy_log;      /* AG, MoE: device int32 or NULL: per copy work item
+  int32_t* copy_log;      /* AG, MoE, GEMM+RS/AR: device int32 or NULL: per copy work item
                              (in queue order), 8 int32, see each op; times are
                              the low 32 bits of the device wall clock
                              (mk_wall_clock_khz) */
@@ -166,18 +168,48 @@ int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
  * GEMM + ReduceScatter)
  *
  * This GPU's contribution is A @ B (A [M x K], B [K x N] bf16, fp32
- * accumulate).  The other R-1 contributions are resident fp32 partial sums
- * partials[p] [M x N].  The reduced S = A@B + P_1 + ... + P_{R-1} (summed in
- * fp32 in exactly that order) is scattered by row block: out_owner[r]
- * [(M/R) x N] of `out_dtype` receives rows [r*M/R, (r+1)*M/R).  Each output
- * tile is reduced and written to its owner as soon as its GEMM tile is done.
+ * accumulate).  The other R-1 contributions are fp32 partial sums
+ * partials[p] [M x N] (resident device buffers standing for the peers).  The
+ * reduced S = A@B + P_1 + ... + P_{R-1} (summed in fp32 in exactly that
+ * order) is scattered by row block: out_owner[r] [(M/R) x N] of `out_dtype`
+ * receives rows [r*M/R, (r+1)*M/R).  Each output tile is reduced and written
+ * to its owner as soon as its GEMM tile is done and the partial sums of its
+ * rows have arrived.
+ *   arrival  NULL: every partial sum is there from the start (read in place).
+ *            Otherwise the partial sums arrive in units u = (p-1)*(M/unit_rows)
+ *            + b, rows [b*unit_rows, (b+1)*unit_rows) of partials[p-1] (peer
+ *            p = 1..R-1), n_units = (R-1)*M/unit_rows (unit_rows must divide
+ *            M), released by copy workgroups in arrival->order no earlier than
+ *            delay_ns[u] after the first copy workgroup starts; a tile's
+ *            reduction waits for the units under its rows.  Needs R >= 2.
+ *   p_landing  NULL, or (arrival given) a host array of R-1 device pointers,
+ *            each [M x N] fp32, caller-owned and overwritten: the copy
+ *            workgroups move each unit's rows from partials[p-1] into
+ *            p_landing[p-1] (items of launch->copy_kib KiB, default 1 MiB) and
+ *            the reduction reads the landing buffers.  NULL with an arrival:
+ *            a unit is only released at its time and read in place.
+ *   launch->n_copy: copy workgroups (default: every workgroup copies first,
+ *            then computes); copy_log as for mk_ag_gemm, {unit, part,
+ *            workgroup, t_start, t_end, 0, 0, 0}, t_end taken once the item's
+ *            stores are complete and before its release.
+ *   The schedule decides when tiles are reduced, never the result: the sum
+ *   order is fixed, so every schedule, role split and landing choice gives
+ *   the same bits.
  *   M must be divisible by R; M/R must be a multiple of the tile height.
  *   tile_log (optional): per output tile id (tile_row*tiles_n + tile_col),
- *   2 int32 {owner, production rank}.
+ *   8 int32 {owner, production rank, reducing workgroup, first row block of
+ *   its rows (-1 without arrival), t_take (the reduction starts waiting for
+ *   its partial sums), t_ready (they have landed), t_done (stores issued),
+ *   0} (low 32 bits of the device wall clock).
+ *   Errors: MK_ERR_SCHEDULE for a bad schedule (not a permutation, unit_rows
+ *   not dividing M, delays over 1 s, R < 2); MK_ERR_INVALID for landing
+ *   buffers without a schedule; MK_ERR_UNSUPPORTED for more than
+ *   MK_MAX_UNITS units or (with a schedule) more than MK_MAX_UNITS tile rows.
  * ------------------------------------------------------------------------- */
 size_t mk_gemm_rs_workspace(int64_t M, int64_t K, int64_t N, int R, int out_dtype);
 int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
                const float* const* partials, int R, void* const* out_owner, int out_dtype,
+               const mk_arrival* arrival, float* const* p_landing,
                const mk_launch* launch, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
@@ -189,13 +221,15 @@ int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
  * out_rank[r] [M x N] of `out_dtype` receives all of S for r = 0..R-1 (the
  * reduce-scatter followed by the all-gather of the owner blocks; on one GPU
  * the R outputs stand for the R ranks' buffers).  Each output tile is reduced
- * and written to every rank as soon as its GEMM tile is done.  M need not be
- * divisible by R.  Workspace, launch options and errors as for mk_gemm_rs;
+ * and written to every rank as soon as its GEMM tile is done and its partial
+ * sums have arrived.  M need not be divisible by R.  Arrival schedule,
+ * landing buffers, workspace, launch options and errors as for mk_gemm_rs;
  * tile_log records owner 0 for every tile.
  * ------------------------------------------------------------------------- */
 size_t mk_gemm_ar_workspace(int64_t M, int64_t K, int64_t N, int R, int out_dtype);
 int mk_gemm_ar(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
                const float* const* partials, int R, void* const* out_rank, int out_dtype,
+               const mk_arrival* arrival, float* const* p_landing,
                const mk_launch* launch, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------

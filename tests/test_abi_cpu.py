@@ -95,10 +95,12 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
     assert _ag(lib) == mk.MK_ERR_HIP
 
 
-def _rs(lib, M=512, K=64, N=64, R=4, out_dtype=mk.MK_F32, ws_bytes=1 << 24, partials=True, lau=None):
+def _rs(lib, M=512, K=64, N=64, R=4, out_dtype=mk.MK_F32, ws_bytes=1 << 24, partials=True, lau=None,
+        arrival=None, landing=None):
     P = (C.c_void_p * R)(*([FAKE] * R))
     O = (C.c_void_p * R)(*([FAKE] * R))
-    return lib.mk_gemm_rs(FAKE, FAKE, M, K, N, P if partials else None, R, O, out_dtype, lau, FAKE, ws_bytes, None)
+    return lib.mk_gemm_rs(FAKE, FAKE, M, K, N, P if partials else None, R, O, out_dtype, arrival, landing, lau,
+                          FAKE, ws_bytes, None)
 
 
 def test_rs_validation(lib):
@@ -122,8 +124,8 @@ def test_rs_validation(lib):
 def _ar(lib, M=510, K=64, N=64, R=4, out_dtype=mk.MK_F32, ws_bytes=1 << 24, partials=True, lau=None, outs=True):
     P = (C.c_void_p * R)(*([FAKE] * R))
     O = (C.c_void_p * R)(*([FAKE] * R))
-    return lib.mk_gemm_ar(FAKE, FAKE, M, K, N, P if partials else None, R, O if outs else None, out_dtype, lau,
-                          FAKE, ws_bytes, None)
+    return lib.mk_gemm_ar(FAKE, FAKE, M, K, N, P if partials else None, R, O if outs else None, out_dtype, None,
+                          None, lau, FAKE, ws_bytes, None)
 
 
 def test_ar_validation(lib):
@@ -141,6 +143,46 @@ def test_ar_validation(lib):
     assert _ar(lib, ws_bytes=64) == mk.MK_ERR_WORKSPACE
     assert lib.mk_gemm_ar_workspace(8192, 3584, 8192, 8, mk.MK_F32) == lib.mk_gemm_rs_workspace(
         8192, 3584, 8192, 8, mk.MK_F32)
+
+
+def _rs_arrival(n_units, unit_rows, order=None, delays=None, withhold=-1):
+    order = list(range(n_units)) if order is None else order
+    arr, keep = mk.make_arrival(order, delays, unit_rows, withhold)
+    return C.byref(arr), keep
+
+
+@pytest.mark.parametrize("order,delays,n_units,unit_rows,R,withhold", [
+    ([0, 1, 2, 3, 4, 5], None, 6, 256, 4, -1),          # 3 peers x 2 blocks = 6 units: fine on the host
+    ([0, 1, 2, 3, 4, 4], None, 6, 256, 4, -1),          # not a permutation
+    ([0, 1, 2, 3, 4, 5], None, 6, 200, 4, -1),          # 6 x 200 rows != 3 x 512
+    ([0, 1], None, 2, 512, 4, -1),                      # 2 units of 512 rows: 3 peers need 3
+    ([0, 1, 2, 3, 4, 5], [0, 0, 0, 2_000_000_000, 0, 0], 6, 256, 4, -1),   # delay over 1 s
+    ([0, 1, 2, 3, 4, 5], None, 6, 256, 4, 6),           # withheld unit out of range
+    ([0, 1, 2, 3], None, 4, 384, 4, -1),                # 4 x 384 = 3 x 512 rows but 384 does not divide M
+    ([0], None, 1, 512, 1, -1),                         # R = 1: no partial sums to schedule
+])
+def test_rs_schedule_rejected(lib, order, delays, n_units, unit_rows, R, withhold):
+    M = 512
+    arr, keep = _rs_arrival(n_units, unit_rows, order, delays, withhold)
+    if order == [0, 1, 2, 3, 4, 5] and delays is None and withhold == -1 and unit_rows == 256:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+        assert _rs(lib, M=M, R=R, arrival=arr) == mk.MK_ERR_HIP   # valid: only the first HIP call fails
+        return
+    assert _rs(lib, M=M, R=R, arrival=arr) == mk.MK_ERR_SCHEDULE
+
+
+def test_rs_landing_rules(lib):
+    L = (C.c_void_p * 3)(*([FAKE] * 3))
+    assert _rs(lib, landing=L) == mk.MK_ERR_INVALID                 # landing buffers need a schedule
+    arr, keep = _rs_arrival(6, 256)
+    bad = (C.c_void_p * 3)(FAKE, None, FAKE)
+    assert _rs(lib, arrival=arr, landing=bad) == mk.MK_ERR_INVALID  # a NULL landing buffer
+    mis = (C.c_void_p * 3)(FAKE, FAKE + 4, FAKE)
+    assert _rs(lib, arrival=arr, landing=mis) == mk.MK_ERR_INVALID  # misaligned
+    lau = mk.make_launch(n_copy=-1)
+    assert _rs(lib, arrival=arr, lau=C.byref(lau)) == mk.MK_ERR_INVALID
 
 
 def test_rs_workspace_sizes(lib):
@@ -229,3 +271,25 @@ def test_moe_combine_validation(lib):
     assert _combine(lib, o=9) == mk.MK_ERR_INVALID
     assert _combine(lib, ws_bytes=16) == mk.MK_ERR_WORKSPACE
     assert lib.mk_moe_combine_workspace(4096, 8) == 4096 * 8 * 4
+
+
+def _run_py(code):
+    import subprocess
+    import sys
+    return subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+
+
+def test_load_binds_to_torch_hip_runtime():
+    # mk.load() imports torch first, so one HIP runtime is mapped
+    r = _run_py("from tile_pipelined_gemm_amd import mk; mk.load(); print(mk._hip_runtimes_mapped())")
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.count("libamdhip64") == 1, r.stdout
+
+
+def test_load_after_foreign_runtime_raises():
+    # the library loaded before torch by other code: two runtimes are mapped,
+    # and mk.load() refuses instead of letting the first call fail
+    r = _run_py("import ctypes; ctypes.CDLL('tile_pipelined_gemm_amd/libmk.so'); "
+                "from tile_pipelined_gemm_amd import mk; mk.load()")
+    assert r.returncode != 0
+    assert "two HIP runtimes" in r.stderr

@@ -125,16 +125,19 @@ def test_tile_log_records_chunk_dependencies(gpu):
     assert sorted(map(tuple, items[:, :2].tolist())) == [(u, p) for u in range(w.M // 64) for p in range(parts)]
     assert [int(items[i * parts, 0]) for i in range(w.M // 64)] == [int(c) for c in w.order]
     assert np.all(CL[n_items:] == -1)
-    # timestamps (wall clock, 32-bit): each tile became ready after every copy of
-    # its units had started, and take <= ready <= done; copies start <= end
+    # timestamps (wall clock, 32-bit): a copy item's end stamp is taken once its
+    # stores are complete and before its release, so consume-on-arrival means
+    # every tile became ready after EVERY copy item of its units had landed;
+    # take <= ready <= done; copies start <= end
     wrap = lambda x: x & 0xffffffff
     base = int(min(L[:n_tiles, 5].min(), items[:, 3].min()))
     rel = lambda x: (wrap(x - base))
     for q in range(n_tiles):
         tm, tn, u0, u1, wg, tt, tr, td = L[q]
         assert rel(tt) <= rel(tr) <= rel(td)
-        starts = [rel(t) for (u, pt, _, t) in items[:, :4] if u0 <= u <= u1]
-        assert rel(tr) >= max(starts)
+        ends = [rel(t_end) for (u, pt, _, _, t_end) in items[:, :5] if u0 <= u <= u1]
+        assert len(ends) == (u1 - u0 + 1) * parts
+        assert rel(tr) >= max(ends), f"tile {q} ready before its rows landed"
     assert np.all([rel(a) <= rel(b) for a, b in items[:, 3:5]])
     assert gpu.mk_wall_clock_khz() > 0
 
@@ -154,25 +157,28 @@ def test_withheld_chunk_times_out_and_kernel_exits(gpu):
     assert_close(out_to_f64(prob.output(), "bf16"), C64, "bf16", "after timeout")
 
 
-def _sampled_rows(w, prob, n_rows, seed, what):
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([rng.choice(w.M, n_rows, replace=False), [0, w.M - 1]]))
-    ref = og.ag_gemm_rows(w.shards, w.B, rows)
-    got = out_to_f64(prob.output()[rows], w.out_dtype)
-    assert_close(got, ref, w.out_dtype, what)
+def _whole_output(w, prob, what):
+    from tests.full_refs import ag_product
+    name = "ag" if w.K == 8192 and w.N == 3584 else "skinny_ag"
+    _, C64 = ag_product(name)
+    assert_close(out_to_f64(prob.output(), w.out_dtype), C64, w.out_dtype, what)
 
 
-def test_full_size_ag_config_sampled(gpu):
-    w = wl.CONFIGS["ag"]["make"]()
+def test_full_size_ag_config_whole_output(gpu):
+    # every one of the 8192 x 3584 outputs against the float64 oracle
+    from tests.full_refs import ag_product
+    w, _ = ag_product("ag")
     prob = _run(gpu, w)
-    _sampled_rows(w, prob, 96, 0, "AG 8192x8192x3584")
-    assert not np.any(np.isnan(out_to_f64(prob.output(), "bf16")))
+    from tile_pipelined_gemm_amd.harness import to_numpy
+    assert np.array_equal(to_numpy(prob.Ag), og.gather(w.shards))
+    _whole_output(w, prob, "AG 8192x8192x3584")
 
 
-def test_full_size_skinny_config_sampled(gpu):
-    w = wl.CONFIGS["skinny_ag"]["make"]()
+def test_full_size_skinny_config_whole_output(gpu):
+    from tests.full_refs import ag_product
+    w, _ = ag_product("skinny_ag")
     prob = _run(gpu, w)
-    _sampled_rows(w, prob, 24, 1, "skinny AG 128x8192x28672")
+    _whole_output(w, prob, "skinny AG 128x8192x28672")
 
 
 # ---- more tiles than workgroups with a partial last round: 272 tiles of
@@ -339,7 +345,7 @@ def test_eight_wave_dma_tile_integer_inputs_bit_exact(gpu):
 def test_eight_wave_dma_tile_full_size_ag_config(gpu):
     w = wl.CONFIGS["ag"]["make"]()
     prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA_W8))
-    _sampled_rows(w, prob, 64, 3, "AG full, 8-wave dma tile")
+    _whole_output(w, prob, "AG full, 8-wave dma tile")
     ref = prob.output().copy()
     prob.run(launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA))
     torch.cuda.synchronize()
@@ -379,7 +385,7 @@ def test_dma_tile_rejects_k_not_multiple_of_128(gpu):
 def test_dma_tile_full_size_ag_config(gpu):
     w = wl.CONFIGS["ag"]["make"]()
     prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA))
-    _sampled_rows(w, prob, 64, 2, "AG full, dma tile")
+    _whole_output(w, prob, "AG full, dma tile")
     ref = prob.output().copy()
     prob.run(launch=gpu.make_launch(tile=gpu.TILE_256x256))
     torch.cuda.synchronize()

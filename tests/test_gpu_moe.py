@@ -143,6 +143,19 @@ def test_tile_and_copy_logs(gpu, tile, bm, bn):
     parts = 64 // 8
     assert sorted((int(b), int(q)) for b, q in C[:, :2]) == [(b, q) for b in range(w.T // 64) for q in range(parts)]
     assert int(C[:, 5].sum()) == prob.local_rows()
+    # consume on arrival: a tile became ready only after every copy item that
+    # holds one of its rows had landed (an item's end stamp is taken once its
+    # stores are complete, before it is counted)
+    out = prob.outputs()
+    perm, offsets = out["perm"], out["offsets"]
+    end_of = {(int(b), int(q)): int(e) for b, q, e in zip(C[:, 0], C[:, 1], C[:, 4])}
+    base = int(min(T[:, 5].min(), C[:, 3].min()))
+    rel = lambda x: (int(x) - base) & 0xffffffff
+    for l, r0, n, _, _, _, t_ready, _ in T:
+        pos0 = int(offsets[6 + l]) + int(r0)
+        toks = perm[pos0:pos0 + int(n)] // w.k
+        items = {(int(t) // 64, (int(t) % 64) // 8) for t in toks}
+        assert rel(t_ready) >= max(rel(end_of[i]) for i in items)
 
 
 def _split_tail_workload(dist, out_dtype):
@@ -211,16 +224,16 @@ def test_withheld_block_times_out(gpu):
     assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
 
 
-def test_full_size_moe_config_sampled(gpu):
+def test_full_size_moe_config_whole_output(gpu):
+    # routing, counts, offsets, perm bit-exact; every landing row (every
+    # expert's ragged last M-tile included) and every output row against the
+    # float64 oracle
     w = wl.CONFIGS["moe"]["make"]()
     prob = _run(gpu, w)
-    topk = om.route_topk(w.logits, w.k)
-    counts, offsets, perm = om.dispatch(topk, w.E)
-    ref = dict(topk=topk, counts=counts, offsets=offsets, perm=perm,
-               n_local=int(offsets[w.L] - offsets[0]))
+    ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 0, "bf16")
     got = _check_exact(prob, ref)
-    rng = np.random.default_rng(4)
     n = ref["n_local"]
-    rows = np.unique(np.concatenate([rng.choice(n, 128, replace=False), [0, n - 1]]))
-    Y64, _ = om.grouped_gemm(w.X, w.W, offsets, perm, w.k, 0, "bf16", rows=rows)
-    assert_close(out_to_f64(got["Y"][rows], "bf16"), Y64, "bf16", "MoE full")
+    toks = om.landing_tokens(ref["perm"], ref["offsets"], w.k, 0, w.L)
+    from tile_pipelined_gemm_amd.harness import to_numpy
+    assert np.array_equal(to_numpy(prob.Xs[:n]), w.X[toks])
+    assert_close(out_to_f64(got["Y"][:n], "bf16"), ref["Y64"], "bf16", "MoE full")

@@ -83,13 +83,14 @@ def test_owner_map_in_tile_log(gpu):
     w = wl.make_rs(2048, 64, 512, 8, seed=25)
     prob = RsProblem(w)
     n_tiles = (2048 // 128) * (512 // 128)
-    log = torch.full((2 * n_tiles,), -1, dtype=torch.int32, device="cuda")
+    log = torch.full((8 * n_tiles,), -1, dtype=torch.int32, device="cuda")
     prob.run(launch=gpu.make_launch(n_reduce=16, tile_log=log))
     torch.cuda.synchronize()
-    L = log.cpu().numpy().reshape(-1, 2)
+    L = log.cpu().numpy().reshape(-1, 8)
     for t in range(n_tiles):
         tm = t // 4
         assert L[t, 0] == orc.tile_owner(tm, 128, w.M, w.R)
+        assert L[t, 3] == -1                                    # no arrival schedule
     assert sorted(L[:, 1].tolist()) == list(range(n_tiles))     # each production slot used once
 
 
@@ -98,22 +99,147 @@ def test_owner_map_in_tile_log_dma_tile(gpu):
     w = wl.make_rs(2048, 256, 512, 8, seed=28)
     prob = RsProblem(w)
     n_tiles = (2048 // 256) * (512 // 256)
-    log = torch.full((2 * n_tiles,), -1, dtype=torch.int32, device="cuda")
+    log = torch.full((8 * n_tiles,), -1, dtype=torch.int32, device="cuda")
     prob.run(launch=gpu.make_launch(tile=5, tile_log=log))
     torch.cuda.synchronize()
-    L = log.cpu().numpy().reshape(-1, 2)
+    L = log.cpu().numpy().reshape(-1, 8)
     for t in range(n_tiles):
         assert L[t, 0] == orc.tile_owner(t // 2, 256, w.M, w.R)
         assert L[t, 1] == t
 
 
-def test_full_size_rs_config_sampled(gpu):
-    w = wl.CONFIGS["rs"]["make"]()
+# ---- partial sums under an arrival schedule: units (peer, row block) ----
+def _arrival_workload(dist="normal", M=1024, N=264, R=4, unit_rows=128, seed=61):
+    # K = 256: the direct-to-LDS 256x256 default tile; N = 264 ragged
+    return wl.make_rs(M, 256, N, R, seed=seed, dist=dist, unit_rows=unit_rows, max_delay_ns=20000)
+
+
+def _run_arrival(gpu, w, landing=True, launch=None, order=None, delay_ns=None):
+    from tile_pipelined_gemm_amd.harness import RsProblem
+    prob = RsProblem(w, landing=landing)
+    for o in prob.out:
+        o.fill_(float("nan"))
+    if landing:
+        for b in prob.landing:
+            b.fill_(float("nan"))                  # a tile that read before its unit landed shows NaN
+    prob.run(launch=launch, order=order, delay_ns=delay_ns)
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+    return prob
+
+
+def test_arrival_integer_inputs_bit_exact(gpu):
+    w = _arrival_workload("int")
+    _, _, outs = orc.gemm_rs(w.A, w.B, w.partials, w.R, "f32", order=w.order, delay_ns=w.delay_ns,
+                             unit_rows=w.unit_rows)
+    for landing in (True, False):
+        prob = _run_arrival(gpu, w, landing=landing)
+        assert np.array_equal(prob.output(), np.vstack(outs)), f"landing={landing}"
+        if landing:                                # the landing buffers hold the partial sums
+            for q in range(w.R - 1):
+                assert np.array_equal(prob.landing[q].cpu().numpy(), w.partials[q])
+
+
+def test_arrival_outputs_independent_of_schedule(gpu):
+    # the sum order is fixed, so every schedule, landing choice, role split and
+    # the unfused baseline give the bits of the resident path
+    from tile_pipelined_gemm_amd.harness import RsProblem
+    w = _arrival_workload("normal")
+    n = len(w.order)
+    base = RsProblem(w)
+    for o in base.out:
+        o.fill_(float("nan"))
+    base.run(arrival=False)                        # every partial sum resident: no schedule
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(base.ws) == gpu.MK_OK
+    resident = base.output()
+    S, _, _ = orc.gemm_rs(w.A, w.B, w.partials, w.R)
+    assert_close(out_to_f64(resident, "f32"), S, "f32", "RS resident")
+    rev = w.order[::-1].copy()
+    ident = np.arange(n, dtype=np.int32)
+    for kw in [dict(), dict(order=rev), dict(order=ident, delay_ns=np.zeros(n, np.uint32)),
+               dict(launch=gpu.make_launch(n_copy=8)), dict(launch=gpu.make_launch(n_copy=1)),
+               dict(launch=gpu.make_launch(n_reduce=16)), dict(launch=gpu.make_launch(mode=1)),
+               dict(launch=gpu.make_launch(copy_kib=8)), dict(launch=gpu.make_launch(grid=40, n_copy=3)),
+               dict(landing=False), dict(landing=False, order=rev), dict(landing=False, launch=gpu.make_launch(mode=1)),
+               dict(launch=gpu.make_launch(tile=2)), dict(launch=gpu.make_launch(tile=2, n_reduce=8))]:
+        got = _run_arrival(gpu, w, **kw).output()
+        assert np.array_equal(got, resident), f"variant {kw} differs"
+
+
+def test_arrival_units_spanning_tiles_and_all_reduce(gpu):
+    # 64-row units under 256-row tiles (four row blocks per tile); the
+    # all-reduce of the same contributions equals the owner blocks stacked
+    from tile_pipelined_gemm_amd.harness import ArProblem
+    w = _arrival_workload("normal", M=1024, N=512, R=4, unit_rows=64, seed=62)
+    S, _, _ = orc.gemm_rs(w.A, w.B, w.partials, w.R)
+    rs = _run_arrival(gpu, w).output()
+    assert_close(out_to_f64(rs, "f32"), S, "f32", "RS 64-row units")
+    ar = ArProblem(w, landing=True)
+    ar.run()
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(ar.ws) == gpu.MK_OK
+    for o in ar.outputs():
+        assert np.array_equal(o, rs)
+
+
+def test_arrival_tile_and_copy_logs(gpu):
+    # every copy item logged once, in arrival order of its units; every tile's
+    # reduction became ready only after every copy item of every peer's units
+    # under its rows had landed (an item's end stamp is taken once its stores
+    # are complete, before its release)
+    from tile_pipelined_gemm_amd.harness import RsProblem
+    w = _arrival_workload("normal", M=1024, N=512, R=4, unit_rows=128, seed=63)
+    prob = RsProblem(w, landing=True)
+    n_tiles = (1024 // 256) * (512 // 256)
+    parts = 128 * 512 * 4 // (64 * 1024)           # 64 KiB copy items: 4 per unit
+    n_units = (w.R - 1) * (w.M // 128)
+    tlog = torch.full((8 * n_tiles,), -1, dtype=torch.int32, device="cuda")
+    clog = torch.full((8 * n_units * parts,), -1, dtype=torch.int32, device="cuda")
+    prob.run(launch=gpu.make_launch(tile_log=tlog, copy_log=clog, copy_kib=64))
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+    T = tlog.cpu().numpy().reshape(-1, 8).astype(np.int64)
+    CL = clog.cpu().numpy().reshape(-1, 8).astype(np.int64)
+    assert sorted(map(tuple, CL[:, :2].tolist())) == [(u, p) for u in range(n_units) for p in range(parts)]
+    assert [int(CL[i * parts, 0]) for i in range(n_units)] == [int(u) for u in w.order]
+    base = int(min(T[:, 4].min(), CL[:, 3].min()))
+    rel = lambda x: (int(x) - base) & 0xffffffff
+    end_of = {}
+    for u, _, _, _, t_end in CL[:, :5]:
+        end_of.setdefault(int(u), []).append(rel(t_end))
+    for t in range(n_tiles):
+        tm = t // 2
+        owner, _, wg, b0, t_take, t_ready, t_done, _ = T[t]
+        assert owner == orc.tile_owner(tm, 256, w.M, w.R)
+        assert b0 == tm * 256 // 128
+        assert rel(t_take) <= rel(t_ready) <= rel(t_done)
+        units = {orc.unit_of(p, r, w.M, 128) for p in range(1, w.R) for r in (tm * 256, tm * 256 + 255)}
+        ends = [e for u in units for e in end_of[u]]
+        assert len(ends) == len(units) * parts
+        assert rel(t_ready) >= max(ends), f"tile {t} reduced before its partial sums landed"
+
+
+def test_arrival_withheld_unit_times_out_and_kernel_exits(gpu):
+    from tile_pipelined_gemm_amd.harness import RsProblem
+    w = _arrival_workload("normal", seed=64)
+    prob = RsProblem(w, landing=True)
+    prob.run(withhold=int(w.order[5]), launch=gpu.make_launch(spin_limit_us=20000))
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_ERR_TIMEOUT
+    # the workspace is reusable and the status was cleared
+    prob.run()
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+    S, _, _ = orc.gemm_rs(w.A, w.B, w.partials, w.R)
+    assert_close(out_to_f64(prob.output(), "f32"), S, "f32", "RS after timeout")
+
+
+def test_full_size_rs_config_whole_output(gpu):
+    # every element of the 8 owner blocks against the float64 oracle; the
+    # owner blocks stacked are the whole reduced sum (reduce-scatter over all
+    # owners equals the all-reduce)
+    from tests.full_refs import rs_reduced_sum, rs_workload
+    w = rs_workload()
     prob = _run(gpu, w)
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([rng.choice(w.M, 64, replace=False), [0, 1023, 1024, w.M - 1]]))
-    ref = orc.gemm_rs_rows(w.A, w.B, w.partials, rows)
-    got = out_to_f64(prob.output()[rows], "f32")
-    assert_close(got, ref, "f32", "RS 8192x3584x8192")
-    # the reduce-scatter over all owners is the all-reduce: every owner block filled
-    assert not np.any(np.isnan(prob.output()))
+    assert_close(out_to_f64(prob.output(), "f32"), rs_reduced_sum(), "f32", "RS 8192x3584x8192")

@@ -134,3 +134,19 @@ def test_wide_store_register_range_overlap():
         v_pk_mov_b32 v[12:13], v[0:1], v[0:1] op_sel:[0,1]
     """.splitlines()
     assert len(isa_check.wide_store_data_overwrites(body)) == 1
+
+
+def test_lds_dma_right_after_m0_write_is_flagged():
+    lines = ["s_mov_b32 m0, s11", "buffer_load_dwordx4 v2, s[56:59], s14 offen lds", "s_endpgm"]
+    assert len(isa_check.m0_lds_dma_hazards(lines)) == 1
+    lines = ["s_cselect_b32 m0, 0x400, -1", "global_load_lds_dword v[2:3], off lds", "s_endpgm"]
+    assert len(isa_check.m0_lds_dma_hazards(lines)) == 1
+
+
+def test_lds_dma_after_m0_write_and_wait_state_passes():
+    lines = ["s_mov_b32 m0, s11", "s_nop 0", "buffer_load_dwordx4 v2, s[56:59], s14 offen lds",
+             "s_mov_b32 s4, m0", "buffer_load_dwordx4 v2, s[56:59], s14 offen lds",   # reads M0, no write
+             "s_mov_b32 m0, s11", "v_add_u32 v1, v1, v2", "buffer_load_dwordx4 v2, s[56:59], s14 offen lds",
+             "s_mov_b32 m0, s11", "buffer_load_dwordx4 v2, s[56:59], s14 offen",      # not an LDS DMA
+             "s_endpgm"]
+    assert isa_check.m0_lds_dma_hazards(lines) == []

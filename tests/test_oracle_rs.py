@@ -4,6 +4,7 @@ degenerate cases (no partials, zero A)."""
 import math
 
 import numpy as np
+import pytest
 
 import oracle.gemm_rs as orc
 from oracle.numerics import bf16_to_f64
@@ -97,3 +98,38 @@ def test_mutants_are_caught():
     assert pin_slice_then_sum(orc.gemm_rs, w)
     assert not pin_slice_then_sum(_mut_drop_partial, w)
     assert not pin_slice_then_sum(_mut_interleaved_owner, w)
+
+
+def test_partial_units_are_peer_major_row_blocks():
+    # M = 8 rows in blocks of 2, R = 3 (peers 1 and 2): 8 units, peer-major
+    M, R, ur = 8, 3, 2
+    assert orc.partial_units(M, R, ur) == 8
+    ids = [[orc.unit_of(p, r, M, ur) for r in range(M)] for p in (1, 2)]
+    assert ids == [[0, 0, 1, 1, 2, 2, 3, 3], [4, 4, 5, 5, 6, 6, 7, 7]]
+    # every (peer, row) lands in exactly one unit and every unit is hit
+    assert sorted({u for row in ids for u in row}) == list(range(8))
+
+
+def test_rs_schedule_validated_and_ignored():
+    from oracle.schedule import ScheduleError
+    w = wl.make_rs(64, 16, 24, 4, seed=5, unit_rows=16, max_delay_ns=20000)
+    assert w.order.shape == (3 * 4,) and sorted(w.order.tolist()) == list(range(12))
+    assert np.all(w.delay_ns <= 20000)
+    S0, _, _ = orc.gemm_rs(w.A, w.B, w.partials, w.R)
+    S1, _, _ = orc.gemm_rs(w.A, w.B, w.partials, w.R, order=w.order, delay_ns=w.delay_ns, unit_rows=16)
+    assert np.array_equal(S0, S1)
+    with pytest.raises(ScheduleError):
+        orc.gemm_rs(w.A, w.B, w.partials, w.R, order=w.order[:-1], unit_rows=16)
+    bad = w.order.copy()
+    bad[0] = bad[1]
+    with pytest.raises(ScheduleError):
+        orc.gemm_rs(w.A, w.B, w.partials, w.R, order=bad, unit_rows=16)
+    with pytest.raises(ScheduleError):
+        orc.partial_units(64, 4, 24)
+
+
+def test_rs_schedule_draw_leaves_the_tensors_unchanged():
+    a = wl.make_rs(64, 16, 24, 4, seed=5)
+    b = wl.make_rs(64, 16, 24, 4, seed=5, unit_rows=16)
+    assert np.array_equal(a.A, b.A) and np.array_equal(a.B, b.B)
+    assert all(np.array_equal(x, y) for x, y in zip(a.partials, b.partials))

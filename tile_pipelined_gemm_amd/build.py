@@ -53,8 +53,8 @@ def _compile(src):
     if found:
         lines = [f"  {k}: {v[:3]}" for k, v in found.items()]
         raise RuntimeError(f"{src}: barrier loop with a per-lane exit (kernel could spin for ever), "
-                           "register spills inside an MFMA loop, or a wide store whose data is "
-                           "rewritten right after it:\n" + "\n".join(lines))
+                           "register spills inside an MFMA loop, a wide store whose data is "
+                           "rewritten right after it, or an LDS DMA right after an M0 write:\n" + "\n".join(lines))
     return obj
 
 

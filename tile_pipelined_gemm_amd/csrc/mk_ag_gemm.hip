@@ -53,20 +53,6 @@ struct AgParams {
   uint32_t delay_ticks[MK_MAX_UNITS];
 };
 
-constexpr int COPY_UNROLL = 16;   // 16-byte loads in flight per thread (64 KiB per workgroup)
-
-template <int POLICY>
-__device__ __forceinline__ void copy_part(__amdgpu_buffer_rsrc_t src, __amdgpu_buffer_rsrc_t dst, int n16, int tid,
-                                          int nt) {
-  for (int base = 0; base < n16; base += nt * COPY_UNROLL) {
-    u32x4 v[COPY_UNROLL];
-#pragma unroll
-    for (int u = 0; u < COPY_UNROLL; ++u) v[u] = bload(src, (uint32_t)(base + u * nt + tid) * 16u, 0);
-#pragma unroll
-    for (int u = 0; u < COPY_UNROLL; ++u) bstore<POLICY>(dst, (uint32_t)(base + u * nt + tid) * 16u, 0, v[u]);
-  }
-}
-
 // Role loops take their next work index at the bottom of the body and test it
 // at the top (no `continue`), so every barrier stays in wave-uniform control
 // flow.  Log timestamps are the low 32 bits of the 100 MHz wall clock.
@@ -100,20 +86,23 @@ __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uin
       const __amdgpu_buffer_rsrc_t src =
           make_rsrc(uni(p.shard[row0 / p.m_shard] + (int64_t)(row0 % p.m_shard) * p.K), p.part_bytes);
       const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Ag + (int64_t)row0 * p.K), p.part_bytes);
-      if (p.copy_wt) copy_part<16>(src, dst, n16, tid, nt);
-      else copy_part<0>(src, dst, n16, tid, nt);
+      if (p.copy_wt) copy_block<16>(src, dst, n16, tid, nt);
+      else copy_block<0>(src, dst, n16, tid, nt);
       // Release only: the copier never reads what others publish, so the
       // acquire half of a full fence (an L2 invalidate that would also drop
       // the lines of the GEMM tiles running on this XCD) is not needed.
       fence_release();
       __syncthreads();
       if (tid == 0) {
+        // t_end is stamped once every thread's stores are complete and before
+        // the release, so a consumer that sees the release reads a later clock
+        const uint32_t t_end = (uint32_t)now_ticks();
         add_release(&p.unit_cnt[c], 1u);
         add_release(&h->aux[0], 1u);                 // parts landed in total
         if (p.copy_log) {
           int32_t* L = p.copy_log + 8 * (int64_t)w;
           L[0] = c; L[1] = part; L[2] = (int32_t)blockIdx.x;
-          L[3] = (int32_t)t_start; L[4] = (int32_t)(uint32_t)now_ticks();
+          L[3] = (int32_t)t_start; L[4] = (int32_t)t_end;
         }
       }
     }

@@ -222,6 +222,26 @@ __device__ __forceinline__ void bstore_alu16(__amdgpu_buffer_rsrc_t r, uint32_t 
   __builtin_amdgcn_raw_buffer_store_b64(u32x2{u[2], u[3]}, r, voff, soff + 8u, 0);
 }
 
+// Copy n16 16-byte chunks from src to dst (buffer resources bounded to the
+// block: past the end loads return zero and stores are dropped, so the loop
+// has no per-element guard -- a guarded store would be its own branch, and
+// the compiler would wait for every earlier memory operation before each
+// one).  Each thread keeps COPY_UNROLL loads in flight (64 KiB per 256-thread
+// workgroup).  POLICY is the stores' cache-policy field (16 = written through
+// the L2).
+constexpr int COPY_UNROLL = 16;
+template <int POLICY>
+__device__ __forceinline__ void copy_block(__amdgpu_buffer_rsrc_t src, __amdgpu_buffer_rsrc_t dst, int n16, int tid,
+                                           int nt) {
+  for (int base = 0; base < n16; base += nt * COPY_UNROLL) {
+    u32x4 v[COPY_UNROLL];
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) v[u] = bload(src, (uint32_t)(base + u * nt + tid) * 16u, 0);
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) bstore<POLICY>(dst, (uint32_t)(base + u * nt + tid) * 16u, 0, v[u]);
+  }
+}
+
 // Values the caller knows to be the same in every lane, moved to scalar
 // registers (buffer descriptors must live there).  The builtin works on int:
 // each 32-bit half is taken back as uint32_t before widening, so a low half

@@ -58,12 +58,16 @@ __device__ __forceinline__ u32x4 buf_desc(const void* p, uint32_t bytes) {
 }
 
 // One 16-byte-per-lane DMA: lane i's 16 bytes land at LDS byte lds + 16*i.
-// M0 is saved and restored around it.
+// M0 is saved and restored around it.  A scalar write of M0 followed by an
+// LDS DMA needs one wait state on gfx9-family parts (the DMA could otherwise
+// take the previous M0 as its LDS address); inline asm is outside the
+// compiler's hazard recognizer, so the s_nop is written here.
 __device__ __forceinline__ void dma16(u32x4 desc, uint32_t lds, uint32_t voff, uint32_t soff) {
   uint32_t save;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
       "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(save)

@@ -6,8 +6,21 @@
 // ranks' contributions are resident fp32 partial sums, and the owners are the
 // R row blocks of the output.
 //
+// The other ranks' partial sums may also arrive over time: with an arrival
+// schedule, units (peer, row block) are released in a given order and at
+// given times by copy workgroups, which move each unit's rows from the
+// resident partial sum into a landing buffer when the caller passes one (or
+// only publish it, the partial then being read in place); the reduction of a
+// tile waits for the units under its rows.  Without a schedule every partial
+// sum is resident from the start.
+//
 // Roles:
-//   compute  tickets [0, n_compute): GEMM tiles from a queue.  With reduce
+//   copy     tickets [0, n_copy) (arrival schedule only): take (unit, part)
+//            items in arrival order, wait for the unit's release time, copy,
+//            publish with an agent-scope release on the unit's counter; then
+//            continue as a compute (or reduce) workgroup.
+//   compute  tickets [0, n_compute): GEMM tiles from a queue (tile rows in the
+//            order their partial sums land).  With reduce
 //            workgroups present, a finished fp32 tile is staged, published
 //            (release) and its id appended to a produced-tile FIFO; a compute
 //            workgroup whose queue is empty turns into a reduce workgroup.
@@ -32,22 +45,39 @@ using namespace mk;
 
 namespace {
 
-enum { MODE_EPI = 0, MODE_ROLES = 1, MODE_GEMM = 2, MODE_REDUCE = 3 };
+enum { MODE_EPI = 0, MODE_ROLES = 1, MODE_GEMM = 2, MODE_REDUCE = 3, MODE_COPY = 4 };
 
 struct RsParams {
   const uint16_t* A;
   const uint16_t* B;
-  const float* P[MK_MAX_RANKS];   // R-1 partial sums
+  const float* P[MK_MAX_RANKS];   // R-1 partial sums as the reduction reads them (landing buffers if given)
+  const float* Psrc[MK_MAX_RANKS];// the resident partial sums the copy role moves into P (copy_data)
   void* out[MK_MAX_RANKS];        // R owner blocks
   float* stage;                   // fp32 staging [M x N], or NULL to stage in out (fp32)
   WsHeader* hdr;
   uint32_t* fifo;                 // [n_tiles] produced tile id + 1
+  uint32_t* unit_cnt;             // [n_units] parts landed per unit; NULL: every partial resident
   int32_t* tile_log;
+  int32_t* copy_log;
   uint64_t spin_limit;
   int M, K, N, R, out_bf16, mb;   // mb = rows per owner
   int n_dst;                      // outputs per row block: 1 (reduce-scatter) or R (all-reduce)
   int mode, n_compute, tiles_m, tiles_n, n_tiles;
+  // arrival schedule of the partial sums: unit u = q * n_blocks + b is row
+  // block b (unit_rows rows) of partial q (0-based peer), copied in `parts`
+  // items of part_rows rows
+  int n_units, unit_rows, n_blocks, parts, part_rows, n_copy, withhold, copy_data;
+  uint32_t part_bytes;
+  uint16_t order[MK_MAX_UNITS];
+  uint16_t rb_order[MK_MAX_UNITS];   // tile rows in landing order (arrival schedule only)
+  uint32_t delay_ticks[MK_MAX_UNITS];
 };
+static_assert(sizeof(RsParams) <= 4096, "kernel argument size");
+
+// Tile row of queue position q (tiles are queued row by row).
+__device__ __forceinline__ int queued_tile_row(const RsParams& p, int q) {
+  return p.unit_cnt ? (int)p.rb_order[q / p.tiles_n] : q / p.tiles_n;
+}
 
 __device__ __forceinline__ float* stage_ptr(const RsParams& p, int gr, int gc) {
   if (p.stage) return p.stage + (int64_t)gr * p.N + gc;
@@ -289,6 +319,88 @@ __device__ __forceinline__ void reduce_from_acc_lds(const G& g, const RsParams& 
 // The role loops take their next work index at the bottom of the body and
 // test it at the top, with no `continue`: one uniform exit and one latch, so
 // the compiler keeps every barrier in wave-uniform control flow.
+
+// Copy role: (unit, part) items in arrival order.  Log stamps are the low 32
+// bits of the 100 MHz wall clock; t_end is taken once the item's stores are
+// complete and before its release.
+__device__ __forceinline__ void rs_copy_role(const RsParams& p, WsHeader* h, uint32_t* sb) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  uint64_t t0 = 0;
+  if (tid == 0) {
+    const uint64_t now = now_ticks();
+    const uint64_t old = atomicCAS((unsigned long long*)&h->t0, 0ull, (unsigned long long)now);
+    t0 = old ? old : now;
+  }
+  const uint32_t n_work = (uint32_t)p.n_units * p.parts;
+  const int n16 = p.part_rows * (p.N / 4);       // 16-byte chunks of fp32 per part
+  uint32_t w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
+  while (w < n_work) {
+    const int j = w / p.parts, part = w % p.parts;
+    const int u = p.order[j];
+    if (u != p.withhold) {                         // a withheld unit never lands (failure tests)
+      uint32_t t_start = 0;
+      if (tid == 0) {
+        wait_until(t0 + p.delay_ticks[u], p.spin_limit);
+        t_start = (uint32_t)now_ticks();
+      }
+      __syncthreads();
+      if (p.copy_data) {
+        // rows of one row block of one partial: one contiguous block on both sides
+        const int q = u / p.n_blocks, b = u % p.n_blocks;
+        const int64_t ofs = ((int64_t)b * p.unit_rows + (int64_t)part * p.part_rows) * p.N;
+        const __amdgpu_buffer_rsrc_t src = make_rsrc(uni(p.Psrc[q] + ofs), p.part_bytes);
+        const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.P[q] + ofs), p.part_bytes);
+        copy_block<16>(src, dst, n16, tid, nt);    // written through the L2
+        fence_release();                           // release only: the copier reads nothing others publish
+      }
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t t_end = (uint32_t)now_ticks();
+        add_release(&p.unit_cnt[u], 1u);
+        add_release(&h->aux[0], 1u);               // parts landed in total
+        if (p.copy_log) {
+          int32_t* L = p.copy_log + 8 * (int64_t)w;
+          L[0] = u; L[1] = part; L[2] = (int32_t)blockIdx.x;
+          L[3] = (int32_t)t_start; L[4] = (int32_t)t_end; L[5] = 0; L[6] = 0; L[7] = 0;
+        }
+      }
+    }
+    w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
+  }
+}
+
+// Before a tile with BM rows starting at m0 is reduced: thread 0 waits until
+// every peer's units under those rows have landed, then takes one acquire for
+// all of them.  Returns (broadcast to the workgroup) bit 0 = ok (0: the
+// watchdog expired, the tile is dropped) and bit 1 = every part of every unit
+// had landed (later tiles of this workgroup need not wait).
+template <int BM>
+__device__ __forceinline__ uint32_t wait_partials(const RsParams& p, WsHeader* h, int m0, uint32_t* sb) {
+  uint32_t ok = 1, all = 0;
+  if (threadIdx.x == 0) {
+    const int b0 = m0 / p.unit_rows, b1 = (min(p.M, m0 + BM) - 1) / p.unit_rows;
+    for (int q = 0; q + 1 < p.R && ok; ++q)
+      for (int b = b0; b <= b1 && ok; ++b)
+        ok = wait_geq_relaxed(&p.unit_cnt[q * p.n_blocks + b], (uint32_t)p.parts, h, p.spin_limit);
+    if (ok) {
+      all = ld_relaxed(&h->aux[0]) >= (uint32_t)p.n_units * p.parts;
+      fence_acquire();
+    }
+  }
+  return wg_bcast(ok | (all << 1), sb);
+}
+
+// Tile log record of tile t: {owner, production rank, reducing workgroup,
+// first row block (-1: partials resident), t_take (reduction about to wait
+// for its partial sums), t_ready (they had landed), t_done (stores issued),
+// 0}.
+__device__ __forceinline__ void log_reduction(const RsParams& p, int t, int m0, uint32_t t_take, uint32_t t_ready) {
+  int32_t* L = p.tile_log + 8 * (int64_t)t;
+  L[2] = (int32_t)blockIdx.x;
+  L[3] = p.unit_cnt ? m0 / p.unit_rows : -1;
+  L[4] = (int32_t)t_take; L[5] = (int32_t)t_ready; L[6] = (int32_t)(uint32_t)now_ticks(); L[7] = 0;
+}
+
 template <class G, class SM>
 __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, SM sm, uint32_t* sb) {
   const int tid = threadIdx.x;
@@ -306,10 +418,12 @@ __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, 
     __syncthreads();
   }
   bool first = true;
+  // partial sums all landed (or resident): no more waits before reductions
+  bool all_landed = p.unit_cnt == nullptr;
   uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
   while (q < (uint32_t)p.n_tiles) {
-    const int t = (int)q;
-    const int tm = t / p.tiles_n, tn = t % p.tiles_n;
+    const int tm = queued_tile_row(p, (int)q), tn = (int)q % p.tiles_n;
+    const int t = tm * p.tiles_n + tn;             // tile id (row-major)
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     g.bind(p.A + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
     uint32_t* mark = offset && first && !(blockIdx.x & 1) ? &h->aux[1] : nullptr;
@@ -321,16 +435,31 @@ __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, 
     }
     first = false;
     if (p.mode == MODE_EPI) {
-      // the LDS path needs 32 KiB of stage buffers per wave: 256x256 tile only
-      if constexpr (G::STAGES == 4 && G::BM == 256 && G::BN == 256) {
-        if (p.R <= 8) {
-          reduce_from_acc_lds(g, p, m0, n0, sm);
-          __syncthreads();                         // LDS back to the K loop of the next tile
+      const uint32_t t_take = (uint32_t)now_ticks();
+      uint32_t ready = 1;
+      if (!all_landed) {
+        const uint32_t v = wait_partials<G::BM>(p, h, m0, sb);
+        ready = v & 1u;
+        all_landed = (v >> 1) & 1u;
+      }
+      const uint32_t t_ready = (uint32_t)now_ticks();
+      if (ready) {                                 // else the watchdog expired: the tile is dropped
+        // the LDS path needs 32 KiB of stage buffers per wave: 256x256 tile only
+        if constexpr (G::STAGES == 4 && G::BM == 256 && G::BN == 256) {
+          if (p.R <= 8) {
+            reduce_from_acc_lds(g, p, m0, n0, sm);
+            __syncthreads();                       // LDS back to the K loop of the next tile
+          } else {
+            reduce_from_acc(g, p, m0, n0);
+          }
         } else {
           reduce_from_acc(g, p, m0, n0);
         }
-      } else {
-        reduce_from_acc(g, p, m0, n0);
+        if (p.tile_log && tid == 0) {
+          p.tile_log[8 * t] = m0 / p.mb;
+          p.tile_log[8 * t + 1] = t;
+          log_reduction(p, t, m0, t_take, t_ready);
+        }
       }
     } else {
       // Stage the fp32 tile (in the owner block for fp32 output, else in the
@@ -347,14 +476,11 @@ __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, 
     if (tid == 0) {
       if (p.mode == MODE_ROLES) {
         const uint32_t slot = add_relaxed(&h->prod_next, 1u);
-        st_release(&p.fifo[slot], (uint32_t)t + 1u);
-        if (p.tile_log) {
-          p.tile_log[2 * t] = m0 / p.mb;
-          p.tile_log[2 * t + 1] = (int32_t)slot;
+        if (p.tile_log) {                          // before the release: the reducer may log next
+          p.tile_log[8 * t] = m0 / p.mb;
+          p.tile_log[8 * t + 1] = (int32_t)slot;
         }
-      } else if (p.mode == MODE_EPI && p.tile_log) {
-        p.tile_log[2 * t] = m0 / p.mb;
-        p.tile_log[2 * t + 1] = t;
+        st_release(&p.fifo[slot], (uint32_t)t + 1u);
       }
       next = add_relaxed(&h->tile_next, 1u);
     }
@@ -365,6 +491,8 @@ __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, 
 template <class G>
 __device__ __forceinline__ void rs_reduce_role(const RsParams& p, WsHeader* h, uint32_t* sb) {
   const int tid = threadIdx.x;
+  // the unfused reduce kernel runs after the copy kernel: everything has landed
+  bool all_landed = p.unit_cnt == nullptr || p.mode == MODE_REDUCE;
   uint32_t i = wg_bcast(tid == 0 ? add_relaxed(&h->red_next, 1u) : 0u, sb);
   while (i < (uint32_t)p.n_tiles) {
     uint32_t t = i;
@@ -374,16 +502,28 @@ __device__ __forceinline__ void rs_reduce_role(const RsParams& p, WsHeader* h, u
       v = wg_bcast(v, sb);
       t = v - 1u;                                // v == 0: watchdog expired, nothing to reduce
     }
-    if (t < (uint32_t)p.n_tiles) reduce_tile<G::BM, G::BN>(p, (int)t);
-    uint32_t next = 0;
-    if (tid == 0) {
-      if (p.mode == MODE_REDUCE && p.tile_log) {
-        const int tm = (int)t / p.tiles_n;
-        p.tile_log[2 * t] = tm * G::BM / p.mb;
-        p.tile_log[2 * t + 1] = (int32_t)t;
+    if (t < (uint32_t)p.n_tiles) {
+      const int m0 = (int)(t / p.tiles_n) * G::BM;
+      const uint32_t t_take = (uint32_t)now_ticks();
+      uint32_t ready = 1;
+      if (!all_landed) {
+        const uint32_t v = wait_partials<G::BM>(p, h, m0, sb);
+        ready = v & 1u;
+        all_landed = (v >> 1) & 1u;
       }
-      next = add_relaxed(&h->red_next, 1u);
+      const uint32_t t_ready = (uint32_t)now_ticks();
+      if (ready) {
+        reduce_tile<G::BM, G::BN>(p, (int)t);
+        if (p.tile_log && tid == 0) {
+          if (p.mode == MODE_REDUCE) {
+            p.tile_log[8 * t] = m0 / p.mb;
+            p.tile_log[8 * t + 1] = (int32_t)t;
+          }
+          log_reduction(p, (int)t, m0, t_take, t_ready);
+        }
+      }
     }
+    const uint32_t next = tid == 0 ? add_relaxed(&h->red_next, 1u) : 0u;
     i = wg_bcast(next, sb);
   }
 }
@@ -400,13 +540,18 @@ __device__ __forceinline__ void rs_finish(const RsParams& p, WsHeader* h, uint32
   if (!last) return;
   if (p.mode == MODE_ROLES)
     for (int i = threadIdx.x; i < p.n_tiles; i += blockDim.x) st_relaxed(&p.fifo[i], 0u);
+  if (p.unit_cnt && (p.mode == MODE_COPY || p.mode == MODE_EPI || p.mode == MODE_ROLES))
+    for (int i = threadIdx.x; i < p.n_units; i += blockDim.x) st_relaxed(&p.unit_cnt[i], 0u);
   if (threadIdx.x == 0) {
     st_relaxed(&h->ticket, 0u);
     st_relaxed(&h->tile_next, 0u);
     st_relaxed(&h->red_next, 0u);
     st_relaxed(&h->prod_next, 0u);
+    st_relaxed(&h->copy_next, 0u);
+    st_relaxed(&h->aux[0], 0u);
     st_relaxed(&h->aux[1], 0u);
     st_relaxed(&h->abort, 0u);
+    __hip_atomic_store(&h->t0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     st_relaxed(&h->done, 0u);
   }
 }
@@ -415,9 +560,16 @@ template <class G, class SM>
 __device__ __forceinline__ void rs_body(const RsParams& p, SM sm, uint32_t* sb) {
   WsHeader* h = p.hdr;
   const uint32_t ticket = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->ticket, 1u) : 0u, sb);
-  const bool reducer = p.mode == MODE_REDUCE || (p.mode == MODE_ROLES && ticket >= (uint32_t)p.n_compute);
-  if (!reducer) rs_compute_role<G>(p, h, sm, sb);
-  if (p.mode == MODE_ROLES || p.mode == MODE_REDUCE) rs_reduce_role<G>(p, h, sb);
+  // copy workgroups hold the earliest tickets, so every wait for a unit is a
+  // wait for a workgroup that is already running
+  const bool copier = p.mode == MODE_COPY ||
+                      (p.unit_cnt && (p.mode == MODE_EPI || p.mode == MODE_ROLES) && ticket < (uint32_t)p.n_copy);
+  if (copier) rs_copy_role(p, h, sb);
+  if (p.mode != MODE_COPY) {
+    const bool reducer = p.mode == MODE_REDUCE || (p.mode == MODE_ROLES && ticket >= (uint32_t)p.n_compute);
+    if (!reducer) rs_compute_role<G>(p, h, sm, sb);
+    if (p.mode == MODE_ROLES || p.mode == MODE_REDUCE) rs_reduce_role<G>(p, h, sb);
+  }
   rs_finish(p, h, sb);
 }
 
@@ -445,21 +597,45 @@ inline int rs_tile(int64_t, int64_t, int64_t K, int mb) {
 
 }  // namespace
 
+// Workspace: header, per-unit arrival counters, produced-tile FIFO, then
+// (bf16 output) the fp32 staging area of the reduce role.
+constexpr size_t RS_UNIT_BYTES = MK_MAX_UNITS * sizeof(uint32_t);
+
 extern "C" size_t mk_gemm_rs_workspace(int64_t M, int64_t K, int64_t N, int R, int out_dtype) {
   (void)K; (void)R;
-  if (M <= 0 || N <= 0) return sizeof(WsHeader);
+  if (M <= 0 || N <= 0) return sizeof(WsHeader) + RS_UNIT_BYTES;
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  size_t bytes = sizeof(WsHeader) + (size_t)tiles * 4;
+  size_t bytes = sizeof(WsHeader) + RS_UNIT_BYTES + (size_t)tiles * 4;
   bytes = (bytes + 255) & ~(size_t)255;
   if (out_dtype == MK_BF16) bytes += (size_t)M * N * 4;   // fp32 staging for the reduce role
   return bytes;
 }
 
 template <class G>
-static int run_rs(RsParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStream_t st, bool can_stage) {
+static int run_rs(RsParams& p, const mk_launch& o, const mkh::Schedule* s, const mkh::DevInfo* d, hipStream_t st,
+                  bool can_stage) {
   p.tiles_m = (p.M + G::BM - 1) / G::BM;
   p.tiles_n = (p.N + G::BN - 1) / G::BN;
   p.n_tiles = p.tiles_m * p.tiles_n;
+  if (s) {
+    // Tile rows ordered by the issue position of the last unit (over every
+    // peer) under them, so the GEMM tiles whose partial sums land first are
+    // produced first.
+    if (p.tiles_m > MK_MAX_UNITS)
+      return mkh::fail(MK_ERR_UNSUPPORTED, "%d tile rows: at most %d with an arrival schedule", p.tiles_m,
+                       MK_MAX_UNITS);
+    std::vector<int> rb(p.tiles_m), key(p.tiles_m);
+    for (int t = 0; t < p.tiles_m; ++t) {
+      const int b0 = t * G::BM / p.unit_rows, b1 = (std::min(p.M, (t + 1) * G::BM) - 1) / p.unit_rows;
+      int k = 0;
+      for (int q = 0; q + 1 < p.R; ++q)
+        for (int b = b0; b <= b1; ++b) k = std::max(k, s->pos[q * p.n_blocks + b]);
+      rb[t] = t;
+      key[t] = k;
+    }
+    std::stable_sort(rb.begin(), rb.end(), [&](int a, int b) { return key[a] < key[b]; });
+    for (int t = 0; t < p.tiles_m; ++t) p.rb_order[t] = (uint16_t)rb[t];
+  }
   int occ = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, rs_kernel<G>, G::NT, 0);
   if (e != hipSuccess) return mkh::hip_fail(e, "occupancy query");
@@ -467,8 +643,16 @@ static int run_rs(RsParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStr
   const int full = d->n_cu * occ;
   const int grid = o.grid > 0 ? std::min(o.grid, full) : full;
   if (!can_stage) return mkh::fail(MK_ERR_WORKSPACE, "bf16 output needs the fp32 staging workspace");
-  if (o.mode == 1) {   // unfused baseline: GEMM to fp32 staging, then a reduce-scatter kernel
-    if (!can_stage) return mkh::fail(MK_ERR_WORKSPACE, "bf16 output needs the fp32 staging workspace");
+  // Copy workgroups (arrival schedule): every workgroup copies first by
+  // default, then computes; n_copy selects fewer.
+  const uint32_t n_work = (uint32_t)p.n_units * p.parts;
+  p.n_copy = s ? (int)std::min<int64_t>(o.n_copy > 0 ? o.n_copy : grid, std::min<int64_t>(grid, n_work)) : 0;
+  if (o.mode == 1) {   // unfused baseline: copies, GEMM to fp32 staging, then a reduce-scatter kernel
+    if (s) {
+      p.mode = MODE_COPY;
+      hipLaunchKernelGGL(rs_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+      if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "copy kernel launch");
+    }
     p.mode = MODE_GEMM;
     hipLaunchKernelGGL(rs_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "gemm kernel launch");
@@ -479,7 +663,6 @@ static int run_rs(RsParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStr
   }
   const int n_reduce = o.n_reduce;   // 0 = default (epilogue reduction), -1 = epilogue
   if (n_reduce > 0) {
-    if (!can_stage) return mkh::fail(MK_ERR_WORKSPACE, "bf16 output needs the fp32 staging workspace");
     if (n_reduce >= grid) return mkh::fail(MK_ERR_INVALID, "n_reduce %d leaves no compute workgroup", n_reduce);
     p.mode = MODE_ROLES;
     p.n_compute = grid - n_reduce;
@@ -497,8 +680,9 @@ static int run_rs(RsParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStr
 // every outs[r]); one kernel for both, the all-reduce writing each reduced
 // tile R times.
 static int gemm_reduce(const void* A, const void* B, int64_t M, int64_t K, int64_t N, const float* const* partials,
-                       int R, void* const* outs, int out_dtype, const mk_launch* launch, void* workspace,
-                       size_t workspace_bytes, void* stream, bool all_reduce) {
+                       int R, void* const* outs, int out_dtype, const mk_arrival* arrival,
+                       float* const* p_landing, const mk_launch* launch, void* workspace, size_t workspace_bytes,
+                       void* stream, bool all_reduce) {
   using mkh::fail;
   if (!A || !B || !outs) return fail(MK_ERR_INVALID, "A, B and the outputs must be non-NULL");
   if (R < 1 || R > MK_MAX_RANKS) return fail(MK_ERR_UNSUPPORTED, "R=%d outside [1,%d]", R, MK_MAX_RANKS);
@@ -514,10 +698,28 @@ static int gemm_reduce(const void* A, const void* B, int64_t M, int64_t K, int64
   for (int r = 0; r < R; ++r)
     if (!outs[r] || !mkh::aligned16(outs[r])) return fail(MK_ERR_INVALID, "output %d NULL or misaligned", r);
   if (!mkh::aligned16(A) || !mkh::aligned16(B)) return fail(MK_ERR_INVALID, "A and B must be 16-byte aligned");
+  // Arrival schedule of the partial sums: (R-1) * (M / unit_rows) units.
+  mkh::Schedule sched;
+  const mkh::Schedule* s = nullptr;
+  if (arrival) {
+    if (R < 2) return fail(MK_ERR_SCHEDULE, "an arrival schedule needs partial sums (R >= 2)");
+    if (arrival->unit_rows <= 0 || M % arrival->unit_rows)
+      return fail(MK_ERR_SCHEDULE, "unit_rows (%d) must divide M (%lld)", arrival->unit_rows, (long long)M);
+    const int rc = mkh::make_schedule(arrival, (int64_t)(R - 1) * M, 1, &sched);
+    if (rc) return rc;
+    s = &sched;
+  }
+  if (p_landing) {
+    if (!s) return fail(MK_ERR_INVALID, "landing buffers need an arrival schedule");
+    for (int r = 0; r + 1 < R; ++r)
+      if (!p_landing[r] || !mkh::aligned16(p_landing[r]))
+        return fail(MK_ERR_INVALID, "landing buffer %d NULL or misaligned", r);
+  }
   const int mb = all_reduce ? (int)M : (int)(M / R);   // rows per output block
   const mk_launch o = mkh::launch_opts(launch);
   if (o.mode != 0 && o.mode != 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
-  if (o.grid < 0 || o.n_reduce < -1) return fail(MK_ERR_INVALID, "bad grid or n_reduce");
+  if (o.grid < 0 || o.n_reduce < -1 || o.n_copy < 0 || o.copy_kib < 0)
+    return fail(MK_ERR_INVALID, "bad grid, n_reduce, n_copy or copy_kib");
   // Default: the direct-to-LDS 256x256 tile when K is a multiple of 128 and
   // the output blocks hold whole tile rows (all-reduce: one block of M rows,
   // a ragged last tile row is masked), else 128x128.
@@ -545,37 +747,66 @@ static int gemm_reduce(const void* A, const void* B, int64_t M, int64_t K, int64
   memset(&p, 0, sizeof p);
   p.A = (const uint16_t*)A;
   p.B = (const uint16_t*)B;
-  for (int r = 0; r + 1 < R; ++r) p.P[r] = partials[r];
+  for (int r = 0; r + 1 < R; ++r) {
+    p.Psrc[r] = partials[r];
+    p.P[r] = p_landing ? p_landing[r] : partials[r];
+  }
   for (int r = 0; r < R; ++r) p.out[r] = outs[r];
   p.hdr = (WsHeader*)workspace;
-  p.fifo = (uint32_t*)((char*)workspace + sizeof(WsHeader));
+  p.fifo = (uint32_t*)((char*)workspace + sizeof(WsHeader) + RS_UNIT_BYTES);
   // fp32 output can be staged in place in the output blocks (all-reduce: in
   // output 0, which the reduction then rewrites in place).
   p.stage = out_dtype == MK_F32 ? nullptr : (have_stage ? (float*)((char*)workspace + need_min) : nullptr);
   const bool can_stage = out_dtype == MK_F32 || have_stage;
   p.tile_log = o.tile_log;
+  p.copy_log = o.copy_log;
   p.spin_limit = mkh::spin_ticks(o, d);
   p.M = (int)M; p.K = (int)K; p.N = (int)N; p.R = R; p.mb = mb;
   p.n_dst = all_reduce ? R : 1;
   p.out_bf16 = out_dtype == MK_BF16;
+  p.withhold = -1;
+  if (s) {
+    p.unit_cnt = (uint32_t*)((char*)workspace + sizeof(WsHeader));
+    p.n_units = s->n_units;
+    p.unit_rows = s->unit_rows;
+    p.n_blocks = (int)(M / s->unit_rows);
+    p.withhold = s->withhold;
+    p.copy_data = p_landing != nullptr;
+    // Copy items ("parts") of about copy_kib KiB in whole rows that divide the
+    // unit (1 MiB by default; one release each).  Without landing buffers
+    // nothing is moved and a unit is one item.
+    const int64_t row_bytes = N * 4;
+    const int64_t item_bytes = (int64_t)(o.copy_kib > 0 ? o.copy_kib : 1024) << 10;
+    int part_rows = p.copy_data ? (int)std::max<int64_t>(1, std::min<int64_t>(s->unit_rows, item_bytes / row_bytes))
+                                : s->unit_rows;
+    while (part_rows > 1 && (s->unit_rows % part_rows || (int64_t)part_rows * row_bytes > (1ll << 30))) --part_rows;
+    p.part_rows = part_rows;
+    p.part_bytes = (uint32_t)std::min<int64_t>((int64_t)part_rows * row_bytes, 1ll << 30);
+    p.parts = s->unit_rows / part_rows;
+    for (int j = 0; j < s->n_units; ++j) {
+      p.order[j] = (uint16_t)s->order[j];
+      p.delay_ticks[j] = (uint32_t)mkh::ns_to_ticks(s->delay_ns[j], d->wall_khz);
+    }
+  }
   const hipStream_t st = (hipStream_t)stream;
   switch (tile) {
-    case TILE_128x128: return run_rs<TileGemm<128, 128, 2, 2>>(p, o, d, st, can_stage);
-    case TILE_256x128: return run_rs<TileGemm<256, 128, 2, 2>>(p, o, d, st, can_stage);
-    case TILE_128x256: return run_rs<TileGemm<128, 256, 2, 2>>(p, o, d, st, can_stage);
-    case TILE_256x256_DMA: return run_rs<TileGemmD<256, 256, false>>(p, o, d, st, can_stage);
-    case TILE_128x128_DMA: return run_rs<TileGemmD<128, 128, false>>(p, o, d, st, can_stage);
-    case TILE_256x128_DMA: return run_rs<TileGemmD<256, 128, false>>(p, o, d, st, can_stage);
-    case TILE_128x256_DMA: return run_rs<TileGemmD<128, 256, false>>(p, o, d, st, can_stage);
+    case TILE_128x128: return run_rs<TileGemm<128, 128, 2, 2>>(p, o, s, d, st, can_stage);
+    case TILE_256x128: return run_rs<TileGemm<256, 128, 2, 2>>(p, o, s, d, st, can_stage);
+    case TILE_128x256: return run_rs<TileGemm<128, 256, 2, 2>>(p, o, s, d, st, can_stage);
+    case TILE_256x256_DMA: return run_rs<TileGemmD<256, 256, false>>(p, o, s, d, st, can_stage);
+    case TILE_128x128_DMA: return run_rs<TileGemmD<128, 128, false>>(p, o, s, d, st, can_stage);
+    case TILE_256x128_DMA: return run_rs<TileGemmD<256, 128, false>>(p, o, s, d, st, can_stage);
+    case TILE_128x256_DMA: return run_rs<TileGemmD<128, 256, false>>(p, o, s, d, st, can_stage);
   }
   return fail(MK_ERR_INVALID, "tile id %d", tile);
 }
 
 extern "C" int mk_gemm_rs(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
                           const float* const* partials, int R, void* const* out_owner, int out_dtype,
-                          const mk_launch* launch, void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_reduce(A, B, M, K, N, partials, R, out_owner, out_dtype, launch, workspace, workspace_bytes, stream,
-                     false);
+                          const mk_arrival* arrival, float* const* p_landing, const mk_launch* launch,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_reduce(A, B, M, K, N, partials, R, out_owner, out_dtype, arrival, p_landing, launch, workspace,
+                     workspace_bytes, stream, false);
 }
 
 extern "C" size_t mk_gemm_ar_workspace(int64_t M, int64_t K, int64_t N, int R, int out_dtype) {
@@ -584,7 +815,8 @@ extern "C" size_t mk_gemm_ar_workspace(int64_t M, int64_t K, int64_t N, int R, i
 
 extern "C" int mk_gemm_ar(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
                           const float* const* partials, int R, void* const* out_rank, int out_dtype,
-                          const mk_launch* launch, void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_reduce(A, B, M, K, N, partials, R, out_rank, out_dtype, launch, workspace, workspace_bytes, stream,
-                     true);
+                          const mk_arrival* arrival, float* const* p_landing, const mk_launch* launch,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_reduce(A, B, M, K, N, partials, R, out_rank, out_dtype, arrival, p_landing, launch, workspace,
+                     workspace_bytes, stream, true);
 }

@@ -315,6 +315,8 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
       // and an L2 invalidate would drop the lines of GEMM tiles on this XCD).
       fence_release();
       __syncthreads();
+      // stores complete, not yet counted: a tile that sees the counts reads a later clock
+      const uint32_t t_end = (uint32_t)now_ticks();
       if (tid < 64) {
         for (int q = tid; q < n; q += 64) add_relaxed(&p.tile_cnt[s_tile[q]], 1u);
       }
@@ -322,7 +324,7 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
       if (p.copy_log && tid == 0) {
         int32_t* L = p.copy_log + 8 * (int64_t)w;
         L[0] = blk; L[1] = part; L[2] = (int32_t)blockIdx.x; L[3] = (int32_t)t_start;
-        L[4] = (int32_t)(uint32_t)now_ticks(); L[5] = n; L[6] = (int32_t)t_indexed; L[7] = (int32_t)t_copied;
+        L[4] = (int32_t)t_end; L[5] = n; L[6] = (int32_t)t_indexed; L[7] = (int32_t)t_copied;
       }
       __syncthreads();
     }

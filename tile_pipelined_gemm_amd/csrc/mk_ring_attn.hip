@@ -129,12 +129,13 @@ __device__ __forceinline__ void ring_copy_role(const RingParams& p, WsHeader* h,
       fence_release();
       __syncthreads();
       if (tid == 0) {
+        const uint32_t t_end = (uint32_t)now_ticks();   // stores complete, not yet released
         add_release(&p.unit_cnt[u], 1u);
         add_release(&h->aux[0], 1u);              // parts landed in total
         if (p.copy_log) {
           int32_t* L = p.copy_log + 8 * (int64_t)w;
           L[0] = u; L[1] = part; L[2] = (int32_t)blockIdx.x;
-          L[3] = (int32_t)t_start; L[4] = (int32_t)(uint32_t)now_ticks();
+          L[3] = (int32_t)t_start; L[4] = (int32_t)t_end;
           L[5] = 0; L[6] = 0; L[7] = 0;
         }
       }

@@ -57,7 +57,7 @@ class AgProblem:
 
 
 class RsProblem:
-    def __init__(self, w, device="cuda"):
+    def __init__(self, w, device="cuda", landing=False):
         self.w = w
         self.A = bf16_tensor(w.A, device)
         self.B = bf16_tensor(w.B, device)
@@ -66,13 +66,25 @@ class RsProblem:
         self.out = [torch.empty(mb, w.N, dtype=_out_dtype(w.out_dtype), device=device) for _ in range(w.R)]
         code = mk.MK_BF16 if w.out_dtype == "bf16" else mk.MK_F32
         self.ws = mk.workspace(mk.mk_gemm_rs_workspace(w.M, w.K, w.N, w.R, code), device)
+        # landing buffers for the partial sums the copy workgroups move
+        self.landing = [torch.empty_like(p) for p in self.P] if landing else None
 
     @property
     def flops(self):
         return 2.0 * self.w.M * self.w.N * self.w.K
 
-    def run(self, launch=None, stream=None, check=True):
-        return mk.mk_gemm_rs(self.A, self.B, self.P, self.out, self.ws, launch=launch, stream=stream, check=check)
+    def _sched(self, arrival, order, delay_ns):
+        """The workload's arrival schedule (or the given order/delays) when
+        arrival is True and the workload has one, else none."""
+        if not arrival or self.w.unit_rows is None:
+            return dict()
+        return dict(order=self.w.order if order is None else order,
+                    delay_ns=self.w.delay_ns if delay_ns is None else delay_ns, unit_rows=self.w.unit_rows)
+
+    def run(self, launch=None, stream=None, check=True, arrival=True, order=None, delay_ns=None, withhold=-1):
+        return mk.mk_gemm_rs(self.A, self.B, self.P, self.out, self.ws, launch=launch, stream=stream, check=check,
+                             withhold=withhold, landing=self.landing if arrival else None,
+                             **self._sched(arrival, order, delay_ns))
 
     def output(self):
         return np.vstack([to_numpy(o) for o in self.out])
@@ -81,7 +93,7 @@ class RsProblem:
 class ArProblem:
     """GEMM -> AllReduce on an RsWorkload: every rank's output is the whole S."""
 
-    def __init__(self, w, device="cuda"):
+    def __init__(self, w, device="cuda", landing=False):
         self.w = w
         self.A = bf16_tensor(w.A, device)
         self.B = bf16_tensor(w.B, device)
@@ -89,13 +101,18 @@ class ArProblem:
         self.out = [torch.empty(w.M, w.N, dtype=_out_dtype(w.out_dtype), device=device) for _ in range(w.R)]
         code = mk.MK_BF16 if w.out_dtype == "bf16" else mk.MK_F32
         self.ws = mk.workspace(mk.mk_gemm_ar_workspace(w.M, w.K, w.N, w.R, code), device)
+        self.landing = [torch.empty_like(p) for p in self.P] if landing else None
 
     @property
     def flops(self):
         return 2.0 * self.w.M * self.w.N * self.w.K
 
-    def run(self, launch=None, stream=None, check=True):
-        return mk.mk_gemm_ar(self.A, self.B, self.P, self.out, self.ws, launch=launch, stream=stream, check=check)
+    _sched = RsProblem._sched
+
+    def run(self, launch=None, stream=None, check=True, arrival=True, order=None, delay_ns=None, withhold=-1):
+        return mk.mk_gemm_ar(self.A, self.B, self.P, self.out, self.ws, launch=launch, stream=stream, check=check,
+                             withhold=withhold, landing=self.landing if arrival else None,
+                             **self._sched(arrival, order, delay_ns))
 
     def outputs(self):
         return [to_numpy(o) for o in self.out]

@@ -1,7 +1,8 @@
 """Build-time checks of the gfx950 assembly of every kernel: no loop that
 holds a workgroup barrier may be left on an exec-mask branch, no register
-spill may sit among the MFMAs of a K loop, and no 12/16-byte buffer store may
-have its data registers rewritten right after it.
+spill may sit among the MFMAs of a K loop, no 12/16-byte buffer store may
+have its data registers rewritten right after it, and no LDS DMA may follow
+a scalar write of M0 without a wait state between them.
 
 A persistent kernel's role loops contain s_barrier and end in a
 `if (threadIdx.x == 0) { ... }` block (queue atomics, releases).  When the
@@ -181,6 +182,22 @@ def wide_store_data_overwrites(lines, wait_states=2):
     return bad
 
 
+_M0_WRITE = re.compile(r"^s_\w+\s+m0\s*,")
+_LDS_DMA = re.compile(r"^(buffer|global)_load_\w+\s.*\blds\b")
+
+
+def m0_lds_dma_hazards(lines):
+    """Return the LDS DMA loads (buffer/global loads with the lds bit) that
+    come directly after a scalar instruction writing M0.  On gfx9-family parts
+    the DMA reads M0 (its LDS address) one wait state after such a write: with
+    no instruction or s_nop in between it can use the old value and fill the
+    wrong LDS slot.  The compiler's hazard recognizer inserts the s_nop for
+    the loads it emits, but not inside inline asm."""
+    ins = [ln.split(";")[0].strip() for ln in lines]
+    ins = [x for x in ins if x and not x.startswith(".") and not x.endswith(":")]
+    return [f"{a} | {b}" for a, b in zip(ins, ins[1:]) if _M0_WRITE.match(a) and _LDS_DMA.match(b)]
+
+
 def check_file(path):
     """Return {kernel symbol: findings} for kernels with findings."""
     with open(path) as f:
@@ -194,6 +211,9 @@ def check_file(path):
         ow = wide_store_data_overwrites(lines)
         if ow:
             b = b + [("store data rewritten", x) for x in ow[:3]]
+        m0 = m0_lds_dma_hazards(lines)
+        if m0:
+            b = b + [("LDS DMA right after an M0 write", x) for x in m0[:3]]
         if b:
             found[name] = b
     return found

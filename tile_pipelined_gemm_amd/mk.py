@@ -57,15 +57,38 @@ class mk_launch(C.Structure):
 _lib = None
 
 
+def _hip_runtimes_mapped():
+    """Distinct HIP runtime files mapped into this process (Linux)."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
 def load(path: Optional[str] = None):
-    """Load libmk.so (once).  Raises if it has not been built."""
+    """Load libmk.so (once).  Raises if it has not been built.
+
+    torch is imported first: it carries its own HIP runtime, and libmk.so must
+    bind to that same runtime (the dynamic loader reuses an already loaded
+    libamdhip64.so.7).  Loaded the other way round, the process would map two
+    runtimes, and the streams and device pointers torch hands over would be
+    foreign to the one libmk calls (stream synchronisation then fails).  The
+    check after loading turns that state into an error instead of a failed
+    first call.
+    """
     global _lib
     if _lib is not None:
         return _lib
     path = path or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: run `python -m tile_pipelined_gemm_amd.build`")
+    import torch  # noqa: F401  (binds the process to torch's HIP runtime first)
     lib = C.CDLL(path)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise RuntimeError("two HIP runtimes are mapped into this process " + ", ".join(runtimes) +
+                           ": libmk.so was loaded before torch by other code; import torch first")
     vp, i32, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
     pp = C.POINTER(C.c_void_p)
     lib.mk_ag_gemm_workspace.restype = sz
@@ -77,12 +100,12 @@ def load(path: Optional[str] = None):
     lib.mk_gemm_rs_workspace.argtypes = [i64, i64, i64, i32, i32]
     lib.mk_gemm_rs.restype = i32
     lib.mk_gemm_rs.argtypes = [vp, vp, i64, i64, i64, pp, i32, pp, i32,
-                               C.POINTER(mk_launch), vp, sz, vp]
+                               C.POINTER(mk_arrival), pp, C.POINTER(mk_launch), vp, sz, vp]
     lib.mk_gemm_ar_workspace.restype = sz
     lib.mk_gemm_ar_workspace.argtypes = [i64, i64, i64, i32, i32]
     lib.mk_gemm_ar.restype = i32
     lib.mk_gemm_ar.argtypes = [vp, vp, i64, i64, i64, pp, i32, pp, i32,
-                               C.POINTER(mk_launch), vp, sz, vp]
+                               C.POINTER(mk_arrival), pp, C.POINTER(mk_launch), vp, sz, vp]
     lib.mk_moe_dispatch_gemm_workspace.restype = sz
     lib.mk_moe_dispatch_gemm_workspace.argtypes = [i64, i64, i32, i32, i32, i64]
     lib.mk_moe_dispatch_gemm.restype = i32
@@ -261,32 +284,38 @@ def mk_ag_gemm(shards, B, C_out, a_gathered, ws, *, order=None, delay_ns=None, u
     return _check(rc) if check else rc
 
 
-def mk_gemm_rs(A, B, partials, out_owner, ws, *, launch=None, stream=None, check=True) -> int:
-    lib = load()
+def _gemm_reduce(fn, A, B, partials, outs, ws, order, delay_ns, unit_rows, withhold, landing, launch, stream,
+                 check):
     M, K = A.shape
     N = B.shape[1]
-    R = len(out_owner)
+    R = len(outs)
+    arr, keep = make_arrival(order, delay_ns, unit_rows, withhold)
     lau = launch if launch is not None else make_launch()
-    rc = lib.mk_gemm_rs(_ptr(A), _ptr(B), M, K, N, _ptr_array(partials), R, _ptr_array(out_owner),
-                        _dtype_code(out_owner[0]), C.byref(lau), _ptr(ws), ws.numel() * ws.element_size(),
-                        _stream(stream))
+    land = _ptr_array(landing) if landing is not None else None
+    rc = fn(_ptr(A), _ptr(B), M, K, N, _ptr_array(partials), R, _ptr_array(outs), _dtype_code(outs[0]),
+            C.byref(arr) if arr is not None else None, land, C.byref(lau), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(stream))
+    del keep
     return _check(rc) if check else rc
+
+
+def mk_gemm_rs(A, B, partials, out_owner, ws, *, order=None, delay_ns=None, unit_rows=0, withhold=-1,
+               landing=None, launch=None, stream=None, check=True) -> int:
+    """order/delay_ns/unit_rows: optional arrival schedule of the partial sums
+    (units of unit_rows rows of one peer); landing: optional R-1 fp32 [M, N]
+    buffers the copy workgroups move the units into."""
+    return _gemm_reduce(load().mk_gemm_rs, A, B, partials, out_owner, ws, order, delay_ns, unit_rows, withhold,
+                        landing, launch, stream, check)
 
 
 def mk_gemm_ar_workspace(M, K, N, R, out_dtype=MK_F32) -> int:
     return load().mk_gemm_ar_workspace(M, K, N, R, out_dtype)
 
 
-def mk_gemm_ar(A, B, partials, out_rank, ws, *, launch=None, stream=None, check=True) -> int:
-    lib = load()
-    M, K = A.shape
-    N = B.shape[1]
-    R = len(out_rank)
-    lau = launch if launch is not None else make_launch()
-    rc = lib.mk_gemm_ar(_ptr(A), _ptr(B), M, K, N, _ptr_array(partials), R, _ptr_array(out_rank),
-                        _dtype_code(out_rank[0]), C.byref(lau), _ptr(ws), ws.numel() * ws.element_size(),
-                        _stream(stream))
-    return _check(rc) if check else rc
+def mk_gemm_ar(A, B, partials, out_rank, ws, *, order=None, delay_ns=None, unit_rows=0, withhold=-1,
+               landing=None, launch=None, stream=None, check=True) -> int:
+    return _gemm_reduce(load().mk_gemm_ar, A, B, partials, out_rank, ws, order, delay_ns, unit_rows, withhold,
+                        landing, launch, stream, check)
 
 
 def mk_moe_dispatch_gemm(X, logits, W, k, expert_begin, topk_idx, counts, offsets, perm, n_local_rows,

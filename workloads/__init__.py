@@ -98,12 +98,21 @@ class AgWorkload:
 
 @dataclasses.dataclass
 class RsWorkload:
-    """GEMM -> ReduceScatter: A (M x K), B (K x N), R-1 resident fp32 partials (M x N)."""
+    """GEMM -> ReduceScatter: A (M x K), B (K x N), R-1 resident fp32 partials (M x N).
+
+    Optional arrival schedule of the partial sums: unit u = (p - 1) * (M /
+    unit_rows) + b is rows [b * unit_rows, (b + 1) * unit_rows) of partial p
+    (p = 1..R-1); ``order`` is a permutation of the units, ``delay_ns`` their
+    release times.  ``unit_rows`` None: every partial resident from the start.
+    """
     A: np.ndarray                   # uint16[M, K]
     B: np.ndarray                   # uint16[K, N]
     partials: List[np.ndarray]      # (R-1) x float32[M, N]
     R: int
     out_dtype: str
+    order: Optional[np.ndarray] = None      # int32[(R-1) * M / unit_rows]
+    delay_ns: Optional[np.ndarray] = None   # uint32[(R-1) * M / unit_rows]
+    unit_rows: Optional[int] = None
 
     @property
     def M(self): return self.A.shape[0]
@@ -198,9 +207,13 @@ def make_ag(R: int, m_shard: int, K: int, N: int, *, seed: int = 0, dist: str = 
 
 
 def make_rs(M: int, K: int, N: int, R: int, *, seed: int = 0, dist: str = "normal",
-            out_dtype: str = "f32") -> RsWorkload:
-    """GEMM->ReduceScatter inputs. Stream order: A, B, partial 1..R-1."""
-    st = _streams(seed, 2 + (R - 1))
+            out_dtype: str = "f32", unit_rows: Optional[int] = None, max_delay_ns: int = 0) -> RsWorkload:
+    """GEMM->ReduceScatter inputs. Stream order: A, B, partial 1..R-1, schedule.
+
+    unit_rows (optional): the partial sums arrive in units of (peer, row
+    block of unit_rows rows), in a seeded order with release delays uniform
+    in [0, max_delay_ns]."""
+    st = _streams(seed, 2 + (R - 1) + 1)
     if dist == "normal":
         A = _normal_bf16(st[0], (M, K), 1.0)
         B = _normal_bf16(st[1], (K, N), 1.0 / K)
@@ -212,7 +225,18 @@ def make_rs(M: int, K: int, N: int, R: int, *, seed: int = 0, dist: str = "norma
              for p in range(R - 1)]
     else:
         raise ValueError(dist)
-    return RsWorkload(A, B, P, R, out_dtype)
+    if unit_rows is None:
+        return RsWorkload(A, B, P, R, out_dtype)
+    if M % unit_rows:
+        raise ValueError("unit_rows must divide M")
+    n_units = (R - 1) * (M // unit_rows)
+    sch = st[2 + (R - 1)]
+    order = sch.permutation(n_units).astype(np.int32)
+    if max_delay_ns > 0:
+        delay = sch.integers(0, max_delay_ns, size=n_units, endpoint=True).astype(np.uint32)
+    else:
+        delay = np.zeros(n_units, np.uint32)
+    return RsWorkload(A, B, P, R, out_dtype, order, delay, unit_rows)
 
 
 def zipf_gumbel_logits(rng: np.random.Generator, T: int, E: int, s: float) -> np.ndarray:
