@@ -164,6 +164,29 @@ int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * AllGather -> GEMM without a workspace argument.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments and results as mk_ag_gemm, but the workspace is a
+ * fixed 4 KiB device array inside the library (one per GPU, held until the
+ * process ends); the call allocates nothing.  On its first call on a device
+ * the library looks up that array's address (hipGetSymbolAddress, with the
+ * device current); every call clears it with a fill kernel on `stream` before
+ * the operation's kernels (no memset node).
+ *   All calls on one GPU share the array: calls that overlap on one GPU (on
+ *   different streams without ordering between them, or from several host
+ *   threads) race and give undefined results.  Order them.
+ *   The workspace needed (mk_ag_gemm_workspace) must fit in 4 KiB, else
+ *   MK_ERR_UNSUPPORTED.  arrival->withhold must be -1 (MK_ERR_INVALID
+ *   otherwise): with no workspace there is no status for mk_poll_status, so
+ *   a watchdog expiry is not reported (the kernels still exit).
+ * ------------------------------------------------------------------------- */
+int mk_ag_gemm_noalloc(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
+                       const void* B, int64_t N, void* C, int c_dtype, void* a_gathered,
+                       const mk_arrival* arrival, const mk_launch* launch, void* stream);
+
+/* ---------------------------------------------------------------------------
  * GEMM -> ReduceScatter  ([P1] "Los cinco núcleos fusionados", row
  * GEMM + ReduceScatter)
  *

@@ -95,6 +95,30 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
     assert _ag(lib) == mk.MK_ERR_HIP
 
 
+def _ag_noalloc(lib, R=2, m=64, K=128, N=64, c_dtype=mk.MK_BF16, arrival=None, shards=None, launch=None):
+    sh = (C.c_void_p * R)(*([FAKE] * R)) if shards is None else shards
+    return lib.mk_ag_gemm_noalloc(sh, R, m, K, FAKE, N, FAKE, c_dtype, FAKE, arrival, launch, None)
+
+
+def test_ag_noalloc_validation(lib):
+    # the same argument checks as mk_ag_gemm, before any HIP call
+    assert _ag_noalloc(lib, R=0) == mk.MK_ERR_UNSUPPORTED
+    assert _ag_noalloc(lib, K=100) == mk.MK_ERR_UNSUPPORTED
+    assert _ag_noalloc(lib, c_dtype=7) == mk.MK_ERR_INVALID
+    assert _ag_noalloc(lib, shards=(C.c_void_p * 2)(FAKE, FAKE + 2)) == mk.MK_ERR_INVALID
+    arr, keep = mk.make_arrival([0, 1, 1, 3], None, 32, -1)
+    assert _ag_noalloc(lib, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE
+    # a withheld unit could only be reported through a workspace's status
+    arr, keep = mk.make_arrival([0, 1, 2, 3], None, 32, 2)
+    assert _ag_noalloc(lib, arrival=C.byref(arr)) == mk.MK_ERR_INVALID
+    assert b"withhold" in lib.mk_last_error()
+    lau = mk.make_launch(mode=4)
+    assert _ag_noalloc(lib, launch=C.byref(lau)) == mk.MK_ERR_INVALID
+    import torch
+    if not torch.cuda.is_available():                  # valid: the first HIP call fails cleanly
+        assert _ag_noalloc(lib) == mk.MK_ERR_HIP
+
+
 def _rs(lib, M=512, K=64, N=64, R=4, out_dtype=mk.MK_F32, ws_bytes=1 << 24, partials=True, lau=None,
         arrival=None, landing=None):
     P = (C.c_void_p * R)(*([FAKE] * R))

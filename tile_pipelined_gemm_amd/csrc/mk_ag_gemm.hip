@@ -20,6 +20,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "mk_device.h"
 #include "mk_gemm_dma.h"
@@ -227,9 +228,38 @@ extern "C" size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_
   return sizeof(WsHeader) + MK_MAX_UNITS * sizeof(uint32_t);
 }
 
+// ------------------------------------------------- entry point without allocation
+// mk_ag_gemm_noalloc keeps its workspace (header and per-unit arrival
+// counters) in this file-scope device array instead of a caller buffer.  Each
+// GPU holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// its device address is looked up once per device with hipGetSymbolAddress,
+// with that device current, and only that address is used.
+constexpr size_t AG_SCRATCH_BYTES = 4096;
+static __device__ __align__(256) uint32_t scratch[AG_SCRATCH_BYTES / 4];
+
+// Device address of `scratch` on device `dev` (looked up on first use).
+static int scratch_address(int dev, void** out) {
+  static std::mutex mu;
+  static void* addr[64];
+  if (dev < 0 || dev >= 64) return mkh::fail(MK_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return mkh::hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return mkh::fail(MK_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return MK_OK;
+}
+
+// clear_bytes > 0: zero that many workspace bytes (fill kernel) on the
+// stream before the first launch.
 template <class G>
 static int run_ag(AgParams& p, const mk_launch& o, const mkh::Schedule& s, const mkh::DevInfo* d,
-                  hipStream_t st) {
+                  hipStream_t st, size_t clear_bytes) {
   p.tiles_m = (p.M + G::BM - 1) / G::BM;
   p.tiles_n = (p.N + G::BN - 1) / G::BN;
   p.n_tiles = p.tiles_m * p.tiles_n;
@@ -253,6 +283,10 @@ static int run_ag(AgParams& p, const mk_launch& o, const mkh::Schedule& s, const
   const int full = d->n_cu * occ;
   const int grid = o.grid > 0 ? std::min(o.grid, full) : full;
   const uint32_t n_work = (uint32_t)p.n_units * p.parts;
+  if (clear_bytes) {
+    const int rc = mkh::zero_fill(p.hdr, clear_bytes, st);
+    if (rc) return rc;
+  }
 
   if (o.mode >= 1) {   // unfused baseline: copy kernel, then GEMM kernel (modes 2/3: one of them)
     if (o.mode != 3) {
@@ -282,10 +316,11 @@ static int run_ag(AgParams& p, const mk_launch& o, const mkh::Schedule& s, const
   return MK_OK;
 }
 
-extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
-                          const void* B, int64_t N, void* C, int c_dtype, void* a_gathered,
-                          const mk_arrival* arrival, const mk_launch* launch,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+// mk_ag_gemm, and (no_alloc) mk_ag_gemm_noalloc, whose workspace is the
+// device's `scratch` array, cleared on the stream before the kernel.
+static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K, const void* B, int64_t N,
+                   void* C, int c_dtype, void* a_gathered, const mk_arrival* arrival, const mk_launch* launch,
+                   void* workspace, size_t workspace_bytes, void* stream, bool no_alloc) {
   using mkh::fail;
   if (!a_shards) return fail(MK_ERR_INVALID, "a_shards is NULL");
   if (R < 1 || R > MK_MAX_RANKS) return fail(MK_ERR_UNSUPPORTED, "R=%d outside [1,%d]", R, MK_MAX_RANKS);
@@ -304,10 +339,18 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   mkh::Schedule s;
   int rc = mkh::make_schedule(arrival, M, R, &s);
   if (rc) return rc;
-  if (!workspace) return fail(MK_ERR_WORKSPACE, "workspace is NULL");
-  if (workspace_bytes < mk_ag_gemm_workspace(R, m_shard, K, N, s.unit_rows))
-    return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes,
-                mk_ag_gemm_workspace(R, m_shard, K, N, s.unit_rows));
+  const size_t ws_need = mk_ag_gemm_workspace(R, m_shard, K, N, s.unit_rows);
+  if (no_alloc) {
+    if (s.withhold != -1)
+      return fail(MK_ERR_INVALID, "withhold is not available without a workspace (no status to poll)");
+    if (ws_need > AG_SCRATCH_BYTES)
+      return fail(MK_ERR_UNSUPPORTED, "needs %zu bytes of scratch, the built-in array holds %zu", ws_need,
+                  AG_SCRATCH_BYTES);
+  } else {
+    if (!workspace) return fail(MK_ERR_WORKSPACE, "workspace is NULL");
+    if (workspace_bytes < ws_need)
+      return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, ws_need);
+  }
   const mk_launch o = mkh::launch_opts(launch);
   if (o.mode < 0 || o.mode > 3) return fail(MK_ERR_INVALID, "mode %d", o.mode);
   if (o.grid < 0 || o.n_copy < 0 || o.copy_kib < 0) return fail(MK_ERR_INVALID, "negative grid, n_copy or copy_kib");
@@ -315,6 +358,10 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   if (o.queue_mode < 0 || o.queue_mode > 1) return fail(MK_ERR_INVALID, "queue_mode %d", o.queue_mode);
   const mkh::DevInfo* d = mkh::dev_info();
   if (!d) return MK_ERR_HIP;
+  if (no_alloc) {
+    rc = scratch_address(d->device, &workspace);
+    if (rc) return rc;
+  }
 
   AgParams p;
   memset(&p, 0, sizeof p);
@@ -354,6 +401,7 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
     p.delay_ticks[j] = (uint32_t)mkh::ns_to_ticks(s.delay_ns[j], d->wall_khz);
   }
   const hipStream_t st = (hipStream_t)stream;
+  const size_t clear = no_alloc ? ws_need : 0;
   int tile = o.tile ? o.tile : mk_default_tile(M, N, K);
   // The 256x256 tile switches to the direct-to-LDS engine by default.  A
   // single 128-row tile row (a skinny A, the GEMM streams B) takes the
@@ -375,16 +423,31 @@ extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, i
   if (tile == TILE_256x256_DMA_W8 && !TileGemmD<256, 256, true, 4, 8>::supports_k((int)K))
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
   switch (tile) {
-    case TILE_256x256: return run_ag<TileGemm<256, 256, 2, 2>>(p, o, s, d, st);
-    case TILE_128x128: return run_ag<TileGemm<128, 128, 2, 2>>(p, o, s, d, st);
-    case TILE_256x128: return run_ag<TileGemm<256, 128, 2, 2>>(p, o, s, d, st);
-    case TILE_128x256: return run_ag<TileGemm<128, 256, 2, 2>>(p, o, s, d, st);
-    case TILE_256x256_DMA: return run_ag<TileGemmD<256, 256>>(p, o, s, d, st);
-    case TILE_128x128_DMA: return run_ag<TileGemmD<128, 128>>(p, o, s, d, st);
-    case TILE_256x128_DMA: return run_ag<TileGemmD<256, 128>>(p, o, s, d, st);
-    case TILE_128x256_DMA: return run_ag<TileGemmD<128, 256>>(p, o, s, d, st);
-    case TILE_128x128_DMA8: return run_ag<TileGemmD<128, 128, true, 8>>(p, o, s, d, st);
-    case TILE_256x256_DMA_W8: return run_ag<TileGemmD<256, 256, true, 4, 8>>(p, o, s, d, st);
+    case TILE_256x256: return run_ag<TileGemm<256, 256, 2, 2>>(p, o, s, d, st, clear);
+    case TILE_128x128: return run_ag<TileGemm<128, 128, 2, 2>>(p, o, s, d, st, clear);
+    case TILE_256x128: return run_ag<TileGemm<256, 128, 2, 2>>(p, o, s, d, st, clear);
+    case TILE_128x256: return run_ag<TileGemm<128, 256, 2, 2>>(p, o, s, d, st, clear);
+    case TILE_256x256_DMA: return run_ag<TileGemmD<256, 256>>(p, o, s, d, st, clear);
+    case TILE_128x128_DMA: return run_ag<TileGemmD<128, 128>>(p, o, s, d, st, clear);
+    case TILE_256x128_DMA: return run_ag<TileGemmD<256, 128>>(p, o, s, d, st, clear);
+    case TILE_128x256_DMA: return run_ag<TileGemmD<128, 256>>(p, o, s, d, st, clear);
+    case TILE_128x128_DMA8: return run_ag<TileGemmD<128, 128, true, 8>>(p, o, s, d, st, clear);
+    case TILE_256x256_DMA_W8: return run_ag<TileGemmD<256, 256, true, 4, 8>>(p, o, s, d, st, clear);
     default: return fail(MK_ERR_INVALID, "tile id %d", tile);
   }
+}
+
+extern "C" int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
+                          const void* B, int64_t N, void* C, int c_dtype, void* a_gathered,
+                          const mk_arrival* arrival, const mk_launch* launch,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return ag_gemm(a_shards, R, m_shard, K, B, N, C, c_dtype, a_gathered, arrival, launch, workspace,
+                 workspace_bytes, stream, false);
+}
+
+extern "C" int mk_ag_gemm_noalloc(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
+                                  const void* B, int64_t N, void* C, int c_dtype, void* a_gathered,
+                                  const mk_arrival* arrival, const mk_launch* launch, void* stream) {
+  return ag_gemm(a_shards, R, m_shard, K, B, N, C, c_dtype, a_gathered, arrival, launch, nullptr, 0, stream,
+                 true);
 }

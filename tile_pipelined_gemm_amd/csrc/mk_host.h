@@ -39,6 +39,10 @@ struct Schedule {
 // order, zero delay) against `total_rows`.  Returns MK_OK or an error code.
 int make_schedule(const mk_arrival* a, int64_t total_rows, int default_units, Schedule* out);
 
+// Zero `bytes` (a multiple of 4) at device address p with a fill kernel on
+// stream st (never a memset node).  MK_OK or MK_ERR_HIP.
+int zero_fill(void* p, size_t bytes, hipStream_t st);
+
 // Resolved launch options (0 fields replaced by defaults by each op).
 mk_launch launch_opts(const mk_launch* l);
 uint64_t spin_ticks(const mk_launch& l, const DevInfo* d);

@@ -107,9 +107,6 @@ uint64_t spin_ticks(const mk_launch& l, const DevInfo* d) {
   return ns_to_ticks(us * 1000ull, d->wall_khz);
 }
 
-}  // namespace mkh
-
-// ---------------------------------------------------------------- support ABI
 namespace {
 __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -117,16 +114,23 @@ __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
 }
 }  // namespace
 
+int zero_fill(void* p, size_t bytes, hipStream_t st) {
+  const size_t n = bytes / 4;
+  const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, st, (uint32_t*)p, n);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MK_OK : hip_fail(e, "fill kernel launch");
+}
+
+}  // namespace mkh
+
+// ---------------------------------------------------------------- support ABI
 extern "C" int mk_workspace_init(void* ws, size_t bytes, void* stream) {
   if (!ws) return mkh::fail(MK_ERR_WORKSPACE, "workspace is NULL");
   if (bytes < sizeof(mk::WsHeader) || (bytes & 3u))
     return mkh::fail(MK_ERR_WORKSPACE, "workspace size %zu too small or not a multiple of 4", bytes);
   if (!mkh::aligned16(ws)) return mkh::fail(MK_ERR_INVALID, "workspace not 16-byte aligned");
-  const size_t n = bytes / 4;
-  const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (uint32_t*)ws, n);
-  hipError_t e = hipGetLastError();
-  return e == hipSuccess ? MK_OK : mkh::hip_fail(e, "fill kernel launch");
+  return mkh::zero_fill(ws, bytes, (hipStream_t)stream);
 }
 
 extern "C" int mk_poll_status(void* ws, void* stream) {

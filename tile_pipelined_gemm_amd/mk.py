@@ -26,7 +26,7 @@ TILE_256x256_DMA_W8 = 10
 
 # Symbols declared in include/mk.h (checked by the CPU tests).
 EXPORTS = [
-    "mk_ag_gemm_workspace", "mk_ag_gemm", "mk_gemm_rs_workspace", "mk_gemm_rs",
+    "mk_ag_gemm_workspace", "mk_ag_gemm", "mk_ag_gemm_noalloc", "mk_gemm_rs_workspace", "mk_gemm_rs",
     "mk_gemm_ar_workspace", "mk_gemm_ar",
     "mk_moe_dispatch_gemm_workspace", "mk_moe_dispatch_gemm", "mk_moe_combine_workspace", "mk_moe_combine",
     "mk_ring_attn_workspace", "mk_ring_attn",
@@ -96,6 +96,9 @@ def load(path: Optional[str] = None):
     lib.mk_ag_gemm.restype = i32
     lib.mk_ag_gemm.argtypes = [pp, i32, i64, i64, vp, i64, vp, i32, vp,
                                C.POINTER(mk_arrival), C.POINTER(mk_launch), vp, sz, vp]
+    lib.mk_ag_gemm_noalloc.restype = i32
+    lib.mk_ag_gemm_noalloc.argtypes = [pp, i32, i64, i64, vp, i64, vp, i32, vp,
+                                       C.POINTER(mk_arrival), C.POINTER(mk_launch), vp]
     lib.mk_gemm_rs_workspace.restype = sz
     lib.mk_gemm_rs_workspace.argtypes = [i64, i64, i64, i32, i32]
     lib.mk_gemm_rs.restype = i32
@@ -280,6 +283,22 @@ def mk_ag_gemm(shards, B, C_out, a_gathered, ws, *, order=None, delay_ns=None, u
     rc = lib.mk_ag_gemm(_ptr_array(shards), R, m_shard, K, _ptr(B), N, _ptr(C_out), _dtype_code(C_out),
                         _ptr(a_gathered), C.byref(arr) if arr is not None else None, C.byref(lau),
                         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    del keep
+    return _check(rc) if check else rc
+
+
+def mk_ag_gemm_noalloc(shards, B, C_out, a_gathered, *, order=None, delay_ns=None, unit_rows=0, launch=None,
+                       stream=None, check=True) -> int:
+    """mk_ag_gemm with the library's built-in scratch instead of a workspace."""
+    lib = load()
+    R = len(shards)
+    m_shard, K = shards[0].shape
+    N = B.shape[1]
+    arr, keep = make_arrival(order, delay_ns, unit_rows or m_shard, -1)
+    lau = launch if launch is not None else make_launch()
+    rc = lib.mk_ag_gemm_noalloc(_ptr_array(shards), R, m_shard, K, _ptr(B), N, _ptr(C_out), _dtype_code(C_out),
+                                _ptr(a_gathered), C.byref(arr) if arr is not None else None, C.byref(lau),
+                                _stream(stream))
     del keep
     return _check(rc) if check else rc
 
