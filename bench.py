@@ -31,6 +31,17 @@ def log(*a):
 
 AG_KERNEL_SOURCES = ["mk_ag_gemm.hip", "mk_device.h", "mk_gemm_dma.h", "mk_host.h", "mk_host.hip", "mk_tiles.h"]
 AG_COUNTERS = os.path.join(ROOT, "profiles", "ag_gemm_8192x8192x3584_counters.md")
+_COMMON = ["mk_device.h", "mk_gemm_dma.h", "mk_host.h", "mk_host.hip", "mk_tiles.h"]
+# per workload: (bound, kernel sources whose hash the counter summary records, summary)
+ROOFLINES = {
+    "ag": ("mfma", AG_KERNEL_SOURCES, AG_COUNTERS),
+    "skinny_ag": ("hbm", AG_KERNEL_SOURCES, os.path.join(ROOT, "profiles", "skinny_ag_128x8192x28672.md")),
+    "rs": ("hbm", ["mk_gemm_rs.hip"] + _COMMON, os.path.join(ROOT, "profiles", "gemm_rs_8192x3584x8192_r8.md")),
+    "ar": ("hbm", ["mk_gemm_rs.hip"] + _COMMON, os.path.join(ROOT, "profiles", "gemm_ar_8192x3584x8192_r8.md")),
+    "moe": ("mfma", ["mk_moe.hip"] + _COMMON,
+            os.path.join(ROOT, "profiles", "moe_dispatch_gemm_t4096_h7168_e256_k8_f2048.md")),
+    "ring": ("mfma", ["mk_ring_attn.hip"] + _COMMON, os.path.join(ROOT, "profiles", "ring_attn_16x4096x128_r8.md")),
+}
 
 
 def counter_traffic(sources, summary, csrc=os.path.join(ROOT, "tile_pipelined_gemm_amd", "csrc")):
@@ -64,6 +75,7 @@ def parse():
     ap.add_argument("--only", default="", help="comma list of workloads to run (ag,skinny_ag,rs,ar,moe)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the unfused and library yardsticks")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA and HBM peaks")
     ap.add_argument("--copies", type=int, default=0, help="rotated input copies (0 = auto)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--ag-launch", default="",
@@ -224,6 +236,13 @@ def bench_rs(args, stream, extra=True):
         _, uk = timed(lambda i: probs[i % copies].run(launch=lau, stream=stream, check=False), 3, 1, stream)
         r["unfused_ms"] = uk
         r["speedup_vs_unfused"] = uk / kern
+        # the baseline's phases alone: its GEMM kernel (to fp32 staging) and its reduce kernel
+        for tag, md in (("gemm_only", 3), ("reduce_only", 2)):
+            lv = mk.make_launch(mode=md)
+            _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 3, 1, stream)
+            r[f"variant_{tag}_ms"] = vk
+        tg, tr = r["variant_gemm_only_ms"], r["variant_reduce_only_ms"]
+        r["overlap_eff"] = (tg + tr - kern) / min(tg, tr)
     return r
 
 
@@ -305,16 +324,15 @@ def bench_moe(args, stream, extra=True):
         r["combine_gbs"] = cbytes / ck / 1e6
         r["combine_hbm_frac"] = cbytes / ck / 1e6 / PEAK_HBM_GBS
         del Yp
-        for tag, kw in [("n_copy64", dict(n_copy=64)), ("n_copy128", dict(n_copy=128)),
-                        ("xcd_queues", dict(queue_mode=1)), ("xcd_queues_n_copy128", dict(queue_mode=1, n_copy=128)),
-                        ("unfused_xcd_queues", dict(mode=1, queue_mode=1)),
-                        ("tile_reg", dict(tile=mk.TILE_256x256)),
-                        ("tile_128x256dma", dict(tile=mk.TILE_128x256_DMA)),
-                        ("tile_256x128dma", dict(tile=mk.TILE_256x128_DMA)),
-                        ("tile_128x128dma", dict(tile=mk.TILE_128x128_DMA))]:
+        for tag, kw in [("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
+                        ("n_copy128", dict(n_copy=128)), ("xcd_queues", dict(queue_mode=1)),
+                        ("expert_order", dict(queue_mode=2)), ("hold", dict(queue_mode=3)),
+                        ("tile_128x256dma", dict(tile=mk.TILE_128x256_DMA))]:
             lv = mk.make_launch(**kw)
             _, vk = timed(lambda i: probs[i % copies].run(launch=lv, stream=stream, check=False), 5, 2, stream)
             r[f"variant_{tag}_ms"] = vk
+        tc, tg = r["variant_copy_only_ms"], r["variant_gemm_only_ms"]
+        r["overlap_eff"] = (tc + tg - kern) / min(tc, tg)
     return r
 
 
@@ -352,6 +370,66 @@ def bench_ring(args, stream, extra=True):
             _, vk = timed(lambda i: prob.run(launch=lv, stream=stream, check=False), 3, 1, stream)
             r[f"variant_{tag}_ms"] = vk
     return r
+
+
+def bench_peaks(stream):
+    """Rates measured on this device (mk_peak_*): an MFMA-only bf16 loop on
+    every CU with the average engine clock during it, an HBM read stream and
+    an HBM copy.  Reported beside the published peaks (which stay the roofline
+    denominators)."""
+    import torch
+    from tile_pipelined_gemm_amd import mk
+    ws = mk.workspace(mk.load().mk_peak_workspace())
+    khz = mk.mk_wall_clock_khz()
+    iters = 4096
+    state = {}
+
+    def mfma(i):
+        state["f"], state["n"] = mk.mk_peak_mfma(iters, ws, stream=stream)
+
+    settle(mfma, 0.3)
+    _, mk_ms = timed(mfma, 10, 3, stream)
+    ck = ws[256:256 + 16 * state["n"]].view(torch.int64).cpu().numpy().reshape(-1, 2)
+    clock_ghz = float(ck[:, 0].sum()) / float(ck[:, 1].sum()) * khz / 1e6
+    src = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    moved = {}
+
+    def rd(i):
+        moved["r"] = mk.mk_peak_hbm(src, None, 0, ws, stream=stream)
+
+    _, rd_ms = timed(rd, 10, 3, stream)
+    half = src[:2 << 30]
+    dst = src[2 << 30:]
+
+    def cp(i):
+        moved["c"] = mk.mk_peak_hbm(half, dst, 1, ws, stream=stream)
+
+    _, cp_ms = timed(cp, 10, 3, stream)
+    del src, half, dst
+    return dict(mfma_bf16_tflops=state["f"] / mk_ms / 1e9, mfma_loop_clock_ghz=clock_ghz,
+                mfma_frac_of_published=state["f"] / mk_ms / 1e9 / PEAK_BF16_TFLOPS,
+                hbm_read_gbs=moved["r"] / rd_ms / 1e6, hbm_copy_gbs=moved["c"] / cp_ms / 1e6,
+                published_bf16_tflops=PEAK_BF16_TFLOPS, published_hbm_gbs=PEAK_HBM_GBS)
+
+
+def roofline(name, r, peaks):
+    """Roofline object of workload `name` from its result r: algorithmic work
+    per launch over the mean launch time, against the published peak (and the
+    measured one), with the counter-measured HBM traffic when the committed
+    summary was taken on the current kernel sources."""
+    bound, sources, summary = ROOFLINES[name]
+    if bound == "mfma":
+        achieved, peak, unit = r["flops"] / r["kernel_ms"] / 1e9, PEAK_BF16_TFLOPS, "TFLOP/s"
+        measured = peaks.get("mfma_bf16_tflops") if peaks else None
+    else:
+        achieved, peak, unit = r["alg_bytes"] / r["kernel_ms"] / 1e6, PEAK_HBM_GBS, "GB/s"
+        measured = peaks.get("hbm_read_gbs") if peaks else None
+    out = dict(bound=bound, achieved=round(achieved, 2), peak=peak, unit=unit, frac=round(achieved / peak, 4),
+               traffic=counter_traffic(sources, summary))
+    if measured:
+        out["frac_of_measured_peak"] = round(achieved / measured, 4)
+    return out
 
 
 def cpu_baseline(seed):
@@ -445,6 +523,16 @@ def main():
     if want("ring"):
         log("bench: ring")
         configs["ring"] = bench_ring(args, stream, extra)
+    peaks = None
+    if not args.no_peaks:
+        log("bench: peaks")
+        peaks = bench_peaks(stream)
+    for k, v in configs.items():
+        if k in ROOFLINES:
+            v["roofline"] = roofline(k, v, peaks)
+        if k == "moe" and "combine_gbs" in v:
+            v["combine_roofline"] = dict(bound="hbm", achieved=round(v["combine_gbs"], 2), peak=PEAK_HBM_GBS,
+                                         unit="GB/s", frac=round(v["combine_gbs"] / PEAK_HBM_GBS, 4), traffic=None)
     cpu = None
     if primary is not None and not args.no_cpu:
         log("bench: cpu baseline")
@@ -476,6 +564,7 @@ def main():
                      "frac": round(primary["flops"] / primary["kernel_ms"] / 1e9 / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,
+        "peaks_measured": {k: round(v, 4) for k, v in peaks.items()} if peaks else None,
         "configs": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in configs.items()},
     }

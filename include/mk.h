@@ -93,9 +93,13 @@ typedef struct mk_arrival {
 typedef struct mk_launch {
   int32_t mode;           /* 0 fused persistent kernel; 1 unfused baseline:
                              the same steps as separate kernels in stream order;
-                             AG only, for measurement: 2 = the baseline's copy
-                             kernel alone, 3 = its GEMM kernel alone (reads
-                             a_gathered as it is) */
+                             for measurement, one phase of the baseline alone:
+                             AG 2 = the copy kernel, 3 = the GEMM kernel (reads
+                             a_gathered as it is); GEMM+RS/AR (no arrival) 2 =
+                             the reduce kernel (on what is staged), 3 = the GEMM
+                             kernel; MoE 2 = routing and the permute kernel,
+                             3 = routing and the grouped GEMM kernel (reads Xs
+                             as it is) */
   int32_t grid;           /* persistent workgroups; 0 = CUs x occupancy */
   int32_t n_copy;         /* copy-role workgroups (AG, MoE, GEMM+RS/AR with an
                              arrival schedule); 0 = default
@@ -133,10 +137,16 @@ typedef struct mk_launch {
                              1 = 8 per-XCD queues (the tiles that share an A
                              row block run on one XCD and share its L2; a
                              drained queue's workgroups help the others).
-                             MoE: 1 = 8 per-XCD queues keyed by tile column
-                             (when the tile columns split evenly over them:
-                             the tiles on one XCD share the same column blocks
-                             of the expert weights); 0 = one queue */
+                             MoE (fused): 0 = one queue of M-tiles in readiness
+                             order (the latest arrival position among the source
+                             blocks their rows come from); 1 = the same order in 8
+                             per-XCD queues keyed by tile column (when the tile
+                             columns split evenly over them: the tiles on one XCD
+                             share the same column blocks of the expert weights);
+                             2 = one queue in expert order; 3 = expert order with
+                             every tile held until all copy items have landed;
+                             4 = as 3 in per-XCD queues; 5 = expert order in
+                             per-XCD queues */
 } mk_launch;
 
 /* ---------------------------------------------------------------------------
@@ -347,6 +357,28 @@ int mk_ring_attn(const void* Q, const void* const* k_shards, const void* const* 
                  int64_t S, int D, void* O, int o_dtype, void* k_recv, void* v_recv,
                  const mk_arrival* arrival, const mk_launch* launch, void* workspace,
                  size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement (the rates the operations are compared with; not part of the
+ * hot path)
+ *
+ * mk_peak_mfma: an MFMA-only loop on every CU (two 256-thread workgroups per
+ * CU, each wave `iters` rounds of 16 bf16 32x32x16 MFMA updates on 8
+ * independent accumulators, the operands rotating through 8 random register
+ * fragments so that they switch as in a GEMM on real data).  *flops = floating-point operations of the launch (time
+ * it with events on `stream`); *waves = waves launched.  The workspace
+ * (mk_peak_workspace() bytes, device) receives at byte offset 256 one pair
+ * of uint64 per wave: {core clock ticks, wall clock ticks} of its loop, from
+ * which the average engine clock under a full MFMA load follows.
+ * mk_peak_hbm: mode 0 reads `bytes` of src (16-byte loads, every CU), mode 1
+ * copies them to dst; *bytes_moved = bytes read plus written (the region is
+ * rounded down to whole 64 KiB per workgroup).  Limits: iters in [1, 2^24];
+ * each workgroup's region below 2 GiB.
+ * ------------------------------------------------------------------------- */
+size_t mk_peak_workspace(void);
+int mk_peak_mfma(int iters, void* workspace, size_t workspace_bytes, double* flops, int* waves, void* stream);
+int mk_peak_hbm(const void* src, void* dst, size_t bytes, int mode, void* workspace, size_t workspace_bytes,
+                double* bytes_moved, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Support

@@ -207,6 +207,20 @@ def test_rs_landing_rules(lib):
     assert _rs(lib, arrival=arr, landing=mis) == mk.MK_ERR_INVALID  # misaligned
     lau = mk.make_launch(n_copy=-1)
     assert _rs(lib, arrival=arr, lau=C.byref(lau)) == mk.MK_ERR_INVALID
+    lau = mk.make_launch(mode=2)                                   # one phase alone: no schedule
+    assert _rs(lib, arrival=arr, lau=C.byref(lau)) == mk.MK_ERR_INVALID
+    lau = mk.make_launch(mode=4)
+    assert _rs(lib, lau=C.byref(lau)) == mk.MK_ERR_INVALID
+
+
+def test_peak_probe_validation(lib):
+    f, n, b = C.c_double(0), C.c_int(0), C.c_double(0)
+    assert lib.mk_peak_mfma(0, FAKE, 1 << 20, C.byref(f), C.byref(n), None) == mk.MK_ERR_INVALID
+    assert lib.mk_peak_mfma(10, None, 1 << 20, C.byref(f), C.byref(n), None) == mk.MK_ERR_WORKSPACE
+    assert lib.mk_peak_hbm(FAKE, FAKE, 1 << 30, 2, FAKE, 4096, C.byref(b), None) == mk.MK_ERR_INVALID
+    assert lib.mk_peak_hbm(None, FAKE, 1 << 30, 0, FAKE, 4096, C.byref(b), None) == mk.MK_ERR_INVALID
+    assert lib.mk_peak_hbm(FAKE, None, 1 << 30, 1, FAKE, 4096, C.byref(b), None) == mk.MK_ERR_INVALID
+    assert lib.mk_peak_workspace() >= 256
 
 
 def test_rs_workspace_sizes(lib):
@@ -233,7 +247,7 @@ def test_moe_validation(lib):
     arr, keep = mk.make_arrival([0, 1, 1, 3], None, 64)
     assert _moe(lib, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE
     # launch options are checked before any HIP call
-    for bad in (dict(mode=2), dict(grid=-1), dict(n_copy=-1), dict(queue_mode=2), dict(queue_mode=-1)):
+    for bad in (dict(mode=4), dict(mode=-1), dict(grid=-1), dict(n_copy=-1), dict(queue_mode=6), dict(queue_mode=-1)):
         lau = mk.make_launch(**bad)
         assert _moe(lib, lau=C.byref(lau)) == mk.MK_ERR_INVALID, bad
 

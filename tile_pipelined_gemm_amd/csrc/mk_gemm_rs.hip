@@ -85,50 +85,70 @@ __device__ __forceinline__ float* stage_ptr(const RsParams& p, int gr, int gc) {
   return (float*)p.out[o] + (int64_t)(gr - o * p.mb) * p.N + gc;
 }
 
-// Reduce one staged tile: out = stage + P_1 + ... + P_{R-1}, 4 columns per access.
+// Reduce one staged tile: out = stage + P_1 + ... + P_{R-1}, 4 columns per
+// access, in that fixed order.  Each thread takes UNROLL 4-column runs; for
+// each group of up to PG partial sums every load is issued before the first
+// add (PG x UNROLL 16-byte loads in flight per thread), so the kernel streams
+// instead of waiting one load latency per partial.  All accesses go through
+// buffer descriptors bounded to the tile's rows; a run past N gets the
+// out-of-range offset (loads return zero, stores are dropped).
 template <int BM, int BN>
 __device__ __forceinline__ void reduce_tile(const RsParams& p, int t) {
   const int tm = t / p.tiles_n, tn = t % p.tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
-  constexpr int V = BN / 4;                  // float4 per tile row
-  constexpr int UNROLL = 4;
+  constexpr int V = BN / 4;                  // 4-column runs per tile row
+  constexpr int UNROLL = 4, PG = 8;
   const int nt = blockDim.x;
+  const int rows = min(BM, p.M - m0);
+  const int o = m0 / p.mb;                   // a tile never straddles two owners
+  const uint32_t rb4 = (uint32_t)p.N * 4u;
+  const uint32_t esz = p.out_bf16 ? 2u : 4u, rbo = (uint32_t)p.N * esz;
+  const uint32_t in_bytes = uni((uint32_t)rows * rb4), out_bytes = uni((uint32_t)rows * rbo);
+  const __amdgpu_buffer_rsrc_t ds = make_rsrc(uni(stage_ptr(p, m0, 0)), in_bytes);
+  const int64_t dofs = (int64_t)(m0 - o * p.mb) * p.N * esz;
+  const int nq = p.R - 1;
   for (int base = 0; base < BM * V; base += nt * UNROLL) {
+    uint32_t vin[UNROLL], vout[UNROLL];
     f32x4 v[UNROLL];
-    int gr[UNROLL], gc[UNROLL];
-    bool ok[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int idx = base + u * nt + threadIdx.x;
-      gr[u] = m0 + idx / V;
-      gc[u] = n0 + (idx % V) * 4;
-      ok[u] = idx < BM * V && gr[u] < p.M && gc[u] < p.N;
-      if (ok[u]) v[u] = *(const f32x4*)stage_ptr(p, gr[u], gc[u]);
+      const int r = idx / V, c = n0 + (idx % V) * 4;
+      const bool ok = idx < BM * V && r < rows && c < p.N;
+      vin[u] = ok ? (uint32_t)r * rb4 + (uint32_t)c * 4u : OOB;
+      vout[u] = ok ? (uint32_t)r * rbo + (uint32_t)c * esz : OOB;
+      v[u] = __builtin_bit_cast(f32x4, bload(ds, vin[u], 0));
     }
-    for (int q = 0; q < p.R - 1; ++q) {
+    for (int q0 = 0; q0 < nq; q0 += PG) {
+      f32x4 w[PG][UNROLL];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
-        if (ok[u]) {
-          const f32x4 w = *(const f32x4*)(p.P[q] + (int64_t)gr[u] * p.N + gc[u]);
-          v[u] += w;
+      for (int g = 0; g < PG; ++g) {
+        const int q = q0 + g < nq ? q0 + g : nq - 1;
+        const __amdgpu_buffer_rsrc_t dp = make_rsrc(uni(p.P[q] + (int64_t)m0 * p.N), in_bytes);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) w[g][u] = __builtin_bit_cast(f32x4, bload(dp, vin[u], 0));
+      }
+#pragma unroll
+      for (int g = 0; g < PG; ++g)
+        if (q0 + g < nq) {
+#pragma unroll
+          for (int u = 0; u < UNROLL; ++u) v[u] += w[g][u];
         }
     }
+    for (int d = 0; d < p.n_dst; ++d) {
+      const __amdgpu_buffer_rsrc_t dout = make_rsrc(uni((const char*)p.out[o + d] + dofs), out_bytes);
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
-      if (ok[u]) {
-        const int o = gr[u] / p.mb;
-        const int64_t i = (int64_t)(gr[u] - o * p.mb) * p.N + gc[u];
-        for (int d = 0; d < p.n_dst; ++d) {
-          if (p.out_bf16) {
-            u32x2 b;
-            b[0] = (uint32_t)f2bf(v[u][0]) | ((uint32_t)f2bf(v[u][1]) << 16);
-            b[1] = (uint32_t)f2bf(v[u][2]) | ((uint32_t)f2bf(v[u][3]) << 16);
-            *(u32x2*)((uint16_t*)p.out[o + d] + i) = b;
-          } else {
-            *(f32x4*)((float*)p.out[o + d] + i) = v[u];
-          }
+      for (int u = 0; u < UNROLL; ++u) {
+        if (p.out_bf16) {
+          u32x2 b;
+          b[0] = (uint32_t)f2bf(v[u][0]) | ((uint32_t)f2bf(v[u][1]) << 16);
+          b[1] = (uint32_t)f2bf(v[u][2]) | ((uint32_t)f2bf(v[u][3]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(b, dout, vout[u], 0, 0);
+        } else {
+          bstore_alu16(dout, vout[u], 0, v[u]);
         }
       }
+    }
   }
 }
 
@@ -647,18 +667,23 @@ static int run_rs(RsParams& p, const mk_launch& o, const mkh::Schedule* s, const
   // default, then computes; n_copy selects fewer.
   const uint32_t n_work = (uint32_t)p.n_units * p.parts;
   p.n_copy = s ? (int)std::min<int64_t>(o.n_copy > 0 ? o.n_copy : grid, std::min<int64_t>(grid, n_work)) : 0;
-  if (o.mode == 1) {   // unfused baseline: copies, GEMM to fp32 staging, then a reduce-scatter kernel
-    if (s) {
+  if (o.mode >= 1) {   // unfused baseline: copies, GEMM to fp32 staging, then a reduce-scatter kernel
+    // (measurement: mode 2 = the reduce kernel alone on what is staged, 3 = the GEMM kernel alone)
+    if (s && o.mode == 1) {
       p.mode = MODE_COPY;
       hipLaunchKernelGGL(rs_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
       if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "copy kernel launch");
     }
-    p.mode = MODE_GEMM;
-    hipLaunchKernelGGL(rs_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
-    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "gemm kernel launch");
-    p.mode = MODE_REDUCE;
-    hipLaunchKernelGGL(rs_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
-    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "reduce kernel launch");
+    if (o.mode != 2) {
+      p.mode = MODE_GEMM;
+      hipLaunchKernelGGL(rs_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+      if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "gemm kernel launch");
+    }
+    if (o.mode != 3) {
+      p.mode = MODE_REDUCE;
+      hipLaunchKernelGGL(rs_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+      if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "reduce kernel launch");
+    }
     return MK_OK;
   }
   const int n_reduce = o.n_reduce;   // 0 = default (epilogue reduction), -1 = epilogue
@@ -717,7 +742,8 @@ static int gemm_reduce(const void* A, const void* B, int64_t M, int64_t K, int64
   }
   const int mb = all_reduce ? (int)M : (int)(M / R);   // rows per output block
   const mk_launch o = mkh::launch_opts(launch);
-  if (o.mode != 0 && o.mode != 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
+  if (o.mode < 0 || o.mode > 3) return fail(MK_ERR_INVALID, "mode %d", o.mode);
+  if (o.mode >= 2 && arrival) return fail(MK_ERR_INVALID, "modes 2 and 3 (one phase alone) take no arrival schedule");
   if (o.grid < 0 || o.n_reduce < -1 || o.n_copy < 0 || o.copy_kib < 0)
     return fail(MK_ERR_INVALID, "bad grid, n_reduce, n_copy or copy_kib");
   // Default: the direct-to-LDS 256x256 tile when K is a multiple of 128 and

@@ -38,8 +38,12 @@ constexpr int RB = 64;          // tokens per routing block
 constexpr int ROUTE_NT = 1024;  // 16 waves, 4 tokens each
 
 struct MoeWs {                  // device workspace layout (offsets in bytes)
-  size_t block_cnt, rank, tile_base, tile_cnt, kp_cnt, kp_slots, total;
+  size_t block_cnt, rank, tile_base, tile_cnt, mt_order, kp_cnt, kp_slots, total;
 };
+
+// M-tiles ranked by readiness in one workgroup (a rank count over all pairs)
+// up to this many; beyond it the queue keeps expert order.
+constexpr int ORDER_CAP = 2048;
 
 // K parts of a tail tile.  More parts shorten the parts but lengthen the
 // finishing part's read-back of the parked sums (one workgroup reads
@@ -61,7 +65,8 @@ inline MoeWs moe_ws_layout(int64_t T, int E, int k, int L, int n_cu) {
   w.rank = up(w.block_cnt + (size_t)nrb * E * 4);
   w.tile_base = up(w.rank + (size_t)T * k * 4);
   w.tile_cnt = up(w.tile_base + (size_t)(L + 1) * 4 + 4);
-  w.kp_cnt = up(w.tile_cnt + (size_t)max_tiles * 4);
+  w.mt_order = up(w.tile_cnt + (size_t)max_tiles * 4);
+  w.kp_cnt = up(w.mt_order + (size_t)max_tiles * 4);
   w.kp_slots = up(w.kp_cnt + (size_t)n_cu * 4);
   w.total = w.kp_slots + (size_t)n_cu * 256 * 256 * 4;
   return w;
@@ -153,12 +158,26 @@ __global__ __launch_bounds__(ROUTE_NT) void route_kernel(const float* __restrict
   for (int e = threadIdx.x; e < E; e += ROUTE_NT) block_cnt[(int64_t)blockIdx.x * E + e] = __popcll(s_mask[e]);
 }
 
-// One workgroup of 1024 threads.
+// Arrival positions of the source blocks, for the readiness order.
+struct ScanOrder {
+  int T, block_tokens, n_blocks;
+  uint16_t pos[MK_MAX_UNITS];     // pos[b] = issue position of source block b
+};
+
+// One workgroup of 1024 threads.  After the counts, offsets and M-tile table,
+// the M-tiles are ranked by readiness: the latest issue position among the
+// source blocks their rows come from (an M-tile's rows are tokens in
+// ascending order, so they span the routing blocks between those of its first
+// and last row), ties in M-tile (expert) order.  mt_order[i] = the i-th
+// M-tile to queue.
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ block_cnt, int nrb, int E,
                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ n_local, int eb, int L, int BM,
-                                                    int32_t* __restrict__ tile_base) {
+                                                    int32_t* __restrict__ tile_base, int32_t* __restrict__ mt_order,
+                                                    const ScanOrder so) {
   __shared__ int32_t s[1024];
+  __shared__ int32_t s_tb[MK_MAX_LOCAL + 1];
+  __shared__ int32_t s_key[ORDER_CAP];
   const int e = threadIdx.x;
   int tot = 0;
   if (e < E) {
@@ -194,10 +213,48 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ block_
     int acc = 0;
     for (int l = 0; l < L; ++l) {
       tile_base[l] = acc;
+      s_tb[l] = acc;
       const int c = s[eb + l] - (eb + l > 0 ? s[eb + l - 1] : 0);
       acc += (c + BM - 1) / BM;
     }
     tile_base[L] = acc;
+    s_tb[L] = acc;
+  }
+  __syncthreads();
+  const int n_mt = s_tb[L];
+  if (n_mt > ORDER_CAP) {
+    for (int mt = e; mt < n_mt; mt += 1024) mt_order[mt] = mt;
+    return;
+  }
+  // routing block holding row r of expert x: the last block whose offset
+  // within x is <= r (empty blocks share their successor's offset)
+  auto row_block = [&](int x, int r) {
+    int lo = 0, hi = nrb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (block_cnt[(int64_t)mid * E + x] <= r) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  for (int mt = e; mt < n_mt; mt += 1024) {
+    int l = 0;
+    while (l + 1 < L && s_tb[l + 1] <= mt) ++l;
+    const int x = eb + l;
+    const int cnt = s[x] - (x > 0 ? s[x - 1] : 0);
+    const int r0 = (mt - s_tb[l]) * BM, r1 = min(r0 + BM, cnt) - 1;
+    const int t_first = row_block(x, r0) * RB, t_last = min(so.T, (row_block(x, r1) + 1) * RB) - 1;
+    int key = 0;
+    for (int b = t_first / so.block_tokens; b <= t_last / so.block_tokens && b < so.n_blocks; ++b)
+      key = max(key, (int)so.pos[b]);
+    s_key[mt] = key;
+  }
+  __syncthreads();
+  for (int mt = e; mt < n_mt; mt += 1024) {
+    const int key = s_key[mt];
+    int rk = 0;
+    for (int i = 0; i < n_mt; ++i) rk += (s_key[i] < key) || (s_key[i] == key && i < mt);
+    mt_order[rk] = mt;
   }
 }
 
@@ -216,6 +273,7 @@ struct MoeParams {
   const int32_t* offsets;
   int32_t* perm;
   const int32_t* tile_base;     // [L+1]
+  const int32_t* mt_order;      // [tiles] M-tiles in readiness order (fused queue)
   uint32_t* tile_cnt;           // [tiles] rows landed per M-tile
   WsHeader* hdr;
   int32_t* tile_log;
@@ -226,6 +284,8 @@ struct MoeParams {
   int mode, n_copy, tiles_n, withhold;
   int full_grid;                // CUs x occupancy of this kernel (the split plan's grid)
   int xcd_queues;               // whole tiles from per-XCD queues keyed by tile column
+  int ready_order;              // fused queue in readiness order (else expert order)
+  int hold;                     // fused: no tile before every copy item has landed
   int kp_len;                   // K-part counters in the workspace
   uint32_t* kp_cnt;             // [kp_len] parts of a split tail tile finished
   float* kp_slots;              // parked K parts
@@ -233,13 +293,18 @@ struct MoeParams {
   uint32_t delay_ticks[MK_MAX_UNITS];
 };
 
-constexpr int MAX_PAIRS = 8 * MK_MAX_TOPK;   // part_tokens (<= 8) x k
-constexpr int COPY_ROWS = 8;                 // rows per copy round trip (32 x 16 B loads per thread)
+constexpr int PART_TOKENS = 8;               // tokens per copy item (at most)
 constexpr int SC1 = 16;                      // cache-policy bits: write through the L2
 
+// Copy role.  An item is (source block, part of at most PART_TOKENS tokens).
+// Its pairs' positions are computed first (perm for every pair; for a local
+// expert the landing row and its M-tile), grouped by token; then each token
+// row with at least one local pair is loaded ONCE and stored to every landing
+// row of that token (a token picks up to k local experts: one read, up to k
+// writes).
 __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, uint32_t* sb, int BM) {
-  __shared__ int32_t s_src[MAX_PAIRS], s_dst[MAX_PAIRS], s_tile[MAX_PAIRS];
-  __shared__ int32_t s_n;
+  __shared__ int32_t s_dst[PART_TOKENS][MK_MAX_TOPK], s_tile[PART_TOKENS][MK_MAX_TOPK];
+  __shared__ int32_t s_cnt[PART_TOKENS];
   const int tid = threadIdx.x, nt = blockDim.x;
   uint64_t t0 = 0;
   if (tid == 0) {
@@ -262,51 +327,55 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
       if (tid == 0) {
         wait_until(t0 + p.delay_ticks[blk], p.spin_limit);
         t_start = (uint32_t)now_ticks();
-        s_n = 0;
       }
+      if (tid < PART_TOKENS) s_cnt[tid] = 0;
       __syncthreads();
       const int t0k = blk * p.block_tokens + part * p.part_tokens;
-      const int npair = min(p.part_tokens, p.T - t0k) * p.k;
+      const int ntok = min(p.part_tokens, p.T - t0k);
+      const int npair = ntok * p.k;
       // Positions of this part's pairs; perm for all of them, landing rows for local ones.
       if (tid < npair) {
-        const int t = t0k + tid / p.k, jj = tid % p.k;
+        const int tl = tid / p.k, jj = tid % p.k, t = t0k + tl;
         const int e = p.topk[(int64_t)t * p.k + jj];
         const int pos = p.offsets[e] + p.block_off[(int64_t)(t / RB) * p.E + e] + p.rank[(int64_t)t * p.k + jj];
         p.perm[pos] = t * p.k + jj;
         const int l = e - p.eb;
         if (l >= 0 && l < p.L) {
-          const int slot = atomicAdd(&s_n, 1);
-          s_src[slot] = t;
-          s_dst[slot] = pos - base_local;
-          s_tile[slot] = p.tile_base[l] + (pos - p.offsets[e]) / BM;
+          const int slot = atomicAdd(&s_cnt[tl], 1);
+          s_dst[tl][slot] = pos - base_local;
+          s_tile[tl][slot] = p.tile_base[l] + (pos - p.offsets[e]) / BM;
         }
       }
       __syncthreads();
       const uint32_t t_indexed = (uint32_t)now_ticks();
-      const int n = (int)uni((uint32_t)s_n);
-      // Rows COPY_ROWS at a time, each through a descriptor bounded to its
+      // Every token's row: all loads first (one round trip for the item),
+      // then its stores to each landing row.  Descriptors are bounded to one
       // row: chunks past the row end load zero and their stores are dropped,
-      // so no per-element guard; a short last group repeats its last row.
-      // All loads of a group are issued before its first store (loads and
-      // stores share one in-order counter, so a group is one round trip).
-      // Stores write through the L2 (sc1): the release below then has little
-      // to write back.
-      for (int r0 = 0; r0 < n; r0 += COPY_ROWS) {
-        for (int c0 = 0; c0 < cpr; c0 += 4 * nt) {
-          u32x4 v[COPY_ROWS][4];
+      // so there is no per-element guard.  A token with no local pair loads
+      // nothing (its count is uniform: read from LDS by every lane).  Stores
+      // write through the L2 (sc1): the release below then has little to write
+      // back.
+      int n = 0;                                   // local rows of the item
 #pragma unroll
-          for (int rr = 0; rr < COPY_ROWS; ++rr) {
-            const int r = min(r0 + rr, n - 1);
-            const __amdgpu_buffer_rsrc_t src = make_rsrc(uni(p.X + (int64_t)uni((uint32_t)s_src[r]) * p.H), row_bytes);
+      for (int tl = 0; tl < PART_TOKENS; ++tl) n += tl < ntok ? uni(s_cnt[tl]) : 0;
+      for (int c0 = 0; c0 < cpr; c0 += 4 * nt) {
+        u32x4 v[PART_TOKENS][4];
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) v[rr][cc] = bload(src, (uint32_t)(c0 + cc * nt + tid) * 16u, 0);
+        for (int tl = 0; tl < PART_TOKENS; ++tl) {
+          const int cnt = uni(s_cnt[tl]);
+          if (tl < ntok && cnt > 0) {
+            const __amdgpu_buffer_rsrc_t src = make_rsrc(uni(p.X + (int64_t)(t0k + tl) * p.H), row_bytes);
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) v[tl][cc] = bload(src, (uint32_t)(c0 + cc * nt + tid) * 16u, 0);
           }
+        }
 #pragma unroll
-          for (int rr = 0; rr < COPY_ROWS; ++rr) {
-            const int r = min(r0 + rr, n - 1);
-            const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Xs + (int64_t)uni((uint32_t)s_dst[r]) * p.H), row_bytes);
+        for (int tl = 0; tl < PART_TOKENS; ++tl) {
+          const int cnt = tl < ntok ? uni(s_cnt[tl]) : 0;
+          for (int d = 0; d < cnt; ++d) {
+            const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Xs + (int64_t)uni(s_dst[tl][d]) * p.H), row_bytes);
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) bstore<SC1>(dst, (uint32_t)(c0 + cc * nt + tid) * 16u, 0, v[rr][cc]);
+            for (int cc = 0; cc < 4; ++cc) bstore<SC1>(dst, (uint32_t)(c0 + cc * nt + tid) * 16u, 0, v[tl][cc]);
           }
         }
       }
@@ -317,8 +386,9 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
       __syncthreads();
       // stores complete, not yet counted: a tile that sees the counts reads a later clock
       const uint32_t t_end = (uint32_t)now_ticks();
-      if (tid < 64) {
-        for (int q = tid; q < n; q += 64) add_relaxed(&p.tile_cnt[s_tile[q]], 1u);
+      if (tid < PART_TOKENS * MK_MAX_TOPK) {
+        const int tl = tid / MK_MAX_TOPK, d = tid % MK_MAX_TOPK;
+        if (tl < ntok && d < s_cnt[tl]) add_relaxed(&p.tile_cnt[s_tile[tl][d]], 1u);
       }
       if (tid == 0) add_relaxed(&h->aux[0], 1u);        // items landed in total
       if (p.copy_log && tid == 0) {
@@ -391,6 +461,14 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
     }
     return wg_bcast(it, sb);
   };
+  if (p.hold && !all_landed) {
+    uint32_t ok = 1;
+    if (tid == 0) {
+      ok = wait_geq_relaxed(&h->aux[0], all_items, h, p.spin_limit);
+      if (ok) fence_acquire();
+    }
+    all_landed = wg_bcast(ok, sb) != 0u;            // on a watchdog expiry the per-tile waits give up too
+  }
   G g;
   int l = 0;
   for (;;) {
@@ -404,8 +482,11 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
       kp = (int)((it - sp.n_whole) % sp.split);
     }
     const uint32_t t_take = (uint32_t)now_ticks();
-    const int mt = (int)(q / p.tiles_n), tn = (int)(q % p.tiles_n);
-    while (l + 1 < p.L && p.tile_base[l + 1] <= mt) ++l;        // queue is expert-ordered
+    // queue slot -> M-tile: readiness order in the fused kernel, expert order
+    // in the baseline's GEMM kernel
+    const int slot = (int)(q / p.tiles_n), tn = (int)(q % p.tiles_n);
+    const int mt = p.mode == MODE_FUSED && p.ready_order ? uni(p.mt_order[slot]) : slot;
+    while (l + 1 < p.L && p.tile_base[l + 1] <= mt) ++l;
     while (l > 0 && p.tile_base[l] > mt) --l;
     const int e = p.eb + l;
     const int r0 = (mt - p.tile_base[l]) * G::BM;              // expert-relative first row
@@ -448,7 +529,7 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
       }
     }
     if (done && p.tile_log && tid == 0) {
-      int32_t* L = p.tile_log + 8 * (int64_t)q;
+      int32_t* L = p.tile_log + 8 * ((int64_t)mt * p.tiles_n + tn);
       L[0] = l; L[1] = r0; L[2] = rows;
       L[3] = p.mode == MODE_FUSED ? (int32_t)ld_relaxed(&p.tile_cnt[mt]) : rows;
       L[4] = (int32_t)blockIdx.x; L[5] = (int32_t)t_take; L[6] = (int32_t)t_ready;
@@ -506,10 +587,10 @@ __global__ __launch_bounds__(G::NT) void moe_kernel(const MoeParams p) {
 
 template <class G>
 int run_moe(MoeParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStream_t st, int32_t* counts,
-            int32_t* offsets, int32_t* n_local, int32_t* block_cnt, int nrb) {
+            int32_t* offsets, int32_t* n_local, int32_t* block_cnt, int nrb, const ScanOrder& so) {
   hipError_t e;
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, block_cnt, nrb, p.E, counts, offsets, n_local,
-                     p.eb, p.L, G::BM, const_cast<int32_t*>(p.tile_base));
+                     p.eb, p.L, G::BM, const_cast<int32_t*>(p.tile_base), const_cast<int32_t*>(p.mt_order), so);
   if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "scan kernel launch");
   p.tiles_n = (p.F + G::BN - 1) / G::BN;
   int occ = 0;
@@ -522,15 +603,21 @@ int run_moe(MoeParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStream_t
   p.full_grid = full;
   if ((int64_t)full * G::BM * G::BN > (int64_t)d->n_cu * 256 * 256)
     return mkh::fail(MK_ERR_UNSUPPORTED, "tile slots exceed the workspace plan");
-  if (o.mode == 1) {   // unfused baseline: permute kernel, then grouped GEMM kernel
-    p.mode = MODE_COPY;
-    p.n_copy = grid;
-    hipLaunchKernelGGL(moe_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
-    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "permute kernel launch");
-    p.mode = MODE_GEMM;
-    p.n_copy = 0;
-    hipLaunchKernelGGL(moe_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
-    if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "grouped gemm kernel launch");
+  if (o.mode >= 1) {   // unfused baseline: permute kernel, then grouped GEMM kernel
+    // (measurement: mode 2 = routing and the permute kernel alone, 3 = routing
+    // and the grouped GEMM kernel alone on the landing buffer as it is)
+    if (o.mode != 3) {
+      p.mode = MODE_COPY;
+      p.n_copy = grid;
+      hipLaunchKernelGGL(moe_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+      if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "permute kernel launch");
+    }
+    if (o.mode != 2) {
+      p.mode = MODE_GEMM;
+      p.n_copy = 0;
+      hipLaunchKernelGGL(moe_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+      if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "grouped gemm kernel launch");
+    }
     return MK_OK;
   }
   p.mode = MODE_FUSED;
@@ -583,9 +670,9 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   const size_t need0 = moe_ws_layout(T, E, k, L, 0).total;   // before the split-tail slots
   if (workspace_bytes < need0) return fail(MK_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need0);
   const mk_launch o = mkh::launch_opts(launch);
-  if (o.mode != 0 && o.mode != 1) return fail(MK_ERR_INVALID, "mode %d", o.mode);
+  if (o.mode < 0 || o.mode > 3) return fail(MK_ERR_INVALID, "mode %d", o.mode);
   if (o.grid < 0 || o.n_copy < 0) return fail(MK_ERR_INVALID, "negative grid or n_copy");
-  if (o.queue_mode < 0 || o.queue_mode > 1) return fail(MK_ERR_INVALID, "queue_mode %d", o.queue_mode);
+  if (o.queue_mode < 0 || o.queue_mode > 5) return fail(MK_ERR_INVALID, "queue_mode %d", o.queue_mode);
   const mkh::DevInfo* d = mkh::dev_info();
   if (!d) return MK_ERR_HIP;
   const MoeWs lay = moe_ws_layout(T, E, k, L, d->n_cu);
@@ -619,6 +706,7 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   p.perm = perm;
   p.tile_base = (const int32_t*)(ws + lay.tile_base);
   p.tile_cnt = (uint32_t*)(ws + lay.tile_cnt);
+  p.mt_order = (const int32_t*)(ws + lay.mt_order);
   p.kp_cnt = (uint32_t*)(ws + lay.kp_cnt);
   p.kp_slots = (float*)(ws + lay.kp_slots);
   p.kp_len = d->n_cu;
@@ -626,12 +714,18 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   p.tile_log = o.tile_log;
   p.copy_log = o.copy_log;
   p.spin_limit = mkh::spin_ticks(o, d);
-  p.xcd_queues = o.queue_mode == 1;
+  // queue_mode: 0 readiness order, 1 per-XCD queues (readiness order within
+  // each), 2 expert order, 3 expert order with every tile held until all copy
+  // items have landed (the baseline's phases inside one kernel), 4 as 3 with
+  // per-XCD queues, 5 expert order in per-XCD queues
+  p.xcd_queues = o.queue_mode == 1 || o.queue_mode >= 4;
+  p.ready_order = o.queue_mode <= 1;
+  p.hold = o.queue_mode == 3 || o.queue_mode == 4;
   p.T = (int)T; p.H = (int)H; p.E = E; p.k = k; p.L = L; p.F = (int)F; p.eb = expert_begin;
   p.y_bf16 = y_dtype == MK_BF16;
   p.n_blocks = s.n_units;
   p.block_tokens = s.unit_rows;
-  p.part_tokens = std::min(8, s.unit_rows);
+  p.part_tokens = std::min(PART_TOKENS, s.unit_rows);
   while (s.unit_rows % p.part_tokens) --p.part_tokens;
   p.parts = s.unit_rows / p.part_tokens;
   p.withhold = s.withhold;
@@ -639,6 +733,12 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
     p.order[j] = (uint16_t)s.order[j];
     p.delay_ticks[j] = (uint32_t)mkh::ns_to_ticks(s.delay_ns[j], d->wall_khz);
   }
+  ScanOrder so;
+  memset(&so, 0, sizeof so);
+  so.T = (int)T;
+  so.block_tokens = s.unit_rows;
+  so.n_blocks = s.n_units;
+  for (int b = 0; b < s.n_units; ++b) so.pos[b] = (uint16_t)s.pos[b];
   int tile = o.tile ? o.tile : TILE_256x256;
   if (F < 256 && tile == TILE_256x256) tile = TILE_128x128;
   // Only the 256x256 tile switches to the direct-to-LDS engine by default: at
@@ -649,14 +749,14 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   if (tile == TILE_128x128_DMA8 || tile == TILE_256x256_DMA_W8)
     return fail(MK_ERR_UNSUPPORTED, "tile %d is built for AllGather+GEMM only", tile);
   switch (tile) {
-    case TILE_256x256: return run_moe<TileGemm<256, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
-    case TILE_128x128: return run_moe<TileGemm<128, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
-    case TILE_256x128: return run_moe<TileGemm<256, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
-    case TILE_128x256: return run_moe<TileGemm<128, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
-    case TILE_256x256_DMA: return run_moe<TileGemmD<256, 256>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
-    case TILE_128x128_DMA: return run_moe<TileGemmD<128, 128>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
-    case TILE_256x128_DMA: return run_moe<TileGemmD<256, 128>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
-    case TILE_128x256_DMA: return run_moe<TileGemmD<128, 256>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb);
+    case TILE_256x256: return run_moe<TileGemm<256, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_128x128: return run_moe<TileGemm<128, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_256x128: return run_moe<TileGemm<256, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_128x256: return run_moe<TileGemm<128, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_256x256_DMA: return run_moe<TileGemmD<256, 256>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_128x128_DMA: return run_moe<TileGemmD<128, 128>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_256x128_DMA: return run_moe<TileGemmD<256, 128>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_128x256_DMA: return run_moe<TileGemmD<128, 256>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
     default: return fail(MK_ERR_INVALID, "tile id %d", tile);
   }
 }

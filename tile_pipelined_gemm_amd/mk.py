@@ -32,7 +32,7 @@ EXPORTS = [
     "mk_ring_attn_workspace", "mk_ring_attn",
     "mk_workspace_init",
     "mk_poll_status", "mk_status_string", "mk_last_error", "mk_tile_name", "mk_version",
-    "mk_wall_clock_khz",
+    "mk_wall_clock_khz", "mk_peak_workspace", "mk_peak_mfma", "mk_peak_hbm",
 ]
 
 
@@ -138,6 +138,12 @@ def load(path: Optional[str] = None):
     lib.mk_version.argtypes = []
     lib.mk_wall_clock_khz.restype = i32
     lib.mk_wall_clock_khz.argtypes = []
+    lib.mk_peak_workspace.restype = sz
+    lib.mk_peak_workspace.argtypes = []
+    lib.mk_peak_mfma.restype = i32
+    lib.mk_peak_mfma.argtypes = [i32, vp, sz, C.POINTER(C.c_double), C.POINTER(C.c_int), vp]
+    lib.mk_peak_hbm.restype = i32
+    lib.mk_peak_hbm.argtypes = [vp, vp, sz, i32, vp, sz, C.POINTER(C.c_double), vp]
     _lib = lib
     return lib
 
@@ -192,6 +198,24 @@ def make_arrival(order=None, delay_ns=None, unit_rows=0, withhold=-1):
                    C.cast(d, C.POINTER(C.c_uint32)) if d is not None else None,
                    len(order), int(unit_rows), int(withhold))
     return a, (o, d)
+
+
+def mk_peak_mfma(iters, ws, *, stream=None):
+    """Launch the MFMA-only loop; returns (flops of the launch, waves).  The
+    per-wave {core ticks, wall ticks} pairs land in ws at byte 256."""
+    f, n = C.c_double(0.0), C.c_int(0)
+    _check(load().mk_peak_mfma(int(iters), _ptr(ws), ws.numel() * ws.element_size(), C.byref(f), C.byref(n),
+                               _stream(stream)))
+    return f.value, n.value
+
+
+def mk_peak_hbm(src, dst, mode, ws, *, stream=None) -> float:
+    """Launch the HBM read (mode 0) or copy (mode 1) stream over src's bytes;
+    returns the bytes it moves (read plus written)."""
+    b = C.c_double(0.0)
+    _check(load().mk_peak_hbm(_ptr(src), _ptr(dst), src.numel() * src.element_size(), int(mode), _ptr(ws),
+                              ws.numel() * ws.element_size(), C.byref(b), _stream(stream)))
+    return b.value
 
 
 def mk_wall_clock_khz() -> int:
