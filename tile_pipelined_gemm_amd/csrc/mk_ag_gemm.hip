@@ -47,6 +47,7 @@ struct AgParams {
   int n_units, unit_rows, parts, part_rows;
   uint32_t part_bytes;
   int copy_wt;          // copy stores written through the L2
+  int c_wt;             // output tiles written through the L2
   int mode, n_copy, tiles_m, tiles_n, n_tiles, withhold;
   int xcd_queues;       // tiles from per-XCD queues (else one queue in landing order)
   uint16_t order[MK_MAX_UNITS];
@@ -92,14 +93,13 @@ __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uin
       // Release only: the copier never reads what others publish, so the
       // acquire half of a full fence (an L2 invalidate that would also drop
       // the lines of the GEMM tiles running on this XCD) is not needed.
-      fence_release();
-      __syncthreads();
+      wg_release();
       if (tid == 0) {
         // t_end is stamped once every thread's stores are complete and before
-        // the release, so a consumer that sees the release reads a later clock
+        // the counters are raised, so a consumer that sees them reads a later clock
         const uint32_t t_end = (uint32_t)now_ticks();
-        add_release(&p.unit_cnt[c], 1u);
-        add_release(&h->aux[0], 1u);                 // parts landed in total
+        add_relaxed(&p.unit_cnt[c], 1u);
+        add_relaxed(&h->aux[0], 1u);                 // parts landed in total
         if (p.copy_log) {
           int32_t* L = p.copy_log + 8 * (int64_t)w;
           L[0] = c; L[1] = part; L[2] = (int32_t)blockIdx.x;
@@ -164,7 +164,10 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, 
       g.bind(p.Ag + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
       g.run(sm);
       const int64_t esz = p.c_bf16 ? 2 : 4;
-      store_tile(g, (char*)p.C + ((int64_t)m0 * p.N + n0) * esz, p.N, p.M - m0, p.N - n0, p.c_bf16);
+      // written through the L2: a copy workgroup's release on this XCD then
+      // has no output lines to write back
+      if (p.c_wt) store_tile<G, 16>(g, (char*)p.C + ((int64_t)m0 * p.N + n0) * esz, p.N, p.M - m0, p.N - n0, p.c_bf16);
+      else store_tile(g, (char*)p.C + ((int64_t)m0 * p.N + n0) * esz, p.N, p.M - m0, p.N - n0, p.c_bf16);
       if (p.tile_log && tid == 0) {
         int32_t* L = p.tile_log + 8 * (int64_t)q;
         L[0] = tm; L[1] = tn; L[2] = u0; L[3] = u1; L[4] = (int32_t)blockIdx.x;
@@ -354,7 +357,7 @@ static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t 
   const mk_launch o = mkh::launch_opts(launch);
   if (o.mode < 0 || o.mode > 3) return fail(MK_ERR_INVALID, "mode %d", o.mode);
   if (o.grid < 0 || o.n_copy < 0 || o.copy_kib < 0) return fail(MK_ERR_INVALID, "negative grid, n_copy or copy_kib");
-  if (o.copy_policy < 0 || o.copy_policy > 2) return fail(MK_ERR_INVALID, "copy_policy %d", o.copy_policy);
+  if (o.copy_policy < 0 || o.copy_policy > 3) return fail(MK_ERR_INVALID, "copy_policy %d", o.copy_policy);
   if (o.queue_mode < 0 || o.queue_mode > 1) return fail(MK_ERR_INVALID, "queue_mode %d", o.queue_mode);
   const mkh::DevInfo* d = mkh::dev_info();
   if (!d) return MK_ERR_HIP;
@@ -374,6 +377,7 @@ static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t 
   p.tile_log = o.tile_log;
   p.copy_log = o.copy_log;
   p.copy_wt = o.copy_policy != 1;              // default: written through
+  p.c_wt = o.copy_policy != 3;                 // default: output tiles written through too
   p.xcd_queues = o.queue_mode == 1;            // default: one queue in landing order
   p.spin_limit = mkh::spin_ticks(o, d);
   p.R = R; p.m_shard = (int)m_shard; p.M = (int)M; p.K = (int)K; p.N = (int)N;

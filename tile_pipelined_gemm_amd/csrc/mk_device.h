@@ -60,6 +60,19 @@ __device__ __forceinline__ uint32_t add_release(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 
+// Publication of a workgroup's stores at agent scope with ONE release: every
+// wave waits for its own stores to complete, the barrier orders them before
+// thread 0, thread 0 takes the agent-scope release (on gfx950 it writes back
+// the XCD's dirty L2 lines, so one per item instead of one per wave), and
+// after the second barrier any thread may publish with relaxed atomics.
+// Called by every thread of the workgroup.
+__device__ __forceinline__ void wg_release() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) fence_release();
+  __syncthreads();
+}
+
 // Constant-rate (100 MHz on MI300-class parts) wall clock shared by all CUs.
 __device__ __forceinline__ uint64_t now_ticks() { return wall_clock64(); }
 
@@ -216,10 +229,11 @@ constexpr uint32_t OOB = 0x80000000u;   // a voffset that is always past the end
 // took the following value.  The compiler inserts no wait there, and stores
 // of at most 8 bytes are outside that hazard.  Copies (data straight from
 // loads, not rewritten by ALU instructions) keep 16-byte stores.
+template <int POLICY = 0>
 __device__ __forceinline__ void bstore_alu16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, f32x4 v) {
   const u32x4 u = __builtin_bit_cast(u32x4, v);
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{u[0], u[1]}, r, voff, soff, 0);
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{u[2], u[3]}, r, voff, soff + 8u, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{u[0], u[1]}, r, voff, soff, POLICY);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{u[2], u[3]}, r, voff, soff + 8u, POLICY);
 }
 
 // Copy n16 16-byte chunks from src to dst (buffer resources bounded to the
@@ -442,7 +456,10 @@ struct TileGemm {
 // access through a descriptor bounded to the valid rows; a 4-column run past
 // `cols` gets the out-of-range offset.  No store is guarded, so none waits
 // for the ones before it.  cols is a multiple of 4 and rows*ld*esize < 2^32.
-template <class G>
+// POLICY is the stores' cache-policy field: 16 (sc1) writes the tile through
+// the XCD's L2, so it leaves no dirty lines there for a later release fence
+// (a copy workgroup's publication) to write back.
+template <class G, int POLICY = 0>
 __device__ __forceinline__ void store_tile(const G& g, void* C, int64_t ld, int rows, int cols, bool bf16) {
   const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
   const int wm = w % G::WM, wn = w / G::WM;
@@ -468,9 +485,9 @@ __device__ __forceinline__ void store_tile(const G& g, void* C, int64_t ld, int 
           u32x2 b;
           b[0] = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
           b[1] = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-          __builtin_amdgcn_raw_buffer_store_b64(b, d, vo, so, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(b, d, vo, so, POLICY);
         } else {
-          bstore_alu16(d, vo, so, v);
+          bstore_alu16<POLICY>(d, vo, so, v);
         }
       }
     }

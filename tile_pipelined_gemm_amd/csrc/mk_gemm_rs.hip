@@ -371,13 +371,12 @@ __device__ __forceinline__ void rs_copy_role(const RsParams& p, WsHeader* h, uin
         const __amdgpu_buffer_rsrc_t src = make_rsrc(uni(p.Psrc[q] + ofs), p.part_bytes);
         const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.P[q] + ofs), p.part_bytes);
         copy_block<16>(src, dst, n16, tid, nt);    // written through the L2
-        fence_release();                           // release only: the copier reads nothing others publish
       }
-      __syncthreads();
+      wg_release();                                // release only: the copier reads nothing others publish
       if (tid == 0) {
         const uint32_t t_end = (uint32_t)now_ticks();
-        add_release(&p.unit_cnt[u], 1u);
-        add_release(&h->aux[0], 1u);               // parts landed in total
+        add_relaxed(&p.unit_cnt[u], 1u);
+        add_relaxed(&h->aux[0], 1u);               // parts landed in total
         if (p.copy_log) {
           int32_t* L = p.copy_log + 8 * (int64_t)w;
           L[0] = u; L[1] = part; L[2] = (int32_t)blockIdx.x;
@@ -487,10 +486,7 @@ __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, 
       float* __restrict__ S = p.stage ? p.stage + (int64_t)m0 * p.N
                                       : (float*)p.out[m0 / p.mb] + (int64_t)(m0 % p.mb) * p.N;
       store_tile(g, S + n0, p.N, p.M - m0, p.N - n0, false);
-      if (p.mode == MODE_ROLES) {
-        __threadfence();
-        __syncthreads();
-      }
+      if (p.mode == MODE_ROLES) wg_release();      // the staged tile, before its FIFO entry
     }
     uint32_t next = 0;
     if (tid == 0) {
@@ -500,7 +496,7 @@ __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, 
           p.tile_log[8 * t] = m0 / p.mb;
           p.tile_log[8 * t + 1] = (int32_t)slot;
         }
-        st_release(&p.fifo[slot], (uint32_t)t + 1u);
+        st_relaxed(&p.fifo[slot], (uint32_t)t + 1u);   // after wg_release: the tile is visible
       }
       next = add_relaxed(&h->tile_next, 1u);
     }

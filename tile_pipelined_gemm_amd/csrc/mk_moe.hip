@@ -382,8 +382,7 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
       const uint32_t t_copied = (uint32_t)now_ticks();
       // Release only (no acquire: a copier reads nothing that others publish,
       // and an L2 invalidate would drop the lines of GEMM tiles on this XCD).
-      fence_release();
-      __syncthreads();
+      wg_release();
       // stores complete, not yet counted: a tile that sees the counts reads a later clock
       const uint32_t t_end = (uint32_t)now_ticks();
       if (tid < PART_TOKENS * MK_MAX_TOPK) {
@@ -520,8 +519,7 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
       const uint32_t tq = q - sp.n_whole;                        // tail tile index
       float* slots = p.kp_slots + (int64_t)tq * sp.split * (G::BM * G::BN);
       park_acc(g, slots + (int64_t)kp * (G::BM * G::BN));
-      fence_release();
-      __syncthreads();
+      wg_release();
       done = wg_bcast(tid == 0 ? (uint32_t)(add_relaxed(&p.kp_cnt[tq], 1u) == (uint32_t)(sp.split - 1)) : 0u, sb);
       if (done) {
         if (sp.split == 2) store_parked_sum<G, 2>(slots, Yt, p.F, rows, p.F - n0, p.y_bf16);

@@ -126,12 +126,11 @@ __device__ __forceinline__ void ring_copy_role(const RingParams& p, WsHeader* h,
       const uint16_t* src = (part ? p.V[r] : p.K[r]) + (int64_t)hd * p.S * HD;
       uint16_t* dst = (part ? p.Vr : p.Kr) + (int64_t)u * p.S * HD;
       copy_head(make_rsrc(uni(src), p.head_bytes), make_rsrc(uni(dst), p.head_bytes), n16, tid);
-      fence_release();
-      __syncthreads();
+      wg_release();
       if (tid == 0) {
-        const uint32_t t_end = (uint32_t)now_ticks();   // stores complete, not yet released
-        add_release(&p.unit_cnt[u], 1u);
-        add_release(&h->aux[0], 1u);              // parts landed in total
+        const uint32_t t_end = (uint32_t)now_ticks();   // stores complete and released, not yet counted
+        add_relaxed(&p.unit_cnt[u], 1u);
+        add_relaxed(&h->aux[0], 1u);              // parts landed in total
         if (p.copy_log) {
           int32_t* L = p.copy_log + 8 * (int64_t)w;
           L[0] = u; L[1] = part; L[2] = (int32_t)blockIdx.x;
