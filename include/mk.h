@@ -137,9 +137,10 @@ typedef struct mk_launch {
                              1 = 8 per-XCD queues (the tiles that share an A
                              row block run on one XCD and share its L2; a
                              drained queue's workgroups help the others).
-                             MoE (fused): 0 = one queue of M-tiles in readiness
-                             order (the latest arrival position among the source
-                             blocks their rows come from); 1 = the same order in 8
+                             MoE (fused): 0 = one queue of M-tiles, expert by
+                             expert, each expert's M-tiles in readiness order (the
+                             latest arrival position among the source blocks their
+                             rows come from); 1 = the same order in 8
                              per-XCD queues keyed by tile column (when the tile
                              columns split evenly over them: the tiles on one XCD
                              share the same column blocks of the expert weights);

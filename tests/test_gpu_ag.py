@@ -202,7 +202,7 @@ def test_partial_round_output_independent_of_grid_mode_and_engine(gpu):
     prob = AgProblem(w)
     outs = []
     for kw in [dict(), dict(grid=80), dict(grid=1), dict(mode=1), dict(queue_mode=1), dict(n_copy=5),
-               dict(tile=gpu.TILE_256x256)]:
+               dict(tile=gpu.TILE_256x256), dict(copy_policy=3), dict(copy_policy=1)]:
         prob.Ag.fill_(float("nan"))
         prob.C.zero_()
         prob.run(launch=gpu.make_launch(**kw))

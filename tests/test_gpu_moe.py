@@ -86,7 +86,10 @@ def test_schedule_roles_and_baseline_bitwise_identical(gpu):
                dict(launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA)),
                dict(launch=gpu.make_launch(tile=gpu.TILE_128x128_DMA)),
                dict(launch=gpu.make_launch(tile=gpu.TILE_256x128_DMA)),
-               dict(launch=gpu.make_launch(tile=gpu.TILE_128x256_DMA))]:
+               dict(launch=gpu.make_launch(tile=gpu.TILE_128x256_DMA)),
+               dict(launch=gpu.make_launch(n_copy=3)),
+               dict(launch=gpu.make_launch(queue_mode=2)), dict(launch=gpu.make_launch(queue_mode=3)),
+               dict(launch=gpu.make_launch(queue_mode=4)), dict(launch=gpu.make_launch(queue_mode=5))]:
         prob.Xs.fill_(float("nan"))
         prob.Y.zero_()
         prob.run(**kw)
@@ -187,7 +190,8 @@ def test_split_tail_bitwise_identical_across_launches(gpu):
     # queue_mode=1: per-XCD queues keyed by tile column (8 column tiles here)
     for kw in [dict(), dict(mode=1), dict(grid=80), dict(n_copy=5), dict(n_copy=64),
                dict(queue_mode=1), dict(queue_mode=1, n_copy=64), dict(queue_mode=1, grid=80),
-               dict(queue_mode=1, mode=1)]:
+               dict(queue_mode=1, mode=1),
+               dict(queue_mode=3), dict(queue_mode=2), dict(queue_mode=4)]:
         prob = _run(gpu, w, launch=gpu.make_launch(**kw))
         outs.append(prob.outputs()["Y"])
     ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 0, "bf16")

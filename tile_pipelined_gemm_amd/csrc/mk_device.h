@@ -99,6 +99,24 @@ __device__ inline bool wait_geq_relaxed(const uint32_t* p, uint32_t target, WsHe
   return true;
 }
 
+// As wait_geq_relaxed, for a wait that the whole grid may share (every
+// workgroup polling one counter): polls about every 4 us, so hundreds of
+// waiters do not load one memory channel that the work they wait for uses.
+__device__ inline bool wait_geq_sparse(const uint32_t* p, uint32_t target, WsHeader* h, uint64_t limit_ticks) {
+  if (ld_relaxed(p) >= target) return true;
+  const uint64_t t_begin = now_ticks();
+  for (uint32_t it = 0; ld_relaxed(p) < target; ++it) {
+    if ((it & 3u) == 3u && ld_relaxed(&h->abort)) return false;
+    if (now_ticks() - t_begin > limit_ticks) {
+      st_relaxed(&h->status, ST_TIMEOUT);
+      st_relaxed(&h->abort, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(127);
+  }
+  return true;
+}
+
 // As wait_geq_relaxed, then an agent-scope acquire.
 __device__ inline bool wait_geq(const uint32_t* p, uint32_t target, WsHeader* h, uint64_t limit_ticks) {
   const bool ok = wait_geq_relaxed(p, target, h, limit_ticks);

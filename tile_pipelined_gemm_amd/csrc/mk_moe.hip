@@ -165,11 +165,11 @@ struct ScanOrder {
 };
 
 // One workgroup of 1024 threads.  After the counts, offsets and M-tile table,
-// the M-tiles are ranked by readiness: the latest issue position among the
-// source blocks their rows come from (an M-tile's rows are tokens in
-// ascending order, so they span the routing blocks between those of its first
-// and last row), ties in M-tile (expert) order.  mt_order[i] = the i-th
-// M-tile to queue.
+// the M-tiles are ranked expert by expert, and within an expert by readiness:
+// the latest issue position among the source blocks their rows come from (an
+// M-tile's rows are tokens in ascending order, so they span the routing blocks
+// between those of its first and last row), ties in M-tile order.
+// mt_order[i] = the i-th M-tile to queue.
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ block_cnt, int nrb, int E,
                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ n_local, int eb, int L, int BM,
@@ -247,7 +247,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ block_
     int key = 0;
     for (int b = t_first / so.block_tokens; b <= t_last / so.block_tokens && b < so.n_blocks; ++b)
       key = max(key, (int)so.pos[b]);
-    s_key[mt] = key;
+    // expert first: the experts in flight at once stay few, so their weights
+    // stay in the last-level cache (all of them do not); readiness within an
+    // expert
+    s_key[mt] = l * MK_MAX_UNITS + key;
   }
   __syncthreads();
   for (int mt = e; mt < n_mt; mt += 1024) {
@@ -463,7 +466,7 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
   if (p.hold && !all_landed) {
     uint32_t ok = 1;
     if (tid == 0) {
-      ok = wait_geq_relaxed(&h->aux[0], all_items, h, p.spin_limit);
+      ok = wait_geq_sparse(&h->aux[0], all_items, h, p.spin_limit);
       if (ok) fence_acquire();
     }
     all_landed = wg_bcast(ok, sb) != 0u;            // on a watchdog expiry the per-tile waits give up too
@@ -514,7 +517,7 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
     char* const Yt = (char*)p.Y + ((int64_t)q0 * p.F + n0) * esz;
     uint32_t done = 1;
     if (kp < 0) {
-      store_tile(g, Yt, p.F, rows, p.F - n0, p.y_bf16);
+      store_tile<G, 16>(g, Yt, p.F, rows, p.F - n0, p.y_bf16);   // through the L2: little for a release to write back
     } else {
       const uint32_t tq = q - sp.n_whole;                        // tail tile index
       float* slots = p.kp_slots + (int64_t)tq * sp.split * (G::BM * G::BN);
