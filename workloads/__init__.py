@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = [
     "f32_to_bf16_bits", "AgWorkload", "RsWorkload", "MoeWorkload", "CONFIGS",
-    "make_ag", "make_rs", "make_moe", "moe_combine_inputs", "make_ring", "fingerprint",
+    "make_ag", "make_rs", "make_moe", "moe_combine_inputs", "moe_gate_weights", "make_ring", "fingerprint",
 ]
 
 
@@ -285,6 +285,17 @@ def moe_combine_inputs(w: "MoeWorkload", *, seed: int = 0):
     Yl = _normal_bf16(st[0], (w.T * min(w.k, w.L), w.F), 1.0)
     Yp = _normal_bf16(st[1], (w.T * w.k, w.F), 1.0)
     return Yl, Yp
+
+
+def moe_gate_weights(w: "MoeWorkload", seed: int = 0, dist: str = "normal") -> np.ndarray:
+    """Gate weights W_gate [H x E] bf16 for an MoE workload: N(0, 1/H), so the
+    logits have about unit variance; dist="int": integers in {-2..2}.
+    Its own stream (seed, 9001): the workload's tensors are unchanged."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 9001])))
+    H, E = w.X.shape[1], w.logits.shape[1]
+    if dist == "int":
+        return f32_to_bf16_bits(rng.integers(-2, 2, size=(H, E), endpoint=True).astype(np.float32))
+    return _normal_bf16(rng, (H, E), 1.0 / H)
 
 
 def make_ring(H: int, S: int, D: int, R: int, *, seed: int = 0, step_delay_ns: int = 0,
