@@ -324,6 +324,24 @@ def bench_moe(args, stream, extra=True):
         r["combine_gbs"] = cbytes / ck / 1e6
         r["combine_hbm_frac"] = cbytes / ck / 1e6 / PEAK_HBM_GBS
         del Yp
+        # the gate GEMM before routing: logits = X @ W_gate (T x H x E, fp32 out)
+        Wg = torch.from_numpy(wl.moe_gate_weights(w, seed=args.seed).view(np.int16)).cuda().view(torch.bfloat16)
+        glog = torch.empty(w.T, w.E, dtype=torch.float32, device="cuda")
+        gws = mk.workspace(mk.mk_moe_gate_workspace(w.T, w.H, w.E))
+
+        def gate(i):
+            mk.mk_moe_gate(p0.X, Wg, glog, gws, stream=stream, check=False)
+
+        _, gk = timed(gate, 20, 5, stream)
+        gflops = 2.0 * w.T * w.H * w.E
+        gbytes = w.T * w.H * 2 + w.H * w.E * 2 + w.T * w.E * 4
+        r["gate_ms"] = gk
+        r["gate_tflops"] = gflops / gk / 1e9
+        r["gate_gbs"] = gbytes / gk / 1e6
+        r["gate_roofline"] = dict(bound="hbm", achieved=round(gbytes / gk / 1e6, 2), peak=PEAK_HBM_GBS, unit="GB/s",
+                                  frac=round(gbytes / gk / 1e6 / PEAK_HBM_GBS, 4), traffic=None,
+                                  mfma_frac=round(gflops / gk / 1e9 / PEAK_BF16_TFLOPS, 4))
+        del Wg, glog, gws
         for tag, kw in [("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
                         ("n_copy128", dict(n_copy=128)), ("xcd_queues", dict(queue_mode=1)),
                         ("expert_order", dict(queue_mode=2)), ("hold", dict(queue_mode=3)),

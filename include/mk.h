@@ -300,6 +300,25 @@ int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t T, int64_t 
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * MoE gate GEMM  (the step before [P1] "Los cinco núcleos fusionados", row
+ * Envío MoE + GEMM: routing ranks one logit per token and expert; the pages
+ * start from those logits)
+ *
+ * logits [T x E] fp32 = X [T x H] bf16 @ W_gate [H x E] bf16 (column e is
+ * expert e's gate vector), fp32 accumulation of the exact bf16 products, no
+ * bias.  The output feeds mk_moe_dispatch_gemm's `logits`.  When the output
+ * has fewer 128 x 128 tiles than the device has CUs, the contraction is cut
+ * into up to 8 parts whose fp32 sums are parked in the workspace and added in
+ * part order by the part that finishes last (the result does not depend on
+ * timing).  Workspace: mk_moe_gate_workspace(T, H, E) bytes, zero-filled
+ * before first use (mk_workspace_init); every call leaves it ready for the
+ * next.  Limits: H and E multiples of 8, E <= MK_MAX_EXPERTS.
+ * ------------------------------------------------------------------------- */
+size_t mk_moe_gate_workspace(int64_t T, int64_t H, int E);
+int mk_moe_gate(const void* X, const void* W_gate, int64_t T, int64_t H, int E, float* logits,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * MoE combine  (the step after [P1] "Los cinco núcleos fusionados", row
  * Envío MoE + GEMM, which the pages do not describe)
  *

@@ -331,3 +331,19 @@ def test_load_after_foreign_runtime_raises():
                 "from tile_pipelined_gemm_amd import mk; mk.load()")
     assert r.returncode != 0
     assert "two HIP runtimes" in r.stderr
+
+
+def test_moe_gate_validation(lib):
+    g = lambda T=256, H=256, E=64, x=FAKE, ws=FAKE, wb=1 << 26: lib.mk_moe_gate(x, FAKE, T, H, E, FAKE, ws, wb, None)
+    assert g(T=0) == mk.MK_ERR_INVALID
+    assert g(H=4) == mk.MK_ERR_INVALID
+    assert g(H=100) == mk.MK_ERR_UNSUPPORTED
+    assert g(E=12) == mk.MK_ERR_UNSUPPORTED
+    assert g(E=2048) == mk.MK_ERR_UNSUPPORTED
+    assert g(x=None) == mk.MK_ERR_INVALID
+    assert g(x=FAKE + 2) == mk.MK_ERR_INVALID
+    assert g(ws=None) == mk.MK_ERR_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        assert g() == mk.MK_ERR_HIP                                 # valid: the device query fails
+    assert lib.mk_moe_gate_workspace(4096, 7168, 256) >= 256

@@ -29,6 +29,7 @@ EXPORTS = [
     "mk_ag_gemm_workspace", "mk_ag_gemm", "mk_ag_gemm_noalloc", "mk_gemm_rs_workspace", "mk_gemm_rs",
     "mk_gemm_ar_workspace", "mk_gemm_ar",
     "mk_moe_dispatch_gemm_workspace", "mk_moe_dispatch_gemm", "mk_moe_combine_workspace", "mk_moe_combine",
+    "mk_moe_gate_workspace", "mk_moe_gate",
     "mk_ring_attn_workspace", "mk_ring_attn",
     "mk_workspace_init",
     "mk_poll_status", "mk_status_string", "mk_last_error", "mk_tile_name", "mk_version",
@@ -115,6 +116,10 @@ def load(path: Optional[str] = None):
     lib.mk_moe_dispatch_gemm.argtypes = [vp, vp, i64, i64, i32, i32, pp, i32, i32, i64,
                                          vp, vp, vp, vp, vp, vp, vp, i32,
                                          C.POINTER(mk_arrival), C.POINTER(mk_launch), vp, sz, vp]
+    lib.mk_moe_gate_workspace.restype = sz
+    lib.mk_moe_gate_workspace.argtypes = [i64, i64, i32]
+    lib.mk_moe_gate.restype = i32
+    lib.mk_moe_gate.argtypes = [vp, vp, i64, i64, i32, vp, vp, sz, vp]
     lib.mk_moe_combine_workspace.restype = sz
     lib.mk_moe_combine_workspace.argtypes = [i64, i32]
     lib.mk_moe_combine.restype = i32
@@ -246,6 +251,19 @@ def mk_gemm_rs_workspace(M, K, N, R, out_dtype=MK_F32) -> int:
 
 def mk_moe_dispatch_gemm_workspace(T, H, E, k, L, F) -> int:
     return load().mk_moe_dispatch_gemm_workspace(T, H, E, k, L, F)
+
+
+def mk_moe_gate_workspace(T, H, E) -> int:
+    return load().mk_moe_gate_workspace(T, H, E)
+
+
+def mk_moe_gate(X, W_gate, logits, ws, *, stream=None, check=True) -> int:
+    """X [T, H] and W_gate [H, E] bf16; logits [T, E] float32 (written)."""
+    T, H = X.shape
+    E = W_gate.shape[1]
+    rc = load().mk_moe_gate(_ptr(X), _ptr(W_gate), T, H, E, _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream))
+    return _check(rc) if check else rc
 
 
 def mk_moe_combine_workspace(T, k) -> int:
