@@ -113,10 +113,15 @@ typedef struct mk_launch {
                              4-slice ring (K % 128 == 0);
                              9 128x128 direct-to-LDS with an 8-slice ring (AG only,
                              K % 256 == 0; the AG default when M <= 128);
-                             10 256x256 direct-to-LDS with 8 waves (AG only, K % 128 == 0).
+                             10 256x256 direct-to-LDS with 8 waves (AG only, K % 128 == 0);
+                             11 128x128 producer/consumer: B streamed by 4 producer waves
+                             into a 16-slice ring, A read from a packed copy in the
+                             workspace that the copy workgroups write (AG only, M <= 128,
+                             K % 128 == 0, not mk_ag_gemm_noalloc).
                              Defaults: AG 5 when 256x256 tiles give every CU one
-                             (K % 128 == 0), 9 for a single 128-row tile row with N >= 256
-                             (8 if K % 256 != 0), else a register-staged tile; GEMM+RS/AR 5
+                             (K % 128 == 0), 11 for a single 128-row tile row with N >= 256
+                             (9 without a workspace, 8 if K % 256 != 0 as well), else a
+                             register-staged tile; GEMM+RS/AR 5
                              when K % 128 == 0 and the owner blocks hold whole 256-row tiles,
                              else 2; MoE 5 when F >= 256 and H % 128 == 0, 2 when F < 256,
                              else 1.
@@ -125,7 +130,9 @@ typedef struct mk_launch {
   uint32_t spin_limit_us; /* watchdog for every wait; 0 = 2,000,000 us */
   int32_t* tile_log;      /* device int32 or NULL: per-tile record, see each op */
   int32_t copy_kib;       /* AG, GEMM+RS/AR: bytes per copy work item in KiB (one release each);
-                             0 = 1024; rounded to whole rows inside one unit and shard */
+                             0 = 1024 (AG: at most 2 x the bytes of A / CUs, at least one
+                             row, so a small A still spreads over many copy workgroups);
+                             rounded to whole rows inside one unit and shard */
   int32_t copy_policy;    /* AG copy stores: 0 = default (2), 1 = write-back
                              through the XCD L2, 2 = write-through (sc1): the
                              release after each item then has little to write back */
@@ -168,6 +175,9 @@ typedef struct mk_launch {
  *   copy_log (optional): per copy work item (in queue order), 8 int32
  *   {unit, part, workgroup, t_start, t_end, 0, 0, 0}.
  * ------------------------------------------------------------------------- */
+/* Workspace bytes: a 256-byte header, 256 arrival counters and, for a single
+ * 128-row tile row (R*m_shard <= 128) with K % 128 == 0, room for the packed
+ * copy of A (128 x K bf16) that tile 11 reads. */
 size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_t N, int32_t unit_rows);
 int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
                const void* B, int64_t N, void* C, int c_dtype, void* a_gathered,
@@ -188,7 +198,9 @@ int mk_ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t K,
  *   All calls on one GPU share the array: calls that overlap on one GPU (on
  *   different streams without ordering between them, or from several host
  *   threads) race and give undefined results.  Order them.
- *   The workspace needed (mk_ag_gemm_workspace) must fit in 4 KiB, else
+ *   The array holds the header and the arrival counters (1280 bytes; the
+ *   packed copy of A that tile 11 reads is not kept, so that tile is not
+ *   used here: MK_ERR_UNSUPPORTED if launch->tile asks for it); it must fit in 4 KiB, else
  *   MK_ERR_UNSUPPORTED.  arrival->withhold must be -1 (MK_ERR_INVALID
  *   otherwise): with no workspace there is no status for mk_poll_status, so
  *   a watchdog expiry is not reported (the kernels still exit).

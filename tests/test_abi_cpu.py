@@ -34,8 +34,8 @@ def test_support_functions(lib):
     assert lib.mk_version() >= 1
     assert lib.mk_status_string(mk.MK_ERR_TIMEOUT) == b"watchdog timeout"
     assert mk.mk_tile_name(0) == "auto" and mk.mk_tile_name(1) == "256x256"
-    assert [mk.mk_tile_name(i) for i in range(5, 11)] == ["256x256dma", "128x128dma", "256x128dma", "128x256dma",
-                                                         "128x128dma8", "256x256dma_w8"]
+    assert [mk.mk_tile_name(i) for i in range(5, 12)] == ["256x256dma", "128x128dma", "256x128dma", "128x256dma",
+                                                         "128x128dma8", "256x256dma_w8", "128x128pc"]
     assert mk.mk_tile_name(99) is None
 
 
@@ -93,6 +93,18 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _ag(lib) == mk.MK_ERR_HIP
+
+
+def test_ag_workspace_holds_packed_a_for_a_single_tile_row(lib):
+    # header + 256 unit counters; a single 128-row tile row with K % 128 == 0
+    # adds the packed copy of A (128 x K bf16) at a 256-byte aligned offset
+    base = lib.mk_ag_gemm_workspace(8, 1024, 8192, 3584, 0)
+    assert base == 256 + 256 * 4
+    assert lib.mk_ag_gemm_workspace(8, 16, 8192, 28672, 0) == 1280 + 128 * 8192 * 2
+    assert lib.mk_ag_gemm_workspace(3, 40, 640, 392, 0) == 1280 + 128 * 640 * 2
+    assert lib.mk_ag_gemm_workspace(1, 128, 256, 512, 0) == 1280 + 128 * 256 * 2
+    assert lib.mk_ag_gemm_workspace(1, 129, 256, 512, 0) == base       # two tile rows
+    assert lib.mk_ag_gemm_workspace(8, 16, 8192 + 64, 28672, 0) == base  # K % 128 != 0
 
 
 def _ag_noalloc(lib, R=2, m=64, K=128, N=64, c_dtype=mk.MK_BF16, arrival=None, shards=None, launch=None):

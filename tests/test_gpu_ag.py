@@ -181,6 +181,18 @@ def test_full_size_skinny_config_whole_output(gpu):
     _whole_output(w, prob, "skinny AG 128x8192x28672")
 
 
+def test_full_size_skinny_config_producer_consumer_tile(gpu):
+    # tile 11 at the full skinny shape: the same bits as the 8-slice ring tile
+    from tests.full_refs import ag_product
+    w, _ = ag_product("skinny_ag")
+    prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_128x128_PC))
+    _whole_output(w, prob, "skinny AG 128x8192x28672, producer/consumer tile")
+    ref = prob.output().copy()
+    prob.run(launch=gpu.make_launch(tile=gpu.TILE_128x128_DMA8))
+    torch.cuda.synchronize()
+    assert np.array_equal(prob.output(), ref)
+
+
 # ---- more tiles than workgroups with a partial last round: 272 tiles of
 # 256x256 on 256 workgroups ----
 def _round_workload(dist, out_dtype):
@@ -244,7 +256,8 @@ def test_skinny_output_independent_of_grid_mode_and_engine(gpu):
     outs = []
     for kw in [dict(), dict(grid=80), dict(grid=3), dict(mode=1), dict(n_copy=5), dict(queue_mode=1),
                dict(tile=gpu.TILE_128x128_DMA), dict(tile=gpu.TILE_128x128), dict(tile=gpu.TILE_128x256),
-               dict(tile=gpu.TILE_128x128_DMA8), dict(tile=gpu.TILE_256x128_DMA)]:
+               dict(tile=gpu.TILE_128x128_DMA8), dict(tile=gpu.TILE_256x128_DMA), dict(tile=gpu.TILE_128x128_PC),
+               dict(tile=gpu.TILE_128x128_PC, mode=1), dict(tile=gpu.TILE_128x128_PC, grid=7)]:
         prob.Ag.fill_(float("nan"))
         prob.C.zero_()
         prob.run(launch=gpu.make_launch(**kw))
@@ -350,6 +363,79 @@ def test_eight_wave_dma_tile_full_size_ag_config(gpu):
     prob.run(launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA))
     torch.cuda.synchronize()
     assert np.array_equal(prob.output(), ref)
+
+
+def test_producer_consumer_tile_matches_register_and_dma_tiles(gpu):
+    # tile 11 (one 128-row tile row, A read from its packed copy): M = 120 and
+    # N = 392 ragged; K = 640 = 20 slices (one and a quarter turns of the
+    # 16-slice ring, so the producers' DMAs past the end are exercised), 128
+    # (fewer slices than the ring) and 4096
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    for K in (640, 128, 4096):
+        w = wl.make_ag(3, 40, K, 392, seed=54, unit_rows=20, max_delay_ns=5000)
+        prob = AgProblem(w)
+        outs = []
+        for kw in [dict(tile=gpu.TILE_128x128), dict(tile=gpu.TILE_128x128_PC), dict(tile=gpu.TILE_128x128_DMA),
+                   dict(tile=gpu.TILE_128x128_PC, mode=1), dict(tile=gpu.TILE_128x128_PC, grid=3),
+                   dict(tile=gpu.TILE_128x128_PC, copy_kib=16), dict(tile=gpu.TILE_128x128_PC, copy_policy=1), dict()]:
+            prob.Ag.fill_(float("nan"))
+            prob.ws.fill_(255)                     # the packed copy must be rewritten by every call
+            prob.ws[:1280].zero_()                 # header and unit counters
+            prob.C.zero_()
+            prob.run(launch=gpu.make_launch(**kw))
+            torch.cuda.synchronize()
+            assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK, (K, kw)
+            outs.append(prob.output())
+        C64, _ = og.ag_gemm(w.shards, w.B, "bf16")
+        assert_close(out_to_f64(outs[1], "bf16"), C64, "bf16", f"producer/consumer tile, K={K}")
+        for i, o in enumerate(outs[1:], 1):
+            assert np.array_equal(outs[0], o), f"K={K} launch {i} differs"
+
+
+def test_producer_consumer_tile_gemm_alone_packs_the_gathered_rows(gpu):
+    # mode 2 gathers (and packs); mode 3 (the GEMM alone) packs a_gathered as
+    # it is, so a GEMM after a cleared workspace and a changed a_gathered
+    # still follows a_gathered
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = wl.make_ag(4, 32, 1024, 640, seed=57, unit_rows=32)
+    prob = AgProblem(w)
+    prob.run(launch=gpu.make_launch(tile=gpu.TILE_128x128_PC, mode=2))
+    torch.cuda.synchronize()
+    prob.ws.fill_(255)
+    prob.ws[:1280].zero_()
+    prob.Ag[:32] = -prob.Ag[:32]
+    prob.run(launch=gpu.make_launch(tile=gpu.TILE_128x128_PC, mode=3))
+    torch.cuda.synchronize()
+    got = prob.output().copy()
+    prob.run(launch=gpu.make_launch(tile=gpu.TILE_128x128, mode=3))
+    torch.cuda.synchronize()
+    assert np.array_equal(prob.output(), got)
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+
+
+def test_producer_consumer_tile_integer_inputs_bit_exact(gpu):
+    w = wl.make_ag(2, 60, 512, 264, seed=55, dist="int", unit_rows=30, out_dtype="f32")
+    prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_128x128_PC))
+    _, C = og.ag_gemm(w.shards, w.B, "f32")
+    assert np.array_equal(prob.output(), C)
+
+
+def test_producer_consumer_tile_rejections(gpu):
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    lau = gpu.make_launch(tile=gpu.TILE_128x128_PC)
+    # K % 128 != 0
+    prob = AgProblem(wl.make_ag(2, 64, 320, 128, seed=56))
+    assert prob.run(launch=lau, check=False) == gpu.MK_ERR_UNSUPPORTED
+    # two tile rows
+    prob = AgProblem(wl.make_ag(2, 65, 256, 128, seed=56))
+    assert prob.run(launch=lau, check=False) == gpu.MK_ERR_UNSUPPORTED
+    # no workspace for the packed copy
+    prob = AgProblem(wl.make_ag(2, 64, 256, 128, seed=56))
+    rc = gpu.mk_ag_gemm_noalloc(prob.shards, prob.B, prob.C, prob.Ag, launch=lau, check=False)
+    assert rc == gpu.MK_ERR_UNSUPPORTED
+    # a workspace sized before the packed copy was part of it
+    prob.ws = prob.ws[:1280]
+    assert prob.run(launch=gpu.make_launch(), check=False) == gpu.MK_ERR_WORKSPACE
 
 
 def test_deep_ring_dma_tile_integer_inputs_bit_exact(gpu):

@@ -14,6 +14,10 @@
 //   compute take output tiles from a queue ordered by when their rows land,
 //           acquire the arrival counters of the units under the tile, run the
 //           MFMA K loop and store the tile.
+// With the producer/consumer tile (a single 128-row tile row) the copy
+// workgroups also write each part into a packed copy of A in MFMA operand
+// order (in the workspace), which that tile reads instead of the gathered
+// rows; it is published by the same release.
 // Producers always hold earlier tickets than the consumers that wait on
 // them, so the spin waits cannot deadlock even if the grid is not fully
 // co-resident.  Every wait is bounded by a watchdog.
@@ -24,6 +28,7 @@
 
 #include "mk_device.h"
 #include "mk_gemm_dma.h"
+#include "mk_gemm_pc.h"
 #include "mk_host.h"
 #include "mk_tiles.h"
 
@@ -31,13 +36,44 @@ using namespace mk;
 
 namespace {
 
-enum { MODE_FUSED = 0, MODE_COPY = 1, MODE_GEMM = 2 };
+enum { MODE_FUSED = 0, MODE_COPY = 1, MODE_GEMM = 2, MODE_PACK = 3 };
+
+template <class G> struct PackedA { static constexpr bool value = false; };
+template <int S, int P> struct PackedA<TileGemmPC<S, P>> { static constexpr bool value = true; };
+
+// Copy of one part (a contiguous block of n16 16-byte chunks: whole rows of
+// kc chunks, the first being row row0 of the gathered A) that also writes
+// every chunk into the packed copy of A: row r, chunk c at block r / 128,
+// offset TileGemmPC::packed_offset(r % 128, c).  Chunks past the part are
+// loaded as zeros and stored nowhere (their packed offset is made out of
+// range).  store_ag false: the packed copy only (A already gathered).
+template <int POLICY>
+__device__ __forceinline__ void copy_pack_block(__amdgpu_buffer_rsrc_t src, __amdgpu_buffer_rsrc_t dst,
+                                                __amdgpu_buffer_rsrc_t packed, int row0, int kc, int n16, int tid,
+                                                int nt, bool store_ag) {
+  const uint32_t block_bytes = (uint32_t)TileGemmPC<>::BM * (uint32_t)kc * 16u;
+  for (int base = 0; base < n16; base += nt * COPY_UNROLL) {
+    u32x4 v[COPY_UNROLL];
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) v[u] = bload(src, (uint32_t)(base + u * nt + tid) * 16u, 0);
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) {
+      const int e = base + u * nt + tid;
+      if (store_ag) bstore<POLICY>(dst, (uint32_t)e * 16u, 0, v[u]);
+      const int r = row0 + e / kc, c = e % kc;
+      const uint32_t off = e < n16 ? (uint32_t)(r >> 7) * block_bytes + TileGemmPC<>::packed_offset(r & 127, c) : OOB;
+      bstore<POLICY>(packed, off, 0, v[u]);
+    }
+  }
+}
 
 struct AgParams {
   const uint16_t* shard[MK_MAX_RANKS];
   const uint16_t* B;
   void* C;
   uint16_t* Ag;
+  uint16_t* Ap;         // packed copy of A for the producer/consumer tile, else NULL
+  uint32_t ap_bytes;
   WsHeader* hdr;
   uint32_t* unit_cnt;   // [n_units] parts landed
   int32_t* tile_log;
@@ -68,14 +104,17 @@ __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uin
   }
   const uint32_t n_work = (uint32_t)p.n_units * p.parts;
   const int n16 = p.part_rows * (p.K / 8);       // 16-byte chunks per part
+  // MODE_PACK: only the packed copy, from the gathered rows, with no delays
+  const bool pack_only = p.mode == MODE_PACK;
+  const __amdgpu_buffer_rsrc_t packed = make_rsrc(uni(p.Ap), p.Ap ? p.ap_bytes : 0u);
   uint32_t w = wg_bcast(tid == 0 ? add_relaxed(&h->copy_next, 1u) : 0u, sb);
   while (w < n_work) {
     const int j = w / p.parts, part = w % p.parts;
     const int c = p.order[j];
-    if (c != p.withhold) {                         // a withheld unit never lands (failure tests)
+    if (c != p.withhold || pack_only) {            // a withheld unit never lands (failure tests)
       uint32_t t_start = 0;
       if (tid == 0) {
-        wait_until(t0 + p.delay_ticks[c], p.spin_limit);
+        if (!pack_only) wait_until(t0 + p.delay_ticks[c], p.spin_limit);
         t_start = (uint32_t)now_ticks();
       }
       __syncthreads();
@@ -85,11 +124,18 @@ __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uin
       // and stores are dropped, so the loop needs no per-element guard (a
       // guarded store would be its own branch, and the compiler would wait for
       // every earlier memory operation before each one).
-      const __amdgpu_buffer_rsrc_t src =
-          make_rsrc(uni(p.shard[row0 / p.m_shard] + (int64_t)(row0 % p.m_shard) * p.K), p.part_bytes);
       const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Ag + (int64_t)row0 * p.K), p.part_bytes);
-      if (p.copy_wt) copy_block<16>(src, dst, n16, tid, nt);
-      else copy_block<0>(src, dst, n16, tid, nt);
+      const __amdgpu_buffer_rsrc_t src =
+          pack_only ? dst
+                    : make_rsrc(uni(p.shard[row0 / p.m_shard] + (int64_t)(row0 % p.m_shard) * p.K), p.part_bytes);
+      if (p.Ap) {
+        if (p.copy_wt) copy_pack_block<16>(src, dst, packed, row0, p.K / 8, n16, tid, nt, !pack_only);
+        else copy_pack_block<0>(src, dst, packed, row0, p.K / 8, n16, tid, nt, !pack_only);
+      } else if (p.copy_wt) {
+        copy_block<16>(src, dst, n16, tid, nt);
+      } else {
+        copy_block<0>(src, dst, n16, tid, nt);
+      }
       // Release only: the copier never reads what others publish, so the
       // acquire half of a full fence (an L2 invalidate that would also drop
       // the lines of the GEMM tiles running on this XCD) is not needed.
@@ -100,7 +146,7 @@ __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uin
         const uint32_t t_end = (uint32_t)now_ticks();
         add_relaxed(&p.unit_cnt[c], 1u);
         add_relaxed(&h->aux[0], 1u);                 // parts landed in total
-        if (p.copy_log) {
+        if (p.copy_log && !pack_only) {
           int32_t* L = p.copy_log + 8 * (int64_t)w;
           L[0] = c; L[1] = part; L[2] = (int32_t)blockIdx.x;
           L[3] = (int32_t)t_start; L[4] = (int32_t)t_end;
@@ -161,7 +207,8 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, 
     }
     if (ok) {                                      // else the watchdog expired: skip the tile
       const uint32_t t_ready = (uint32_t)now_ticks();
-      g.bind(p.Ag + (int64_t)m0 * p.K, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
+      const uint16_t* A = PackedA<G>::value ? p.Ap + (int64_t)tm * G::BM * p.K : p.Ag + (int64_t)m0 * p.K;
+      g.bind(A, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
       g.run(sm);
       const int64_t esz = p.c_bf16 ? 2 : 4;
       // written through the L2: a copy workgroup's release on this XCD then
@@ -206,8 +253,9 @@ template <class G, class SM>
 __device__ __forceinline__ void ag_body(const AgParams& p, SM sm, uint32_t* sb) {
   WsHeader* h = p.hdr;
   const uint32_t ticket = wg_bcast(threadIdx.x == 0 ? add_relaxed(&h->ticket, 1u) : 0u, sb);
-  if (p.mode == MODE_COPY || (p.mode == MODE_FUSED && ticket < (uint32_t)p.n_copy)) ag_copy_role(p, h, sb);
-  if (p.mode != MODE_COPY) ag_compute_role<G>(p, h, sm, sb);
+  if (p.mode == MODE_COPY || p.mode == MODE_PACK || (p.mode == MODE_FUSED && ticket < (uint32_t)p.n_copy))
+    ag_copy_role(p, h, sb);
+  if (p.mode == MODE_FUSED || p.mode == MODE_GEMM) ag_compute_role<G>(p, h, sm, sb);
   ag_finish(p, h, sb);
 }
 
@@ -226,9 +274,22 @@ __global__ __launch_bounds__(G::NT) void ag_kernel(const AgParams p) {
 
 }  // namespace
 
+// Workspace: header | per-unit arrival counters | (when A is a single
+// 128-row tile row with K % 128 == 0) the packed copy of A for the
+// producer/consumer tile, 128 x K bf16.
+struct AgWs { size_t pack, total; };
+static bool ag_packs(int64_t M, int64_t K) { return M >= 1 && M <= TileGemmPC<>::BM && K >= 8 && TileGemmPC<>::supports_k((int)K); }
+static AgWs ag_ws_layout(int64_t K, bool pack) {
+  AgWs w;
+  const size_t base = sizeof(WsHeader) + MK_MAX_UNITS * sizeof(uint32_t);
+  w.pack = (base + 255) & ~(size_t)255;
+  w.total = pack ? w.pack + (size_t)TileGemmPC<>::BM * (size_t)K * 2 : base;
+  return w;
+}
+
 extern "C" size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_t N, int32_t unit_rows) {
-  (void)R; (void)m_shard; (void)K; (void)N; (void)unit_rows;
-  return sizeof(WsHeader) + MK_MAX_UNITS * sizeof(uint32_t);
+  (void)N; (void)unit_rows;
+  return ag_ws_layout(K, ag_packs((int64_t)R * m_shard, K)).total;
 }
 
 // ------------------------------------------------- entry point without allocation
@@ -297,6 +358,11 @@ static int run_ag(AgParams& p, const mk_launch& o, const mkh::Schedule& s, const
       p.n_copy = grid;
       hipLaunchKernelGGL(ag_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
       if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "copy kernel launch");
+    } else if (p.Ap) {   // the GEMM alone reads the packed copy: pack a_gathered as it is first
+      p.mode = MODE_PACK;
+      p.n_copy = grid;
+      hipLaunchKernelGGL(ag_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
+      if ((e = hipGetLastError()) != hipSuccess) return mkh::hip_fail(e, "pack kernel launch");
     }
     if (o.mode != 2) {
       p.mode = MODE_GEMM;
@@ -342,7 +408,11 @@ static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t 
   mkh::Schedule s;
   int rc = mkh::make_schedule(arrival, M, R, &s);
   if (rc) return rc;
-  const size_t ws_need = mk_ag_gemm_workspace(R, m_shard, K, N, s.unit_rows);
+  // Without a workspace argument there is no room for the packed copy of A,
+  // so the producer/consumer tile is not used.
+  const bool pack = !no_alloc && ag_packs(M, K);
+  const AgWs lay = ag_ws_layout(K, pack);
+  const size_t ws_need = lay.total;
   if (no_alloc) {
     if (s.withhold != -1)
       return fail(MK_ERR_INVALID, "withhold is not available without a workspace (no status to poll)");
@@ -392,7 +462,12 @@ static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t 
   const int64_t row_bytes = K * 2;
   int g = s.unit_rows, b = (int)m_shard;
   while (b) { const int t = g % b; g = b; b = t; }   // gcd(unit_rows, m_shard)
-  const int64_t item_bytes = (int64_t)(o.copy_kib > 0 ? o.copy_kib : 1024) << 10;
+  // Default: 1 MiB, or less where A is small, so that the items still keep
+  // about half the CUs copying (a single item's copy is bound by load and
+  // store latency; at M = 128, K = 8192 eight 256 KiB items took 40 us
+  // to land, 128 one-row items 12 us).
+  int64_t item_bytes = (int64_t)(o.copy_kib > 0 ? o.copy_kib : 1024) << 10;
+  if (o.copy_kib == 0) item_bytes = std::min<int64_t>(item_bytes, std::max<int64_t>(row_bytes, M * row_bytes * 2 / std::max(d->n_cu, 2)));
   int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(g, item_bytes / row_bytes));
   // whole rows that divide the unit and the shard; at most 1 GiB per part so
   // 32-bit buffer offsets cover it
@@ -408,16 +483,20 @@ static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t 
   const size_t clear = no_alloc ? ws_need : 0;
   int tile = o.tile ? o.tile : mk_default_tile(M, N, K);
   // The 256x256 tile switches to the direct-to-LDS engine by default.  A
-  // single 128-row tile row (a skinny A, the GEMM streams B) takes the
-  // 128x128 direct-to-LDS tile with the 8-slice ring at one workgroup per CU:
-  // every CU with a tile streams its own B column stripe, with no MFMA work
-  // spent on empty rows (at M = 128, K = 8192, N = 28672 the GEMM phase
-  // measured 0.154 ms against 0.177 ms for the 128x256 tile, which only
-  // gives 112 CUs a tile, and 0.160 ms for the half-empty 256x128 tile).
-  // Where K is not a multiple of 256 the 128x256 direct-to-LDS tile is used.
+  // single 128-row tile row (a skinny A, the GEMM streams B) takes a 128x128
+  // tile at one workgroup per CU: every CU with a tile streams its own B
+  // column stripe, with no MFMA work spent on empty rows.  The
+  // producer/consumer tile (A from its packed copy) is the default there: at
+  // M = 128, K = 8192, N = 28672 its GEMM kernel took 0.128 ms against
+  // 0.152 ms for the direct-to-LDS tile with the 8-slice ring (which loads A
+  // through the same DMA stream as B), 0.177 ms for the 128x256 tile (112
+  // CUs with a tile) and 0.160 ms for the half-empty 256x128 tile.  Without
+  // a workspace for the packed copy the 8-slice ring is used, and where K is
+  // not a multiple of 256 the 128x256 direct-to-LDS tile.
   if (!o.tile && tile == TILE_256x256 && TileGemmD<256, 256>::supports_k((int)K)) tile = TILE_256x256_DMA;
   if (!o.tile && tile == TILE_128x128 && M <= 128 && N >= 256) {
-    if (TileGemmD<128, 128, true, 8>::supports_k((int)K)) tile = TILE_128x128_DMA8;
+    if (pack) tile = TILE_128x128_PC;
+    else if (TileGemmD<128, 128, true, 8>::supports_k((int)K)) tile = TILE_128x128_DMA8;
     else if (TileGemmD<128, 256>::supports_k((int)K)) tile = TILE_128x256_DMA;
   }
   if (mk_is_dma_tile(tile) && !TileGemmD<256, 256>::supports_k((int)K))
@@ -426,6 +505,12 @@ static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t 
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 256 == 0", tile);
   if (tile == TILE_256x256_DMA_W8 && !TileGemmD<256, 256, true, 4, 8>::supports_k((int)K))
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
+  if (tile == TILE_128x128_PC && !pack)
+    return fail(MK_ERR_UNSUPPORTED, "tile %d needs M <= 128, K %% 128 == 0 and a workspace (packed copy of A)", tile);
+  if (tile == TILE_128x128_PC) {
+    p.Ap = (uint16_t*)((char*)workspace + lay.pack);
+    p.ap_bytes = (uint32_t)(lay.total - lay.pack);
+  }
   switch (tile) {
     case TILE_256x256: return run_ag<TileGemm<256, 256, 2, 2>>(p, o, s, d, st, clear);
     case TILE_128x128: return run_ag<TileGemm<128, 128, 2, 2>>(p, o, s, d, st, clear);
@@ -437,6 +522,7 @@ static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t 
     case TILE_128x256_DMA: return run_ag<TileGemmD<128, 256>>(p, o, s, d, st, clear);
     case TILE_128x128_DMA8: return run_ag<TileGemmD<128, 128, true, 8>>(p, o, s, d, st, clear);
     case TILE_256x256_DMA_W8: return run_ag<TileGemmD<256, 256, true, 4, 8>>(p, o, s, d, st, clear);
+    case TILE_128x128_PC: return run_ag<TileGemmPC<>>(p, o, s, d, st, clear);
     default: return fail(MK_ERR_INVALID, "tile id %d", tile);
   }
 }

@@ -480,6 +480,7 @@ struct TileGemm {
 template <class G, int POLICY = 0>
 __device__ __forceinline__ void store_tile(const G& g, void* C, int64_t ld, int rows, int cols, bool bf16) {
   const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
+  if (w >= G::WM * G::WN) return;                   // waves that hold no accumulators (producers)
   const int wm = w % G::WM, wn = w / G::WM;
   const uint32_t esz = bf16 ? 2u : 4u;
   const uint32_t rbo = uni((uint32_t)ld * esz);

@@ -751,7 +751,7 @@ static int gemm_reduce(const void* A, const void* B, int64_t M, int64_t K, int64
   // the partial sums added from its accumulators its K loop spills.
   if (tile == TILE_256x256)
     return fail(MK_ERR_UNSUPPORTED, "tile %d is not available for GEMM+RS/AR (use tile %d)", tile, TILE_256x256_DMA);
-  if (tile == TILE_128x128_DMA8 || tile == TILE_256x256_DMA_W8)
+  if (tile == TILE_128x128_DMA8 || tile == TILE_256x256_DMA_W8 || tile == TILE_128x128_PC)
     return fail(MK_ERR_UNSUPPORTED, "tile %d is built for AllGather+GEMM only", tile);
   if (mk_is_dma_tile(tile) && !TileGemmD<256, 256>::supports_k((int)K))
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);

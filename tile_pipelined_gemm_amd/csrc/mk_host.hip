@@ -176,6 +176,6 @@ extern "C" int mk_wall_clock_khz(void) {
 extern "C" const char* mk_tile_name(int id) {
   static const char* names[TILE_COUNT] = {"auto",       "256x256",    "128x128",    "256x128",   "128x256",
                                                "256x256dma", "128x128dma", "256x128dma", "128x256dma",
-                                               "128x128dma8", "256x256dma_w8"};
+                                               "128x128dma8", "256x256dma_w8", "128x128pc"};
   return (id >= 0 && id < TILE_COUNT) ? names[id] : nullptr;
 }

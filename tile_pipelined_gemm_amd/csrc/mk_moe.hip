@@ -747,7 +747,7 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   if (!o.tile && tile == TILE_256x256 && TileGemmD<256, 256>::supports_k((int)H)) tile = TILE_256x256_DMA;
   if (mk_is_dma_tile(tile) && !TileGemmD<256, 256>::supports_k((int)H))
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs H %% 128 == 0", tile);
-  if (tile == TILE_128x128_DMA8 || tile == TILE_256x256_DMA_W8)
+  if (tile == TILE_128x128_DMA8 || tile == TILE_256x256_DMA_W8 || tile == TILE_128x128_PC)
     return fail(MK_ERR_UNSUPPORTED, "tile %d is built for AllGather+GEMM only", tile);
   switch (tile) {
     case TILE_256x256: return run_moe<TileGemm<256, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);

@@ -16,6 +16,8 @@ enum MkTile {
   TILE_128x128_DMA8 = 9,  // 128x128 direct-to-LDS with an 8-slice ring (128 KiB LDS, 1 workgroup per CU,
                           // K % 256 == 0): twice the operand bytes in flight, for GEMMs that stream B
   TILE_256x256_DMA_W8 = 10,  // 256x256 direct-to-LDS with 8 waves (2x4, two per SIMD; K % 128 == 0)
+  TILE_128x128_PC = 11,  // 128x128 producer/consumer: 4 compute waves load A into registers, 4 producer
+                         // waves stream B into a 16-slice LDS ring (K % 128 == 0; skinny, bandwidth-bound)
   TILE_COUNT
 };
 

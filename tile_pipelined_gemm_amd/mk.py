@@ -23,6 +23,7 @@ TILE_256x256, TILE_128x128, TILE_256x128, TILE_128x256, TILE_256x256_DMA = 1, 2,
 TILE_128x128_DMA, TILE_256x128_DMA, TILE_128x256_DMA = 6, 7, 8
 TILE_128x128_DMA8 = 9
 TILE_256x256_DMA_W8 = 10
+TILE_128x128_PC = 11
 
 # Symbols declared in include/mk.h (checked by the CPU tests).
 EXPORTS = [
