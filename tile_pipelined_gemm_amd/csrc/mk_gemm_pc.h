@@ -3,10 +3,13 @@
 // A while it streams its own column stripe of B).  128 x 128 output tile,
 // 8 waves:
 //
-//  * waves 0-3 compute (2 x 2, each a 64 x 64 block of 32x32 MFMA tiles).
-//    They load their A fragments straight from global memory into registers
-//    (A is L2-resident: all tiles share it), PA slices ahead, and read their
-//    B fragments from LDS with the transposing ds_read_b64_tr_b16;
+//  * waves 0-3 compute (by default 4 x 1, each a 32 x 128 block of 32x32
+//    MFMA tiles, so every A fragment is loaded once per workgroup; 2 x 2
+//    waves load each one twice and measured 2 % slower at M = 128,
+//    K = 8192, N = 28672).  They load their A fragments straight from global
+//    memory into registers (A is L2-resident: all tiles share it), PA slices
+//    ahead, and read their B fragments from LDS with the transposing
+//    ds_read_b64_tr_b16;
 //  * waves 4-7 produce: they only move B from HBM into a ring of STAGES
 //    32-deep K slices in LDS (buffer_load_dwordx4 ... lds, 8 KiB per slice),
 //    so the whole LDS holds B in flight.
@@ -47,12 +50,13 @@
 
 namespace mk {
 
-template <int STAGES_ = 16, int PA_ = 4>
+template <int STAGES_ = 16, int PA_ = 4, int CWM_ = 4>
 struct TileGemmPC {
   static constexpr int BM = 128, BN = 128, BK = 32, STAGES = STAGES_, PA = PA_;
-  static constexpr int WM = 2, WN = 2, CW = 4, PW = 4, WAVES = CW + PW;
+  static constexpr int WM = CWM_, WN = 4 / CWM_, CW = 4, PW = 4, WAVES = CW + PW;
   static constexpr int NT = 64 * WAVES;
-  static constexpr int TM = 64, TN = 64, FM = 2, FN = 2;
+  static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  static_assert(WM * WN == CW && FM >= 1 && FN >= 1, "compute wave grid");
   static constexpr bool PACKED_A = true;                      // A from a packed copy (packed_offset)
   static constexpr int B_BYTES = BK * BN * 2;                 // 8 KiB per stage
   static constexpr int B_INS = B_BYTES / 1024 / PW;           // DMA per producer wave per slice
@@ -66,7 +70,7 @@ struct TileGemmPC {
   f32x16 acc[FM][FN];
   __amdgpu_buffer_rsrc_t rA;
   u32x4 dB;
-  uint32_t wmA, ldbB, voA, voB;   // wmA: the wave's 64-row half of the tile
+  uint32_t wmA, ldbB, voA, voB;   // wmA: the wave's first 32-row group
   int nk;
 
   static __host__ __device__ constexpr bool supports_k(int K) { return K % (PA * BK) == 0; }
@@ -100,7 +104,7 @@ struct TileGemmPC {
     nk = uni(K) / BK;
     rA = make_rsrc(uni(A), uni((uint32_t)nk * (BM * BK * 2)));
     const int wm = (w % CW) % WM;
-    wmA = uni((uint32_t)wm);                       // 32-row groups 2 wm and 2 wm + 1
+    wmA = uni((uint32_t)(wm * FM));                // first of the wave's FM 32-row groups
     voA = (uint32_t)lane * 16u;
     // B: DMA instruction blk of a slice covers k-rows 4 blk .. 4 blk + 3;
     // lane L lands at 16 L, k-row L / 16, physical chunk L % 16 = logical
@@ -142,7 +146,7 @@ struct TileGemmPC {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        a.v[ks][i] = bload(rA, more ? voA : OOB, uni((((uint32_t)kt * 4u + wmA * 2u + (uint32_t)i) * 2u + (uint32_t)ks) * 1024u));
+        a.v[ks][i] = bload(rA, more ? voA : OOB, uni((((uint32_t)kt * 4u + wmA + (uint32_t)i) * 2u + (uint32_t)ks) * 1024u));
   }
 
   // byte offset of B fragment j's first transposing read in a stage
