@@ -359,6 +359,7 @@ def bench_moe(args, stream, extra=True):
         # the unfused sequence, where the GEMM follows its permute kernel
         r["overlap_eff"] = (tc + tg - kern) / min(tc, tg)
         r["overlap_eff_vs_unfused"] = (uk - kern) / tc
+    return r
 
 
 def bench_ring(args, stream, extra=True):
