@@ -172,14 +172,15 @@ def bench_ag(name, args, stream, extra=True):
         r["speedup_vs_unfused"] = uk / kern
         # role split and scheduling variants of the fused kernel
         variants = [("n_copy64", dict(n_copy=64)), ("copy_writeback", dict(copy_policy=1)),
-                    ("copy_kib512", dict(copy_kib=512)),
+                    ("copy_kib256", dict(copy_kib=256)),
                     ("xcd_queues", dict(queue_mode=1)),
                     ("copy_only", dict(mode=2)), ("gemm_only", dict(mode=3)),
                     ("gemm_only_xcd_queues", dict(mode=3, queue_mode=1))]
         if w.M >= 256:
             variants += [("tile_reg", dict(tile=mk.TILE_256x256)),
-                         ("tile_dma_w8", dict(tile=mk.TILE_256x256_DMA_W8)),
-                         ("gemm_only_dma_w8", dict(mode=3, tile=mk.TILE_256x256_DMA_W8))]
+                         ("tile_dma4", dict(tile=mk.TILE_256x256_DMA)),
+                         ("gemm_only_dma4", dict(mode=3, tile=mk.TILE_256x256_DMA)),
+                         ("copy_kib1024", dict(copy_kib=1024))]
         else:                                        # skinny: the 128-row tiles
             variants += [("tile_128x128", dict(tile=mk.TILE_128x128)),
                          ("tile_128x256_dma", dict(tile=mk.TILE_128x256_DMA)),

@@ -118,7 +118,7 @@ typedef struct mk_launch {
                              into a 16-slice ring, A read from a packed copy in the
                              workspace that the copy workgroups write (AG only, M <= 128,
                              K % 128 == 0, not mk_ag_gemm_noalloc).
-                             Defaults: AG 5 when 256x256 tiles give every CU one
+                             Defaults: AG 10 when 256x256 tiles give every CU one
                              (K % 128 == 0), 11 for a single 128-row tile row with N >= 256
                              (9 without a workspace, 8 if K % 256 != 0 as well), else a
                              register-staged tile; GEMM+RS/AR 5
@@ -130,8 +130,8 @@ typedef struct mk_launch {
   uint32_t spin_limit_us; /* watchdog for every wait; 0 = 2,000,000 us */
   int32_t* tile_log;      /* device int32 or NULL: per-tile record, see each op */
   int32_t copy_kib;       /* AG, GEMM+RS/AR: bytes per copy work item in KiB (one release each);
-                             0 = 1024 (AG: at most 2 x the bytes of A / CUs, at least one
-                             row, so a small A still spreads over many copy workgroups);
+                             0 = 1024 (AG: at most the bytes of A / CUs, at least one row,
+                             so every workgroup starts with about one item);
                              rounded to whole rows inside one unit and shard */
   int32_t copy_policy;    /* AG copy stores: 0 = default (2), 1 = write-back
                              through the XCD L2, 2 = write-through (sc1): the
