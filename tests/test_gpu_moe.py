@@ -112,6 +112,24 @@ def test_dma_tile_ragged_experts_integer_exact(gpu):
     assert np.array_equal(got["Y"], ref["Y"])
 
 
+def test_half_height_tail_tiles_integer_exact(gpu):
+    # expert row counts with tails of at most 128 rows (run by the 128x256
+    # engine) and of more (the 256x256 one), F ragged: exact on integer inputs,
+    # and the same bits as the register-staged engine, which has no half tile
+    w = wl.make_moe(2048, 256, 16, 4, 8, 520, seed=39, dist="int", block_tokens=256, out_dtype="f32")
+    prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA))
+    ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 0, "f32")
+    tails = [int(c) % 256 for c in ref["counts"][:8]]
+    assert any(0 < t <= 128 for t in tails) and any(t > 128 for t in tails), tails
+    got = _check_exact(prob, ref)
+    assert np.array_equal(got["Y"], ref["Y"])
+    y_dma = prob.outputs()["Y"].copy()
+    prob.Y.zero_()
+    prob.run(launch=gpu.make_launch(tile=gpu.TILE_256x256))
+    torch.cuda.synchronize()
+    assert np.array_equal(prob.outputs()["Y"], y_dma)
+
+
 def test_dma_tile_rejects_h_not_multiple_of_128(gpu):
     from tile_pipelined_gemm_amd.harness import MoeProblem
     w = wl.make_moe(128, 136, 16, 2, 8, 64, seed=37, block_tokens=64)

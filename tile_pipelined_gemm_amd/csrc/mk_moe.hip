@@ -24,6 +24,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "mk_device.h"
 #include "mk_gemm_dma.h"
@@ -426,8 +427,19 @@ __device__ __forceinline__ MoeSplit moe_split_plan(uint32_t n_tiles, int full, i
   return sp;
 }
 
+// Half-height engine for the last M-tile of an expert that holds at most 128
+// rows: a 256x256 tile would spend half its MFMAs on padding rows (at the MoE
+// shape about a tenth of the M-tiles are such tails).  The 128x256 tile runs
+// the same MFMA sequence per output element, so the bits do not change; it
+// uses the same stage buffers (smaller stages).
+template <class G> struct HalfTile { using type = void; };
+template <bool I, int S> struct HalfTile<TileGemmD<256, 256, I, S, 4>> {
+  using type = TileGemmD<128, 256, I, S, 4>;
+};
+
 template <class G, class SM>
 __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h, SM sm, uint32_t* sb) {
+  using G2 = typename HalfTile<G>::type;
   const int tid = threadIdx.x;
   const int n_mt = (int)uni((uint32_t)p.tile_base[p.L]);
   const uint32_t n_tiles = (uint32_t)n_mt * p.tiles_n;
@@ -510,23 +522,35 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
     const int q0 = p.offsets[e] - base_local + r0;              // landing row of the tile
     const int n0 = tn * G::BN;
     const int kpart = p.H / sp.split, k0 = kp < 0 ? 0 : kp * kpart;
-    g.bind(p.Xs + (int64_t)q0 * p.H + k0, p.H, rows, p.W[l] + (int64_t)k0 * p.F + n0, p.F, p.F - n0,
-           p.W[l] + (int64_t)p.H * p.F, kp < 0 ? p.H : kpart);
-    g.run(sm);
     const int64_t esz = p.y_bf16 ? 2 : 4;
     char* const Yt = (char*)p.Y + ((int64_t)q0 * p.F + n0) * esz;
     uint32_t done = 1;
-    if (kp < 0) {
-      store_tile<G, 16>(g, Yt, p.F, rows, p.F - n0, p.y_bf16);   // through the L2: little for a release to write back
-    } else {
-      const uint32_t tq = q - sp.n_whole;                        // tail tile index
-      float* slots = p.kp_slots + (int64_t)tq * sp.split * (G::BM * G::BN);
-      park_acc(g, slots + (int64_t)kp * (G::BM * G::BN));
-      wg_release();
-      done = wg_bcast(tid == 0 ? (uint32_t)(add_relaxed(&p.kp_cnt[tq], 1u) == (uint32_t)(sp.split - 1)) : 0u, sb);
-      if (done) {
-        if (sp.split == 2) store_parked_sum<G, 2>(slots, Yt, p.F, rows, p.F - n0, p.y_bf16);
-        else store_parked_sum<G, 4>(slots, Yt, p.F, rows, p.F - n0, p.y_bf16);
+    bool half = false;
+    if constexpr (!std::is_void<G2>::value) {
+      if (kp < 0 && rows <= G2::BM) {             // a whole tail tile of at most 128 rows
+        G2 g2;
+        g2.bind(p.Xs + (int64_t)q0 * p.H, p.H, rows, p.W[l] + n0, p.F, p.F - n0, p.W[l] + (int64_t)p.H * p.F, p.H);
+        g2.run(sm);
+        store_tile<G2, 16>(g2, Yt, p.F, rows, p.F - n0, p.y_bf16);
+        half = true;
+      }
+    }
+    if (!half) {
+      g.bind(p.Xs + (int64_t)q0 * p.H + k0, p.H, rows, p.W[l] + (int64_t)k0 * p.F + n0, p.F, p.F - n0,
+             p.W[l] + (int64_t)p.H * p.F, kp < 0 ? p.H : kpart);
+      g.run(sm);
+      if (kp < 0) {
+        store_tile<G, 16>(g, Yt, p.F, rows, p.F - n0, p.y_bf16);   // through the L2: little for a release to write back
+      } else {
+        const uint32_t tq = q - sp.n_whole;                        // tail tile index
+        float* slots = p.kp_slots + (int64_t)tq * sp.split * (G::BM * G::BN);
+        park_acc(g, slots + (int64_t)kp * (G::BM * G::BN));
+        wg_release();
+        done = wg_bcast(tid == 0 ? (uint32_t)(add_relaxed(&p.kp_cnt[tq], 1u) == (uint32_t)(sp.split - 1)) : 0u, sb);
+        if (done) {
+          if (sp.split == 2) store_parked_sum<G, 2>(slots, Yt, p.F, rows, p.F - n0, p.y_bf16);
+          else store_parked_sum<G, 4>(slots, Yt, p.F, rows, p.F - n0, p.y_bf16);
+        }
       }
     }
     if (done && p.tile_log && tid == 0) {
