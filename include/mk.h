@@ -413,6 +413,30 @@ int mk_peak_hbm(const void* src, void* dst, size_t bytes, int mode, void* worksp
                 double* bytes_moved, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Per-shape defaults  ([P1] "¿Qué hace mKernel?": how many workgroups each
+ * role gets, and the tile, are chosen per shape)
+ *
+ * mk_plan fills *out with the launch options an operation uses for a shape
+ * when the caller leaves them 0 -- the same functions the entry points call
+ * for those fields -- so a caller can read, log, adjust and pass them back
+ * as the launch.  Fields set: tile (the tile id), n_copy (0: every
+ * workgroup starts as a copier), n_reduce (0: each compute workgroup reduces
+ * the tiles it produced), copy_kib (AG: the copy item size in KiB, rounded
+ * up; the entry point then rounds items to whole rows; RS/AR: 1024),
+ * queue_mode (0); every other field is zero.
+ *   op MK_OP_AG_GEMM: M = R * m_shard, N, K as in mk_ag_gemm (R >= 1); the
+ *     tile assumes a caller workspace (mk_ag_gemm_noalloc keeps tile 9 where
+ *     this gives 11); the item size uses the current device's CU count, or
+ *     256 CUs when no device is present.
+ *   op MK_OP_GEMM_RS / MK_OP_GEMM_AR: M, N, K and R as in mk_gemm_rs.
+ *   op MK_OP_MOE: N = F, K = H (M and R unused: routing decides the rows).
+ * Returns MK_OK, or MK_ERR_INVALID (unknown op, NULL out, non-positive
+ * dimension).  No GPU work.
+ * ------------------------------------------------------------------------- */
+enum { MK_OP_AG_GEMM = 0, MK_OP_GEMM_RS = 1, MK_OP_GEMM_AR = 2, MK_OP_MOE = 3 };
+int mk_plan(int op, int64_t M, int64_t N, int64_t K, int R, mk_launch* out);
+
+/* ---------------------------------------------------------------------------
  * Support
  * ------------------------------------------------------------------------- */
 /* Zero-fill a workspace with a fill kernel (no memset node), asynchronously. */

@@ -359,3 +359,25 @@ def test_moe_gate_validation(lib):
     if not torch.cuda.is_available():
         assert g() == mk.MK_ERR_HIP                                 # valid: the device query fails
     assert lib.mk_moe_gate_workspace(4096, 7168, 256) >= 256
+
+
+def test_plan_reports_the_per_shape_defaults(lib):
+    # the five workloads' shapes (no GPU here: the AG item size assumes 256 CUs)
+    ag = mk.mk_plan(mk.MK_OP_AG_GEMM, 8192, 3584, 8192, 8)
+    assert (ag.tile, ag.copy_kib, ag.n_copy, ag.n_reduce, ag.queue_mode) == (mk.TILE_256x256_DMA_W8, 512, 0, 0, 0)
+    sk = mk.mk_plan(mk.MK_OP_AG_GEMM, 128, 28672, 8192, 8)
+    assert (sk.tile, sk.copy_kib) == (mk.TILE_128x128_PC, 16)          # one 16 KiB row per item
+    assert mk.mk_plan(mk.MK_OP_AG_GEMM, 256, 96, 128, 4).tile == mk.TILE_128x128
+    assert mk.mk_plan(mk.MK_OP_AG_GEMM, 128, 28672, 8192 + 128, 8).tile == mk.TILE_128x128_PC
+    assert mk.mk_plan(mk.MK_OP_AG_GEMM, 128, 28672, 8192 + 64, 8).tile == mk.TILE_128x128
+    rs = mk.mk_plan(mk.MK_OP_GEMM_RS, 8192, 8192, 3584, 8)
+    assert (rs.tile, rs.copy_kib) == (mk.TILE_256x256_DMA, 1024)
+    assert mk.mk_plan(mk.MK_OP_GEMM_RS, 8192 - 1024, 8192, 3584, 7).tile == mk.TILE_256x256_DMA
+    assert mk.mk_plan(mk.MK_OP_GEMM_RS, 8 * 200, 512, 384, 8).tile == mk.TILE_128x128   # 200-row owner blocks
+    assert mk.mk_plan(mk.MK_OP_GEMM_AR, 8 * 200, 512, 384, 8).tile == mk.TILE_256x256_DMA
+    assert mk.mk_plan(mk.MK_OP_MOE, 0, 2048, 7168).tile == mk.TILE_256x256_DMA
+    assert mk.mk_plan(mk.MK_OP_MOE, 0, 200, 384).tile == mk.TILE_128x128
+    assert mk.mk_plan(mk.MK_OP_MOE, 0, 2048, 136).tile == mk.TILE_256x256
+    assert [mk.mk_plan(7, 1, 1, 1, 1, check=False), mk.mk_plan(0, 0, 1, 1, 1, check=False),
+            mk.mk_plan(1, 8, 8, 8, 0, check=False)] == [mk.MK_ERR_INVALID] * 3
+    assert lib.mk_plan(0, 8, 8, 8, 1, None) == mk.MK_ERR_INVALID

@@ -287,6 +287,49 @@ static AgWs ag_ws_layout(int64_t K, bool pack) {
   return w;
 }
 
+// ------------------------------------------------------------ per-shape defaults
+// (mk_plan reports these; the entry point applies them to zero launch fields)
+namespace mkp {
+
+// The 256x256 tile switches to the direct-to-LDS engine with 8 waves by
+// default (bit-identical to the 4-wave one; at M = 8192, K = 8192,
+// N = 3584 with 512 KiB copy items the fused call measured 0.463 against
+// 0.476 ms, interleaved on one box; its copy workgroups run 512 threads).  A
+// single 128-row tile row (a skinny A, the GEMM streams B) takes a 128x128
+// tile at one workgroup per CU: every CU with a tile streams its own B
+// column stripe, with no MFMA work spent on empty rows.  The
+// producer/consumer tile (A from its packed copy) is the default there: at
+// M = 128, K = 8192, N = 28672 its GEMM kernel took 0.128 ms against
+// 0.152 ms for the direct-to-LDS tile with the 8-slice ring (which loads A
+// through the same DMA stream as B), 0.177 ms for the 128x256 tile (112
+// CUs with a tile) and 0.160 ms for the half-empty 256x128 tile.  Without
+// a workspace for the packed copy the 8-slice ring is used, and where K is
+// not a multiple of 256 the 128x256 direct-to-LDS tile.
+int ag_default_tile(int64_t M, int64_t N, int64_t K, bool pack) {
+  int tile = mk_default_tile(M, N, K);
+  if (tile == TILE_256x256 && TileGemmD<256, 256>::supports_k((int)K)) return TILE_256x256_DMA_W8;
+  if (tile == TILE_128x128 && M <= 128 && N >= 256) {
+    if (pack) return TILE_128x128_PC;
+    if (TileGemmD<128, 128, true, 8>::supports_k((int)K)) return TILE_128x128_DMA8;
+    if (TileGemmD<128, 256>::supports_k((int)K)) return TILE_128x256_DMA;
+  }
+  return tile;
+}
+
+// Copy item size: the bytes of A over the CUs (at most 1 MiB, at least one
+// row), so every workgroup starts with about one item: a single item's copy
+// is bound by load and store latency (at M = 128, K = 8192 eight 256 KiB
+// items took 40 us to land, 128 one-row items 12 us), and at M = 8192,
+// K = 8192 items of 512 KiB measured 1-2 % faster than 1 MiB.
+int64_t ag_default_item_bytes(int64_t M, int64_t K, int n_cu) {
+  const int64_t row_bytes = K * 2;
+  return std::min<int64_t>(1 << 20, std::max<int64_t>(row_bytes, M * row_bytes / std::max(n_cu, 1)));
+}
+
+bool ag_default_pack(int64_t M, int64_t K) { return ag_packs(M, K); }
+
+}  // namespace mkp
+
 extern "C" size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_t N, int32_t unit_rows) {
   (void)N; (void)unit_rows;
   return ag_ws_layout(K, ag_packs((int64_t)R * m_shard, K)).total;
@@ -462,13 +505,7 @@ static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t 
   const int64_t row_bytes = K * 2;
   int g = s.unit_rows, b = (int)m_shard;
   while (b) { const int t = g % b; g = b; b = t; }   // gcd(unit_rows, m_shard)
-  // Default: the bytes of A over the CUs (at most 1 MiB, at least one row),
-  // so every workgroup starts with about one item: a single item's copy is
-  // bound by load and store latency (at M = 128, K = 8192 eight 256 KiB
-  // items took 40 us to land, 128 one-row items 12 us), and at M = 8192,
-  // K = 8192 items of 512 KiB measured 1-2 % faster than 1 MiB.
-  int64_t item_bytes = (int64_t)(o.copy_kib > 0 ? o.copy_kib : 1024) << 10;
-  if (o.copy_kib == 0) item_bytes = std::min<int64_t>(item_bytes, std::max<int64_t>(row_bytes, M * row_bytes / std::max(d->n_cu, 1)));
+  const int64_t item_bytes = o.copy_kib > 0 ? (int64_t)o.copy_kib << 10 : mkp::ag_default_item_bytes(M, K, d->n_cu);
   int part_rows = (int)std::max<int64_t>(1, std::min<int64_t>(g, item_bytes / row_bytes));
   // whole rows that divide the unit and the shard; at most 1 GiB per part so
   // 32-bit buffer offsets cover it
@@ -482,27 +519,7 @@ static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t 
   }
   const hipStream_t st = (hipStream_t)stream;
   const size_t clear = no_alloc ? ws_need : 0;
-  int tile = o.tile ? o.tile : mk_default_tile(M, N, K);
-  // The 256x256 tile switches to the direct-to-LDS engine with 8 waves by
-  // default (bit-identical to the 4-wave one; at M = 8192, K = 8192,
-  // N = 3584 with 512 KiB copy items the fused call measured 0.463 against
-  // 0.476 ms, interleaved on one box; its copy workgroups run 512 threads).  A
-  // single 128-row tile row (a skinny A, the GEMM streams B) takes a 128x128
-  // tile at one workgroup per CU: every CU with a tile streams its own B
-  // column stripe, with no MFMA work spent on empty rows.  The
-  // producer/consumer tile (A from its packed copy) is the default there: at
-  // M = 128, K = 8192, N = 28672 its GEMM kernel took 0.128 ms against
-  // 0.152 ms for the direct-to-LDS tile with the 8-slice ring (which loads A
-  // through the same DMA stream as B), 0.177 ms for the 128x256 tile (112
-  // CUs with a tile) and 0.160 ms for the half-empty 256x128 tile.  Without
-  // a workspace for the packed copy the 8-slice ring is used, and where K is
-  // not a multiple of 256 the 128x256 direct-to-LDS tile.
-  if (!o.tile && tile == TILE_256x256 && TileGemmD<256, 256>::supports_k((int)K)) tile = TILE_256x256_DMA_W8;
-  if (!o.tile && tile == TILE_128x128 && M <= 128 && N >= 256) {
-    if (pack) tile = TILE_128x128_PC;
-    else if (TileGemmD<128, 128, true, 8>::supports_k((int)K)) tile = TILE_128x128_DMA8;
-    else if (TileGemmD<128, 256>::supports_k((int)K)) tile = TILE_128x256_DMA;
-  }
+  const int tile = o.tile ? o.tile : mkp::ag_default_tile(M, N, K, pack);
   if (mk_is_dma_tile(tile) && !TileGemmD<256, 256>::supports_k((int)K))
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
   if (tile == TILE_128x128_DMA8 && !TileGemmD<128, 128, true, 8>::supports_k((int)K))

@@ -607,11 +607,17 @@ __global__ __launch_bounds__(G::NT) void rs_kernel(const RsParams p) {
 inline int tile_bm(int t) {
   return (t == TILE_256x256 || t == TILE_256x128 || t == TILE_256x256_DMA || t == TILE_256x128_DMA) ? 256 : 128;
 }
-inline int rs_tile(int64_t, int64_t, int64_t K, int mb) {
-  return (TileGemmD<256, 256>::supports_k((int)K) && mb % 256 == 0) ? TILE_256x256_DMA : TILE_128x128;
-}
 
 }  // namespace
+
+// Per-shape default tile (mk_plan reports it): the 256x256 direct-to-LDS tile
+// when K % 128 == 0 and every owner row block (mb rows; 256 for the
+// all-reduce) holds whole 256-row tiles, else 128x128.
+namespace mkp {
+int rs_default_tile(int64_t, int64_t, int64_t K, int mb) {
+  return (TileGemmD<256, 256>::supports_k((int)K) && mb % 256 == 0) ? TILE_256x256_DMA : TILE_128x128;
+}
+}  // namespace mkp
 
 // Workspace: header, per-unit arrival counters, produced-tile FIFO, then
 // (bf16 output) the fp32 staging area of the reduce role.
@@ -745,7 +751,7 @@ static int gemm_reduce(const void* A, const void* B, int64_t M, int64_t K, int64
   // Default: the direct-to-LDS 256x256 tile when K is a multiple of 128 and
   // the output blocks hold whole tile rows (all-reduce: one block of M rows,
   // a ragged last tile row is masked), else 128x128.
-  const int tile = o.tile ? o.tile : rs_tile(M, N, K, all_reduce ? 256 : mb);
+  const int tile = o.tile ? o.tile : mkp::rs_default_tile(M, N, K, all_reduce ? 256 : mb);
   if (tile <= 0 || tile >= TILE_COUNT) return fail(MK_ERR_INVALID, "tile id %d", tile);
   // The register-staged 256x256 tile is not built for this operation: with
   // the partial sums added from its accumulators its K loop spills.

@@ -48,3 +48,13 @@ mk_launch launch_opts(const mk_launch* l);
 uint64_t spin_ticks(const mk_launch& l, const DevInfo* d);
 
 }  // namespace mkh
+
+// Per-shape defaults of each operation (defined beside its kernels; mk_plan
+// reports them, the entry points apply them).
+namespace mkp {
+int ag_default_tile(int64_t M, int64_t N, int64_t K, bool pack);
+int64_t ag_default_item_bytes(int64_t M, int64_t K, int n_cu);
+bool ag_default_pack(int64_t M, int64_t K);
+int rs_default_tile(int64_t M, int64_t N, int64_t K, int mb);
+int moe_default_tile(int64_t H, int64_t F);
+}  // namespace mkp

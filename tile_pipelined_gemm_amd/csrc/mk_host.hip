@@ -173,6 +173,40 @@ extern "C" int mk_wall_clock_khz(void) {
 
 #include "mk_tiles.h"
 
+extern "C" int mk_plan(int op, int64_t M, int64_t N, int64_t K, int R, mk_launch* out) {
+  using mkh::fail;
+  if (!out) return fail(MK_ERR_INVALID, "out is NULL");
+  const bool shaped = op == MK_OP_MOE ? (N > 0 && K > 0) : (M > 0 && N > 0 && K > 0 && R >= 1);
+  if (!shaped) return fail(MK_ERR_INVALID, "non-positive dimension");
+  mk_launch o;
+  memset(&o, 0, sizeof o);
+  switch (op) {
+    case MK_OP_AG_GEMM: {
+      int dev = 0, n_cu = 256;
+      hipDeviceProp_t prop;
+      if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+        n_cu = prop.multiProcessorCount;
+      else
+        (void)hipGetLastError();
+      o.tile = mkp::ag_default_tile(M, N, K, mkp::ag_default_pack(M, K));
+      o.copy_kib = (int32_t)((mkp::ag_default_item_bytes(M, K, n_cu) + 1023) >> 10);
+      break;
+    }
+    case MK_OP_GEMM_RS:
+    case MK_OP_GEMM_AR:
+      o.tile = mkp::rs_default_tile(M, N, K, op == MK_OP_GEMM_AR ? 256 : (int)(M / R));
+      o.copy_kib = 1024;
+      break;
+    case MK_OP_MOE:
+      o.tile = mkp::moe_default_tile(K, N);
+      break;
+    default:
+      return fail(MK_ERR_INVALID, "op %d", op);
+  }
+  *out = o;
+  return MK_OK;
+}
+
 extern "C" const char* mk_tile_name(int id) {
   static const char* names[TILE_COUNT] = {"auto",       "256x256",    "128x128",    "256x128",   "128x256",
                                                "256x256dma", "128x128dma", "256x128dma", "128x256dma",

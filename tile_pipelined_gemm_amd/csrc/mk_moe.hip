@@ -657,6 +657,17 @@ int run_moe(MoeParams& p, const mk_launch& o, const mkh::DevInfo* d, hipStream_t
 
 }  // namespace
 
+// Per-shape default tile (mk_plan reports it): 256x256, direct-to-LDS when
+// H % 128 == 0; 128x128 when F < 256.  Only the 256x256 tile switches to the
+// direct-to-LDS engine by default: at 128 rows the register-staged engine
+// measured faster.
+namespace mkp {
+int moe_default_tile(int64_t H, int64_t F) {
+  if (F < 256) return TILE_128x128;
+  return TileGemmD<256, 256>::supports_k((int)H) ? TILE_256x256_DMA : TILE_256x256;
+}
+}  // namespace mkp
+
 extern "C" size_t mk_moe_dispatch_gemm_workspace(int64_t T, int64_t H, int E, int k, int L, int64_t F) {
   (void)H; (void)F;
   if (T <= 0 || E <= 0 || k <= 0 || L <= 0) return sizeof(WsHeader);
@@ -764,11 +775,7 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   so.block_tokens = s.unit_rows;
   so.n_blocks = s.n_units;
   for (int b = 0; b < s.n_units; ++b) so.pos[b] = (uint16_t)s.pos[b];
-  int tile = o.tile ? o.tile : TILE_256x256;
-  if (F < 256 && tile == TILE_256x256) tile = TILE_128x128;
-  // Only the 256x256 tile switches to the direct-to-LDS engine by default: at
-  // 128 rows the register-staged engine measured faster (skinny shapes).
-  if (!o.tile && tile == TILE_256x256 && TileGemmD<256, 256>::supports_k((int)H)) tile = TILE_256x256_DMA;
+  const int tile = o.tile ? o.tile : mkp::moe_default_tile(H, F);
   if (mk_is_dma_tile(tile) && !TileGemmD<256, 256>::supports_k((int)H))
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs H %% 128 == 0", tile);
   if (tile == TILE_128x128_DMA8 || tile == TILE_256x256_DMA_W8 || tile == TILE_128x128_PC)

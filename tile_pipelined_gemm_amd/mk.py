@@ -33,7 +33,7 @@ EXPORTS = [
     "mk_moe_gate_workspace", "mk_moe_gate",
     "mk_ring_attn_workspace", "mk_ring_attn",
     "mk_workspace_init",
-    "mk_poll_status", "mk_status_string", "mk_last_error", "mk_tile_name", "mk_version",
+    "mk_poll_status", "mk_status_string", "mk_last_error", "mk_tile_name", "mk_version", "mk_plan",
     "mk_wall_clock_khz", "mk_peak_workspace", "mk_peak_mfma", "mk_peak_hbm",
 ]
 
@@ -140,6 +140,8 @@ def load(path: Optional[str] = None):
     lib.mk_last_error.argtypes = []
     lib.mk_tile_name.restype = C.c_char_p
     lib.mk_tile_name.argtypes = [i32]
+    lib.mk_plan.restype = i32
+    lib.mk_plan.argtypes = [i32, i64, i64, i64, i32, C.POINTER(mk_launch)]
     lib.mk_version.restype = i32
     lib.mk_version.argtypes = []
     lib.mk_wall_clock_khz.restype = i32
@@ -397,6 +399,19 @@ def mk_moe_dispatch_gemm(X, logits, W, k, expert_begin, topk_idx, counts, offset
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     del keep
     return _check(rc) if check else rc
+
+
+MK_OP_AG_GEMM, MK_OP_GEMM_RS, MK_OP_GEMM_AR, MK_OP_MOE = 0, 1, 2, 3
+
+
+def mk_plan(op: int, M: int, N: int, K: int, R: int = 1, check=True):
+    """The per-shape default launch of an operation (see include/mk.h); a
+    mk_launch that can be passed back as `launch`."""
+    out = mk_launch()
+    rc = load().mk_plan(op, M, N, K, R, C.byref(out))
+    if check:
+        _check(rc)
+    return out if rc == MK_OK else rc
 
 
 def mk_tile_name(i: int):
