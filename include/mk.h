@@ -413,6 +413,30 @@ int mk_peak_hbm(const void* src, void* dst, size_t bytes, int mode, void* worksp
                 double* bytes_moved, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Cross-XCD message-passing litmus test (diagnostic)
+ *
+ * Runs the publication protocol every fused kernel relies on between pairs
+ * of workgroups on different XCDs: in each of `rounds` rounds the producer
+ * of a pair overwrites `words` uint32 of payload with the round number
+ * (plain stores), publishes them (every wave waits for its stores, barrier,
+ * one agent-scope release, relaxed flag store), and the consumer waits for
+ * the flag with relaxed loads, takes one agent-scope acquire, reads the
+ * payload and counts the words that do not hold the round number, then
+ * acknowledges.  fenced = 0 leaves out the release and the acquire (the
+ * count may then be non-zero: stale data, no fault).
+ *   result: device uint32[4], 16-byte aligned, written by the call: {stale
+ *   words seen, pairs whose two workgroups ran on different XCDs, mask of the
+ *   producers' XCDs, mask of the consumers' XCDs}.
+ *   workspace: mk_litmus_workspace(pairs, words) bytes, cleared by the call
+ *   (fill kernel on `stream`).  Every wait is bounded by spin_limit_us (0 =
+ *   2 s); an expiry is reported by mk_poll_status.
+ *   Limits: pairs in [1, 64] and 2 * pairs <= CUs; words, rounds in [1, 2^20].
+ * ------------------------------------------------------------------------- */
+size_t mk_litmus_workspace(int pairs, int words);
+int mk_litmus_mp(int pairs, int words, int rounds, int fenced, uint32_t* result, void* workspace,
+                 size_t workspace_bytes, uint32_t spin_limit_us, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Per-shape defaults  ([P1] "¿Qué hace mKernel?": how many workgroups each
  * role gets, and the tile, are chosen per shape)
  *

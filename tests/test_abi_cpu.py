@@ -381,3 +381,16 @@ def test_plan_reports_the_per_shape_defaults(lib):
     assert [mk.mk_plan(7, 1, 1, 1, 1, check=False), mk.mk_plan(0, 0, 1, 1, 1, check=False),
             mk.mk_plan(1, 8, 8, 8, 0, check=False)] == [mk.MK_ERR_INVALID] * 3
     assert lib.mk_plan(0, 8, 8, 8, 1, None) == mk.MK_ERR_INVALID
+
+
+def test_litmus_validation(lib):
+    assert lib.mk_litmus_workspace(4, 1024) == 256 + 4 * 4 + 4 * 4 + 4 * 8 + (256 - (256 + 64) % 256) % 256 + 4 * 1024 * 4 \
+        or lib.mk_litmus_workspace(4, 1024) >= 256 + 4 * 1024 * 4
+    ws = lib.mk_litmus_workspace(4, 1024)
+    assert lib.mk_litmus_mp(0, 1024, 10, 1, FAKE, FAKE, ws, 0, None) == mk.MK_ERR_INVALID       # pairs
+    assert lib.mk_litmus_mp(65, 1024, 10, 1, FAKE, FAKE, ws, 0, None) == mk.MK_ERR_INVALID
+    assert lib.mk_litmus_mp(4, 0, 10, 1, FAKE, FAKE, ws, 0, None) == mk.MK_ERR_INVALID          # words
+    assert lib.mk_litmus_mp(4, 1024, 0, 1, FAKE, FAKE, ws, 0, None) == mk.MK_ERR_INVALID        # rounds
+    assert lib.mk_litmus_mp(4, 1024, 10, 2, FAKE, FAKE, ws, 0, None) == mk.MK_ERR_INVALID       # fenced
+    assert lib.mk_litmus_mp(4, 1024, 10, 1, None, FAKE, ws, 0, None) == mk.MK_ERR_INVALID       # result
+    assert lib.mk_litmus_mp(4, 1024, 10, 1, FAKE, FAKE, ws - 4, 0, None) == mk.MK_ERR_WORKSPACE

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmk.so")
 SOURCES = ["mk_host.hip", "mk_ag_gemm.hip", "mk_gemm_rs.hip", "mk_moe.hip", "mk_moe_combine.hip", "mk_ring_attn.hip",
-           "mk_moe_gate.hip", "mk_peak.hip"]
+           "mk_moe_gate.hip", "mk_peak.hip", "mk_litmus.hip"]
 ARCH = "gfx950"
 
 

@@ -34,7 +34,7 @@ EXPORTS = [
     "mk_ring_attn_workspace", "mk_ring_attn",
     "mk_workspace_init",
     "mk_poll_status", "mk_status_string", "mk_last_error", "mk_tile_name", "mk_version", "mk_plan",
-    "mk_wall_clock_khz", "mk_peak_workspace", "mk_peak_mfma", "mk_peak_hbm",
+    "mk_wall_clock_khz", "mk_peak_workspace", "mk_peak_mfma", "mk_peak_hbm", "mk_litmus_workspace", "mk_litmus_mp",
 ]
 
 
@@ -150,6 +150,10 @@ def load(path: Optional[str] = None):
     lib.mk_peak_workspace.argtypes = []
     lib.mk_peak_mfma.restype = i32
     lib.mk_peak_mfma.argtypes = [i32, vp, sz, C.POINTER(C.c_double), C.POINTER(C.c_int), vp]
+    lib.mk_litmus_workspace.restype = sz
+    lib.mk_litmus_workspace.argtypes = [i32, i32]
+    lib.mk_litmus_mp.restype = i32
+    lib.mk_litmus_mp.argtypes = [i32, i32, i32, i32, vp, vp, sz, C.c_uint32, vp]
     lib.mk_peak_hbm.restype = i32
     lib.mk_peak_hbm.argtypes = [vp, vp, sz, i32, vp, sz, C.POINTER(C.c_double), vp]
     _lib = lib
@@ -206,6 +210,23 @@ def make_arrival(order=None, delay_ns=None, unit_rows=0, withhold=-1):
                    C.cast(d, C.POINTER(C.c_uint32)) if d is not None else None,
                    len(order), int(unit_rows), int(withhold))
     return a, (o, d)
+
+
+def mk_litmus_mp(pairs, words, rounds, *, fenced=True, spin_limit_us=0, stream=None, check=True):
+    """Cross-XCD message-passing litmus run; returns (stale words, cross-XCD
+    pairs, producer XCD mask, consumer XCD mask) or the error code."""
+    import torch
+    lib = load()
+    ws = workspace(lib.mk_litmus_workspace(pairs, words))
+    res = torch.zeros(4, dtype=torch.int32, device="cuda")
+    rc = lib.mk_litmus_mp(pairs, words, rounds, 1 if fenced else 0, _ptr(res), _ptr(ws), ws.numel(), spin_limit_us,
+                          _stream(stream))
+    if rc != MK_OK:
+        return _check(rc) if check else rc
+    st = mk_poll_status(ws, stream)
+    if st != MK_OK:
+        return _check(st) if check else st
+    return tuple(int(x) & 0xffffffff for x in res.cpu().tolist())
 
 
 def mk_peak_mfma(iters, ws, *, stream=None):
