@@ -102,8 +102,9 @@ typedef struct mk_launch {
                              as it is) */
   int32_t grid;           /* persistent workgroups; 0 = CUs x occupancy */
   int32_t n_copy;         /* copy-role workgroups (AG, MoE, GEMM+RS/AR with an
-                             arrival schedule); 0 = default
-                             (every workgroup copies first, then computes) */
+                             arrival schedule); 0 = default (AG: three quarters
+                             of the grid copy first, a quarter starts on tiles;
+                             others: every workgroup copies first, then computes) */
   int32_t n_reduce;       /* GEMM+RS: reduce-role workgroups; 0 = default;
                              -1 = each compute workgroup reduces its own tiles */
   int32_t tile;           /* tile configuration id (name: mk_tile_name); 0 = per-shape default.
@@ -443,9 +444,10 @@ int mk_litmus_mp(int pairs, int words, int rounds, int fenced, uint32_t* result,
  * mk_plan fills *out with the launch options an operation uses for a shape
  * when the caller leaves them 0 -- the same functions the entry points call
  * for those fields -- so a caller can read, log, adjust and pass them back
- * as the launch.  Fields set: tile (the tile id), n_copy (0: every
- * workgroup starts as a copier), n_reduce (0: each compute workgroup reduces
- * the tiles it produced), copy_kib (AG: the copy item size in KiB, rounded
+ * as the launch.  Fields set: tile (the tile id), n_copy (0: the default
+ * split, which depends on the grid: AG three quarters of it copy first,
+ * other operations every workgroup), n_reduce (0: each compute workgroup
+ * reduces the tiles it produced), copy_kib (AG: the copy item size in KiB, rounded
  * up; the entry point then rounds items to whole rows; RS/AR: 1024),
  * queue_mode (0); every other field is zero.
  *   op MK_OP_AG_GEMM: M = R * m_shard, N, K as in mk_ag_gemm (R >= 1); the

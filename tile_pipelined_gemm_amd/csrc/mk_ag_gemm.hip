@@ -328,6 +328,15 @@ int64_t ag_default_item_bytes(int64_t M, int64_t K, int n_cu) {
 
 bool ag_default_pack(int64_t M, int64_t K) { return ag_packs(M, K); }
 
+// Copy workgroups: three quarters of the grid start as copiers (while copy
+// work remains, then compute) and a quarter starts on the tiles whose rows
+// land first.  At M = 8192, K = 8192, N = 3584 (512 KiB items) this measured
+// 0.460 against 0.472 ms with every workgroup copying first, and 0.467 with
+// 160 or 224 copiers of 256 (settled, interleaved, on two boxes).  Far fewer
+// copiers are slower: one workgroup's copy rate is bound by load latency, so
+// a few copiers cannot keep ahead of the tiles.
+int ag_default_n_copy(int grid) { return grid > 1 ? grid - grid / 4 : 1; }
+
 }  // namespace mkp
 
 extern "C" size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_t N, int32_t unit_rows) {
@@ -416,11 +425,7 @@ static int run_ag(AgParams& p, const mk_launch& o, const mkh::Schedule& s, const
     return MK_OK;
   }
   p.mode = MODE_FUSED;
-  // Default split: every workgroup starts as a copy workgroup while copy work
-  // remains, then computes.  (Copying with only the workgroups left over by
-  // whole compute rounds measured slower: one workgroup's copy rate is bound
-  // by load latency, so a few copiers cannot keep ahead of the tiles.)
-  int n_copy = o.n_copy > 0 ? o.n_copy : grid;
+  int n_copy = o.n_copy > 0 ? o.n_copy : mkp::ag_default_n_copy(grid);
   n_copy = std::min<int>(n_copy, (int)std::min<uint32_t>(n_work, (uint32_t)grid));
   p.n_copy = n_copy;
   hipLaunchKernelGGL(ag_kernel<G>, dim3(grid), dim3(G::NT), 0, st, p);
