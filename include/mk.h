@@ -141,10 +141,15 @@ typedef struct mk_launch {
                              (in queue order), 8 int32, see each op; times are
                              the low 32 bits of the device wall clock
                              (mk_wall_clock_khz) */
-  int32_t queue_mode;     /* AG: 0 = default: one tile queue in landing order;
+  int32_t queue_mode;     /* AG: 0 = default: one tile queue in landing order
+                             (with the 8-wave 256x256 tile, 256-wide column
+                             tiles and then, where that shortens the schedule
+                             on the grid, 192-wide ones: M = 8192, N = 3584 on
+                             256 workgroups gives 8 of each per tile row);
                              1 = 8 per-XCD queues (the tiles that share an A
                              row block run on one XCD and share its L2; a
-                             drained queue's workgroups help the others).
+                             drained queue's workgroups help the others);
+                             2 = one queue, 256-wide column tiles only.
                              MoE (fused): 0 = one queue of M-tiles, expert by
                              expert, each expert's M-tiles in readiness order (the
                              latest arrival position among the source blocks their
@@ -173,6 +178,9 @@ typedef struct mk_launch {
  *   tile_col, first unit, last unit, workgroup, t_take, t_ready, t_done}:
  *   when the tile was taken from the queue, when its units had landed, and
  *   when its stores were issued (low 32 bits of the device wall clock).
+ *   With 192-wide column tiles (queue_mode 0) tile_col counts the 256-wide
+ *   ones first.  The number of tiles depends on the tile and the plan; at
+ *   most ceil(M/128) * ceil(N/128) records are written.
  *   copy_log (optional): per copy work item (in queue order), 8 int32
  *   {unit, part, workgroup, t_start, t_end, 0, 0, 0}.
  * ------------------------------------------------------------------------- */

@@ -80,7 +80,7 @@ def test_ag_bad_launch_options(lib):
     assert _ag(lib, launch=C.byref(lau)) == mk.MK_ERR_INVALID
     lau = mk.make_launch(copy_kib=-1)
     assert _ag(lib, launch=C.byref(lau)) == mk.MK_ERR_INVALID
-    lau = mk.make_launch(queue_mode=2)
+    lau = mk.make_launch(queue_mode=3)
     assert _ag(lib, launch=C.byref(lau)) == mk.MK_ERR_INVALID
     lau = mk.make_launch(tile=42)
     rc = _ag(lib, launch=C.byref(lau))

@@ -355,6 +355,40 @@ def test_eight_wave_dma_tile_integer_inputs_bit_exact(gpu):
     assert np.array_equal(prob.output(), C)
 
 
+@pytest.mark.parametrize("N,per_row", [(3584, 16), (3000, 16)])
+def test_narrow_column_tiles_integer_exact_and_same_bits_as_wide(gpu, N, per_row):
+    # The 8-wave 256x256 tile at M = 2048 (8 tile rows) on 64 workgroups:
+    # all-256-wide tiles take two rounds (8 x 14 = 112 tiles for N = 3584), so
+    # the column plan takes 8 wide and 8 narrow (192-wide) tiles per tile row;
+    # for N = 3000 (8 x 12 tiles in two rounds) two rounds of narrow tiles,
+    # 16 per tile row, the last 120 columns wide, are shorter still.  The tile
+    # log holds one record per tile; the output is exact on integer inputs
+    # and the same bits as with 256-wide tiles only (queue_mode 2), the
+    # unfused sequence and the GEMM alone.
+    from tile_pipelined_gemm_amd.harness import AgProblem
+    w = wl.make_ag(8, 256, 256, N, seed=59, dist="int", unit_rows=128, max_delay_ns=3000, out_dtype="f32")
+    prob = AgProblem(w)
+    n_tiles = 8 * per_row
+    W8 = gpu.TILE_256x256_DMA_W8
+    log = torch.full((8 * 8 * 16 * 2,), -1, dtype=torch.int32, device="cuda")   # room for every tile of either plan
+    prob.Ag.fill_(float("nan"))
+    prob.run(launch=gpu.make_launch(tile=W8, grid=64, tile_log=log))
+    torch.cuda.synchronize()
+    assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
+    L = log.cpu().numpy().reshape(-1, 8)
+    assert np.all(L[:n_tiles, 0] >= 0) and np.all(L[n_tiles:] == -1)
+    assert sorted(map(tuple, L[:n_tiles, :2].tolist())) == [(tm, tn) for tm in range(8)
+                                                             for tn in range(per_row)]
+    _, C = og.ag_gemm(w.shards, w.B, "f32")
+    assert np.array_equal(prob.output(), C)
+    for kw in [dict(queue_mode=2), dict(mode=1), dict(mode=3), dict(n_copy=1), dict(queue_mode=1)]:
+        prob.C.fill_(float("nan"))
+        prob.run(launch=gpu.make_launch(tile=W8, grid=64, **kw))
+        torch.cuda.synchronize()
+        assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK, kw
+        assert np.array_equal(prob.output(), C), kw
+
+
 def test_eight_wave_dma_tile_full_size_ag_config(gpu):
     w = wl.CONFIGS["ag"]["make"]()
     prob = _run(gpu, w, launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA_W8))

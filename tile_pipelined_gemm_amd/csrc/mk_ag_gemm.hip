@@ -41,6 +41,17 @@ enum { MODE_FUSED = 0, MODE_COPY = 1, MODE_GEMM = 2, MODE_PACK = 3 };
 template <class G> struct PackedA { static constexpr bool value = false; };
 template <int S, int P> struct PackedA<TileGemmPC<S, P>> { static constexpr bool value = true; };
 
+// Narrow companion of the 8-wave 256x256 tile: 256 rows by 192 columns,
+// the same LDS stages and DMA pattern (B loaded 256 wide, the columns past
+// 192 not fetched), 4x2 waves of 64x96.  Tiles of the two widths can share
+// one queue (every column block comes out bit for bit the same).
+template <class G> struct NarrowTile { static constexpr bool ok = false; static constexpr int cn = G::BN; using type = G; };
+template <bool I, int S> struct NarrowTile<TileGemmD<256, 256, I, S, 8>> {
+  static constexpr bool ok = true;
+  static constexpr int cn = 192;
+  using type = TileGemmD<256, 256, I, S, 8, 4, cn>;
+};
+
 // Copy of one part (a contiguous block of n16 16-byte chunks: whole rows of
 // kc chunks, the first being row row0 of the gathered A) that also writes
 // every chunk into the packed copy of A: row r, chunk c at block r / 128,
@@ -85,6 +96,10 @@ struct AgParams {
   int copy_wt;          // copy stores written through the L2
   int c_wt;             // output tiles written through the L2
   int mode, n_copy, tiles_m, tiles_n, n_tiles, withhold;
+  // Column tiles: tn_wide of G::BN columns, then (NarrowTile) tn_narrow of
+  // 192 columns; the queue holds all wide tiles (tile rows in landing order,
+  // tn_wide per row: n_wide in all), then all narrow ones in the same order.
+  int tn_wide, tn_narrow, n_wide;
   int xcd_queues;       // tiles from per-XCD queues (else one queue in landing order)
   uint16_t order[MK_MAX_UNITS];
   uint16_t rb_order[MK_MAX_UNITS];   // tile rows in landing order
@@ -159,14 +174,16 @@ __device__ __forceinline__ void ag_copy_role(const AgParams& p, WsHeader* h, uin
 
 template <class G, class SM>
 __device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, SM sm, uint32_t* sb) {
+  using GN = typename NarrowTile<G>::type;
   const int tid = threadIdx.x;
   const uint32_t all_parts = (uint32_t)p.n_units * p.parts;
   bool all_landed = (p.mode == MODE_GEMM);
-  G g;
-  // Tile q covers tile row rb_order[q / tiles_n] (tile rows in landing
-  // order) and tile column q % tiles_n.  Per-XCD queues: queue x holds the
-  // tile rows at landing positions x, x + XQ, x + 2*XQ, ..., each with all
-  // its columns, so the tiles that share an A row block run on one XCD.
+  // Tile q < n_wide covers tile row rb_order[q / tn_wide] (tile rows in
+  // landing order) and column tile q % tn_wide (G::BN wide); a later q the
+  // narrow tiles after them, in the same row order.  Per-XCD queues (no
+  // narrow tiles): queue x holds the tile rows at landing positions x, x +
+  // XQ, x + 2*XQ, ..., each with all its columns, so the tiles that share an
+  // A row block run on one XCD.
   XcdQueues xq(&h->aux[XQ_AUX]);
   const int tm_n = p.tiles_m, tn_n = p.tiles_n;
   auto qlen = [tm_n, tn_n](int x) -> uint32_t { return x < tm_n ? (uint32_t)((tm_n - 1 - x) / XQ + 1) * tn_n : 0u; };
@@ -185,8 +202,10 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, 
   };
   uint32_t q = next_tile();
   while (q < (uint32_t)p.n_tiles) {
-    const int tm = p.rb_order[q / p.tiles_n], tn = q % p.tiles_n;
-    const int m0 = tm * G::BM, n0 = tn * G::BN;
+    const bool narrow = NarrowTile<G>::ok && q >= (uint32_t)p.n_wide;
+    const int qq = narrow ? (int)q - p.n_wide : (int)q, per_row = narrow ? p.tn_narrow : p.tn_wide;
+    const int tm = p.rb_order[qq / per_row], tn = (narrow ? p.tn_wide : 0) + qq % per_row;
+    const int m0 = tm * G::BM, n0 = narrow ? p.tn_wide * G::BN + (qq % per_row) * NarrowTile<G>::cn : tn * G::BN;
     const int u0 = m0 / p.unit_rows, u1 = (min(p.M, m0 + G::BM) - 1) / p.unit_rows;
     const uint32_t t_take = (uint32_t)now_ticks();
     uint32_t ok = 1;
@@ -208,13 +227,24 @@ __device__ __forceinline__ void ag_compute_role(const AgParams& p, WsHeader* h, 
     if (ok) {                                      // else the watchdog expired: skip the tile
       const uint32_t t_ready = (uint32_t)now_ticks();
       const uint16_t* A = PackedA<G>::value ? p.Ap + (int64_t)tm * G::BM * p.K : p.Ag + (int64_t)m0 * p.K;
-      g.bind(A, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
-      g.run(sm);
       const int64_t esz = p.c_bf16 ? 2 : 4;
-      // written through the L2: a copy workgroup's release on this XCD then
-      // has no output lines to write back
-      if (p.c_wt) store_tile<G, 16>(g, (char*)p.C + ((int64_t)m0 * p.N + n0) * esz, p.N, p.M - m0, p.N - n0, p.c_bf16);
-      else store_tile(g, (char*)p.C + ((int64_t)m0 * p.N + n0) * esz, p.N, p.M - m0, p.N - n0, p.c_bf16);
+      char* const C = (char*)p.C + ((int64_t)m0 * p.N + n0) * esz;
+      if (!narrow) {
+        G g;
+        g.bind(A, p.K, p.M - m0, p.B + n0, p.N, p.N - n0, p.B + (int64_t)p.K * p.N, p.K);
+        g.run(sm);
+        // written through the L2: a copy workgroup's release on this XCD then
+        // has no output lines to write back
+        if (p.c_wt) store_tile<G, 16>(g, C, p.N, p.M - m0, p.N - n0, p.c_bf16);
+        else store_tile(g, C, p.N, p.M - m0, p.N - n0, p.c_bf16);
+      } else if constexpr (NarrowTile<G>::ok) {
+        const int cols = min(NarrowTile<G>::cn, p.N - n0);   // the DMA fetches no column past these
+        GN g;
+        g.bind(A, p.K, p.M - m0, p.B + n0, p.N, cols, p.B + (int64_t)p.K * p.N, p.K);
+        g.run(sm);
+        if (p.c_wt) store_tile<GN, 16>(g, C, p.N, p.M - m0, cols, p.c_bf16);
+        else store_tile(g, C, p.N, p.M - m0, cols, p.c_bf16);
+      }
       if (p.tile_log && tid == 0) {
         int32_t* L = p.tile_log + 8 * (int64_t)q;
         L[0] = tm; L[1] = tn; L[2] = u0; L[3] = u1; L[4] = (int32_t)blockIdx.x;
@@ -328,6 +358,52 @@ int64_t ag_default_item_bytes(int64_t M, int64_t K, int n_cu) {
 
 bool ag_default_pack(int64_t M, int64_t K) { return ag_packs(M, K); }
 
+// Finishing time of a greedy schedule on `grid` workgroups: W tiles of cost
+// 1 first, then Nn of cost r, each taken by the first free workgroup.  After
+// the wide tiles, grid - W % grid workgroups are free at k = W / grid and the
+// others at k + 1; the narrow tiles take the earliest start times k + i r
+// and k + 1 + i r.
+static double ag_makespan(int64_t W, int64_t Nn, int grid, double r) {
+  const int64_t k = W / grid, B = W % grid, A = grid - B;
+  const double wide_end = (double)k + (B > 0 ? 1.0 : 0.0);
+  if (Nn == 0) return wide_end;
+  int64_t ia = 0, ib = 0, left = Nn;
+  double last = 0.0;
+  while (left > 0) {
+    const double ta = (double)k + (double)ia * r, tb = B > 0 ? (double)(k + 1) + (double)ib * r : 1e300;
+    if (ta <= tb) { last = ta; left -= A; ++ia; }
+    else { last = tb; left -= B; ++ib; }
+  }
+  return std::max(wide_end, last + r);
+}
+
+// Column tiles of the 8-wave 256x256 tile: tn_wide tiles 256 wide, then
+// tn_narrow 192 wide.  The whole width in 256-wide tiles leaves the last
+// round part empty when the tile count is not a multiple of the grid; at
+// M = 8192, N = 3584 on 256 workgroups 448 tiles take two rounds, while 8
+// wide and 8 narrow tiles per tile row give every workgroup one of each.  A
+// narrow tile does 3/4 of the work; AG_NARROW_COST is its measured time
+// relative to a wide one.  A mix is taken when the greedy schedule finishes
+// at least 3 % earlier; with more than 8 tiles per workgroup the last round
+// matters little and the plan is not searched.
+constexpr double AG_NARROW_COST = 0.8;
+void ag_column_plan(int tiles_m, int64_t N, int grid, int* tn_wide, int* tn_narrow) {
+  const int a0 = (int)((N + 255) / 256);
+  *tn_wide = a0;
+  *tn_narrow = 0;
+  if (grid < 1 || (int64_t)tiles_m * a0 > 8ll * grid) return;
+  double best = ag_makespan((int64_t)tiles_m * a0, 0, grid, AG_NARROW_COST);
+  for (int a = a0 - 1; a >= 0 && a >= a0 - 64; --a) {
+    const int b = (int)((N - 256ll * a + 191) / 192);
+    const double m = ag_makespan((int64_t)tiles_m * a, (int64_t)tiles_m * b, grid, AG_NARROW_COST);
+    if (m < 0.97 * best) {
+      best = m;
+      *tn_wide = a;
+      *tn_narrow = b;
+    }
+  }
+}
+
 // Copy workgroups: three quarters of the grid start as copiers (while copy
 // work remains, then compute) and a quarter starts on the tiles whose rows
 // land first.  At M = 8192, K = 8192, N = 3584 (512 KiB items) this measured
@@ -377,8 +453,6 @@ template <class G>
 static int run_ag(AgParams& p, const mk_launch& o, const mkh::Schedule& s, const mkh::DevInfo* d,
                   hipStream_t st, size_t clear_bytes) {
   p.tiles_m = (p.M + G::BM - 1) / G::BM;
-  p.tiles_n = (p.N + G::BN - 1) / G::BN;
-  p.n_tiles = p.tiles_m * p.tiles_n;
   if (p.tiles_m > MK_MAX_UNITS) return mkh::fail(MK_ERR_UNSUPPORTED, "M too large: %d tile rows", p.tiles_m);
   // Tile rows ordered by the issue position of the last unit under them.
   std::vector<int> rb(p.tiles_m), key(p.tiles_m);
@@ -399,6 +473,16 @@ static int run_ag(AgParams& p, const mk_launch& o, const mkh::Schedule& s, const
   const int full = d->n_cu * occ;
   const int grid = o.grid > 0 ? std::min(o.grid, full) : full;
   const uint32_t n_work = (uint32_t)p.n_units * p.parts;
+  // Column tiles: all G::BN wide, or (one queue, queue_mode 0) a mix with
+  // 192-wide tiles where that shortens the schedule on this grid.
+  int tn_wide = (p.N + G::BN - 1) / G::BN, tn_narrow = 0;
+  if constexpr (NarrowTile<G>::ok)
+    if (o.queue_mode == 0) mkp::ag_column_plan(p.tiles_m, p.N, grid, &tn_wide, &tn_narrow);
+  p.tn_wide = tn_wide;
+  p.tn_narrow = tn_narrow;
+  p.tiles_n = tn_wide + tn_narrow;
+  p.n_tiles = p.tiles_m * p.tiles_n;
+  p.n_wide = p.tiles_m * tn_wide;
   if (clear_bytes) {
     const int rc = mkh::zero_fill(p.hdr, clear_bytes, st);
     if (rc) return rc;
@@ -476,7 +560,7 @@ static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t 
   if (o.mode < 0 || o.mode > 3) return fail(MK_ERR_INVALID, "mode %d", o.mode);
   if (o.grid < 0 || o.n_copy < 0 || o.copy_kib < 0) return fail(MK_ERR_INVALID, "negative grid, n_copy or copy_kib");
   if (o.copy_policy < 0 || o.copy_policy > 3) return fail(MK_ERR_INVALID, "copy_policy %d", o.copy_policy);
-  if (o.queue_mode < 0 || o.queue_mode > 1) return fail(MK_ERR_INVALID, "queue_mode %d", o.queue_mode);
+  if (o.queue_mode < 0 || o.queue_mode > 2) return fail(MK_ERR_INVALID, "queue_mode %d", o.queue_mode);
   const mkh::DevInfo* d = mkh::dev_info();
   if (!d) return MK_ERR_HIP;
   if (no_alloc) {

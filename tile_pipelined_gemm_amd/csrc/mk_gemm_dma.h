@@ -92,14 +92,23 @@ __device__ __forceinline__ void wait_barrier() {
 // KiB of B (1024 / (2*BN) k-rows per instruction); block blk is moved by
 // wave blk % WAVES.
 //
+// A narrow tile computes only the first CN < BN columns of the BN loaded
+// (CN a multiple of 32 * WN; the caller binds at most CN columns, so the DMA
+// of the columns past them reads nothing and writes zeros), with WM wave
+// rows: 256x192 with 8 waves as 4x2, each wave 64x96.  Every 32x32 output
+// block is formed by the same MFMA sequence as in the full-width tile, so
+// the two give identical bits.
+//
 // INTERLEAVE pins one LDS read after each MFMA inside a chunk.  It helps
 // when registers are to spare; a kernel that keeps more state live across
 // the K loop (GEMM+RS) turns it off to keep the loop free of spills.
-template <int BM_ = 256, int BN_ = 256, bool INTERLEAVE = true, int STAGES_ = 4, int WAVES_ = 4>
+template <int BM_ = 256, int BN_ = 256, bool INTERLEAVE = true, int STAGES_ = 4, int WAVES_ = 4, int WM_ = 2,
+          int CN_ = BN_>
 struct TileGemmD {
-  static constexpr int BM = BM_, BN = BN_, WAVES = WAVES_, WM = 2, WN = WAVES_ / 2, BK = 32, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, WAVES = WAVES_, WM = WM_, WN = WAVES_ / WM_, BK = 32, STAGES = STAGES_;
+  static constexpr int CN = CN_;                                       // columns computed
   static constexpr int NT = 64 * WAVES;
-  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int TM = BM / WM, TN = CN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;   // per stage
   static constexpr int A_INS = A_BYTES / 1024 / WAVES, B_INS = B_BYTES / 1024 / WAVES;  // DMA per wave per slice
@@ -109,6 +118,7 @@ struct TileGemmD {
   static constexpr int LDS_U4 = STAGES * (SA_U4 + SB_U4);
   static constexpr int READS = 2 * (FM + 2 * FN), MFMAS = 2 * FM * FN;  // per slice and wave
   static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile shape");
+  static_assert(WAVES % WM == 0 && TM % 32 == 0 && TN % 32 == 0 && CN <= BN, "wave grid of 32x32 blocks");
   static_assert(STAGES == 4 || STAGES == 8, "ring depth");
   static_assert(WAVES == 4 || WAVES == 8, "waves per workgroup");
   static_assert(A_INS >= 1 && B_INS >= 1 && (WAVES * B_ROWS) % 4 == 0, "DMA blocks per wave; B swizzle phase");
