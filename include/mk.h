@@ -470,6 +470,18 @@ int mk_litmus_mp(int pairs, int words, int rounds, int fenced, uint32_t* result,
 enum { MK_OP_AG_GEMM = 0, MK_OP_GEMM_RS = 1, MK_OP_GEMM_AR = 2, MK_OP_MOE = 3 };
 int mk_plan(int op, int64_t M, int64_t N, int64_t K, int R, mk_launch* out);
 
+/* mk_ag_column_plan: the column tiles mk_ag_gemm uses with the 8-wave 256x256
+ * tile (tile 10) and queue_mode 0 on `grid` workgroups for M rows and N
+ * columns: *tn_wide tiles 256 wide, then *tn_narrow tiles 192 wide, per tile
+ * row (the last tile may be ragged).  A mix is chosen when a greedy schedule
+ * of the one tile queue (wide tiles first, a narrow tile costing 0.8 of a
+ * wide one) finishes at least 3 % earlier than 256-wide tiles alone; with more
+ * than 8 tiles per workgroup the plan keeps 256-wide tiles.  grid is the
+ * workgroup count of the launch (the CU count at one workgroup per CU).
+ * Returns MK_OK, or MK_ERR_INVALID (NULL outputs, non-positive M, N or grid).
+ * No GPU work. */
+int mk_ag_column_plan(int64_t M, int64_t N, int grid, int* tn_wide, int* tn_narrow);
+
 /* ---------------------------------------------------------------------------
  * Support
  * ------------------------------------------------------------------------- */

@@ -383,6 +383,63 @@ def test_plan_reports_the_per_shape_defaults(lib):
     assert lib.mk_plan(0, 8, 8, 8, 1, None) == mk.MK_ERR_INVALID
 
 
+def _greedy_finish(wide, narrow, grid, cost=0.8):
+    """Finishing time of the one tile queue on `grid` workgroups, simulated
+    tile by tile: wide tiles (cost 1) first, then narrow ones, each taken by
+    the first free workgroup."""
+    import heapq
+    free = [0.0] * grid
+    end = 0.0
+    for c in [1.0] * wide + [cost] * narrow:
+        t = heapq.heappop(free) + c
+        end = max(end, t)
+        heapq.heappush(free, t)
+    return end
+
+
+def _column_plan(M, N, grid):
+    tm, a0 = -(-M // 256), -(-N // 256)
+    if tm * a0 > 8 * grid:
+        return (a0, 0), False
+    best, plan, close = _greedy_finish(tm * a0, 0, grid), (a0, 0), False
+    for a in range(a0 - 1, max(-1, a0 - 65), -1):
+        b = -(-(N - 256 * a) // 192)
+        m = _greedy_finish(tm * a, tm * b, grid)
+        close |= abs(m - 0.97 * best) < 1e-9
+        if m < 0.97 * best:
+            best, plan = m, (a, b)
+    return plan, close
+
+
+def test_ag_column_plan(lib):
+    # the AG workload on 256 workgroups: 8 wide and 8 narrow tiles per tile row
+    assert mk.mk_ag_column_plan(8192, 3584, 256) == (8, 8)
+    assert 8 * 256 + 8 * 192 == 3584
+    # on fewer workgroups, or other widths (the GPU tests run these)
+    assert mk.mk_ag_column_plan(2048, 3584, 64) == (8, 8)
+    assert mk.mk_ag_column_plan(2048, 3000, 64) == (0, 16)
+    assert mk.mk_ag_column_plan(4096, 4352, 256) == (14, 4)         # 14 x 256 + 4 x 192 = 4352
+    # fewer tiles than workgroups: 19 narrow tiles per row spread the work over
+    # 152 workgroups instead of 112; many rounds: the plan is not searched
+    assert mk.mk_ag_column_plan(2048, 3584, 256) == (0, 19)
+    assert mk.mk_ag_column_plan(65536, 3584, 256) == (14, 0)
+    assert mk.mk_ag_column_plan(8192, 2048, 256) == (8, 0)           # 256 tiles: one full round
+    # every plan covers N with no empty tile and matches a tile-by-tile
+    # simulation of the queue (shapes whose comparison is a tie are skipped)
+    import random
+    rng = random.Random(7)
+    for _ in range(150):
+        M, N, grid = 256 * rng.randint(1, 48), 8 * rng.randint(1, 900), rng.choice([16, 64, 100, 256])
+        a, b = mk.mk_ag_column_plan(M, N, grid)
+        assert 256 * a + 192 * b >= N and (b == 0 or 256 * a + 192 * (b - 1) < N) and 256 * a < N + 256
+        want, close = _column_plan(M, N, grid)
+        if not close:
+            assert (a, b) == want, (M, N, grid)
+    for bad in [(0, 8, 1), (8, 0, 1), (8, 8, 0)]:
+        assert mk.mk_ag_column_plan(*bad, check=False) == mk.MK_ERR_INVALID
+    assert lib.mk_ag_column_plan(8, 8, 1, None, None) == mk.MK_ERR_INVALID
+
+
 def test_litmus_validation(lib):
     assert lib.mk_litmus_workspace(4, 1024) == 256 + 4 * 4 + 4 * 4 + 4 * 8 + (256 - (256 + 64) % 256) % 256 + 4 * 1024 * 4 \
         or lib.mk_litmus_workspace(4, 1024) >= 256 + 4 * 1024 * 4

@@ -415,6 +415,14 @@ int ag_default_n_copy(int grid) { return grid > 1 ? grid - grid / 4 : 1; }
 
 }  // namespace mkp
 
+extern "C" int mk_ag_column_plan(int64_t M, int64_t N, int grid, int* tn_wide, int* tn_narrow) {
+  if (!tn_wide || !tn_narrow) return mkh::fail(MK_ERR_INVALID, "tn_wide and tn_narrow must be non-NULL");
+  if (M < 1 || N < 1 || grid < 1) return mkh::fail(MK_ERR_INVALID, "non-positive M, N or grid");
+  if (M > (1 << 30) || N > MK_MAX_COLS) return mkh::fail(MK_ERR_INVALID, "dimension too large");
+  mkp::ag_column_plan((int)((M + 255) / 256), N, grid, tn_wide, tn_narrow);
+  return MK_OK;
+}
+
 extern "C" size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_t N, int32_t unit_rows) {
   (void)N; (void)unit_rows;
   return ag_ws_layout(K, ag_packs((int64_t)R * m_shard, K)).total;

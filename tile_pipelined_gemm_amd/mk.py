@@ -34,6 +34,7 @@ EXPORTS = [
     "mk_ring_attn_workspace", "mk_ring_attn",
     "mk_workspace_init",
     "mk_poll_status", "mk_status_string", "mk_last_error", "mk_tile_name", "mk_version", "mk_plan",
+    "mk_ag_column_plan",
     "mk_wall_clock_khz", "mk_peak_workspace", "mk_peak_mfma", "mk_peak_hbm", "mk_litmus_workspace", "mk_litmus_mp",
 ]
 
@@ -142,6 +143,8 @@ def load(path: Optional[str] = None):
     lib.mk_tile_name.argtypes = [i32]
     lib.mk_plan.restype = i32
     lib.mk_plan.argtypes = [i32, i64, i64, i64, i32, C.POINTER(mk_launch)]
+    lib.mk_ag_column_plan.restype = i32
+    lib.mk_ag_column_plan.argtypes = [i64, i64, i32, C.POINTER(C.c_int), C.POINTER(C.c_int)]
     lib.mk_version.restype = i32
     lib.mk_version.argtypes = []
     lib.mk_wall_clock_khz.restype = i32
@@ -433,6 +436,16 @@ def mk_plan(op: int, M: int, N: int, K: int, R: int = 1, check=True):
     if check:
         _check(rc)
     return out if rc == MK_OK else rc
+
+
+def mk_ag_column_plan(M: int, N: int, grid: int, check=True):
+    """(tn_wide, tn_narrow): the 256- and 192-wide column tiles per tile row
+    that mk_ag_gemm uses with tile 10 on `grid` workgroups (see include/mk.h)."""
+    a, b = C.c_int(), C.c_int()
+    rc = load().mk_ag_column_plan(M, N, grid, C.byref(a), C.byref(b))
+    if check:
+        _check(rc)
+    return (a.value, b.value) if rc == MK_OK else rc
 
 
 def mk_tile_name(i: int):
