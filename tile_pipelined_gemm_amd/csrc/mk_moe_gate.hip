@@ -55,9 +55,14 @@ __device__ __forceinline__ void gate_finish(const GateParams& p, const G& g, int
 
 template <class G, int KP, class SM>
 __device__ __forceinline__ void gate_body(const GateParams& p, SM sm, uint32_t* sb) {
+  // Workgroups are dispatched to the 8 XCDs in turn (i to XCD i mod 8): with
+  // the tile row fastest-varying, both column tiles and every part of a tile
+  // row run on one XCD, so its rows of X are fetched into one L2 and shared.
+  // (Only the speed depends on this; any mapping gives the same bits.)
   const int item = blockIdx.x;
-  const int t = item / KP, part = item % KP;
-  const int tm = t / p.tiles_n, tn = t % p.tiles_n;
+  const int tiles_m = p.n_tiles / p.tiles_n;
+  const int tm = item % tiles_m, tn = (item / tiles_m) % p.tiles_n, part = item / p.n_tiles;
+  const int t = tm * p.tiles_n + tn;
   const int m0 = tm * G::BM, n0 = tn * G::BN;
   const int kpart = p.H / KP, k0 = part * kpart;
   G g;
