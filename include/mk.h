@@ -119,10 +119,12 @@ typedef struct mk_launch {
                              into a 16-slice ring, A read from a packed copy in the
                              workspace that the copy workgroups write (AG only, M <= 128,
                              K % 128 == 0, not mk_ag_gemm_noalloc).
-                             Defaults: AG 10 when 256x256 tiles give every CU one
-                             (K % 128 == 0), 11 for a single 128-row tile row with N >= 256
-                             (9 without a workspace, 8 if K % 256 != 0 as well), else a
-                             register-staged tile; GEMM+RS/AR 5
+                             Defaults: AG 11 for a single 128-row tile row with N >= 256
+                             (9 without a workspace, 8 if K % 256 != 0 as well); with M and
+                             N >= 256 and K % 128 == 0 whichever of 10 (with its column plan),
+                             8 and 7 an estimate of the schedule on the CU count finishes
+                             first (10 on ties: always where 256x256 tiles give every CU at
+                             least one); else a register-staged tile; GEMM+RS/AR 5
                              when K % 128 == 0 and the owner blocks hold whole 256-row tiles,
                              else 2; MoE 5 when F >= 256 and H % 128 == 0, 2 when F < 256,
                              else 1.

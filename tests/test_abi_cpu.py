@@ -368,6 +368,12 @@ def test_plan_reports_the_per_shape_defaults(lib):
     sk = mk.mk_plan(mk.MK_OP_AG_GEMM, 128, 28672, 8192, 8)
     assert (sk.tile, sk.copy_kib) == (mk.TILE_128x128_PC, 16)          # one 16 KiB row per item
     assert mk.mk_plan(mk.MK_OP_AG_GEMM, 256, 96, 128, 4).tile == mk.TILE_128x128
+    # below one round of 256x256 tiles the half-size direct-to-LDS tile spreads the work
+    for M, N, K in [(1024, 3584, 8192), (2048, 3584, 8192), (2048, 4096, 4096), (3072, 2048, 8192)]:
+        assert mk.mk_plan(mk.MK_OP_AG_GEMM, M, N, K, 8).tile == mk.TILE_128x256_DMA, (M, N, K)
+    for M, N, K in [(4096, 3584, 8192), (4096, 8192, 4096), (4096, 4352, 512)]:
+        assert mk.mk_plan(mk.MK_OP_AG_GEMM, M, N, K, 8).tile == mk.TILE_256x256_DMA_W8, (M, N, K)
+    assert mk.mk_plan(mk.MK_OP_AG_GEMM, 1024, 3584, 8200, 8).tile == mk.TILE_128x128   # K % 128 != 0
     assert mk.mk_plan(mk.MK_OP_AG_GEMM, 128, 28672, 8192 + 128, 8).tile == mk.TILE_128x128_PC
     assert mk.mk_plan(mk.MK_OP_AG_GEMM, 128, 28672, 8192 + 64, 8).tile == mk.TILE_128x128
     rs = mk.mk_plan(mk.MK_OP_GEMM_RS, 8192, 8192, 3584, 8)

@@ -321,31 +321,6 @@ static AgWs ag_ws_layout(int64_t K, bool pack) {
 // (mk_plan reports these; the entry point applies them to zero launch fields)
 namespace mkp {
 
-// The 256x256 tile switches to the direct-to-LDS engine with 8 waves by
-// default (bit-identical to the 4-wave one; at M = 8192, K = 8192,
-// N = 3584 with 512 KiB copy items the fused call measured 0.463 against
-// 0.476 ms, interleaved on one box; its copy workgroups run 512 threads).  A
-// single 128-row tile row (a skinny A, the GEMM streams B) takes a 128x128
-// tile at one workgroup per CU: every CU with a tile streams its own B
-// column stripe, with no MFMA work spent on empty rows.  The
-// producer/consumer tile (A from its packed copy) is the default there: at
-// M = 128, K = 8192, N = 28672 its GEMM kernel took 0.128 ms against
-// 0.152 ms for the direct-to-LDS tile with the 8-slice ring (which loads A
-// through the same DMA stream as B), 0.177 ms for the 128x256 tile (112
-// CUs with a tile) and 0.160 ms for the half-empty 256x128 tile.  Without
-// a workspace for the packed copy the 8-slice ring is used, and where K is
-// not a multiple of 256 the 128x256 direct-to-LDS tile.
-int ag_default_tile(int64_t M, int64_t N, int64_t K, bool pack) {
-  int tile = mk_default_tile(M, N, K);
-  if (tile == TILE_256x256 && TileGemmD<256, 256>::supports_k((int)K)) return TILE_256x256_DMA_W8;
-  if (tile == TILE_128x128 && M <= 128 && N >= 256) {
-    if (pack) return TILE_128x128_PC;
-    if (TileGemmD<128, 128, true, 8>::supports_k((int)K)) return TILE_128x128_DMA8;
-    if (TileGemmD<128, 256>::supports_k((int)K)) return TILE_128x256_DMA;
-  }
-  return tile;
-}
-
 // Copy item size: the bytes of A over the CUs (at most 1 MiB, at least one
 // row), so every workgroup starts with about one item: a single item's copy
 // is bound by load and store latency (at M = 128, K = 8192 eight 256 KiB
@@ -413,6 +388,52 @@ void ag_column_plan(int tiles_m, int64_t N, int grid, int* tn_wide, int* tn_narr
 // a few copiers cannot keep ahead of the tiles.
 int ag_default_n_copy(int grid) { return grid > 1 ? grid - grid / 4 : 1; }
 
+// Tile choice.  A single 128-row tile row (a skinny A, the GEMM streams B)
+// takes a 128x128 tile at one workgroup per CU: every CU with a tile streams
+// its own B column stripe, with no MFMA work spent on empty rows.  The
+// producer/consumer tile (A from its packed copy) is the default there: at
+// M = 128, K = 8192, N = 28672 its GEMM kernel took 0.128 ms against
+// 0.152 ms for the direct-to-LDS tile with the 8-slice ring (which loads A
+// through the same DMA stream as B), 0.177 ms for the 128x256 tile (112
+// CUs with a tile) and 0.160 ms for the half-empty 256x128 tile.  Without
+// a workspace for the packed copy the 8-slice ring is used, and where K is
+// not a multiple of 256 the 128x256 direct-to-LDS tile.
+//
+// With M and N of at least 256 and K % 128 == 0 the direct-to-LDS tiles
+// compete on an estimate of when the last tile ends on the grid (one
+// workgroup per CU), in units of one 256x256 tile: the 8-wave 256x256 tile
+// with its column plan (a 192-wide tile 0.8, see ag_column_plan), or the
+// 4-wave 128x256 and 256x128 tiles at 0.55 each (half the work; measured
+// 0.54 of the 8-wave tile at M = 4096, N = 3584, K = 8192, where 448 of them
+// took 0.266 ms against 0.247 ms for 224 tiles of 256x256).  The 8-wave tile
+// wins ties.  At M = 8192, N = 3584 (448 tiles of 256x256) it is the 8-wave
+// tile; below one round of 256x256 tiles the half tiles spread the work over
+// more CUs: at K = 8192, N = 3584 the fused call took 0.129 ms (128x256)
+// against 0.149 ms (8-wave, 192-wide tiles) and 0.216 ms (the register-staged
+// 128x128 tile chosen before) at M = 1024, and 0.152 against 0.170 and 0.230
+// ms at M = 2048.  Otherwise the register-staged tiles by size.
+constexpr double AG_HALF_COST = 0.55;
+int ag_default_tile(int64_t M, int64_t N, int64_t K, bool pack, int n_cu) {
+  if (M <= 128 && N >= 256) {
+    if (pack) return TILE_128x128_PC;
+    if (TileGemmD<128, 128, true, 8>::supports_k((int)K)) return TILE_128x128_DMA8;
+    if (TileGemmD<128, 256>::supports_k((int)K)) return TILE_128x256_DMA;
+  }
+  if (M >= 256 && N >= 256 && TileGemmD<256, 256>::supports_k((int)K)) {
+    const int grid = std::max(n_cu, 1);
+    const int tm = (int)((M + 255) / 256);
+    int a = 0, b = 0;
+    ag_column_plan(tm, N, grid, &a, &b);
+    const double w8 = ag_makespan((int64_t)tm * a, (int64_t)tm * b, grid, AG_NARROW_COST);
+    auto rounds = [grid](int64_t tiles) { return (double)((tiles + grid - 1) / grid); };
+    const double t8 = AG_HALF_COST * rounds(((M + 127) / 128) * ((N + 255) / 256));
+    const double t7 = AG_HALF_COST * rounds(((M + 255) / 256) * ((N + 127) / 128));
+    if (w8 <= t8 && w8 <= t7) return TILE_256x256_DMA_W8;
+    return t8 <= t7 ? TILE_128x256_DMA : TILE_256x128_DMA;
+  }
+  return mk_default_tile(M, N, K);
+}
+
 }  // namespace mkp
 
 extern "C" int mk_ag_column_plan(int64_t M, int64_t N, int grid, int* tn_wide, int* tn_narrow) {
@@ -422,6 +443,7 @@ extern "C" int mk_ag_column_plan(int64_t M, int64_t N, int grid, int* tn_wide, i
   mkp::ag_column_plan((int)((M + 255) / 256), N, grid, tn_wide, tn_narrow);
   return MK_OK;
 }
+
 
 extern "C" size_t mk_ag_gemm_workspace(int R, int64_t m_shard, int64_t K, int64_t N, int32_t unit_rows) {
   (void)N; (void)unit_rows;
@@ -616,7 +638,7 @@ static int ag_gemm(const void* const* a_shards, int R, int64_t m_shard, int64_t 
   }
   const hipStream_t st = (hipStream_t)stream;
   const size_t clear = no_alloc ? ws_need : 0;
-  const int tile = o.tile ? o.tile : mkp::ag_default_tile(M, N, K, pack);
+  const int tile = o.tile ? o.tile : mkp::ag_default_tile(M, N, K, pack, d->n_cu);
   if (mk_is_dma_tile(tile) && !TileGemmD<256, 256>::supports_k((int)K))
     return fail(MK_ERR_UNSUPPORTED, "tile %d needs K %% 128 == 0", tile);
   if (tile == TILE_128x128_DMA8 && !TileGemmD<128, 128, true, 8>::supports_k((int)K))

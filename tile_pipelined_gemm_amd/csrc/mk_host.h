@@ -52,7 +52,7 @@ uint64_t spin_ticks(const mk_launch& l, const DevInfo* d);
 // Per-shape defaults of each operation (defined beside its kernels; mk_plan
 // reports them, the entry points apply them).
 namespace mkp {
-int ag_default_tile(int64_t M, int64_t N, int64_t K, bool pack);
+int ag_default_tile(int64_t M, int64_t N, int64_t K, bool pack, int n_cu);
 int64_t ag_default_item_bytes(int64_t M, int64_t K, int n_cu);
 bool ag_default_pack(int64_t M, int64_t K);
 int ag_default_n_copy(int grid);

@@ -188,7 +188,7 @@ extern "C" int mk_plan(int op, int64_t M, int64_t N, int64_t K, int R, mk_launch
         n_cu = prop.multiProcessorCount;
       else
         (void)hipGetLastError();
-      o.tile = mkp::ag_default_tile(M, N, K, mkp::ag_default_pack(M, K));
+      o.tile = mkp::ag_default_tile(M, N, K, mkp::ag_default_pack(M, K), n_cu);
       o.copy_kib = (int32_t)((mkp::ag_default_item_bytes(M, K, n_cu) + 1023) >> 10);
       break;
     }
