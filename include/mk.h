@@ -124,8 +124,9 @@ typedef struct mk_launch {
                              N >= 256 and K % 128 == 0 whichever of 10 (with its column plan),
                              8 and 7 an estimate of the schedule on the CU count finishes
                              first (10 on ties: always where 256x256 tiles give every CU at
-                             least one); else a register-staged tile; GEMM+RS/AR 5
-                             when K % 128 == 0 and the owner blocks hold whole 256-row tiles,
+                             least one); else a register-staged tile; GEMM+RS/AR with
+                             K % 128 == 0 whichever of 5 and 8 the same estimate favours
+                             among those whose height divides the owner blocks (5 on ties),
                              else 2; MoE 5 when F >= 256 and H % 128 == 0, 2 when F < 256,
                              else 1.
                              An id an operation does not build returns MK_ERR_UNSUPPORTED

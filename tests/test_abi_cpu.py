@@ -380,7 +380,12 @@ def test_plan_reports_the_per_shape_defaults(lib):
     assert (rs.tile, rs.copy_kib) == (mk.TILE_256x256_DMA, 1024)
     assert mk.mk_plan(mk.MK_OP_GEMM_RS, 8192 - 1024, 8192, 3584, 7).tile == mk.TILE_256x256_DMA
     assert mk.mk_plan(mk.MK_OP_GEMM_RS, 8 * 200, 512, 384, 8).tile == mk.TILE_128x128   # 200-row owner blocks
-    assert mk.mk_plan(mk.MK_OP_GEMM_AR, 8 * 200, 512, 384, 8).tile == mk.TILE_256x256_DMA
+    assert mk.mk_plan(mk.MK_OP_GEMM_AR, 8 * 200, 512, 384, 8).tile == mk.TILE_128x256_DMA  # 14 tiles: spread
+    # below one round of 256x256 tiles the 128x256 tile spreads the work
+    assert mk.mk_plan(mk.MK_OP_GEMM_RS, 2048, 4096, 4096, 8).tile == mk.TILE_128x256_DMA
+    assert mk.mk_plan(mk.MK_OP_GEMM_AR, 2048, 4096, 4096, 8).tile == mk.TILE_128x256_DMA
+    assert mk.mk_plan(mk.MK_OP_GEMM_RS, 4096, 4096, 3584, 8).tile == mk.TILE_256x256_DMA
+    assert mk.mk_plan(mk.MK_OP_GEMM_RS, 8 * 384, 8192, 512, 8).tile == mk.TILE_128x256_DMA   # 384-row owners
     assert mk.mk_plan(mk.MK_OP_MOE, 0, 2048, 7168).tile == mk.TILE_256x256_DMA
     assert mk.mk_plan(mk.MK_OP_MOE, 0, 200, 384).tile == mk.TILE_128x128
     assert mk.mk_plan(mk.MK_OP_MOE, 0, 2048, 136).tile == mk.TILE_256x256

@@ -84,7 +84,7 @@ def test_owner_map_in_tile_log(gpu):
     prob = RsProblem(w)
     n_tiles = (2048 // 128) * (512 // 128)
     log = torch.full((8 * n_tiles,), -1, dtype=torch.int32, device="cuda")
-    prob.run(launch=gpu.make_launch(n_reduce=16, tile_log=log))
+    prob.run(launch=gpu.make_launch(tile=gpu.TILE_128x128, n_reduce=16, tile_log=log))
     torch.cuda.synchronize()
     L = log.cpu().numpy().reshape(-1, 8)
     for t in range(n_tiles):
@@ -196,7 +196,7 @@ def test_arrival_tile_and_copy_logs(gpu):
     n_units = (w.R - 1) * (w.M // 128)
     tlog = torch.full((8 * n_tiles,), -1, dtype=torch.int32, device="cuda")
     clog = torch.full((8 * n_units * parts,), -1, dtype=torch.int32, device="cuda")
-    prob.run(launch=gpu.make_launch(tile_log=tlog, copy_log=clog, copy_kib=64))
+    prob.run(launch=gpu.make_launch(tile=gpu.TILE_256x256_DMA, tile_log=tlog, copy_log=clog, copy_kib=64))
     torch.cuda.synchronize()
     assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
     T = tlog.cpu().numpy().reshape(-1, 8).astype(np.int64)

@@ -610,12 +610,27 @@ inline int tile_bm(int t) {
 
 }  // namespace
 
-// Per-shape default tile (mk_plan reports it): the 256x256 direct-to-LDS tile
-// when K % 128 == 0 and every owner row block (mb rows; 256 for the
-// all-reduce) holds whole 256-row tiles, else 128x128.
+// Per-shape default tile (mk_plan reports it).  With K % 128 == 0 the
+// direct-to-LDS tiles whose height divides the owner row blocks (mb rows;
+// 256 for the all-reduce, where a ragged last tile row is masked) compete on
+// an estimate of when the last tile ends on the CU count, in units of one
+// 256x256 tile: rounds of 256x256 tiles at 1, or rounds of 128x256 tiles at
+// 0.6 (measured 0.57 at M = N = 8192, K = 3584); the 256x256 tile wins ties.  Below one round of 256x256 tiles the
+// 128x256 tile spreads the work over more CUs: at K = 4096 GEMM+RS over 8
+// owners took 0.149 against 0.169 ms at M = 2048, N = 4096 (0.238 against
+// 0.285 ms as GEMM+AR), and 0.203 against 0.220 ms at M = 4096, N = 2048,
+// K = 8192, R = 4; from one round up the 256x256 tile was as fast or faster
+// (0.736 against 0.842 ms at M = N = 8192, K = 3584).  Without a direct-to-LDS
+// fit, the register-staged 128x128 tile.
 namespace mkp {
-int rs_default_tile(int64_t, int64_t, int64_t K, int mb) {
-  return (TileGemmD<256, 256>::supports_k((int)K) && mb % 256 == 0) ? TILE_256x256_DMA : TILE_128x128;
+int rs_default_tile(int64_t M, int64_t N, int64_t K, int mb, int n_cu) {
+  if (!TileGemmD<256, 256>::supports_k((int)K)) return TILE_128x128;
+  const int64_t grid = std::max(n_cu, 1);
+  const int64_t t5 = ((M + 255) / 256) * ((N + 255) / 256), t8 = ((M + 127) / 128) * ((N + 255) / 256);
+  const double c5 = (double)((t5 + grid - 1) / grid), c8 = 0.6 * (double)((t8 + grid - 1) / grid);
+  if (mb % 256 == 0 && c5 <= c8) return TILE_256x256_DMA;
+  if (mb % 128 == 0) return TILE_128x256_DMA;
+  return TILE_128x128;
 }
 }  // namespace mkp
 
@@ -748,10 +763,13 @@ static int gemm_reduce(const void* A, const void* B, int64_t M, int64_t K, int64
   if (o.mode >= 2 && arrival) return fail(MK_ERR_INVALID, "modes 2 and 3 (one phase alone) take no arrival schedule");
   if (o.grid < 0 || o.n_reduce < -1 || o.n_copy < 0 || o.copy_kib < 0)
     return fail(MK_ERR_INVALID, "bad grid, n_reduce, n_copy or copy_kib");
-  // Default: the direct-to-LDS 256x256 tile when K is a multiple of 128 and
-  // the output blocks hold whole tile rows (all-reduce: one block of M rows,
-  // a ragged last tile row is masked), else 128x128.
-  const int tile = o.tile ? o.tile : mkp::rs_default_tile(M, N, K, all_reduce ? 256 : mb);
+  // Default: by shape and the CU count (mkp::rs_default_tile; 256 CUs when
+  // no device answers, which then fails below).
+  int tile = o.tile;
+  if (!tile) {
+    const mkh::DevInfo* dd = mkh::dev_info();
+    tile = mkp::rs_default_tile(M, N, K, all_reduce ? 256 : mb, dd ? dd->n_cu : 256);
+  }
   if (tile <= 0 || tile >= TILE_COUNT) return fail(MK_ERR_INVALID, "tile id %d", tile);
   // The register-staged 256x256 tile is not built for this operation: with
   // the partial sums added from its accumulators its K loop spills.

@@ -57,6 +57,6 @@ int64_t ag_default_item_bytes(int64_t M, int64_t K, int n_cu);
 bool ag_default_pack(int64_t M, int64_t K);
 int ag_default_n_copy(int grid);
 void ag_column_plan(int tiles_m, int64_t N, int grid, int* tn_wide, int* tn_narrow);
-int rs_default_tile(int64_t M, int64_t N, int64_t K, int mb);
+int rs_default_tile(int64_t M, int64_t N, int64_t K, int mb, int n_cu);
 int moe_default_tile(int64_t H, int64_t F);
 }  // namespace mkp

@@ -180,21 +180,22 @@ extern "C" int mk_plan(int op, int64_t M, int64_t N, int64_t K, int R, mk_launch
   if (!shaped) return fail(MK_ERR_INVALID, "non-positive dimension");
   mk_launch o;
   memset(&o, 0, sizeof o);
+  // the CU count of the current device, or 256 when none answers
+  int dev = 0, n_cu = 256;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+    n_cu = prop.multiProcessorCount;
+  else
+    (void)hipGetLastError();
   switch (op) {
     case MK_OP_AG_GEMM: {
-      int dev = 0, n_cu = 256;
-      hipDeviceProp_t prop;
-      if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-        n_cu = prop.multiProcessorCount;
-      else
-        (void)hipGetLastError();
       o.tile = mkp::ag_default_tile(M, N, K, mkp::ag_default_pack(M, K), n_cu);
       o.copy_kib = (int32_t)((mkp::ag_default_item_bytes(M, K, n_cu) + 1023) >> 10);
       break;
     }
     case MK_OP_GEMM_RS:
     case MK_OP_GEMM_AR:
-      o.tile = mkp::rs_default_tile(M, N, K, op == MK_OP_GEMM_AR ? 256 : (int)(M / R));
+      o.tile = mkp::rs_default_tile(M, N, K, op == MK_OP_GEMM_AR ? 256 : (int)(M / R), n_cu);
       o.copy_kib = 1024;
       break;
     case MK_OP_MOE:
