@@ -163,7 +163,15 @@ typedef struct mk_launch {
                              2 = one queue in expert order; 3 = expert order with
                              every tile held until all copy items have landed;
                              4 = as 3 in per-XCD queues; 5 = expert order in
-                             per-XCD queues */
+                             per-XCD queues.
+                             GEMM+RS/AR: 0 = one queue, tile row after tile row
+                             (in landing order with an arrival schedule);
+                             1 = 8 per-XCD queues where the tile columns split
+                             evenly over them: queue x holds columns x, x + 8,
+                             ... of band after band of tile rows (about one
+                             tile per workgroup of an XCD per band), so the
+                             tiles on one XCD share few operand blocks in its
+                             L2; else as 0.  Any other value: MK_ERR_INVALID. */
 } mk_launch;
 
 /* ---------------------------------------------------------------------------

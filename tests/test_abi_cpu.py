@@ -155,6 +155,10 @@ def test_rs_validation(lib):
     assert _rs(lib, ws_bytes=64) == mk.MK_ERR_WORKSPACE
     lau = mk.make_launch(n_reduce=-5)
     assert _rs(lib, lau=C.byref(lau)) == mk.MK_ERR_INVALID
+    for qm in (-1, 2):                                        # 0 one queue, 1 per-XCD band queues
+        lau = mk.make_launch(queue_mode=qm)
+        assert _rs(lib, lau=C.byref(lau)) == mk.MK_ERR_INVALID, qm
+        assert _ar(lib, lau=C.byref(lau)) == mk.MK_ERR_INVALID, qm
 
 
 def _ar(lib, M=510, K=64, N=64, R=4, out_dtype=mk.MK_F32, ws_bytes=1 << 24, partials=True, lau=None, outs=True):

@@ -69,7 +69,7 @@ def test_roles_tiles_and_baseline_bitwise_identical(gpu):
     outs = []
     for lau in [dict(), dict(n_reduce=-1), dict(n_reduce=16), dict(n_reduce=64, grid=96), dict(mode=1),
                 dict(tile=2), dict(tile=2, n_reduce=32), dict(tile=5, mode=1), dict(tile=6), dict(tile=7),
-                dict(tile=8)]:
+                dict(tile=8), dict(queue_mode=1, tile=2), dict(queue_mode=1, tile=2, n_reduce=16)]:
         o = _run(gpu, w, gpu.make_launch(**lau)).outputs()
         _same_on_every_rank(o)
         outs.append(o[0])

@@ -61,6 +61,31 @@ def test_roles_and_baseline_bitwise_identical(gpu):
         assert np.array_equal(outs[0], o), f"variant {i} differs"
 
 
+def test_xcd_band_queues_same_bits(gpu):
+    # queue_mode 1 only changes which workgroup takes which tile: 8 tile
+    # columns of 256 (and 16 of 128) split over the 8 per-XCD queues, and the
+    # bits equal the one-queue default's for every role split, tile, grid and
+    # the unfused baseline; integer inputs are exact against the oracle
+    w = wl.make_rs(2048, 256, 2048, 4, seed=27)
+    base = _run(gpu, w).output()
+    S, _, _ = orc.gemm_rs(w.A, w.B, w.partials, w.R)
+    assert_close(out_to_f64(base, "f32"), S, "f32", "RS one queue")
+    for lau in [dict(queue_mode=1), dict(queue_mode=1, tile=2), dict(queue_mode=1, n_reduce=16),
+                dict(queue_mode=1, mode=1), dict(queue_mode=1, grid=40), dict(queue_mode=1, grid=3),
+                dict(queue_mode=1, tile=5)]:
+        got = _run(gpu, w, gpu.make_launch(**lau)).output()
+        assert np.array_equal(got, base), f"variant {lau} differs"
+    wi = wl.make_rs(2048, 256, 2048, 4, seed=28, dist="int")
+    _, _, outs = orc.gemm_rs(wi.A, wi.B, wi.partials, wi.R, "f32")
+    assert np.array_equal(_run(gpu, wi, gpu.make_launch(queue_mode=1)).output(), np.vstack(outs))
+    # under an arrival schedule the queue rows are the tile rows in landing order
+    wa = _arrival_workload("normal", M=1024, N=2048, R=4, unit_rows=128, seed=29)
+    ref = _run_arrival(gpu, wa).output()
+    for lau in [dict(queue_mode=1), dict(queue_mode=1, n_copy=3), dict(queue_mode=1, mode=1)]:
+        got = _run_arrival(gpu, wa, launch=gpu.make_launch(**lau)).output()
+        assert np.array_equal(got, ref), f"arrival variant {lau} differs"
+
+
 @pytest.mark.parametrize("tile", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("n_reduce", [8, -1])
 def test_every_tile_config(gpu, tile, n_reduce):

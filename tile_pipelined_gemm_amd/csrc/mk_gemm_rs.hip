@@ -63,6 +63,10 @@ struct RsParams {
   int M, K, N, R, out_bf16, mb;   // mb = rows per owner
   int n_dst;                      // outputs per row block: 1 (reduce-scatter) or R (all-reduce)
   int mode, n_compute, tiles_m, tiles_n, n_tiles;
+  // per-XCD band queues (tiles_n % XQ == 0): queue x holds the columns
+  // x, x + XQ, x + 2 XQ, ... of band after band of band_rows tile rows,
+  // row-major within a band
+  int xcd_queues, band_rows;
   // arrival schedule of the partial sums: unit u = q * n_blocks + b is row
   // block b (unit_rows rows) of partial q (0-based peer), copied in `parts`
   // items of part_rows rows
@@ -439,7 +443,25 @@ __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, 
   bool first = true;
   // partial sums all landed (or resident): no more waits before reductions
   bool all_landed = p.unit_cnt == nullptr;
-  uint32_t q = wg_bcast(tid == 0 ? add_relaxed(&h->tile_next, 1u) : 0u, sb);
+  // Queue position of the next tile.  With per-XCD band queues (opt-in) the
+  // 32 or so tiles that run at once on one XCD lie in one band of band_rows
+  // tile rows and tiles_n / XQ columns, so they share few A row blocks and B
+  // column blocks in that XCD's L2, and every XCD works on the same band at
+  // the same time.  A drained queue's workgroups help the others.  (This
+  // speeds up the K loops but slows the partial-sum reads, which then come
+  // from a few columns of each row per XCD.)
+  const int cw = p.tiles_n / XQ;
+  XcdQueues xq(&h->aux[XQ_AUX]);
+  auto take_tile = [&]() -> uint32_t {
+    if (!p.xcd_queues) return add_relaxed(&h->tile_next, 1u);
+    int x;
+    uint32_t j;
+    if (!xq.take([&](int) { return (uint32_t)(p.tiles_m * cw); }, x, j)) return (uint32_t)p.n_tiles;
+    const uint32_t per_band = (uint32_t)(p.band_rows * cw), b = j / per_band, w = j % per_band;
+    const uint32_t c = (uint32_t)x + XQ * (w % (uint32_t)cw);
+    return (b * (uint32_t)p.band_rows + w / (uint32_t)cw) * (uint32_t)p.tiles_n + c;
+  };
+  uint32_t q = wg_bcast(tid == 0 ? take_tile() : 0u, sb);
   while (q < (uint32_t)p.n_tiles) {
     const int tm = queued_tile_row(p, (int)q), tn = (int)q % p.tiles_n;
     const int t = tm * p.tiles_n + tn;             // tile id (row-major)
@@ -498,7 +520,7 @@ __device__ __forceinline__ void rs_compute_role(const RsParams& p, WsHeader* h, 
         }
         st_relaxed(&p.fifo[slot], (uint32_t)t + 1u);   // after wg_release: the tile is visible
       }
-      next = add_relaxed(&h->tile_next, 1u);
+      next = take_tile();
     }
     q = wg_bcast(next, sb);
   }
@@ -566,6 +588,7 @@ __device__ __forceinline__ void rs_finish(const RsParams& p, WsHeader* h, uint32
     st_relaxed(&h->copy_next, 0u);
     st_relaxed(&h->aux[0], 0u);
     st_relaxed(&h->aux[1], 0u);
+    for (int i = 0; i < XQ; ++i) st_relaxed(&h->aux[XQ_AUX + i], 0u);
     st_relaxed(&h->abort, 0u);
     __hip_atomic_store(&h->t0, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     st_relaxed(&h->done, 0u);
@@ -680,6 +703,10 @@ static int run_rs(RsParams& p, const mk_launch& o, const mkh::Schedule* s, const
   const int full = d->n_cu * occ;
   const int grid = o.grid > 0 ? std::min(o.grid, full) : full;
   if (!can_stage) return mkh::fail(MK_ERR_WORKSPACE, "bf16 output needs the fp32 staging workspace");
+  // Per-XCD band queues where the tile columns split evenly over the XCDs; a
+  // band holds about as many tiles per XCD as the XCD has workgroups.
+  p.xcd_queues = o.queue_mode == 1 && p.tiles_n % XQ == 0;
+  p.band_rows = p.xcd_queues ? std::max(1, grid / (XQ * (p.tiles_n / XQ))) : 1;
   // Copy workgroups (arrival schedule): every workgroup copies first by
   // default, then computes; n_copy selects fewer.
   const uint32_t n_work = (uint32_t)p.n_units * p.parts;
@@ -763,6 +790,7 @@ static int gemm_reduce(const void* A, const void* B, int64_t M, int64_t K, int64
   if (o.mode >= 2 && arrival) return fail(MK_ERR_INVALID, "modes 2 and 3 (one phase alone) take no arrival schedule");
   if (o.grid < 0 || o.n_reduce < -1 || o.n_copy < 0 || o.copy_kib < 0)
     return fail(MK_ERR_INVALID, "bad grid, n_reduce, n_copy or copy_kib");
+  if (o.queue_mode < 0 || o.queue_mode > 1) return fail(MK_ERR_INVALID, "queue_mode %d", o.queue_mode);
   // Default: by shape and the CU count (mkp::rs_default_tile; 256 CUs when
   // no device answers, which then fails below).
   int tile = o.tile;
