@@ -298,7 +298,10 @@ def bench_moe(args, stream, extra=True):
     stream.synchronize()
     rows = probs[0].local_rows()
     flops = 2.0 * rows * w.H * w.F
-    abytes = (w.L * w.H * w.F * 2 + 2 * rows * w.H * 2 + rows * w.F * 2 + w.T * w.H * 2 + w.T * w.E * 4)
+    # weights, the received token rows (read from X, written to Xs, read by the
+    # tiles), Y and the logits
+    recv = probs[0].received_rows()
+    abytes = (w.L * w.H * w.F * 2 + 3 * recv * w.H * 2 + rows * w.F * 2 + w.T * w.E * 4)
 
     def fused(i):
         probs[i % copies].run(stream=stream, check=False)
@@ -308,6 +311,7 @@ def bench_moe(args, stream, extra=True):
     for p in probs:
         assert mk.mk_poll_status(p.ws, stream) == mk.MK_OK
     r = dict(workload=wl.CONFIGS["moe"]["desc"], T=w.T, H=w.H, E=w.E, k=w.k, L=w.L, F=w.F, local_rows=rows,
+             received_rows=recv,
              ms=wall, kernel_ms=kern, tflops=flops / kern / 1e9, gbs=abytes / kern / 1e6,
              flops=flops, alg_bytes=abytes)
     if extra:

@@ -99,7 +99,7 @@ typedef struct mk_launch {
                              the reduce kernel (on what is staged), 3 = the GEMM
                              kernel; MoE 2 = routing and the permute kernel,
                              3 = routing and the grouped GEMM kernel (reads Xs
-                             as it is) */
+                             and perm as they are) */
   int32_t grid;           /* persistent workgroups; 0 = CUs x occupancy */
   int32_t n_copy;         /* copy-role workgroups (AG, MoE, GEMM+RS/AR with an
                              arrival schedule); 0 = default (AG: three quarters
@@ -308,20 +308,24 @@ int mk_gemm_ar(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
  * (E+1 entries); perm[p] = t*k + j for the p-th (token, slot) pair in
  * (expert, token) ascending order.  n_local_rows[0] = offsets[expert_begin+L]
  * - offsets[expert_begin].
- * Landing: row q of Xs is X[token of perm[offsets[expert_begin] + q]]; copy
- * workgroups write it as the token's source block lands (blocks of
+ * Landing: Xs is the receive buffer [T x H] bf16: row t of Xs is X[t] for
+ * every token t with at least one local expert (received once, however many
+ * local experts it picked); the other rows are not written.  Copy workgroups
+ * write the rows as the tokens' source blocks land (blocks of
  * arrival->unit_rows tokens, issued in arrival->order).  Grouped GEMM: for
- * local expert e, Y rows of e = Xs rows of e @ W[e] (W[e] [H x F] bf16),
- * each M-tile starting once all of its rows have landed.
- *   Xs has room for T*min(k, L) rows [x H] bf16, Y for T*min(k, L) rows [x F].
+ * local expert e, Y row q (q = p - offsets[expert_begin] for the pair at
+ * position p) = Xs[perm[p] / k] @ W[e] (W[e] [H x F] bf16), each M-tile
+ * starting once all of its rows have landed.
+ *   Xs has room for T rows [x H] bf16 (T * H * 2 < 2^31 bytes), Y for
+ *   T*min(k, L) rows [x F].
  *   tile_log (optional): per output tile q = m_tile*ceil(F/BN) + tile_col
  *   (BN the tile width of the chosen tile), 8 int32 {local expert, first row
  *   (expert-relative), rows, landed count seen, workgroup, t_take, t_ready,
  *   t_done} (times as in the AG tile log).
  *   copy_log (optional): per copy work item (source block x part of 8 or
  *   fewer tokens, in queue order), 8 int32 {block, part, workgroup, t_start,
- *   t_end, local rows copied, t_indexed, t_copied}: t_indexed when the
- *   item's landing rows were known, t_copied when its stores were issued.
+ *   t_end, local pairs, t_indexed, t_copied}: t_indexed when the item's
+ *   pairs were placed, t_copied when its stores were issued.
  * ------------------------------------------------------------------------- */
 size_t mk_moe_dispatch_gemm_workspace(int64_t T, int64_t H, int E, int k, int L, int64_t F);
 int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t T, int64_t H, int E, int k,

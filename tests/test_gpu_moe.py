@@ -39,6 +39,7 @@ def test_small_matches_oracle(gpu, eb, L):
     prob = _run(gpu, w)
     ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, eb, "bf16")
     got = _check_exact(prob, ref)
+    _check_received(prob, w, ref)
     assert_close(out_to_f64(got["Y"], "bf16"), ref["Y64"], "bf16", "MoE small")
 
 
@@ -246,16 +247,25 @@ def test_withheld_block_times_out(gpu):
     assert gpu.mk_poll_status(prob.ws) == gpu.MK_OK
 
 
+def _check_received(prob, w, ref):
+    # the receive buffer holds every token with a local expert in its own row;
+    # the rows of the other tokens are never written (still the NaN poison)
+    from tile_pipelined_gemm_amd.harness import to_numpy
+    toks = np.unique(om.landing_tokens(ref["perm"], ref["offsets"], w.k, w.expert_begin, w.L))
+    xs = to_numpy(prob.Xs)
+    assert np.array_equal(xs[toks], w.X[toks])
+    rest = np.setdiff1d(np.arange(w.T), toks)
+    assert np.all(np.isnan(prob.Xs[torch.as_tensor(rest, device=prob.Xs.device)].float().cpu().numpy()))
+
+
 def test_full_size_moe_config_whole_output(gpu):
-    # routing, counts, offsets, perm bit-exact; every landing row (every
-    # expert's ragged last M-tile included) and every output row against the
-    # float64 oracle
+    # routing, counts, offsets, perm bit-exact; every received token row and
+    # every output row (every expert's ragged last M-tile included) against
+    # the float64 oracle
     w = wl.CONFIGS["moe"]["make"]()
     prob = _run(gpu, w)
     ref = om.moe_dispatch_gemm(w.X, w.logits, w.W, w.k, 0, "bf16")
     got = _check_exact(prob, ref)
     n = ref["n_local"]
-    toks = om.landing_tokens(ref["perm"], ref["offsets"], w.k, 0, w.L)
-    from tile_pipelined_gemm_amd.harness import to_numpy
-    assert np.array_equal(to_numpy(prob.Xs[:n]), w.X[toks])
+    _check_received(prob, w, ref)
     assert_close(out_to_f64(got["Y"][:n], "bf16"), ref["Y64"], "bf16", "MoE full")

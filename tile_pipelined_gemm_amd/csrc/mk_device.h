@@ -300,7 +300,9 @@ __device__ __forceinline__ const T* uni(const T* p) {
 struct Smem1 { u32x4* lds; };
 struct Smem4 { u32x4* a[4]; u32x4* b[4]; };
 
-template <int BM_, int BN_, int WM_, int WN_>
+// GA (gathered A): tile row r is A row idx[r] / div for an index array idx
+// given at bind time (bind_rows); each A load then has its own row offset.
+template <int BM_, int BN_, int WM_, int WN_, bool GA = false>
 struct TileGemm {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 64, STAGES = 2;
   static __host__ __device__ constexpr bool supports_k(int) { return true; }
@@ -322,6 +324,7 @@ struct TileGemm {
   f32x16 acc[FM][FN];
   __amdgpu_buffer_rsrc_t rsA, rsB;
   uint32_t voA, voB, ldaB, ldbB;   // per-thread byte offsets; row pitches in bytes
+  uint32_t voG[GA ? A_PT : 1];     // gathered A: per-load row offsets
   int K, ncols;
 
   __device__ __forceinline__ void zero_acc() {
@@ -353,14 +356,37 @@ struct TileGemm {
     voB = (nb * 8 < ncols) ? (uint32_t)(kb * 8) * ldbB + (uint32_t)nb * 16u : OOB;
   }
 
+  // Gathered A (GA): tile row r (r < mrows) is row idx[r] / div of A, which
+  // has a_rows rows of lda elements, starting at column k0; rows past mrows
+  // or whose index falls outside [0, a_rows) read as zero.  A * lda * 2 must
+  // stay below 2^32 bytes (32-bit buffer offsets).
+  __device__ __forceinline__ void bind_rows(const uint16_t* A, int64_t lda, int a_rows, const int32_t* idx,
+                                            int div, int mrows, int k0, const uint16_t* B, int64_t ldb,
+                                            int ncols_, const uint16_t* B_end, int K_) {
+    static_assert(GA, "gathered-A engine");
+    bind(A, lda, 0, B, ldb, ncols_, B_end, K_);
+    rsA = make_rsrc(uni(A), uni((uint32_t)a_rows * ldaB));
+    const int tid = threadIdx.x;
+    const int rows = mrows < BM ? mrows : BM;
+#pragma unroll
+    for (int i = 0; i < A_PT; ++i) {
+      const int r = (tid >> 3) + i * (NT / 8);
+      const int t = r < rows ? idx[r] / div : -1;
+      voG[i] = (uint32_t)t < (uint32_t)a_rows ? (uint32_t)t * ldaB + (uint32_t)(tid & 7) * 16u + (uint32_t)k0 * 2u
+                                              : OOB;
+    }
+  }
+
   // Global -> registers for the K-step starting at k0.
   __device__ __forceinline__ void load(int k0) {
     const int tid = threadIdx.x;
-    const uint32_t va = (k0 + (tid & 7) * 8 < K) ? voA : OOB;
+    const bool kin = k0 + (tid & 7) * 8 < K;
 #pragma unroll
     for (int i = 0; i < A_PT; ++i)
-      if (A_CH % NT == 0 || tid + i * NT < A_CH)
-        ra[i] = bload(rsA, va, (uint32_t)(i * (NT / 8)) * ldaB + (uint32_t)k0 * 2u);
+      if (A_CH % NT == 0 || tid + i * NT < A_CH) {
+        if constexpr (GA) ra[i] = bload(rsA, kin ? voG[i] : OOB, (uint32_t)k0 * 2u);
+        else ra[i] = bload(rsA, kin ? voA : OOB, (uint32_t)(i * (NT / 8)) * ldaB + (uint32_t)k0 * 2u);
+      }
 #pragma unroll
     for (int i = 0; i < B_PT; ++i)
       if (B_BL % NT == 0 || tid + i * NT < B_BL) {

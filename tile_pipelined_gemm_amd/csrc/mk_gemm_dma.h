@@ -102,8 +102,14 @@ __device__ __forceinline__ void wait_barrier() {
 // INTERLEAVE pins one LDS read after each MFMA inside a chunk.  It helps
 // when registers are to spare; a kernel that keeps more state live across
 // the K loop (GEMM+RS) turns it off to keep the loop free of spills.
+//
+// GA (gathered A): tile row r is A row idx[r] / div for an index array idx
+// given at bind time (the MoE grouped GEMM reads each expert's rows from the
+// received tokens through the dispatch permutation); each A DMA instruction
+// then has its own per-lane row offset, and only the K slice goes into the
+// scalar offset.
 template <int BM_ = 256, int BN_ = 256, bool INTERLEAVE = true, int STAGES_ = 4, int WAVES_ = 4, int WM_ = 2,
-          int CN_ = BN_>
+          int CN_ = BN_, bool GA = false>
 struct TileGemmD {
   static constexpr int BM = BM_, BN = BN_, WAVES = WAVES_, WM = WM_, WN = WAVES_ / WM_, BK = 32, STAGES = STAGES_;
   static constexpr int CN = CN_;                                       // columns computed
@@ -127,6 +133,7 @@ struct TileGemmD {
   f32x16 acc[FM][FN];
   u32x4 dA, dB;
   uint32_t ldaB, ldbB, voA, voB;
+  uint32_t voG[GA ? A_INS : 1];   // gathered A: per-instruction row offsets
   int nk;
 
   static __host__ __device__ constexpr bool supports_k(int K) { return K % (STAGES * BK) == 0; }
@@ -153,6 +160,35 @@ struct TileGemmD {
     voB = (lchunk * 8 < ncols) ? (uint32_t)rin * ldbB + (uint32_t)lchunk * 16u : OOB;
   }
 
+  // Gathered A (GA): tile row r (r < mrows) is row idx[r] / div of A, which
+  // has a_rows rows of lda elements, starting at column k0; rows past mrows
+  // or whose index falls outside [0, a_rows) read as zero.  A * lda * 2 must
+  // stay below 2^32 bytes (32-bit buffer offsets).
+  __device__ __forceinline__ void bind_rows(const uint16_t* A, int64_t lda, int a_rows, const int32_t* idx,
+                                            int div, int mrows, int k0, const uint16_t* B, int64_t ldb, int ncols,
+                                            const uint16_t* B_end, int K) {
+    static_assert(GA, "gathered-A engine");
+    bind(A, lda, 0, B, ldb, ncols, B_end, K);
+    dA = buf_desc(A, uni((uint32_t)a_rows * ldaB));
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int rows = mrows < BM ? mrows : BM;
+    const uint32_t chunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u + (uint32_t)k0 * 2u;
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+      const int r = (i * WAVES + w) * 16 + (lane >> 2);
+      const int t = r < rows ? idx[r] / div : -1;
+      voG[i] = (uint32_t)t < (uint32_t)a_rows ? (uint32_t)t * ldaB + chunk : OOB;
+    }
+  }
+  __device__ __forceinline__ uint32_t a_voff(int i) const {
+    if constexpr (GA) return voG[i];
+    else return voA;
+  }
+  __device__ __forceinline__ uint32_t a_soff(int blk, int kt) const {
+    if constexpr (GA) return (uint32_t)(kt * BK * 2);
+    else return (uint32_t)(blk * 16) * ldaB + (uint32_t)(kt * BK * 2);
+  }
+
   // DMA of K slice kt into stage buffers (sa, sb): each wave fills A_INS KiB
   // of A (16-row blocks) and B_INS KiB of B (B_ROWS-row blocks).
   __device__ __forceinline__ void issue(u32x4* sa, u32x4* sb, int kt) {
@@ -161,7 +197,7 @@ struct TileGemmD {
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
       const int blk = i * WAVES + w;
-      dma16(dA, uni(la + blk * 1024), voA, uni((uint32_t)(blk * 16) * ldaB + (uint32_t)(kt * BK * 2)));
+      dma16(dA, uni(la + blk * 1024), a_voff(i), uni(a_soff(blk, kt)));
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
@@ -234,8 +270,7 @@ struct TileGemmD {
     const int w = uni((int)(threadIdx.x >> 6));   // wave index: the same in every lane
     if (d < A_INS) {
       const int blk = d * WAVES + w;
-      dma16(dA, uni(lds_addr(sa) + blk * 1024), more ? voA : OOB,
-            uni((uint32_t)(blk * 16) * ldaB + (uint32_t)(kt * BK * 2)));
+      dma16(dA, uni(lds_addr(sa) + blk * 1024), more ? a_voff(d) : OOB, uni(a_soff(blk, kt)));
     } else {
       const int blk = (d - A_INS) * WAVES + w;
       dma16(dB, uni(lds_addr(sb) + blk * 1024), more ? voB : OOB, uni((uint32_t)(kt * BK + blk * B_ROWS) * ldbB));

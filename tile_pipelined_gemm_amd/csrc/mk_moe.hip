@@ -3,8 +3,10 @@
 // [P1] "Los cinco núcleos fusionados", row Envío MoE + GEMM: tokens are routed
 // to the ranks of their experts (all-to-all) and the per-expert grouped GEMM
 // runs in the same kernel on the tokens as they land, with no staging round
-// trip.  Here the landing buffer Xs is the one copy of each routed token row
-// and the grouped GEMM reads it tile by tile as rows arrive.
+// trip.  Here each token with at least one local expert lands once, in row
+// t of the receive buffer Xs (a rank receives a token once, however many of
+// its experts the token picked), and the grouped GEMM gathers each expert's
+// rows from Xs through the dispatch permutation, tile by tile as they arrive.
 //
 // Kernels, in stream order:
 //   route_kernel   one wave per token: top-k of the fp32 logits by k rounds of
@@ -16,11 +18,12 @@
 //                  (offsets) and the grouped-GEMM M-tile table of the local
 //                  experts.  Everything is integer and deterministic.
 //   moe_kernel     persistent.  copy role: source blocks in arrival order; for
-//                  each (token, slot) write perm and, for local experts, copy
-//                  the token row into its landing row, then count the row into
-//                  its M-tile's arrival counter (release).  compute role:
-//                  grouped-GEMM tiles, each started once its M-tile's counter
-//                  equals the tile's row count (acquire).
+//                  each (token, slot) write perm; copy each token with a local
+//                  expert into its row of Xs, then count each of its local
+//                  pairs into its M-tile's arrival counter (release).  compute
+//                  role: grouped-GEMM tiles, each started once its M-tile's
+//                  counter equals the tile's row count (acquire), its A rows
+//                  read from Xs at the tokens that perm names.
 #include <string.h>
 
 #include <algorithm>
@@ -302,12 +305,12 @@ constexpr int SC1 = 16;                      // cache-policy bits: write through
 
 // Copy role.  An item is (source block, part of at most PART_TOKENS tokens).
 // Its pairs' positions are computed first (perm for every pair; for a local
-// expert the landing row and its M-tile), grouped by token; then each token
-// row with at least one local pair is loaded ONCE and stored to every landing
-// row of that token (a token picks up to k local experts: one read, up to k
-// writes).
+// expert its M-tile), grouped by token; then each token row with at least
+// one local pair is loaded and stored once, into its own row of Xs (a token
+// that picks several local experts is received once; the grouped GEMM reads
+// the row for each of them).
 __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, uint32_t* sb, int BM) {
-  __shared__ int32_t s_dst[PART_TOKENS][MK_MAX_TOPK], s_tile[PART_TOKENS][MK_MAX_TOPK];
+  __shared__ int32_t s_tile[PART_TOKENS][MK_MAX_TOPK];
   __shared__ int32_t s_cnt[PART_TOKENS];
   const int tid = threadIdx.x, nt = blockDim.x;
   uint64_t t0 = 0;
@@ -317,7 +320,6 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
     t0 = old ? old : now;
   }
   const uint32_t n_work = (uint32_t)p.n_blocks * p.parts;
-  const int base_local = p.offsets[p.eb];
   const int cpr = p.H / 8;                        // 16-byte chunks per row
   const uint32_t row_bytes = (uint32_t)p.H * 2u;
   // One uniform exit at the top, next item taken at the bottom: every barrier
@@ -346,16 +348,15 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
         const int l = e - p.eb;
         if (l >= 0 && l < p.L) {
           const int slot = atomicAdd(&s_cnt[tl], 1);
-          s_dst[tl][slot] = pos - base_local;
           s_tile[tl][slot] = p.tile_base[l] + (pos - p.offsets[e]) / BM;
         }
       }
       __syncthreads();
       const uint32_t t_indexed = (uint32_t)now_ticks();
       // Every token's row: all loads first (one round trip for the item),
-      // then its stores to each landing row.  Descriptors are bounded to one
+      // then its store into its row of Xs.  Descriptors are bounded to one
       // row: chunks past the row end load zero and their stores are dropped,
-      // so there is no per-element guard.  A token with no local pair loads
+      // so there is no per-element guard.  A token with no local pair moves
       // nothing (its count is uniform: read from LDS by every lane).  Stores
       // write through the L2 (sc1): the release below then has little to write
       // back.
@@ -375,9 +376,8 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
         }
 #pragma unroll
         for (int tl = 0; tl < PART_TOKENS; ++tl) {
-          const int cnt = tl < ntok ? uni(s_cnt[tl]) : 0;
-          for (int d = 0; d < cnt; ++d) {
-            const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Xs + (int64_t)uni(s_dst[tl][d]) * p.H), row_bytes);
+          if (tl < ntok && uni(s_cnt[tl]) > 0) {
+            const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Xs + (int64_t)(t0k + tl) * p.H), row_bytes);
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) bstore<SC1>(dst, (uint32_t)(c0 + cc * nt + tid) * 16u, 0, v[tl][cc]);
           }
@@ -433,8 +433,8 @@ __device__ __forceinline__ MoeSplit moe_split_plan(uint32_t n_tiles, int full, i
 // the same MFMA sequence per output element, so the bits do not change; it
 // uses the same stage buffers (smaller stages).
 template <class G> struct HalfTile { using type = void; };
-template <bool I, int S> struct HalfTile<TileGemmD<256, 256, I, S, 4>> {
-  using type = TileGemmD<128, 256, I, S, 4>;
+template <bool I, int S> struct HalfTile<TileGemmD<256, 256, I, S, 4, 2, 256, true>> {
+  using type = TileGemmD<128, 256, I, S, 4, 2, 256, true>;
 };
 
 template <class G, class SM>
@@ -519,25 +519,27 @@ __device__ __forceinline__ void moe_compute_role(const MoeParams& p, WsHeader* h
       if (!(v & 1u)) continue;
     }
     const uint32_t t_ready = (uint32_t)now_ticks();
-    const int q0 = p.offsets[e] - base_local + r0;              // landing row of the tile
+    const int q0 = p.offsets[e] - base_local + r0;              // first Y row (local pair) of the tile
     const int n0 = tn * G::BN;
     const int kpart = p.H / sp.split, k0 = kp < 0 ? 0 : kp * kpart;
     const int64_t esz = p.y_bf16 ? 2 : 4;
     char* const Yt = (char*)p.Y + ((int64_t)q0 * p.F + n0) * esz;
+    // A rows: the received token of each of the tile's pairs (pair id / k)
+    const int32_t* const ix = p.perm + p.offsets[e] + r0;
     uint32_t done = 1;
     bool half = false;
     if constexpr (!std::is_void<G2>::value) {
       if (kp < 0 && rows <= G2::BM) {             // a whole tail tile of at most 128 rows
         G2 g2;
-        g2.bind(p.Xs + (int64_t)q0 * p.H, p.H, rows, p.W[l] + n0, p.F, p.F - n0, p.W[l] + (int64_t)p.H * p.F, p.H);
+        g2.bind_rows(p.Xs, p.H, p.T, ix, p.k, rows, 0, p.W[l] + n0, p.F, p.F - n0, p.W[l] + (int64_t)p.H * p.F, p.H);
         g2.run(sm);
         store_tile<G2, 16>(g2, Yt, p.F, rows, p.F - n0, p.y_bf16);
         half = true;
       }
     }
     if (!half) {
-      g.bind(p.Xs + (int64_t)q0 * p.H + k0, p.H, rows, p.W[l] + (int64_t)k0 * p.F + n0, p.F, p.F - n0,
-             p.W[l] + (int64_t)p.H * p.F, kp < 0 ? p.H : kpart);
+      g.bind_rows(p.Xs, p.H, p.T, ix, p.k, rows, k0, p.W[l] + (int64_t)k0 * p.F + n0, p.F, p.F - n0,
+                  p.W[l] + (int64_t)p.H * p.F, kp < 0 ? p.H : kpart);
       g.run(sm);
       if (kp < 0) {
         store_tile<G, 16>(g, Yt, p.F, rows, p.F - n0, p.y_bf16);   // through the L2: little for a release to write back
@@ -692,7 +694,8 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   if (expert_begin < 0 || expert_begin + L > E) return fail(MK_ERR_INVALID, "local experts outside [0,E)");
   if (y_dtype != MK_BF16 && y_dtype != MK_F32) return fail(MK_ERR_INVALID, "y_dtype %d", y_dtype);
   const int64_t cap = T * std::min(k, L);
-  if (T * k > (1 << 30) || cap * H * 2 >= (1ll << 40) || H * F * 2 >= (1ll << 31) || (int64_t)128 * H * 2 >= (1ll << 31) ||
+  // (Xs is read through 32-bit buffer offsets: T * H * 2 bytes at most 2^31)
+  if (T * k > (1 << 30) || T * H * 2 >= (1ll << 31) || cap * F * 4 >= (1ll << 40) || H * F * 2 >= (1ll << 31) ||
       F > MK_MAX_COLS)
     return fail(MK_ERR_UNSUPPORTED, "dimension too large");
   for (int l = 0; l < L; ++l)
@@ -781,14 +784,14 @@ extern "C" int mk_moe_dispatch_gemm(const void* X, const float* logits, int64_t 
   if (tile == TILE_128x128_DMA8 || tile == TILE_256x256_DMA_W8 || tile == TILE_128x128_PC)
     return fail(MK_ERR_UNSUPPORTED, "tile %d is built for AllGather+GEMM only", tile);
   switch (tile) {
-    case TILE_256x256: return run_moe<TileGemm<256, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
-    case TILE_128x128: return run_moe<TileGemm<128, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
-    case TILE_256x128: return run_moe<TileGemm<256, 128, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
-    case TILE_128x256: return run_moe<TileGemm<128, 256, 2, 2>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
-    case TILE_256x256_DMA: return run_moe<TileGemmD<256, 256>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
-    case TILE_128x128_DMA: return run_moe<TileGemmD<128, 128>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
-    case TILE_256x128_DMA: return run_moe<TileGemmD<256, 128>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
-    case TILE_128x256_DMA: return run_moe<TileGemmD<128, 256>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_256x256: return run_moe<TileGemm<256, 256, 2, 2, true>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_128x128: return run_moe<TileGemm<128, 128, 2, 2, true>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_256x128: return run_moe<TileGemm<256, 128, 2, 2, true>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_128x256: return run_moe<TileGemm<128, 256, 2, 2, true>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_256x256_DMA: return run_moe<TileGemmD<256, 256, true, 4, 4, 2, 256, true>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_128x128_DMA: return run_moe<TileGemmD<128, 128, true, 4, 4, 2, 128, true>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_256x128_DMA: return run_moe<TileGemmD<256, 128, true, 4, 4, 2, 128, true>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
+    case TILE_128x256_DMA: return run_moe<TileGemmD<128, 256, true, 4, 4, 2, 256, true>>(p, o, d, st, counts, offsets, n_local_rows, block_cnt, nrb, so);
     default: return fail(MK_ERR_INVALID, "tile id %d", tile);
   }
 }

@@ -131,7 +131,7 @@ class MoeProblem:
         self.offsets = torch.empty(w.E + 1, **i32)
         self.perm = torch.empty(w.T * w.k, **i32)
         self.n_local = torch.empty(1, **i32)
-        self.Xs = torch.empty(cap, w.H, dtype=torch.bfloat16, device=device)
+        self.Xs = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=device)   # receive buffer: row t = token t
         self.Y = torch.empty(cap, w.F, dtype=_out_dtype(w.out_dtype), device=device)
         self.ws = mk.workspace(mk.mk_moe_dispatch_gemm_workspace(w.T, w.H, w.E, w.k, w.L, w.F), device)
 
@@ -145,6 +145,12 @@ class MoeProblem:
 
     def local_rows(self) -> int:
         return int(self.n_local.item())
+
+    def received_rows(self) -> int:
+        """Tokens with at least one local expert (the rows of Xs written)."""
+        lo = int(self.offsets[self.w.expert_begin].item())
+        hi = int(self.offsets[self.w.expert_begin + self.w.L].item())
+        return int(torch.unique(self.perm[lo:hi] // self.w.k).numel())
 
     def flops(self) -> float:
         return 2.0 * self.local_rows() * self.w.H * self.w.F
