@@ -322,7 +322,7 @@ int mk_gemm_ar(const void* A, const void* B, int64_t M, int64_t K, int64_t N,
  *   (BN the tile width of the chosen tile), 8 int32 {local expert, first row
  *   (expert-relative), rows, landed count seen, workgroup, t_take, t_ready,
  *   t_done} (times as in the AG tile log).
- *   copy_log (optional): per copy work item (source block x part of 8 or
+ *   copy_log (optional): per copy work item (source block x part of 4 or
  *   fewer tokens, in queue order), 8 int32 {block, part, workgroup, t_start,
  *   t_end, local pairs, t_indexed, t_copied}: t_indexed when the item's
  *   pairs were placed, t_copied when its stores were issued.

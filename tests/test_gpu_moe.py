@@ -162,7 +162,7 @@ def test_tile_and_copy_logs(gpu, tile, bm, bn):
     assert np.array_equal(T[:, 3], T[:, 2])
     C = clog.cpu().numpy().reshape(-1, 8)
     C = C[C[:, 0] >= 0]
-    parts = 64 // 8
+    parts = 64 // 4                                # copy items of 4 tokens
     assert sorted((int(b), int(q)) for b, q in C[:, :2]) == [(b, q) for b in range(w.T // 64) for q in range(parts)]
     assert int(C[:, 5].sum()) == prob.local_rows()
     # consume on arrival: a tile became ready only after every copy item that
@@ -176,7 +176,7 @@ def test_tile_and_copy_logs(gpu, tile, bm, bn):
     for l, r0, n, _, _, _, t_ready, _ in T:
         pos0 = int(offsets[6 + l]) + int(r0)
         toks = perm[pos0:pos0 + int(n)] // w.k
-        items = {(int(t) // 64, (int(t) % 64) // 8) for t in toks}
+        items = {(int(t) // 64, (int(t) % 64) // 4) for t in toks}
         assert rel(t_ready) >= max(rel(end_of[i]) for i in items)
 
 

@@ -300,7 +300,12 @@ struct MoeParams {
   uint32_t delay_ticks[MK_MAX_UNITS];
 };
 
-constexpr int PART_TOKENS = 8;               // tokens per copy item (at most)
+// Tokens per copy item (at most): an item's fixed costs (index loads, a
+// release, its counts) against how evenly the items spread over the copy
+// workgroups; at the MoE shape 4 measured best (fused 0.767 ms, against 0.776
+// with 8, 0.787 with 2 and 0.848 with 1; 16, one item per workgroup, 0.837).
+constexpr int PART_TOKENS = 4;
+constexpr int COPY_BATCH = PART_TOKENS < 8 ? PART_TOKENS : 8;   // token rows loaded before their stores
 constexpr int SC1 = 16;                      // cache-policy bits: write through the L2
 
 // Copy role.  An item is (source block, part of at most PART_TOKENS tokens).
@@ -353,8 +358,8 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
       }
       __syncthreads();
       const uint32_t t_indexed = (uint32_t)now_ticks();
-      // Every token's row: all loads first (one round trip for the item),
-      // then its store into its row of Xs.  Descriptors are bounded to one
+      // Every token's row, COPY_BATCH rows at a time: all loads first (one
+      // round trip per batch), then the stores into their rows of Xs.  Descriptors are bounded to one
       // row: chunks past the row end load zero and their stores are dropped,
       // so there is no per-element guard.  A token with no local pair moves
       // nothing (its count is uniform: read from LDS by every lane).  Stores
@@ -363,23 +368,26 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
       int n = 0;                                   // local rows of the item
 #pragma unroll
       for (int tl = 0; tl < PART_TOKENS; ++tl) n += tl < ntok ? uni(s_cnt[tl]) : 0;
+      for (int b0 = 0; b0 < PART_TOKENS; b0 += COPY_BATCH)
       for (int c0 = 0; c0 < cpr; c0 += 4 * nt) {
-        u32x4 v[PART_TOKENS][4];
+        u32x4 v[COPY_BATCH][4];
 #pragma unroll
-        for (int tl = 0; tl < PART_TOKENS; ++tl) {
+        for (int i = 0; i < COPY_BATCH; ++i) {
+          const int tl = b0 + i;
           const int cnt = uni(s_cnt[tl]);
           if (tl < ntok && cnt > 0) {
             const __amdgpu_buffer_rsrc_t src = make_rsrc(uni(p.X + (int64_t)(t0k + tl) * p.H), row_bytes);
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) v[tl][cc] = bload(src, (uint32_t)(c0 + cc * nt + tid) * 16u, 0);
+            for (int cc = 0; cc < 4; ++cc) v[i][cc] = bload(src, (uint32_t)(c0 + cc * nt + tid) * 16u, 0);
           }
         }
 #pragma unroll
-        for (int tl = 0; tl < PART_TOKENS; ++tl) {
+        for (int i = 0; i < COPY_BATCH; ++i) {
+          const int tl = b0 + i;
           if (tl < ntok && uni(s_cnt[tl]) > 0) {
             const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Xs + (int64_t)(t0k + tl) * p.H), row_bytes);
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) bstore<SC1>(dst, (uint32_t)(c0 + cc * nt + tid) * 16u, 0, v[tl][cc]);
+            for (int cc = 0; cc < 4; ++cc) bstore<SC1>(dst, (uint32_t)(c0 + cc * nt + tid) * 16u, 0, v[i][cc]);
           }
         }
       }
@@ -601,6 +609,7 @@ __device__ __forceinline__ void moe_body(const MoeParams& p, SM sm, uint32_t* sb
 
 template <class G>
 __global__ __launch_bounds__(G::NT) void moe_kernel(const MoeParams p) {
+  static_assert(G::NT >= PART_TOKENS * MK_MAX_TOPK, "one thread per pair of a copy item");
   __shared__ uint32_t sb[2];
   if constexpr (G::STAGES == 4) {
     __shared__ u32x4 a0[G::SA_U4], a1[G::SA_U4], a2[G::SA_U4], a3[G::SA_U4];
