@@ -414,6 +414,9 @@ def mk_moe_dispatch_gemm(X, logits, W, k, expert_begin, topk_idx, counts, offset
     E = logits.shape[1]
     L = len(W)
     F = W[0].shape[1]
+    # the receive buffer holds row t for token t; Y one row per local pair
+    if Xs.numel() < T * H or Y.numel() < T * min(k, L) * F:
+        raise ValueError(f"Xs needs {T} x {H} elements and Y {T * min(k, L)} x {F}")
     arr, keep = make_arrival(order, delay_ns, block_tokens, withhold)
     lau = launch if launch is not None else make_launch()
     rc = lib.mk_moe_dispatch_gemm(_ptr(X), _ptr(logits), T, H, E, k, _ptr_array(W), expert_begin, L, F,
