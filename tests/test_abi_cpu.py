@@ -260,6 +260,8 @@ def test_moe_validation(lib):
     assert _moe(lib, L=0) == mk.MK_ERR_UNSUPPORTED
     assert _moe(lib, y=3) == mk.MK_ERR_INVALID
     assert _moe(lib, ws_bytes=100) == mk.MK_ERR_WORKSPACE
+    # the receive buffer (T x H bf16) is read through 32-bit offsets
+    assert _moe(lib, T=1 << 16, H=1 << 14) == mk.MK_ERR_UNSUPPORTED
     arr, keep = mk.make_arrival([0, 1, 1, 3], None, 64)
     assert _moe(lib, arrival=C.byref(arr)) == mk.MK_ERR_SCHEDULE
     # launch options are checked before any HIP call
