@@ -359,35 +359,36 @@ __device__ __forceinline__ void moe_copy_role(const MoeParams& p, WsHeader* h, u
       __syncthreads();
       const uint32_t t_indexed = (uint32_t)now_ticks();
       // Every token's row, COPY_BATCH rows at a time: all loads first (one
-      // round trip per batch), then the stores into their rows of Xs.  Descriptors are bounded to one
-      // row: chunks past the row end load zero and their stores are dropped,
-      // so there is no per-element guard.  A token with no local pair moves
-      // nothing (its count is uniform: read from LDS by every lane).  Stores
-      // write through the L2 (sc1): the release below then has little to write
-      // back.
-      int n = 0;                                   // local rows of the item
+      // round trip per batch), then the stores into their rows of Xs.
+      // Descriptors are bounded to one row: chunks past the row end load zero
+      // and their stores are dropped, so there is no per-element guard.  A
+      // token with no local pair moves nothing (its count is uniform: read
+      // from LDS by every lane).  Stores write through the L2 (sc1): the
+      // release below then has little to write back.
+      int n = 0;                                   // local pairs of the item
 #pragma unroll
       for (int tl = 0; tl < PART_TOKENS; ++tl) n += tl < ntok ? uni(s_cnt[tl]) : 0;
-      for (int b0 = 0; b0 < PART_TOKENS; b0 += COPY_BATCH)
-      for (int c0 = 0; c0 < cpr; c0 += 4 * nt) {
-        u32x4 v[COPY_BATCH][4];
+      for (int b0 = 0; b0 < PART_TOKENS; b0 += COPY_BATCH) {
+        for (int c0 = 0; c0 < cpr; c0 += 4 * nt) {
+          u32x4 v[COPY_BATCH][4];
 #pragma unroll
-        for (int i = 0; i < COPY_BATCH; ++i) {
-          const int tl = b0 + i;
-          const int cnt = uni(s_cnt[tl]);
-          if (tl < ntok && cnt > 0) {
-            const __amdgpu_buffer_rsrc_t src = make_rsrc(uni(p.X + (int64_t)(t0k + tl) * p.H), row_bytes);
+          for (int i = 0; i < COPY_BATCH; ++i) {
+            const int tl = b0 + i;
+            const int cnt = uni(s_cnt[tl]);
+            if (tl < ntok && cnt > 0) {
+              const __amdgpu_buffer_rsrc_t src = make_rsrc(uni(p.X + (int64_t)(t0k + tl) * p.H), row_bytes);
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) v[i][cc] = bload(src, (uint32_t)(c0 + cc * nt + tid) * 16u, 0);
+              for (int cc = 0; cc < 4; ++cc) v[i][cc] = bload(src, (uint32_t)(c0 + cc * nt + tid) * 16u, 0);
+            }
           }
-        }
 #pragma unroll
-        for (int i = 0; i < COPY_BATCH; ++i) {
-          const int tl = b0 + i;
-          if (tl < ntok && uni(s_cnt[tl]) > 0) {
-            const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Xs + (int64_t)(t0k + tl) * p.H), row_bytes);
+          for (int i = 0; i < COPY_BATCH; ++i) {
+            const int tl = b0 + i;
+            if (tl < ntok && uni(s_cnt[tl]) > 0) {
+              const __amdgpu_buffer_rsrc_t dst = make_rsrc(uni(p.Xs + (int64_t)(t0k + tl) * p.H), row_bytes);
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) bstore<SC1>(dst, (uint32_t)(c0 + cc * nt + tid) * 16u, 0, v[i][cc]);
+              for (int cc = 0; cc < 4; ++cc) bstore<SC1>(dst, (uint32_t)(c0 + cc * nt + tid) * 16u, 0, v[i][cc]);
+            }
           }
         }
       }
