@@ -162,8 +162,8 @@ struct TileGemmD {
 
   // Gathered A (GA): tile row r (r < mrows) is row idx[r] / div of A, which
   // has a_rows rows of lda elements, starting at column k0; rows past mrows
-  // or whose index falls outside [0, a_rows) read as zero.  A * lda * 2 must
-  // stay below 2^32 bytes (32-bit buffer offsets).
+  // or whose index falls outside [0, a_rows) read as zero.  a_rows * lda * 2
+  // must stay below 2^31 bytes, the out-of-range offset OOB.
   __device__ __forceinline__ void bind_rows(const uint16_t* A, int64_t lda, int a_rows, const int32_t* idx,
                                             int div, int mrows, int k0, const uint16_t* B, int64_t ldb, int ncols,
                                             const uint16_t* B_end, int K) {
